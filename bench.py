@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark of the selective-scan hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C1]
+
+One step is one selective_scan_fwd call (Mamba-1 form: gather of the initial
+state by ids, causal depthwise conv + SiLU fused into the scan, the scan with
+its output contraction, and the packed y | final-state write) on one batch
+of seeded synthetic input of the named workload; --config C4 times the
+reverse-time backward instead, C3 the Mamba-2 form.  Inputs are resident in
+HBM before timing starts.  To keep the working set out of the 256 MB
+last-level cache, steps rotate over enough copies of the inputs and outputs
+that together exceed it.
+
+Before any number is printed the first call's output is checked against the
+float64 oracle (all elements for C0/C1, every token of sampled channels for
+the larger workloads).  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+VALU_PEAK_T = 78.6               # 157.3 TFLOP/s fp32 vector = 78.6 T lane-FMA/s
+TRANS_COST = 4                   # v_exp_f32 / v_rcp_f32 issue at 1/4 of the VALU rate
+MALL_BYTES = 256 << 20
+METRIC = "selective-scan effective HBM GB/s (% of peak) + channel-tokens/s, 1 GPU"
+
+WORKLOADS = {
+    "C0": "Mamba-1 fused conv+SiLU+scan forward, 1x64x32, d_state 16, d_conv 4, fp32",
+    "C1": "Mamba-1 fused conv+SiLU+scan forward, 8x2048x512, d_state 16, d_conv 4, fp32",
+    "C2": "Mamba-1 fused conv+SiLU+scan forward, 8x4096x5120, d_state 16, d_conv 4, "
+          "bf16 x/dt/B/C/y, fp32 state/A/D",
+    "C3": "Mamba-2 scan forward, 4x4096, 80 heads x 64, d_state 128, 1 group, bf16, "
+          "fp32 state, permuted state ids",
+    "C4": "Mamba-1 scan reverse-time backward of the 8x4096x5120 bf16 scan, fp32 grads",
+}
+
+
+def algorithmic_bytes(p, backward=False) -> int:
+    """Each input read once, each output written once (no re-reads, no workspace)."""
+    io = 2 if p.io == "bf16" else 4
+    S, L, H, P, N, G, R = p.n_seqs, p.n_tokens, p.n_head, p.head_dim, p.d_state, p.n_group, p.n_state_rows
+    x = S * L * H * P * io
+    dt = S * L * H * io
+    bc = 2 * S * L * G * N * io
+    a = (H * N if p.a_per_state else H) * 4
+    d = H * 4 if p.has_D else 0
+    w = H * p.d_conv * 4 if p.d_conv else 0
+    state = S * H * P * N * 4
+    ids = S * 4
+    if not backward:
+        y = S * L * H * P * io
+        return x + dt + bc + a + d + w + state + ids + y + state
+    dy = S * L * H * P * io
+    grads = (R * H * P * N + S * L * H * P + S * L * H + (H * N if p.a_per_state else H) +
+             2 * S * L * G * N + (H if p.has_D else 0)) * 4
+    return x + dt + bc + a + d + state + ids + dy + state + grads
+
+
+def valu_slots_per_channel_token(p) -> float:
+    """Issue slots the method needs per (sequence, channel, token), counting a
+    transcendental (exp, reciprocal) as TRANS_COST slots.
+    Per state, Mamba-1 (A per state): decay exp(dt*A) (mul + exp), input term
+    (mul), state update (fma), output term (fma).  Mamba-2 (A per head):
+    input term, state update, output term; the decay is one mul + exp per
+    (token, head), shared by the head's channels.
+    Per channel-token: dt*u (mul), D*u (fma); with the conv, its taps (fma
+    each) and SiLU (mul, exp, add, rcp, mul)."""
+    N = p.d_state
+    if p.a_per_state:
+        total = N * (4 + TRANS_COST)
+    else:
+        total = N * 3 + (1 + TRANS_COST) / p.head_dim
+    total += 2
+    if p.d_conv:
+        total += p.d_conv + 3 + 2 * TRANS_COST
+    return float(total)
+
+
+def _dev(stored, device):
+    import torch
+    bits = stored.bits
+    if stored.dtype == "bf16":
+        return torch.from_numpy(bits.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(bits)).to(device)
+
+
+def parity_gate(name, p, res):
+    """Compares the first call's output with the oracle; raises on mismatch."""
+    import torch
+    import oracle
+    rtol, atol = (1e-4, 1e-5) if p.io == "f32" else (2e-2, 1e-3)
+    if name in ("C0", "C1"):
+        y_o, st_o, _ = oracle.problem_fwd(p)
+        ys, sts = res.y.double().cpu().numpy(), res.state.double().cpu().numpy()
+        checked = y_o.size + st_o.size
+    else:
+        rng = np.random.default_rng(0xB0)
+        heads = np.unique(np.concatenate([[0, p.n_head - 1], rng.choice(p.n_head, 8, replace=False)]))
+        v = p.value
+        grp = oracle.group_of_head(p.n_head, p.n_group)[heads]
+        y_o, st_o, _ = oracle.scan_fwd(
+            v("s")[:, heads], v("x")[:, :, heads], v("dt")[:, :, heads], v("A")[heads], v("B"),
+            v("C"), v("D")[heads] if p.has_D else None, p.ids,
+            conv_w=v("conv_w")[heads] if p.d_conv else None, grp_of_head=grp)
+        hs = torch.as_tensor(heads, device=res.y.device)
+        ys = res.y.index_select(2, hs).double().cpu().numpy()
+        sts = res.state.index_select(1, hs).double().cpu().numpy()
+        checked = y_o.size + st_o.size
+    for got, want, what in ((ys, y_o, "y"), (sts, st_o, "state")):
+        bad = ~(np.abs(got - want) <= atol + rtol * np.abs(want))
+        if bad.any():
+            raise SystemExit(f"parity gate failed on {name} {what}: {int(bad.sum())} elements "
+                             f"outside rtol={rtol} atol={atol}")
+    return {"checked_elements": int(checked), "rtol": rtol, "atol": atol,
+            "max_abs_err_y": float(np.max(np.abs(ys - y_o)))}
+
+
+def cpu_baseline(name, p):
+    """The float64 oracle, as it stands, on the host cores: full workload for
+    C0/C1, a bounded sample of channels for the larger ones."""
+    import oracle
+    threads = oracle.default_threads()
+    v = p.value
+    if name in ("C0", "C1"):
+        heads = np.arange(p.n_head)
+        sample = "full workload"
+    else:
+        n = 1024 if name == "C2" else 8
+        heads = np.arange(n)
+        sample = f"first {n} of {p.n_head} {'channels' if p.head_dim == 1 else 'heads'}, all sequences and tokens"
+    args = (v("s")[:, heads], v("x")[:, :, heads], v("dt")[:, :, heads], v("A")[heads], v("B"),
+            v("C"), v("D")[heads] if p.has_D else None, p.ids)
+    kw = dict(conv_w=v("conv_w")[heads] if p.d_conv else None,
+              grp_of_head=oracle.group_of_head(p.n_head, p.n_group)[heads], n_threads=threads)
+    t0 = time.perf_counter()
+    oracle.scan_fwd(*args, **kw)
+    sec = time.perf_counter() - t0
+    frac = len(heads) / p.n_head
+    gbs = algorithmic_bytes(p) * frac / sec / 1e9
+    ch_tok = p.n_seqs * p.n_tokens * len(heads) * p.head_dim / sec
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": oracle.threads_used(len(heads), threads),
+            "kind": "oracle", "sample": sample, "seconds": round(sec, 3),
+            "channel_tokens_per_s": round(ch_tok, 1), "cpu": platform.processor() or platform.machine(),
+            "nproc": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="C1", choices=sorted(WORKLOADS))
+    ap.add_argument("--chunk", type=int, default=None, help="override the time chunk (tokens)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for "
+              f"--gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import ssm_inputs
+    from selective_scan_recurrence_amd import ops
+    import selective_scan_recurrence_amd as ssm
+
+    ssm.load()
+    dev = torch.device("cuda:0")
+    name = args.config
+    if name == "C4":
+        raise SystemExit("the backward bench is not built yet")
+    p = ssm_inputs.config(name)
+    desc = ops.make_desc(n_seqs=p.n_seqs, n_tokens=p.n_tokens, n_head=p.n_head,
+                         head_dim=p.head_dim, d_state=p.d_state, n_group=p.n_group,
+                         n_state_rows=p.n_state_rows, a_per_state=p.a_per_state,
+                         d_conv=p.d_conv, chunk=p.chunk if args.chunk is None else args.chunk,
+                         io=p.io, has_D=p.has_D, dt_softplus=p.dt_softplus)
+    step_bytes = algorithmic_bytes(p)
+    copies = max(2, math.ceil(3 * MALL_BYTES / step_bytes))
+    sets = []
+    for _ in range(copies):
+        t = {k: _dev(s, dev) for k, s in p.t.items()}
+        t["ids"] = torch.from_numpy(p.ids).to(dev)
+        t["out"] = torch.empty(ssm.ssm_scan_out_bytes(desc), dtype=torch.uint8, device=dev)
+        t["ws"] = ops.workspace(desc, False, dev)
+        sets.append(t)
+
+    def step(t):
+        return ops.scan_fwd(desc, t["s"], t["x"], t["dt"], t["A"], t["B"], t["C"], t.get("D"),
+                            t["ids"], conv_w=t.get("conv_w"), conv_state=t.get("conv_state"),
+                            ws=t["ws"], out=t["out"])
+
+    res = step(sets[0])
+    torch.cuda.synchronize()
+    parity = parity_gate(name, p, res)
+
+    for k in range(args.warmup):
+        step(sets[k % copies])
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        starts[k].record()
+        step(sets[k % copies])
+        ends[k].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    total_ms = starts[0].elapsed_time(ends[-1])
+    ms_per_step = total_ms / args.steps
+    gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    ch_tok = p.n_seqs * p.n_tokens * p.n_head * p.head_dim
+    avg_launch_ms = float(launch_ms.mean())
+    slots = valu_slots_per_channel_token(p) * ch_tok
+    alu_t = slots / (avg_launch_ms * 1e-3) / 1e12
+    hbm_gbs = step_bytes / (avg_launch_ms * 1e-3) / 1e9
+    alu_floor_us = slots / (VALU_PEAK_T * 1e12) * 1e6
+    hbm_floor_us = step_bytes / (HBM_PEAK_GBS * 1e9) * 1e6
+    if alu_floor_us >= hbm_floor_us:
+        roof = {"bound": "alu", "achieved": round(alu_t, 3), "peak": VALU_PEAK_T,
+                "unit": "T VALU-slots/s", "frac": round(alu_t / VALU_PEAK_T, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(hbm_gbs / HBM_PEAK_GBS, 4)}
+    roof.update({"traffic": None, "kernel": "selective_scan_fwd (all launches of one call)",
+                 "avg_launch_us": round(avg_launch_ms * 1e3, 3),
+                 "alu_floor_us": round(alu_floor_us, 2), "hbm_floor_us": round(hbm_floor_us, 2),
+                 "algorithmic_bytes": step_bytes, "valu_slots": int(slots)})
+    line = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32" if p.io == "f32" else "bf16",
+        "data": "synthetic (seeded; distributions of the workload definition)",
+        "config": {"workload": f"{name}: {WORKLOADS[name]}", "n_seqs": p.n_seqs,
+                   "n_tokens": p.n_tokens, "n_head": p.n_head, "head_dim": p.head_dim,
+                   "d_state": p.d_state, "n_group": p.n_group, "d_conv": p.d_conv,
+                   "chunk": desc.chunk, "input_copies": copies},
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "channel_tokens_per_s": round(ch_tok / (ms_per_step * 1e-3), 1),
+        "roofline": roof,
+        "parity": parity,
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(name, p)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

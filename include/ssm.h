@@ -1,0 +1,181 @@
+/*
+ * ssm.h -- C ABI of libssm.so, the selective state-space scan for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Per (sequence i, head h, channel p, state n) the scan computes
+ *
+ *     h_t[n] = exp(dt_t * A_hn) * h_{t-1}[n] + dt_t * B_t[n] * u_t
+ *     y_t    = sum_n C_t[n] * h_t[n] + D_h * u_t
+ *
+ * ("mambazip mamba1/model.rs", forward_impl and selective_scan_state16),
+ * where u is the scan input x, or -- with the fused conv -- SiLU of the
+ * causal depthwise convolution of x ("ggmlR tests/testthat/test-ssm-rwkv.R",
+ * the ssm_conv reference computation).  Operand shapes follow the ggml
+ * ssm_scan contract of that ggmlR page (make_scan): every tensor below is
+ * row-major, slowest axis first, i.e. ggml's ne list read backwards.
+ *
+ *   s          [n_state_rows][n_head][head_dim][d_state]  f32   state pool
+ *   x          [n_seqs][n_tokens][n_head][head_dim]         io
+ *   dt         [n_seqs][n_tokens][n_head]                   io
+ *   A          [n_head][d_state] (a_per_state=1) or [n_head] (a_per_state=0)  f32
+ *   B, C       [n_seqs][n_tokens][n_group][d_state]         io
+ *   D          [n_head]                                     f32  (SSM_HAS_D)
+ *   ids        [n_seqs]                                     i32
+ *   conv_w     [n_head][d_conv]                             f32  (d_conv > 0)
+ *   conv_state [n_state_rows][n_head][d_conv-1]             f32  (optional)
+ *
+ * The Mamba-1 form is head_dim = 1, n_head = d_inner, a_per_state = 1,
+ * n_group = 1.  The Mamba-2 form is a_per_state = 0 (one scalar A per head)
+ * with B/C shared by the heads of a group: head h reads group
+ * h / (n_head / n_group).
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers owned by the caller.  A pointer to
+ *    a tensor with no elements may be NULL.  The library
+ *    never allocates, frees or synchronises on the compute calls; they are
+ *    enqueued on `stream` (a hipStream_t; NULL is the default stream) and
+ *    return as soon as the launches are queued.
+ *  - Arguments are checked on the host before anything is launched: a
+ *    failed check returns a non-zero ssm_status and launches nothing.  The
+ *    checks never read device memory.
+ *  - Outputs must not alias inputs (not checked).
+ *  - Calls on different streams are independent as long as their outputs
+ *    and workspaces differ; the library keeps no mutable global state.
+ *  - io is the element type of x, dt, B, C, y and dy (SSM_F32 or
+ *    SSM_BF16); everything else is f32.  bf16 results are rounded to
+ *    nearest even.
+ */
+#ifndef SSM_H_
+#define SSM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *ssm_stream_t; /* a hipStream_t */
+
+typedef enum {
+    SSM_OK = 0,
+    SSM_ERR_NULL = 1,        /* a required pointer is NULL */
+    SSM_ERR_SHAPE = 2,       /* a dimension is out of range or inconsistent */
+    SSM_ERR_DTYPE = 3,       /* unknown io dtype */
+    SSM_ERR_UNSUPPORTED = 4, /* a valid combination this build has no kernel for */
+    SSM_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
+    SSM_ERR_ALIGN = 6,       /* a pointer is not aligned to its element size (workspace: 256 B) */
+    SSM_ERR_HIP = 7          /* a HIP launch reported an error */
+} ssm_status;
+
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
+
+enum {
+    SSM_HAS_D = 1u,       /* add D_h * u_t to y_t */
+    SSM_DT_SOFTPLUS = 2u  /* use softplus(dt) (x > 20 ? x : log(1 + e^x), "mambazip
+                             mamba1/model.rs" softplus) instead of dt as given */
+};
+
+/* Device-side error bits, read back with ssm_get_device_error(). */
+enum { SSM_DEVERR_IDS = 1u /* an ids[i] was outside [0, n_state_rows) */ };
+
+typedef struct ssm_scan_desc {
+    int64_t n_seqs;       /* sequences (>= 0)                                  */
+    int64_t n_tokens;     /* tokens per sequence (>= 0), equal for all        */
+    int64_t n_head;       /* heads (Mamba-1: d_inner) (>= 1)                  */
+    int64_t head_dim;     /* channels per head (Mamba-1: 1) (>= 1)            */
+    int64_t d_state;      /* states per channel, 1..256                       */
+    int64_t n_group;      /* B/C groups, divides n_head                       */
+    int64_t n_state_rows; /* rows of s and conv_state (>= 1)                  */
+    int32_t a_per_state;  /* 1: A[n_head][d_state]; 0: A[n_head]              */
+    int32_t d_conv;       /* 0: u = x; 2..8: u = SiLU(causal conv of x), head_dim 1 */
+    int32_t chunk;        /* time chunk in tokens, 0 = library's choice; results
+                             do not depend on it beyond rounding               */
+    int32_t io_dtype;     /* ssm_dtype                                        */
+    uint32_t flags;       /* SSM_HAS_D | SSM_DT_SOFTPLUS                      */
+    uint32_t reserved;    /* must be 0                                        */
+} ssm_scan_desc;
+
+/* Human-readable name of a status code (static storage). */
+const char *ssm_status_str(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int ssm_version(void);
+
+/* ---- sizes and offsets of the packed buffers (host only) ----------------
+ * Packed forward result (ggmlR page, "ggml_ssm_scan packs outputs and
+ * states into one flat tensor"): y [n_seqs][n_tokens][n_head][head_dim] in
+ * io, immediately followed by the final states [n_seqs][n_head][head_dim]
+ * [d_state] in f32.  Row i of the state block is sequence i's final state.
+ * For f32 io the state block starts at element nelements(x), as in ggml.
+ * Each returns 0 if the descriptor is invalid. */
+size_t ssm_scan_out_bytes(const ssm_scan_desc *desc);
+size_t ssm_scan_state_offset_bytes(const ssm_scan_desc *desc);
+
+/* Packed gradient of selective_scan_bwd, all f32, in the order of ggml's
+ * ssm_scan_back ("ggml_ssm_scan_back packs all six input gradients"):
+ * d_s (shape of s) | d_x | d_dt | d_A | d_B | d_C, then d_D [n_head] when
+ * SSM_HAS_D.  offsets[k] (k = 0..6) receives the byte offset of block k
+ * (d_D's offset equals the total when there is no D); returns the total
+ * size in bytes, 0 if the descriptor is invalid. */
+size_t ssm_scan_dgrad_layout(const ssm_scan_desc *desc, size_t offsets[7]);
+
+/* Workspace the compute calls need (bytes, a multiple of 256).  backward = 0
+ * for selective_scan_fwd, 1 for selective_scan_bwd.  The first 256 bytes of
+ * a workspace hold the device-error word: zero the workspace once after
+ * allocating it; the library sets bits and never clears them. */
+size_t ssm_scan_workspace_bytes(const ssm_scan_desc *desc, int backward);
+
+/* ---- compute -------------------------------------------------------------
+ * ssm_conv_fwd: the ggml ssm_conv operator ("ggml_ssm_conv matches a
+ * depthwise convolution computed in R"):
+ *   out[s][t][c] = sum_{j<d_conv} sx[s][c][t + j] * w[c][j]
+ * then SiLU when apply_silu != 0.  sx [n_s][d_inner][d_conv-1+n_t] (time
+ * fastest, carrying the d_conv-1 earlier inputs) and out [n_s][n_t][d_inner]
+ * have dtype io; w [d_inner][d_conv] is f32.  The last tap w[c][d_conv-1]
+ * multiplies the newest input. */
+int ssm_conv_fwd(const void *sx, const float *w, void *out, int64_t n_s, int64_t n_t,
+                 int64_t d_inner, int32_t d_conv, int32_t io_dtype, int32_t apply_silu,
+                 ssm_stream_t stream);
+
+/* selective_scan_fwd: the scan over n_tokens tokens for every sequence.
+ *  - Sequence i starts from state row ids[i] of s.  An id outside
+ *    [0, n_state_rows) is not read: that sequence's y and state are written
+ *    as NaN and SSM_DEVERR_IDS is set in the workspace's error word.
+ *  - With d_conv > 0, the conv for token t reads x at t-d_conv+1..t; inputs
+ *    before token 0 come from conv_state row ids[i] (oldest first), or are
+ *    zero when conv_state is NULL.  conv_state_out (may be NULL) receives
+ *    the last d_conv-1 inputs of each sequence, [n_seqs][n_head][d_conv-1].
+ *  - out receives the packed result (see ssm_scan_out_bytes).
+ *  - D may be NULL only without SSM_HAS_D; conv_w only when d_conv = 0.
+ *  - workspace: ssm_scan_workspace_bytes(desc, 0) bytes, 256-byte aligned. */
+int selective_scan_fwd(const ssm_scan_desc *desc, const float *s, const void *x,
+                       const void *dt, const float *A, const void *B, const void *C,
+                       const float *D, const int32_t *ids, const float *conv_w,
+                       const float *conv_state, void *out, float *conv_state_out,
+                       void *workspace, size_t workspace_bytes, ssm_stream_t stream);
+
+/* selective_scan_bwd: reverse-time adjoint of selective_scan_fwd without the
+ * fused conv (d_conv must be 0).  dout is packed like the forward result
+ * (dy in io, then dstate in f32).  dgrad receives the packed f32 gradient
+ * (see ssm_scan_dgrad_layout).  Rows of d_s no id refers to are zero;
+ * repeated ids accumulate.  The adjoint is the one of "kizzasi-model
+ * backprop_ssm.rs" (ssm_backward): dL/dh_{t-1} = a_t dL/dh_t + C_{t-1} dy_{t-1},
+ * with the per-element terms of "mambazip mamba1/model.rs"
+ * (accumulate_token_step_gradients).  Sums over channels and tokens are
+ * taken in a fixed order: results are bitwise repeatable.
+ * workspace: ssm_scan_workspace_bytes(desc, 1) bytes, 256-byte aligned. */
+int selective_scan_bwd(const ssm_scan_desc *desc, const float *s, const void *x,
+                       const void *dt, const float *A, const void *B, const void *C,
+                       const float *D, const int32_t *ids, const void *dout, float *dgrad,
+                       void *workspace, size_t workspace_bytes, ssm_stream_t stream);
+
+/* Copies the device-error word of a workspace to *bits (synchronises the
+ * stream; for tests and debugging, not for the hot path). */
+int ssm_get_device_error(const void *workspace, ssm_stream_t stream, uint32_t *bits);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_H_ */

@@ -1,0 +1,157 @@
+"""ctypes binding of libssm.so: the C ABI of include/ssm.h under the same
+names, with argument marshalling only.  Tensors may be passed as torch
+tensors (their data_ptr is used), raw integer addresses, or None for NULL.
+Every compute call raises SsmError on a non-zero status.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssm.so")
+
+SSM_OK, SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_DTYPE, SSM_ERR_UNSUPPORTED, \
+    SSM_ERR_WORKSPACE, SSM_ERR_ALIGN, SSM_ERR_HIP = range(8)
+SSM_F32, SSM_BF16 = 0, 1
+SSM_HAS_D, SSM_DT_SOFTPLUS = 1, 2
+SSM_DEVERR_IDS = 1
+
+EXPORTS = ("ssm_status_str", "ssm_version", "ssm_scan_out_bytes", "ssm_scan_state_offset_bytes",
+           "ssm_scan_dgrad_layout", "ssm_scan_workspace_bytes", "ssm_conv_fwd",
+           "selective_scan_fwd", "selective_scan_bwd", "ssm_get_device_error")
+
+
+class SsmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({ssm_status_str(status)})")
+
+
+class SsmScanDesc(ctypes.Structure):
+    _fields_ = [("n_seqs", ctypes.c_int64), ("n_tokens", ctypes.c_int64),
+                ("n_head", ctypes.c_int64), ("head_dim", ctypes.c_int64),
+                ("d_state", ctypes.c_int64), ("n_group", ctypes.c_int64),
+                ("n_state_rows", ctypes.c_int64), ("a_per_state", ctypes.c_int32),
+                ("d_conv", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("reserved", ctypes.c_uint32)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load():
+    """Loads libssm.so (built in-tree by selective_scan_recurrence_amd.build).
+    Raises if it is missing: there is no fallback path."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run "
+                               "`python -m selective_scan_recurrence_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        D = ctypes.POINTER(SsmScanDesc)
+        lib.ssm_status_str.argtypes, lib.ssm_status_str.restype = [ctypes.c_int], ctypes.c_char_p
+        lib.ssm_version.argtypes, lib.ssm_version.restype = [], ctypes.c_int
+        for fn in ("ssm_scan_out_bytes", "ssm_scan_state_offset_bytes"):
+            getattr(lib, fn).argtypes, getattr(lib, fn).restype = [D], SZ
+        lib.ssm_scan_dgrad_layout.argtypes = [D, ctypes.POINTER(SZ * 7)]
+        lib.ssm_scan_dgrad_layout.restype = SZ
+        lib.ssm_scan_workspace_bytes.argtypes = [D, ctypes.c_int]
+        lib.ssm_scan_workspace_bytes.restype = SZ
+        lib.ssm_conv_fwd.argtypes = [P, P, P, I64, I64, I64, I32, I32, I32, P]
+        lib.ssm_conv_fwd.restype = ctypes.c_int
+        lib.selective_scan_fwd.argtypes = [D] + [P] * 13 + [SZ, P]
+        lib.selective_scan_fwd.restype = ctypes.c_int
+        lib.selective_scan_bwd.argtypes = [D] + [P] * 11 + [SZ, P]
+        lib.selective_scan_bwd.restype = ctypes.c_int
+        lib.ssm_get_device_error.argtypes = [P, P, ctypes.POINTER(ctypes.c_uint32)]
+        lib.ssm_get_device_error.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int, where: str) -> int:
+    if rc != SSM_OK:
+        raise SsmError(rc, where)
+    return rc
+
+
+def ssm_status_str(status: int) -> str:
+    return load().ssm_status_str(int(status)).decode()
+
+
+def ssm_version() -> int:
+    return load().ssm_version()
+
+
+def ssm_scan_out_bytes(desc: SsmScanDesc) -> int:
+    return load().ssm_scan_out_bytes(ctypes.byref(desc))
+
+
+def ssm_scan_state_offset_bytes(desc: SsmScanDesc) -> int:
+    return load().ssm_scan_state_offset_bytes(ctypes.byref(desc))
+
+
+def ssm_scan_dgrad_layout(desc: SsmScanDesc):
+    """Returns (total_bytes, [offset of d_s, d_x, d_dt, d_A, d_B, d_C, d_D])."""
+    offs = (ctypes.c_size_t * 7)()
+    total = load().ssm_scan_dgrad_layout(ctypes.byref(desc), ctypes.byref(offs))
+    return total, list(offs)
+
+
+def ssm_scan_workspace_bytes(desc: SsmScanDesc, backward: int) -> int:
+    return load().ssm_scan_workspace_bytes(ctypes.byref(desc), int(backward))
+
+
+def ssm_conv_fwd(sx, w, out, n_s, n_t, d_inner, d_conv, io_dtype, apply_silu, stream=None):
+    rc = load().ssm_conv_fwd(_ptr(sx), _ptr(w), _ptr(out), int(n_s), int(n_t), int(d_inner),
+                             int(d_conv), int(io_dtype), int(apply_silu), _stream(stream))
+    return _check(rc, "ssm_conv_fwd")
+
+
+def selective_scan_fwd(desc, s, x, dt, A, B, C, D, ids, conv_w, conv_state, out,
+                       conv_state_out, workspace, workspace_bytes, stream=None):
+    rc = load().selective_scan_fwd(ctypes.byref(desc), _ptr(s), _ptr(x), _ptr(dt), _ptr(A),
+                                   _ptr(B), _ptr(C), _ptr(D), _ptr(ids), _ptr(conv_w),
+                                   _ptr(conv_state), _ptr(out), _ptr(conv_state_out),
+                                   _ptr(workspace), int(workspace_bytes), _stream(stream))
+    return _check(rc, "selective_scan_fwd")
+
+
+def selective_scan_bwd(desc, s, x, dt, A, B, C, D, ids, dout, dgrad, workspace,
+                       workspace_bytes, stream=None):
+    rc = load().selective_scan_bwd(ctypes.byref(desc), _ptr(s), _ptr(x), _ptr(dt), _ptr(A),
+                                   _ptr(B), _ptr(C), _ptr(D), _ptr(ids), _ptr(dout),
+                                   _ptr(dgrad), _ptr(workspace), int(workspace_bytes),
+                                   _stream(stream))
+    return _check(rc, "selective_scan_bwd")
+
+
+def ssm_get_device_error(workspace, stream=None) -> int:
+    bits = ctypes.c_uint32(0)
+    _check(load().ssm_get_device_error(_ptr(workspace), _stream(stream), ctypes.byref(bits)),
+           "ssm_get_device_error")
+    return bits.value

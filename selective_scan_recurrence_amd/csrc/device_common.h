@@ -1,0 +1,39 @@
+// Device helpers shared by the kernel files: element loads/stores for the io
+// dtypes and the fast transcendental forms the kernels use.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// io element types: f32 is stored as float, bf16 as its 16 raw bits.
+using bf16_t = uint16_t;
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16_t v) { return __uint_as_float(uint32_t(v) << 16); }
+
+// f32 -> bf16, round to nearest even (gfx950 converts in hardware).
+__device__ __forceinline__ bf16_t bf16_rne(float v) {
+    return __builtin_bit_cast(bf16_t, static_cast<__bf16>(v));
+}
+
+__device__ __forceinline__ void store_io(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_io(bf16_t* p, float v) { *p = bf16_rne(v); }
+
+// 2^x on the transcendental unit (v_exp_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// SiLU(c) = c / (1 + e^-c), with the hardware reciprocal.
+__device__ __forceinline__ float silu(float c) {
+    return c * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-c * kLog2e));
+}
+
+// softplus with the threshold-20 branch of "mambazip mamba1/model.rs" (softplus).
+__device__ __forceinline__ float softplus(float v) {
+    return v > 20.0f ? v : log1pf(expf(v));
+}
+
+}  // namespace ssm

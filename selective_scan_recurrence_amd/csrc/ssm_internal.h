@@ -1,0 +1,81 @@
+// Internal interface between the C ABI (ssm_api.hip) and the kernel files.
+// Not installed; the public interface is include/ssm.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ssm.h"
+
+namespace ssm {
+
+// Checked, expanded scan dimensions.
+struct Shape {
+    int64_t S, L, H, P, N, G, R;  // seqs, tokens, heads, head_dim, d_state, groups, state rows
+    int a_per_state;
+    int K;                        // conv taps (0 = none)
+    int chunk;                    // requested chunk (0 = auto)
+    int io;                       // SSM_F32 / SSM_BF16
+    uint32_t flags;
+    int64_t d_inner() const { return H * P; }
+    int io_bytes() const { return io == SSM_BF16 ? 2 : 4; }
+    int64_t nelem_x() const { return S * L * H * P; }
+    int64_t nelem_state() const { return S * H * P * N; }
+    int64_t nelem_A() const { return a_per_state ? H * N : H; }
+    int64_t nelem_BC() const { return S * L * G * N; }
+};
+
+struct FwdArgs {
+    Shape sh;
+    const float* s;
+    const void* x;
+    const void* dt;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const int32_t* ids;
+    const float* conv_w;
+    const float* conv_state;
+    void* y;               // y block of the packed result
+    float* state_out;      // state block of the packed result
+    float* conv_state_out;
+    uint32_t* err;         // device-error word (workspace)
+    char* ws;              // workspace after the error word
+    size_t ws_bytes;
+};
+
+struct BwdArgs {
+    Shape sh;
+    const float* s;
+    const void* x;
+    const void* dt;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const int32_t* ids;
+    const void* dy;
+    const float* dstate;
+    float *d_s, *d_x, *d_dt, *d_A, *d_B, *d_C, *d_D;
+    uint32_t* err;
+    char* ws;
+    size_t ws_bytes;
+};
+
+constexpr size_t kErrBytes = 256;  // the device-error word's slot at the workspace start
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Workspace needed after the error slot.
+size_t fwd_workspace_bytes(const Shape& sh);
+size_t bwd_workspace_bytes(const Shape& sh);
+
+// Returns SSM_OK, SSM_ERR_UNSUPPORTED, or SSM_ERR_HIP.
+int launch_scan_fwd(const FwdArgs& a, hipStream_t stream);
+int launch_scan_bwd(const BwdArgs& a, hipStream_t stream);
+int launch_conv_fwd(const void* sx, const float* w, void* out, int64_t n_s, int64_t n_t,
+                    int64_t d_inner, int d_conv, int io, int apply_silu, hipStream_t stream);
+
+}  // namespace ssm

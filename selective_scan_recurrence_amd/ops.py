@@ -1,0 +1,107 @@
+"""Torch-level convenience over the C ABI: builds descriptors, allocates the
+packed outputs and workspaces as torch device tensors, and splits packed
+results into views.  Every computation runs in libssm.so's HIP kernels;
+torch only provides memory and the stream.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _binding as B
+
+IO_DTYPES = {"f32": B.SSM_F32, "bf16": B.SSM_BF16}
+TORCH_IO = {B.SSM_F32: torch.float32, B.SSM_BF16: torch.bfloat16}
+
+
+def make_desc(*, n_seqs, n_tokens, n_head, d_state, head_dim=1, n_group=1, n_state_rows=None,
+              a_per_state=True, d_conv=0, chunk=0, io="f32", has_D=True,
+              dt_softplus=False) -> B.SsmScanDesc:
+    flags = (B.SSM_HAS_D if has_D else 0) | (B.SSM_DT_SOFTPLUS if dt_softplus else 0)
+    return B.SsmScanDesc(int(n_seqs), int(n_tokens), int(n_head), int(head_dim), int(d_state),
+                         int(n_group), int(n_seqs if n_state_rows is None else n_state_rows),
+                         int(bool(a_per_state)), int(d_conv), int(chunk),
+                         IO_DTYPES[io] if isinstance(io, str) else int(io), int(flags), 0)
+
+
+def workspace(desc: B.SsmScanDesc, backward: bool, device="cuda") -> torch.Tensor:
+    """A zeroed workspace (its first word is the sticky device-error word)."""
+    n = B.ssm_scan_workspace_bytes(desc, int(backward))
+    if n == 0:
+        raise B.SsmError(B.SSM_ERR_SHAPE, "ssm_scan_workspace_bytes")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+@dataclass
+class FwdResult:
+    out: torch.Tensor            # packed bytes: y | state
+    y: torch.Tensor              # view [n_seqs][n_tokens][n_head][head_dim], io dtype
+    state: torch.Tensor          # view [n_seqs][n_head][head_dim][d_state], f32
+    conv_state: Optional[torch.Tensor]
+
+
+def split_out(desc: B.SsmScanDesc, out: torch.Tensor):
+    io = TORCH_IO[desc.io_dtype]
+    off = B.ssm_scan_state_offset_bytes(desc)
+    n_y = desc.n_seqs * desc.n_tokens * desc.n_head * desc.head_dim
+    y = out[:off].view(io)[:n_y].view(desc.n_seqs, desc.n_tokens, desc.n_head, desc.head_dim)
+    st = out[off:].view(torch.float32).view(desc.n_seqs, desc.n_head, desc.head_dim, desc.d_state)
+    return y, st
+
+
+def scan_fwd(desc, s, x, dt, A, Bm, Cm, D, ids, conv_w=None, conv_state=None,
+             want_conv_state=False, ws=None, out=None, stream=None) -> FwdResult:
+    if out is None:
+        out = torch.empty(B.ssm_scan_out_bytes(desc), dtype=torch.uint8, device=x.device)
+    cso = None
+    if want_conv_state and desc.d_conv > 1:
+        cso = torch.empty(desc.n_seqs, desc.n_head, desc.d_conv - 1, dtype=torch.float32,
+                          device=x.device)
+    if ws is None:
+        ws = workspace(desc, False, x.device)
+    B.selective_scan_fwd(desc, s, x, dt, A, Bm, Cm, D, ids, conv_w, conv_state, out, cso, ws,
+                         ws.numel(), stream)
+    y, st = split_out(desc, out)
+    return FwdResult(out, y, st, cso)
+
+
+def split_dgrad(desc: B.SsmScanDesc, dgrad: torch.Tensor) -> dict:
+    total, offs = B.ssm_scan_dgrad_layout(desc)
+    S, L, H, P, N, G, R = (desc.n_seqs, desc.n_tokens, desc.n_head, desc.head_dim,
+                           desc.d_state, desc.n_group, desc.n_state_rows)
+    shapes = {"d_s": (R, H, P, N), "d_x": (S, L, H, P), "d_dt": (S, L, H),
+              "d_A": (H, N) if desc.a_per_state else (H,), "d_B": (S, L, G, N),
+              "d_C": (S, L, G, N)}
+    if desc.flags & B.SSM_HAS_D:
+        shapes["d_D"] = (H,)
+    ends = offs[1:] + [total]
+    res = {}
+    for k, (name, shape) in enumerate(shapes.items()):
+        res[name] = dgrad[offs[k]:ends[k]].view(torch.float32).view(*shape)
+    return res
+
+
+def scan_bwd(desc, s, x, dt, A, Bm, Cm, D, ids, dout, ws=None, dgrad=None, stream=None):
+    """Returns (packed dgrad bytes, dict of views)."""
+    total, _ = B.ssm_scan_dgrad_layout(desc)
+    if dgrad is None:
+        dgrad = torch.empty(total, dtype=torch.uint8, device=x.device)
+    if ws is None:
+        ws = workspace(desc, True, x.device)
+    B.selective_scan_bwd(desc, s, x, dt, A, Bm, Cm, D, ids, dout, dgrad, ws, ws.numel(), stream)
+    return dgrad, split_dgrad(desc, dgrad)
+
+
+def conv_fwd(sx: torch.Tensor, w: torch.Tensor, apply_silu=False, out=None, stream=None):
+    """ggml ssm_conv: sx [n_s][d_inner][d_conv-1+n_t], w [d_inner][d_conv] ->
+    out [n_s][n_t][d_inner] (sx's dtype)."""
+    n_s, d_inner, length = sx.shape
+    d_conv = w.shape[1]
+    n_t = length - (d_conv - 1)
+    io = B.SSM_BF16 if sx.dtype == torch.bfloat16 else B.SSM_F32
+    if out is None:
+        out = torch.empty(n_s, n_t, d_inner, dtype=sx.dtype, device=sx.device)
+    B.ssm_conv_fwd(sx, w, out, n_s, n_t, d_inner, d_conv, io, int(bool(apply_silu)), stream)
+    return out

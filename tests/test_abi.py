@@ -1,0 +1,178 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, computes the packed layouts the ggmlR page fixes, and rejects bad
+arguments on the host with the documented codes before launching anything.
+No test here reaches a kernel launch (there is no GPU in the CPU suite)."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import selective_scan_recurrence_amd as ssm
+from selective_scan_recurrence_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = json.load(open(os.path.join(ROOT, "tests", "golden", "ggml_packed_counts.json")))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "ssm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\([^;{]*\)\s*;", text)))
+
+
+def test_library_loads_and_exports_every_declared_function():
+    lib = ssm.load()
+    names = _header_functions()
+    assert set(names) == set(ssm.EXPORTS), names
+    for name in names:
+        assert hasattr(lib, name), name
+    assert ssm.ssm_version() >= 100
+
+
+def test_status_strings():
+    for code in range(8):
+        assert ssm.ssm_status_str(code) != "unknown status"
+    assert ssm.ssm_status_str(99) == "unknown status"
+
+
+def _desc(**kw):
+    base = dict(n_seqs=2, n_tokens=2, n_head=3, head_dim=2, d_state=4, n_group=1,
+                a_per_state=False, io="f32")
+    base.update(kw)
+    return ops.make_desc(**base)
+
+
+def test_packed_forward_counts_match_ggml():
+    g = GOLDEN["make_scan_defaults"]
+    d = _desc(n_seqs=g["n_seqs"], n_tokens=g["n_seq_tokens"], n_head=g["n_head"],
+              head_dim=g["head_dim"], d_state=g["d_state"], n_group=g["n_group"])
+    assert ssm.ssm_scan_out_bytes(d) == 4 * g["nelements_packed"]
+    assert ssm.ssm_scan_state_offset_bytes(d) == 4 * g["nelements_x"]
+    assert ssm.ssm_scan_out_bytes(d) - ssm.ssm_scan_state_offset_bytes(d) == \
+        4 * g["nelements_state_block"]
+
+
+def test_packed_gradient_layout_matches_ggml_order():
+    g = GOLDEN["make_scan_defaults"]
+    d = _desc(n_seqs=g["n_seqs"], n_tokens=g["n_seq_tokens"], n_head=g["n_head"],
+              head_dim=g["head_dim"], d_state=g["d_state"], n_group=g["n_group"], has_D=False)
+    total, offs = ssm.ssm_scan_dgrad_layout(d)
+    assert total == 4 * g["nelements_scan_back"]
+    sizes = [(b - a) // 4 for a, b in zip(offs[:6], offs[1:7])]
+    assert sizes == g["scan_back_sizes"]
+    assert offs[6] == total          # no d_D block without D
+    d2 = _desc(n_seqs=g["n_seqs"], n_tokens=g["n_seq_tokens"], n_head=g["n_head"],
+               head_dim=g["head_dim"], d_state=g["d_state"], n_group=g["n_group"], has_D=True)
+    total2, offs2 = ssm.ssm_scan_dgrad_layout(d2)
+    assert offs2[6] == total and total2 == total + 4 * g["n_head"]
+
+
+def test_bf16_packing_offsets():
+    # y block in bf16, state block in f32 right after it
+    d = ops.make_desc(n_seqs=8, n_tokens=4096, n_head=5120, d_state=16, d_conv=4, io="bf16")
+    assert ssm.ssm_scan_state_offset_bytes(d) == 335_544_320
+    assert ssm.ssm_scan_out_bytes(d) == 335_544_320 + 655_360 * 4
+    d3 = ops.make_desc(n_seqs=4, n_tokens=4096, n_head=80, head_dim=64, d_state=128,
+                       a_per_state=False, io="bf16")
+    assert ssm.ssm_scan_state_offset_bytes(d3) == 167_772_160
+    assert ssm.ssm_scan_out_bytes(d3) == 167_772_160 + 2_621_440 * 4
+
+
+@pytest.mark.parametrize("field,value", [
+    ("n_seqs", -1), ("n_tokens", -1), ("n_head", 0), ("head_dim", 0), ("d_state", 0),
+    ("d_state", 257), ("n_group", 0), ("n_group", 2), ("n_state_rows", 0), ("a_per_state", 2),
+    ("d_conv", -1), ("d_conv", 9), ("chunk", -1), ("flags", 8), ("reserved", 1),
+])
+def test_invalid_descriptor_rejected(field, value):
+    d = _desc()
+    setattr(d, field, value)
+    assert ssm.ssm_scan_out_bytes(d) == 0
+    assert ssm.ssm_scan_workspace_bytes(d, 0) == 0
+    with pytest.raises(ssm.SsmError) as e:
+        ssm.selective_scan_fwd(d, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 256, 1 << 20,
+                               stream=0)
+    assert e.value.status == ssm.SSM_ERR_SHAPE
+
+
+def test_conv_requires_single_channel_heads():
+    d = _desc(d_conv=4, head_dim=2)
+    assert ssm.ssm_scan_out_bytes(d) == 0
+
+
+def test_unknown_dtype_rejected():
+    d = _desc()
+    d.io_dtype = 7
+    with pytest.raises(ssm.SsmError) as e:
+        ssm.selective_scan_fwd(d, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 256, 1 << 20,
+                               stream=0)
+    assert e.value.status == ssm.SSM_ERR_DTYPE
+
+
+def _fwd_args(**over):
+    a = dict(s=256, x=256, dt=256, A=256, B=256, C=256, D=256, ids=256, conv_w=None,
+             conv_state=None, out=256, conv_state_out=None, workspace=256, workspace_bytes=1 << 20)
+    a.update(over)
+    return a
+
+
+def _call_fwd(d, a):
+    return ssm.selective_scan_fwd(d, a["s"], a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"],
+                                  a["ids"], a["conv_w"], a["conv_state"], a["out"],
+                                  a["conv_state_out"], a["workspace"], a["workspace_bytes"],
+                                  stream=0)
+
+
+@pytest.mark.parametrize("name", ["s", "x", "dt", "A", "B", "C", "D", "ids", "out", "workspace"])
+def test_null_pointer_rejected(name):
+    with pytest.raises(ssm.SsmError) as e:
+        _call_fwd(_desc(), _fwd_args(**{name: None}))
+    assert e.value.status == ssm.SSM_ERR_NULL
+
+
+def test_conv_weights_required_with_conv():
+    d = _desc(d_conv=4, head_dim=1)
+    with pytest.raises(ssm.SsmError) as e:
+        _call_fwd(d, _fwd_args())
+    assert e.value.status == ssm.SSM_ERR_NULL
+
+
+def test_small_workspace_rejected():
+    d = _desc()
+    need = ssm.ssm_scan_workspace_bytes(d, 0)
+    assert need >= 256 and need % 256 == 0
+    with pytest.raises(ssm.SsmError) as e:
+        _call_fwd(d, _fwd_args(workspace_bytes=need - 1))
+    assert e.value.status == ssm.SSM_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("name,value", [("x", 258), ("s", 258), ("workspace", 512 + 4),
+                                        ("out", 258)])
+def test_misaligned_pointer_rejected(name, value):
+    with pytest.raises(ssm.SsmError) as e:
+        _call_fwd(_desc(), _fwd_args(**{name: value}))
+    assert e.value.status == ssm.SSM_ERR_ALIGN
+
+
+def test_backward_rejects_fused_conv():
+    d = _desc(d_conv=4, head_dim=1)
+    with pytest.raises(ssm.SsmError) as e:
+        ssm.selective_scan_bwd(d, 256, 256, 256, 256, 256, 256, 256, 256, 256, 256, 256,
+                               1 << 20, stream=0)
+    assert e.value.status == ssm.SSM_ERR_UNSUPPORTED
+
+
+def test_conv_argument_checks():
+    with pytest.raises(ssm.SsmError) as e:
+        ssm.ssm_conv_fwd(None, 256, 256, 1, 4, 2, 3, ssm.SSM_F32, 0, stream=0)
+    assert e.value.status == ssm.SSM_ERR_NULL
+    with pytest.raises(ssm.SsmError) as e:
+        ssm.ssm_conv_fwd(256, 256, 256, 1, 4, 2, 9, ssm.SSM_F32, 0, stream=0)
+    assert e.value.status == ssm.SSM_ERR_SHAPE
+    with pytest.raises(ssm.SsmError) as e:
+        ssm.ssm_conv_fwd(258, 256, 256, 1, 4, 2, 3, ssm.SSM_F32, 0, stream=0)
+    assert e.value.status == ssm.SSM_ERR_ALIGN
+    with pytest.raises(ssm.SsmError) as e:
+        ssm.ssm_conv_fwd(256, 256, 256, 1, 4, 2, 3, 5, 0, stream=0)
+    assert e.value.status == ssm.SSM_ERR_DTYPE
