@@ -72,6 +72,11 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 size_t fwd_workspace_bytes(const Shape& sh);
 size_t bwd_workspace_bytes(const Shape& sh);
 
+// Mamba-1 forward for d_state <= 16 with four lanes per channel.
+bool quad_supported(const Shape& sh);
+size_t quad_workspace_bytes(const Shape& sh);
+int launch_quad_fwd(const FwdArgs& a, hipStream_t stream);
+
 // Returns SSM_OK, SSM_ERR_UNSUPPORTED, or SSM_ERR_HIP.
 int launch_scan_fwd(const FwdArgs& a, hipStream_t stream);
 int launch_scan_bwd(const BwdArgs& a, hipStream_t stream);

@@ -89,6 +89,16 @@ CASES = {
     "m1_N64": dict(d_state=64, d_conv=0, A_kind="uniform"),
     "m1_groups": dict(n_group=7, d_conv=0, A_kind="uniform"),
     "m1_dup_ids": dict(n_state_rows=2, ids=np.array([1, 1, 0], np.int32)),
+    # d_inner a multiple of 64 and d_state 16: the LDS-tiled quad path
+    "tiled_bf16_ragged": dict(n_head=128, n_tokens=101, io="bf16"),
+    "tiled_f32_chunked": dict(n_head=64, n_tokens=300, chunk=64),
+    "tiled_bf16_chunked_ragged": dict(n_head=192, n_tokens=333, chunk=128, io="bf16"),
+    "tiled_conv_state_perm": dict(n_head=64, n_tokens=70, conv_state_std=1.0, n_state_rows=5,
+                                  ids="perm", chunk=32),
+    "tiled_L1": dict(n_head=64, n_tokens=1),
+    "tiled_L5_noconv": dict(n_head=64, n_tokens=5, d_conv=0),
+    "tiled_softplus_noD": dict(n_head=64, n_tokens=77, dt_softplus=True, has_D=False),
+    "untiled_chunked": dict(n_head=70, n_tokens=300, chunk=64),
     "m2_small": dict(n_head=5, head_dim=8, d_state=16, d_conv=0, a_per_state=False,
                      A_kind="uniform", n_state_rows=4, ids="perm"),
     "m2_N128_bf16": dict(n_head=4, head_dim=16, d_state=128, d_conv=0, a_per_state=False,
