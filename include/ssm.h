@@ -159,7 +159,12 @@ int selective_scan_fwd(const ssm_scan_desc *desc, const float *s, const void *x,
  * fused conv (d_conv must be 0).  dout is packed like the forward result
  * (dy in io, then dstate in f32).  dgrad receives the packed f32 gradient
  * (see ssm_scan_dgrad_layout).  Rows of d_s no id refers to are zero;
- * repeated ids accumulate.  The adjoint is the one of "kizzasi-model
+ * repeated ids accumulate.  A sequence whose id is outside [0, n_state_rows)
+ * sets SSM_DEVERR_IDS, adds nothing to d_s, and has its d_x and d_dt written
+ * as NaN; sums it takes part in that depend on its initial state (d_A, d_C)
+ * are NaN as well.
+ * This build supports the Mamba-1 form with d_state <= 16 and one group;
+ * other shapes return SSM_ERR_UNSUPPORTED.  The adjoint is the one of "kizzasi-model
  * backprop_ssm.rs" (ssm_backward): dL/dh_{t-1} = a_t dL/dh_t + C_{t-1} dy_{t-1},
  * with the per-element terms of "mambazip mamba1/model.rs"
  * (accumulate_token_step_gradients).  Sums over channels and tokens are

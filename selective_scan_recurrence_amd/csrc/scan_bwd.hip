@@ -1,11 +1,378 @@
-// Selective-scan backward kernels for gfx950 (reverse-time adjoint).
+// Selective-scan backward for gfx950: reverse-time adjoint of the Mamba-1
+// form with d_state <= 16 and one B/C group (no fused conv).
+//
+// Per (sequence i, channel c) the forward step is h_t = a_t h_{t-1} + dt_t B_t u_t,
+// a_t = exp(dt_t A_c), y_t = C_t . h_t + D_c u_t.  The adjoint carried from
+// the last token to the first is g = dL/dh_t ("kizzasi-model
+// backprop_ssm.rs", ssm_backward: dL/dh_t = C^T dy_t + A_bar dL/dh_{t+1}),
+// and the per-element terms follow "mambazip mamba1/model.rs"
+// (accumulate_token_step_gradients):
+//     g      += C_t dy_t                  (now dL/dh_t)
+//     dC_t   += dy_t h_t                  (summed over channels)
+//     du_t    = D dy_t + dt_t sum_n g_n B_tn
+//     ddt_t   = sum_n g_n (h_{t-1,n} a_tn A_n + B_tn u_t)
+//     dB_t   += g dt_t u_t                (summed over channels)
+//     dA     += g h_{t-1} a_t dt_t        (summed over sequences and tokens)
+//     g      *= a_t                       (now dL/dh_{t-1})
+// and dD += dy_t u_t, dh_0 = g after the first token, scattered to row ids[i].
+//
+// Kernel 1 (scan_fwd_quad.hip, quad_ckpt) stores the state entering every
+// 16-token block.  Kernel 2 (bwd_rev) walks the blocks backwards: it stages
+// the block's inputs in LDS, recomputes the block's decays and states from
+// the checkpoint into registers, then runs the adjoint over the block.  The
+// layout is the forward's quad one: four lanes per channel, four states per
+// lane.  Channel sums (dB, dC) are reduced in a fixed order: across the four
+// channels of a 16-lane row with DPP shifts, across rows and waves through
+// LDS, across channel blocks by kernel 3.  Kernel 3 also sums dA and dD over
+// sequences and gathers dh_0 into d_s by ids; every sum has a fixed order,
+// so results are bitwise repeatable.
 #include "device_common.h"
 #include "ssm_internal.h"
 
 namespace ssm {
+namespace {
 
-size_t bwd_workspace_bytes(const Shape&) { return 0; }
+constexpr int kThreads = 256;
+constexpr int kChan = 64;  // channels per workgroup
+constexpr int kBlk = 16;   // tokens per block (checkpoint spacing)
 
-int launch_scan_bwd(const BwdArgs&, hipStream_t) { return SSM_ERR_UNSUPPORTED; }
+struct BwdKP {
+    const float* A;
+    const float* D;
+    const int32_t* ids;
+    const void* x;
+    const void* dt;
+    const void* B;
+    const void* C;
+    const void* dy;
+    const float* dstate;
+    const float* ckpt;   // [n_blk][S][d_inner][16]
+    float* d_x;
+    float* d_dt;
+    float* dbc_part;     // [n_cb][S][L][32]: dB (16) then dC (16)
+    float* dA_part;      // [S][d_inner][16]
+    float* dD_part;      // [S][d_inner]
+    float* ds_part;      // [S][d_inner][16]
+    int L, d_inner, N, R, S, n_cb;
+    int has_D, softplus;
+};
+
+template <int P0, int P1, int P2, int P3>
+__device__ __forceinline__ float qperm(float v) {
+    constexpr int ctrl = P0 | (P1 << 2) | (P2 << 4) | (P3 << 6);
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl,
+                                                                 0xF, 0xF, true));
+}
+
+// Sum over the 4 lanes of each quad (every lane gets the total).
+__device__ __forceinline__ float quad_sum(float v) {
+    v += qperm<1, 0, 3, 2>(v);
+    v += qperm<2, 3, 0, 1>(v);
+    return v;
+}
+
+// Adds to lane l of each 16-lane row the value of lane l - SHIFT (same row);
+// lanes without a source keep their value.
+template <int SHIFT>
+__device__ __forceinline__ float row_shr_add(float v) {
+    constexpr int ctrl = 0x110 + SHIFT;  // DPP row_shr:SHIFT
+    const float sh = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, v), ctrl, 0xF, 0xF, true));  // out-of-row sources read 0
+    return v + sh;
+}
+
+template <typename T>
+__device__ __forceinline__ float ldv(const void* base, int64_t idx) {
+    return to_f32(static_cast<const T*>(base)[idx]);
+}
+
+template <typename T, bool SOFTPLUS>
+__global__ __launch_bounds__(kThreads) void bwd_rev(BwdKP p) {
+    __shared__ float x_l[kBlk][kChan];
+    __shared__ float dt_l[kBlk][kChan];   // dt as given (before softplus)
+    __shared__ float dy_l[kBlk][kChan];
+    __shared__ __attribute__((aligned(16))) float B_l[kBlk][16];
+    __shared__ __attribute__((aligned(16))) float C_l[kBlk][16];
+    // [token][wave][row][quad lane][dB 4 | dC 4]: sums over the row's four channels
+    __shared__ __attribute__((aligned(16))) float red_l[kBlk][4][4][4][8];
+
+    const int tid = threadIdx.x;
+    const int q = tid & 3;
+    const int cl = tid >> 2;            // channel within the block
+    const int wave = tid >> 6;
+    const int row = (tid >> 4) & 3;     // 16-lane row within the wave
+    const int lane_in_row = tid & 15;
+    const int cb = blockIdx.x, i = blockIdx.y;
+    const int c_raw = cb * kChan + cl;
+    const bool active = c_raw < p.d_inner;
+    const int c = active ? c_raw : p.d_inner - 1;
+    const int64_t seq = (int64_t)i * p.L * p.d_inner;
+    const int rid = p.ids[i];
+    const bool bad = (rid < 0) | (rid >= p.R);  // unknown initial state: d_x, d_dt are NaN
+
+    float a2[4], An[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int n = 4 * q + s;
+        An[s] = n < p.N ? p.A[(int64_t)c * p.N + n] : 0.0f;
+        a2[s] = An[s] * kLog2e;
+    }
+    const float Dc = p.has_D ? p.D[c] : 0.0f;
+    float g[4], dA_acc[4] = {0.f, 0.f, 0.f, 0.f};
+    float dD_acc = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int n = 4 * q + s;
+        g[s] = n < p.N ? p.dstate[((int64_t)i * p.d_inner + c) * p.N + n] : 0.0f;
+    }
+
+    const int n_blk = (p.L + kBlk - 1) / kBlk;
+    for (int b = n_blk - 1; b >= 0; --b) {
+        const int t0 = b * kBlk;
+        const int nk = min(kBlk, p.L - t0);
+        // stage the block's inputs (zeros past the end of the sequence)
+        for (int e = tid; e < kBlk * kChan; e += kThreads) {
+            const int k = e / kChan, ch = e % kChan;
+            const int cc = cb * kChan + ch;
+            const bool ok = (k < nk) && (cc < p.d_inner);
+            const int64_t idx = seq + (int64_t)(t0 + k) * p.d_inner + cc;
+            x_l[k][ch] = ok ? ldv<T>(p.x, idx) : 0.0f;
+            dt_l[k][ch] = ok ? ldv<T>(p.dt, idx) : 0.0f;
+            dy_l[k][ch] = ok ? ldv<T>(p.dy, idx) : 0.0f;
+        }
+        for (int e = tid; e < kBlk * 16; e += kThreads) {
+            const int k = e / 16, n = e % 16;
+            const bool ok = (k < nk) && (n < p.N);
+            const int64_t idx = ((int64_t)i * p.L + t0 + k) * p.N + n;
+            B_l[k][n] = ok ? ldv<T>(p.B, idx) : 0.0f;
+            C_l[k][n] = ok ? ldv<T>(p.C, idx) : 0.0f;
+        }
+        float h0[4];
+        {
+            const float4 ck = *reinterpret_cast<const float4*>(
+                p.ckpt + (((int64_t)b * p.S + i) * p.d_inner + c) * 16 + 4 * q);
+            h0[0] = ck.x; h0[1] = ck.y; h0[2] = ck.z; h0[3] = ck.w;
+        }
+        __syncthreads();
+
+        // recompute the block: decays a[k][s] and states h[k][s] (= h_{t0+k})
+        float a[kBlk][4], h[kBlk][4];
+#pragma unroll
+        for (int k = 0; k < kBlk; ++k) {
+            float dk = dt_l[k][cl];
+            if constexpr (SOFTPLUS) dk = k < nk ? softplus(dk) : 0.0f;
+            const float bk = dk * x_l[k][cl];
+            const float4 Bv = *reinterpret_cast<const float4*>(&B_l[k][4 * q]);
+            const float Bs[4] = {Bv.x, Bv.y, Bv.z, Bv.w};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                a[k][s] = fast_exp2(dk * a2[s]);
+                h[k][s] = fmaf(a[k][s], k == 0 ? h0[s] : h[k - 1][s], bk * Bs[s]);
+            }
+        }
+
+        // adjoint over the block, last token first
+#pragma unroll
+        for (int k = kBlk - 1; k >= 0; --k) {
+            const float dyk = dy_l[k][cl];
+            const float draw = dt_l[k][cl];
+            const float dk = SOFTPLUS ? (k < nk ? softplus(draw) : 0.0f) : draw;
+            const float uk = x_l[k][cl];
+            const float dtuk = dk * uk;
+            const float4 Bv = *reinterpret_cast<const float4*>(&B_l[k][4 * q]);
+            const float4 Cv = *reinterpret_cast<const float4*>(&C_l[k][4 * q]);
+            const float Bs[4] = {Bv.x, Bv.y, Bv.z, Bv.w};
+            const float Cs[4] = {Cv.x, Cv.y, Cv.z, Cv.w};
+            float S1 = 0.0f, S2 = 0.0f, dBp[4], dCp[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                g[s] = fmaf(Cs[s], dyk, g[s]);
+                dCp[s] = dyk * h[k][s];
+                S1 = fmaf(g[s], Bs[s], S1);
+                const float ga = g[s] * a[k][s];
+                const float qv = ga * (k == 0 ? h0[s] : h[k - 1][s]);
+                S2 = fmaf(qv, An[s], S2);
+                dA_acc[s] = fmaf(qv, dk, dA_acc[s]);
+                dBp[s] = g[s] * dtuk;
+                g[s] = ga;
+            }
+            S1 = quad_sum(S1);
+            S2 = quad_sum(S2);
+            if (q == 0 && active && k < nk) {
+                const int64_t idx = seq + (int64_t)(t0 + k) * p.d_inner + c;
+                float ddt = fmaf(uk, S1, S2);
+                if constexpr (SOFTPLUS) ddt *= 1.0f / (1.0f + expf(-draw));
+                p.d_x[idx] = bad ? __builtin_nanf("") : fmaf(Dc, dyk, dk * S1);
+                p.d_dt[idx] = bad ? __builtin_nanf("") : ddt;
+                dD_acc = fmaf(dyk, uk, dD_acc);
+            }
+            // sum the four channels of this 16-lane row (lanes 4j + q)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                float vb = active ? dBp[s] : 0.0f, vc = active ? dCp[s] : 0.0f;
+                vb = row_shr_add<4>(vb);
+                vb = row_shr_add<8>(vb);
+                vc = row_shr_add<4>(vc);
+                vc = row_shr_add<8>(vc);
+                dBp[s] = vb;
+                dCp[s] = vc;
+            }
+            if (lane_in_row >= 12) {
+                float* dst = &red_l[k][wave][row][q][0];
+                *reinterpret_cast<float4*>(dst) = make_float4(dBp[0], dBp[1], dBp[2], dBp[3]);
+                *reinterpret_cast<float4*>(dst + 4) = make_float4(dCp[0], dCp[1], dCp[2], dCp[3]);
+            }
+        }
+        __syncthreads();
+        // the block's channel sums: 16 tokens x (16 dB + 16 dC), 16 terms each, fixed order
+        for (int e = tid; e < kBlk * 32; e += kThreads) {
+            const int k = e / 32, m = e % 32;
+            if (k >= nk) continue;
+            const int which = m >> 4, n = m & 15, qq = n >> 2, s = n & 3;
+            float acc = 0.0f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc += red_l[k][w][r][qq][which * 4 + s];
+            p.dbc_part[(((int64_t)cb * p.S + i) * p.L + t0 + k) * 32 + m] = acc;
+        }
+        __syncthreads();
+    }
+    if (active) {
+        const int64_t row_i = ((int64_t)i * p.d_inner + c) * 16 + 4 * q;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            p.ds_part[row_i + s] = g[s];
+            p.dA_part[row_i + s] = dA_acc[s];
+        }
+    }
+    // dD: lane q == 0 of each quad holds its channel's sum
+    if (active && q == 0) p.dD_part[(int64_t)i * p.d_inner + c] = dD_acc;
+}
+
+// d_B, d_C: sum of the channel-block partials in block order.
+__global__ __launch_bounds__(256) void bwd_reduce_bc(BwdKP p, float* d_B, float* d_C) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t tokens = (int64_t)p.S * p.L;
+    if (e >= tokens * 32) return;
+    const int64_t tok = e >> 5;
+    const int m = (int)(e & 31), n = m & 15;
+    if (n >= p.N) return;
+    float acc = 0.0f;
+    for (int cb = 0; cb < p.n_cb; ++cb) acc += p.dbc_part[((int64_t)cb * tokens + tok) * 32 + m];
+    (m < 16 ? d_B : d_C)[tok * p.N + n] = acc;
+}
+
+// d_A, d_D: sums over sequences in sequence order; d_s: dh_0 of every
+// sequence whose id is this row, in sequence order (zero if none).
+// ds_src rows have stride ds_stride floats (16 for the partials, d_state for
+// dstate itself when there are no tokens).
+__global__ __launch_bounds__(256) void bwd_reduce_params(BwdKP p, const float* ds_src, int ds_stride,
+                                                         float* d_A, float* d_D, float* d_s) {
+    const int64_t per_row = (int64_t)p.d_inner * p.N;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < per_row; e += stride) {
+        const int64_t c = e / p.N;
+        const int n = (int)(e % p.N);
+        float acc = 0.0f;
+        if (p.dA_part)
+            for (int i = 0; i < p.S; ++i) acc += p.dA_part[((int64_t)i * p.d_inner + c) * 16 + n];
+        d_A[e] = acc;
+        if (d_D && n == 0) {
+            float dd = 0.0f;
+            if (p.dD_part)
+                for (int i = 0; i < p.S; ++i) dd += p.dD_part[(int64_t)i * p.d_inner + c];
+            d_D[c] = dd;
+        }
+    }
+    const int64_t ds_total = (int64_t)p.R * per_row;
+    for (int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x; f < ds_total; f += stride) {
+        const int64_t r = f / per_row, rem = f % per_row;
+        const int64_t c = rem / p.N;
+        const int n = (int)(rem % p.N);
+        float acc = 0.0f;
+        for (int i = 0; i < p.S; ++i)
+            if (p.ids[i] == r) acc += ds_src[((int64_t)i * p.d_inner + c) * ds_stride + n];
+        d_s[f] = acc;
+    }
+}
+
+size_t blocks_of(const Shape& sh) { return (size_t)((sh.L + kBlk - 1) / kBlk); }
+
+struct BwdWs {
+    float *ckpt, *dbc, *dA, *dD, *ds;
+    size_t total;
+};
+
+BwdWs carve(const Shape& sh, char* base) {
+    const size_t rows = (size_t)sh.S * sh.d_inner();
+    const size_t n_cb = (size_t)((sh.d_inner() + kChan - 1) / kChan);
+    size_t off = 0;
+    BwdWs w;
+    auto take = [&](size_t bytes) { char* ptr = base ? base + off : nullptr; off += align_up(bytes, 256); return reinterpret_cast<float*>(ptr); };
+    w.ckpt = take(blocks_of(sh) * rows * 16 * 4);
+    w.dbc = take(n_cb * (size_t)sh.S * sh.L * 32 * 4);
+    w.dA = take(rows * 16 * 4);
+    w.dD = take(rows * 4);
+    w.ds = take(rows * 16 * 4);
+    w.total = off;
+    return w;
+}
+
+}  // namespace
+
+bool bwd_supported(const Shape& sh) {
+    return sh.a_per_state && sh.P == 1 && sh.N <= 16 && sh.G == 1 && sh.K == 0;
+}
+
+size_t bwd_workspace_bytes(const Shape& sh) {
+    if (!bwd_supported(sh) || sh.S == 0 || sh.L == 0) return 0;
+    return carve(sh, nullptr).total;
+}
+
+int launch_quad_ckpt(const BwdArgs& a, float* ckpt, hipStream_t stream);
+
+int launch_scan_bwd(const BwdArgs& a, hipStream_t stream) {
+    const Shape& sh = a.sh;
+    if (!bwd_supported(sh)) return SSM_ERR_UNSUPPORTED;
+    const int64_t per_row = sh.d_inner() * sh.N;
+    BwdKP kp = {};
+    kp.A = a.A; kp.D = a.D; kp.ids = a.ids; kp.x = a.x; kp.dt = a.dt; kp.B = a.B; kp.C = a.C;
+    kp.dy = a.dy; kp.dstate = a.dstate; kp.d_x = a.d_x; kp.d_dt = a.d_dt;
+    kp.L = (int)sh.L; kp.d_inner = (int)sh.d_inner(); kp.N = (int)sh.N; kp.R = (int)sh.R;
+    kp.S = (int)sh.S; kp.n_cb = (int)((sh.d_inner() + kChan - 1) / kChan);
+    kp.has_D = (sh.flags & SSM_HAS_D) ? 1 : 0;
+    kp.softplus = (sh.flags & SSM_DT_SOFTPLUS) ? 1 : 0;
+    const int64_t par = sh.R * per_row > per_row ? sh.R * per_row : per_row;
+    const unsigned par_blocks = (unsigned)((par + 255) / 256 > 65535 ? 65535 : (par + 255) / 256);
+    if (sh.S == 0 || sh.L == 0) {
+        // no tokens: dh_0 is dstate itself; dA and dD are zero (no partials)
+        kp.dA_part = nullptr;
+        kp.dD_part = nullptr;
+        hipLaunchKernelGGL(bwd_reduce_params, dim3(par_blocks), dim3(256), 0, stream, kp,
+                           a.dstate, (int)sh.N, a.d_A, a.d_D, a.d_s);
+        return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+    }
+    BwdWs w = carve(sh, a.ws);
+    if (w.total > a.ws_bytes) return SSM_ERR_WORKSPACE;
+    kp.ckpt = w.ckpt; kp.dbc_part = w.dbc; kp.dA_part = w.dA; kp.dD_part = w.dD; kp.ds_part = w.ds;
+    int rc = launch_quad_ckpt(a, w.ckpt, stream);
+    if (rc) return rc;
+    const dim3 grid((unsigned)kp.n_cb, (unsigned)sh.S);
+    const bool bf = sh.io == SSM_BF16;
+    if (bf) {
+        if (kp.softplus) hipLaunchKernelGGL((bwd_rev<bf16_t, true>), grid, dim3(kThreads), 0, stream, kp);
+        else hipLaunchKernelGGL((bwd_rev<bf16_t, false>), grid, dim3(kThreads), 0, stream, kp);
+    } else {
+        if (kp.softplus) hipLaunchKernelGGL((bwd_rev<float, true>), grid, dim3(kThreads), 0, stream, kp);
+        else hipLaunchKernelGGL((bwd_rev<float, false>), grid, dim3(kThreads), 0, stream, kp);
+    }
+    const int64_t tok32 = sh.S * sh.L * 32;
+    hipLaunchKernelGGL(bwd_reduce_bc, dim3((unsigned)((tok32 + 255) / 256)), dim3(256), 0, stream, kp,
+                       a.d_B, a.d_C);
+    hipLaunchKernelGGL(bwd_reduce_params, dim3(par_blocks), dim3(256), 0, stream, kp,
+                       (const float*)w.ds, 16, a.d_A, a.d_D, a.d_s);
+    return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
 
 }  // namespace ssm

@@ -82,7 +82,8 @@ template <typename T>
 __device__ __forceinline__ float ld(const T* p) { return to_f32(*p); }
 
 // The scan over tokens [t_begin, t_end) of one chunk.  MODE 0: end state
-// only (kernel 1); MODE 1: y, and the final state if this is the last chunk.
+// only (kernel 1); MODE 1: y, and the final state if this is the last chunk;
+// MODE 2: the state entering every 16-token block, for the backward pass.
 template <typename T, int K, int MODE>
 __device__ __forceinline__ void quad_chunk(const QuadKP& p, int i, int c_raw, int q,
                                            int t_begin, int t_end, float (&h)[4],
@@ -143,6 +144,12 @@ __device__ __forceinline__ void quad_chunk(const QuadKP& p, int i, int c_raw, in
         const int t0 = t_begin + 4 * g;
         const int tt0 = (4 * g) & (kTile - 1);
         const int buf = ((4 * g) / kTile) & 1;
+        if constexpr (MODE == 2) {  // state entering each 16-token block
+            if (((t0 - t_begin) & 15) == 0 && active) {
+                float* ck = p.agg + ((((int64_t)(t0 >> 4) * p.S + i) * p.d_inner + c) * 16 + 4 * q);
+                *reinterpret_cast<float4*>(ck) = make_float4(h[0], h[1], h[2], h[3]);
+            }
+        }
         if (tt0 == 0 && t0 + kTile < t_end) stage(buf ^ 1, t0 + kTile);  // next tile
         const bool own_ok = (t0 + q) < t_end;
         float xc = x_nx, dtv = dt_nx;
@@ -323,6 +330,12 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int cb, int q
     // One group of four tokens; FULL: every token of the group is < t_end.
     auto group = [&](int g, bool full_tile, int tb) {
         const int tt = 4 * g + q;  // owned row of this tile
+        if constexpr (MODE == 2) {  // state entering each 16-token block
+            if (((tb + 4 * g - t_begin) & 15) == 0) {
+                float* ck = p.agg + ((((int64_t)((tb + 4 * g) >> 4) * p.S + i) * p.d_inner + c) * 16 + 4 * q);
+                *reinterpret_cast<float4*>(ck) = make_float4(h[0], h[1], h[2], h[3]);
+            }
+        }
         const bool own_ok = full_tile || (tb + tt < t_end);
         const float xc = to_f32(*reinterpret_cast<const T*>(x_l + tt * XS + cl * ES));
         float dtv = to_f32(*reinterpret_cast<const T*>(dt_l + tt * XS + cl * ES));
@@ -530,6 +543,34 @@ __global__ __launch_bounds__(kThreads) void quad_out(QuadKP p) {
     }
 }
 
+// Forward scan that stores the state entering every 16-token block to
+// p.agg ([n_blocks][S][d_inner][16]); the backward pass recomputes each block
+// from it.
+template <typename T, bool TILED, bool SOFTPLUS>
+__global__ __launch_bounds__(kThreads) void quad_ckpt(QuadKP p) {
+    const int q = threadIdx.x & 3;
+    const int c_raw = blockIdx.x * kChanPerBlock + (threadIdx.x >> 2);
+    const bool active = c_raw < p.d_inner;
+    const int c = active ? c_raw : p.d_inner - 1;
+    const int i = blockIdx.y;
+    const int r = p.ids[i];
+    const bool bad = (r < 0) | (r >= p.R);
+    if (bad && threadIdx.x == 0 && blockIdx.x == 0) atomicOr(p.err, (uint32_t)SSM_DEVERR_IDS);
+    float h[4], a2[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int n = 4 * q + s;
+        a2[s] = n < p.N ? p.A[(int64_t)c * p.N + n] * kLog2e : 0.0f;
+        h[s] = n < p.N ? (bad ? __builtin_nanf("") : p.s[((int64_t)r * p.d_inner + c) * p.N + n])
+                       : 0.0f;
+    }
+    float dt_acc = 0.0f;
+    if constexpr (TILED)
+        quad_tiled<T, 0, 2, SOFTPLUS>(p, i, blockIdx.x, q, threadIdx.x >> 2, 0, p.L, h, a2, dt_acc, bad);
+    else
+        quad_chunk<T, 0, 2>(p, i, c_raw, q, 0, p.L, h, a2, dt_acc, active, bad);
+}
+
 template <typename T, int K, bool TILED, bool SOFTPLUS>
 int launch_quad_t(const QuadKP& kp, hipStream_t st) {
     const dim3 block(kThreads);
@@ -579,6 +620,38 @@ size_t quad_workspace_bytes(const Shape& sh) {
     const int64_t n = (sh.L + len - 1) / len;
     const int64_t rows = sh.S * sh.d_inner();
     return (size_t)((n - 1) * rows * 16 + (n - 1) * rows + n * rows * 16) * 4 + 3 * 256;
+}
+
+int launch_quad_ckpt(const BwdArgs& a, float* ckpt, hipStream_t stream) {
+    const Shape& sh = a.sh;
+    QuadKP kp = {};
+    kp.s = a.s; kp.x = a.x; kp.dt = a.dt; kp.A = a.A; kp.B = a.B; kp.C = a.C; kp.D = nullptr;
+    kp.ids = a.ids; kp.err = a.err; kp.agg = ckpt;
+    kp.L = (int)sh.L; kp.d_inner = (int)sh.d_inner(); kp.N = (int)sh.N; kp.R = (int)sh.R;
+    kp.S = (int)sh.S;
+    kp.has_D = 0;
+    kp.softplus = (sh.flags & SSM_DT_SOFTPLUS) ? 1 : 0;
+    auto al16 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; };
+    // the tiled path also stages y; the checkpoint pass writes none, so only inputs matter
+    kp.tiled = (sh.N == 16 && sh.d_inner() % 64 == 0 && al16(a.x) && al16(a.dt) && al16(a.B) &&
+                al16(a.C)) ? 1 : 0;
+    kp.chunk_len = (int)sh.L;
+    kp.n_chunks = 1;
+    const dim3 grid((unsigned)((kp.d_inner + kChanPerBlock - 1) / kChanPerBlock), (unsigned)sh.S);
+    const bool bf = sh.io == SSM_BF16;
+    if (kp.tiled) {
+        if (bf) {
+            if (kp.softplus) hipLaunchKernelGGL((quad_ckpt<bf16_t, true, true>), grid, dim3(kThreads), 0, stream, kp);
+            else hipLaunchKernelGGL((quad_ckpt<bf16_t, true, false>), grid, dim3(kThreads), 0, stream, kp);
+        } else {
+            if (kp.softplus) hipLaunchKernelGGL((quad_ckpt<float, true, true>), grid, dim3(kThreads), 0, stream, kp);
+            else hipLaunchKernelGGL((quad_ckpt<float, true, false>), grid, dim3(kThreads), 0, stream, kp);
+        }
+    } else {
+        if (bf) hipLaunchKernelGGL((quad_ckpt<bf16_t, false, false>), grid, dim3(kThreads), 0, stream, kp);
+        else hipLaunchKernelGGL((quad_ckpt<float, false, false>), grid, dim3(kThreads), 0, stream, kp);
+    }
+    return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
 int launch_quad_fwd(const FwdArgs& a, hipStream_t stream) {

@@ -77,6 +77,9 @@ bool quad_supported(const Shape& sh);
 size_t quad_workspace_bytes(const Shape& sh);
 int launch_quad_fwd(const FwdArgs& a, hipStream_t stream);
 
+// Backward: Mamba-1 form, d_state <= 16, one group, no fused conv.
+bool bwd_supported(const Shape& sh);
+
 // Returns SSM_OK, SSM_ERR_UNSUPPORTED, or SSM_ERR_HIP.
 int launch_scan_fwd(const FwdArgs& a, hipStream_t stream);
 int launch_scan_bwd(const BwdArgs& a, hipStream_t stream);

@@ -176,3 +176,15 @@ def test_conv_argument_checks():
     with pytest.raises(ssm.SsmError) as e:
         ssm.ssm_conv_fwd(256, 256, 256, 1, 4, 2, 3, 5, 0, stream=0)
     assert e.value.status == ssm.SSM_ERR_DTYPE
+
+
+@pytest.mark.parametrize("kw", [dict(a_per_state=False, head_dim=2), dict(d_state=17, head_dim=1),
+                                dict(n_group=3, head_dim=1, a_per_state=True)])
+def test_backward_unsupported_shapes_rejected_before_launch(kw):
+    d = _desc(**kw)
+    ws = ssm.ssm_scan_workspace_bytes(d, 1)
+    assert ws >= 256
+    with pytest.raises(ssm.SsmError) as e:
+        ssm.selective_scan_bwd(d, 256, 256, 256, 256, 256, 256, 256, 256, 256, 256, 256, ws,
+                               stream=0)
+    assert e.value.status == ssm.SSM_ERR_UNSUPPORTED
