@@ -186,6 +186,7 @@ int launch_scan_fwd(const FwdArgs& a, hipStream_t stream) {
     const Shape& sh = a.sh;
     if (sh.S == 0 || sh.H * sh.P == 0) return SSM_OK;
     if (quad_supported(sh)) return launch_quad_fwd(a, stream);
+    if (ssd_supported(sh, a)) return launch_ssd_fwd(a, stream);
     FwdKP kp;
     kp.s = a.s; kp.x = a.x; kp.dt = a.dt; kp.A = a.A; kp.B = a.B; kp.C = a.C; kp.D = a.D;
     kp.ids = a.ids; kp.conv_w = a.conv_w; kp.conv_state = a.conv_state;

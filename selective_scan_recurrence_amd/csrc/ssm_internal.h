@@ -77,6 +77,10 @@ bool quad_supported(const Shape& sh);
 size_t quad_workspace_bytes(const Shape& sh);
 int launch_quad_fwd(const FwdArgs& a, hipStream_t stream);
 
+// Mamba-2 form (scalar A per head), bf16 io, no conv: chunked products on MFMA.
+bool ssd_supported(const Shape& sh, const FwdArgs& a);
+int launch_ssd_fwd(const FwdArgs& a, hipStream_t stream);
+
 // Backward: Mamba-1 form, d_state <= 16, one group, no fused conv.
 bool bwd_supported(const Shape& sh);
 

@@ -72,6 +72,8 @@ def _small(seed, **kw):
     return ssm_inputs.make_problem(**base)
 
 
+_M2 = dict(d_conv=0, a_per_state=False, A_kind="uniform", io="bf16", bc_std=1 / np.sqrt(128))
+
 CASES = {
     "m1_ragged": dict(),
     "m1_bf16": dict(io="bf16"),
@@ -105,6 +107,18 @@ CASES = {
                          A_kind="uniform", io="bf16", bc_std=1 / np.sqrt(128)),
     "m2_N256_groups": dict(n_head=4, head_dim=4, d_state=256, n_group=2, d_conv=0,
                            a_per_state=False, A_kind="uniform", bc_std=1 / 16),
+    # bf16, head_dim 32/64, d_state 64/128, no conv: the chunked MFMA (SSD) path
+    "ssd_P64_N128_ragged_perm": dict(n_head=3, head_dim=64, d_state=128, n_tokens=200,
+                                     **_M2, n_state_rows=5, ids="perm"),
+    "ssd_P32_N64_groups_L64": dict(n_head=4, head_dim=32, d_state=64, n_group=2, n_tokens=64,
+                                   **_M2),
+    "ssd_P64_N64_L1": dict(n_head=2, head_dim=64, d_state=64, n_tokens=1, **_M2),
+    "ssd_P32_N128_softplus_noD": dict(n_head=3, head_dim=32, d_state=128, n_tokens=130, **_M2,
+                                      dt_softplus=True, dt_shift=0.0, has_D=False),
+    "ssd_P64_N128_long_noD": dict(n_seqs=2, n_head=2, head_dim=64, d_state=128, n_tokens=1000,
+                                  **_M2, has_D=False, h0_std=0.0),
+    "ssd_P64_N128_dup_ids": dict(n_head=2, head_dim=64, d_state=128, n_tokens=65, **_M2,
+                                 n_state_rows=2, ids=np.array([1, 1, 0], np.int32)),
     "m2_headdim_per_state_A": dict(n_head=6, head_dim=3, d_state=8, d_conv=0,
                                    A_kind="uniform", n_group=3),
 }
@@ -153,6 +167,31 @@ def test_bad_id_gives_nan_rows_and_sets_flag(gpu):
     y_o, st_o, _ = oracle.problem_fwd(p)
     assert_close(y[[0, 2]], y_o, "f32", "good rows y")
     assert_close(st[[0, 2]], st_o, "f32", "good rows state")
+
+
+def test_ssd_dt_zero_and_bad_id(gpu):
+    """Chunked MFMA path: dt = 0 leaves the gathered state bit for bit; an id
+    out of range gives NaN rows for its sequence and sets the flag."""
+    p = _small(14, n_head=2, head_dim=64, d_state=128, n_tokens=90, n_state_rows=4,
+               ids=np.array([3, 0, 3], np.int32), **_M2)
+    p.t["dt"] = ssm_inputs._const(np.zeros_like(p.value("dt")), p.io)
+    d, r = run_fwd(p)
+    np.testing.assert_array_equal(host(r.state), p.value("s")[p.ids].astype(np.float64))
+    q = _small(15, n_head=2, head_dim=32, d_state=64, n_tokens=70, n_state_rows=3,
+               ids=np.array([1, 7, 0], np.int32), **_M2)
+    t = device_inputs(q)
+    ws = ops.workspace(desc_of(q), False)
+    d, r = run_fwd(q, t=t, ws=ws)
+    y, st = host(r.y), host(r.state)
+    assert np.isnan(y[1]).all() and np.isnan(st[1]).all()
+    assert ssm.ssm_get_device_error(ws) & ssm.SSM_DEVERR_IDS
+    q.ids = np.array([1, 0], np.int32)
+    q.n_seqs = 2
+    for k in ("x", "dt", "B", "C"):
+        q.t[k] = ssm_inputs.Stored(q.t[k].bits[[0, 2]], q.t[k].value[[0, 2]], q.t[k].dtype)
+    y_o, st_o, _ = oracle.problem_fwd(q)
+    assert_close(y[[0, 2]], y_o, "bf16", "good rows y")
+    assert_close(st[[0, 2]], st_o, "bf16", "good rows state")
 
 
 def test_output_canaries_untouched(gpu):
