@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 VALU_PEAK_T = 78.6               # 157.3 TFLOP/s fp32 vector = 78.6 T lane-FMA/s
+MFMA_BF16_PEAK_T = 2500.0        # dense bf16 MFMA, TFLOP/s
 TRANS_COST = 4                   # v_exp_f32 / v_rcp_f32 issue at 1/4 of the VALU rate
 MALL_BYTES = 256 << 20
 METRIC = "selective-scan effective HBM GB/s (% of peak) + channel-tokens/s, 1 GPU"
@@ -69,16 +70,22 @@ def algorithmic_bytes(p, backward=False) -> int:
     return x + dt + bc + a + d + state + ids + dy + state + grads
 
 
-def valu_slots_per_channel_token(p) -> float:
+def valu_slots_per_channel_token(p, backward=False) -> float:
     """Issue slots the method needs per (sequence, channel, token), counting a
     transcendental (exp, reciprocal) as TRANS_COST slots.
-    Per state, Mamba-1 (A per state): decay exp(dt*A) (mul + exp), input term
-    (mul), state update (fma), output term (fma).  Mamba-2 (A per head):
-    input term, state update, output term; the decay is one mul + exp per
-    (token, head), shared by the head's channels.
-    Per channel-token: dt*u (mul), D*u (fma); with the conv, its taps (fma
-    each) and SiLU (mul, exp, add, rcp, mul)."""
+    Forward, per state, Mamba-1 (A per state): decay exp(dt*A) (mul + exp),
+    input term (mul), state update (fma), output term (fma).  Mamba-2 (A per
+    head): input term, state update, output term; the decay is one mul + exp
+    per (token, head), shared by the head's channels.  Per channel-token:
+    dt*u (mul), D*u (fma); with the conv, its taps (fma each) and SiLU (mul,
+    exp, add, rcp, mul).
+    Backward (Mamba-1), per state: the recomputed decay and state (mul, exp,
+    fma), the adjoint step (fma for C dy, mul for the decay), its products
+    for du, ddt, dA, dB, dC (mul/fma each: 6), and the channel sums of dB
+    and dC (add each); per channel-token: dt*u, du, ddt, dD (4)."""
     N = p.d_state
+    if backward:
+        return float(N * (TRANS_COST + 12) + 4)
     if p.a_per_state:
         total = N * (4 + TRANS_COST)
     else:
@@ -87,6 +94,25 @@ def valu_slots_per_channel_token(p) -> float:
     if p.d_conv:
         total += p.d_conv + 3 + 2 * TRANS_COST
     return float(total)
+
+
+SSD_Q = 64  # tokens per chunk of the chunked (MFMA) Mamba-2 path
+
+
+def ssd_mfma_flops(p) -> int:
+    """Dense-product flops of the chunked Mamba-2 form, per (sequence, head,
+    64-token chunk): C B^T and M X on the causal triangle (Q(Q+1)/2 token
+    pairs), the carried-state product C h^T and the state update X^T B."""
+    q = SSD_Q
+    chunks = -(-p.n_tokens // q)
+    tri = q * (q + 1) // 2
+    per = 2 * tri * p.d_state + 2 * tri * p.head_dim + 4 * q * p.d_state * p.head_dim
+    return int(p.n_seqs * p.n_head * chunks * per)
+
+
+def uses_ssd(p) -> bool:
+    return (not p.a_per_state and p.io == "bf16" and p.d_conv == 0 and p.head_dim in (32, 64)
+            and p.d_state in (64, 128))
 
 
 def _dev(stored, device):
@@ -138,23 +164,59 @@ def cpu_baseline(name, p):
         heads = np.arange(p.n_head)
         sample = "full workload"
     else:
-        n = 1024 if name == "C2" else 8
+        n = {"C2": 1024, "C4": 512}.get(name, 8)
         heads = np.arange(n)
         sample = f"first {n} of {p.n_head} {'channels' if p.head_dim == 1 else 'heads'}, all sequences and tokens"
     args = (v("s")[:, heads], v("x")[:, :, heads], v("dt")[:, :, heads], v("A")[heads], v("B"),
             v("C"), v("D")[heads] if p.has_D else None, p.ids)
-    kw = dict(conv_w=v("conv_w")[heads] if p.d_conv else None,
-              grp_of_head=oracle.group_of_head(p.n_head, p.n_group)[heads], n_threads=threads)
+    grp = oracle.group_of_head(p.n_head, p.n_group)[heads]
+    backward = name == "C4"
     t0 = time.perf_counter()
-    oracle.scan_fwd(*args, **kw)
+    if backward:
+        oracle.scan_bwd(*args, v("dy")[:, :, heads], v("dstate")[:, heads], grp_of_head=grp,
+                        n_threads=threads)
+    else:
+        oracle.scan_fwd(*args, conv_w=v("conv_w")[heads] if p.d_conv else None, grp_of_head=grp,
+                        n_threads=threads)
     sec = time.perf_counter() - t0
     frac = len(heads) / p.n_head
-    gbs = algorithmic_bytes(p) * frac / sec / 1e9
+    gbs = algorithmic_bytes(p, backward) * frac / sec / 1e9
     ch_tok = p.n_seqs * p.n_tokens * len(heads) * p.head_dim / sec
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": oracle.threads_used(len(heads), threads),
             "kind": "oracle", "sample": sample, "seconds": round(sec, 3),
             "channel_tokens_per_s": round(ch_tok, 1), "cpu": platform.processor() or platform.machine(),
             "nproc": os.cpu_count()}
+
+
+def parity_gate_bwd(p, g):
+    """Backward: every token of sampled channels against the oracle, per-element
+    gradients with rtol 1e-4 and an absolute floor of 1e-5 x rms, channel and
+    token sums with a floor of 1e-4 x rms."""
+    import torch
+    import oracle
+    rng = np.random.default_rng(0xB1)
+    heads = np.unique(np.concatenate([[0, p.n_head - 1], rng.choice(p.n_head, 8, replace=False)]))
+    v = p.value
+    o = oracle.scan_bwd(v("s")[:, heads], v("x")[:, :, heads], v("dt")[:, :, heads], v("A")[heads],
+                        v("B"), v("C"), v("D")[heads] if p.has_D else None, p.ids,
+                        v("dy")[:, :, heads], v("dstate")[:, heads],
+                        grp_of_head=np.zeros(len(heads), np.int64))
+    hs = torch.as_tensor(heads, device=g["d_x"].device)
+    picks = {"d_x": (g["d_x"].index_select(2, hs), 1e-5), "d_dt": (g["d_dt"].index_select(2, hs), 1e-5),
+             "d_A": (g["d_A"].index_select(0, hs), 1e-4), "d_s": (g["d_s"].index_select(1, hs), 1e-4)}
+    if p.has_D:
+        picks["d_D"] = (g["d_D"].index_select(0, hs), 1e-4)
+    checked = 0
+    for k, (got_t, floor) in picks.items():
+        got = got_t.double().cpu().numpy()
+        want = o[k]
+        rms = float(np.sqrt(np.mean(want ** 2))) if want.size else 0.0
+        bad = ~(np.abs(got - want) <= floor * rms + 1e-4 * np.abs(want))
+        if bad.any():
+            raise SystemExit(f"parity gate failed on C4 {k}: {int(bad.sum())} elements outside")
+        checked += want.size
+    return {"checked_elements": int(checked), "rtol": 1e-4, "atol": "1e-5 x rms (per element), "
+            "1e-4 x rms (sums)"}
 
 
 def main():
@@ -168,7 +230,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for "
+        print(f"bench.py measures one GPU: there is no multi-GPU path (asked for "
               f"--gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
 
@@ -180,36 +242,44 @@ def main():
     ssm.load()
     dev = torch.device("cuda:0")
     name = args.config
-    if name == "C4":
-        raise SystemExit("the backward bench is not built yet")
+    backward = name == "C4"
     p = ssm_inputs.config(name)
     desc = ops.make_desc(n_seqs=p.n_seqs, n_tokens=p.n_tokens, n_head=p.n_head,
                          head_dim=p.head_dim, d_state=p.d_state, n_group=p.n_group,
                          n_state_rows=p.n_state_rows, a_per_state=p.a_per_state,
                          d_conv=p.d_conv, chunk=p.chunk if args.chunk is None else args.chunk,
                          io=p.io, has_D=p.has_D, dt_softplus=p.dt_softplus)
-    step_bytes = algorithmic_bytes(p)
+    step_bytes = algorithmic_bytes(p, backward)
     copies = max(2, math.ceil(3 * MALL_BYTES / step_bytes))
     sets = []
     for _ in range(copies):
         t = {k: _dev(s, dev) for k, s in p.t.items()}
         t["ids"] = torch.from_numpy(p.ids).to(dev)
-        t["out"] = torch.empty(ssm.ssm_scan_out_bytes(desc), dtype=torch.uint8, device=dev)
-        t["ws"] = ops.workspace(desc, False, dev)
+        t["ws"] = ops.workspace(desc, backward, dev)
+        if backward:
+            t["dout"] = torch.cat([t.pop("dy").reshape(-1).view(torch.uint8),
+                                   t.pop("dstate").reshape(-1).view(torch.uint8)])
+            t["out"] = torch.empty(ssm.ssm_scan_dgrad_layout(desc)[0], dtype=torch.uint8, device=dev)
+        else:
+            t["out"] = torch.empty(ssm.ssm_scan_out_bytes(desc), dtype=torch.uint8, device=dev)
         sets.append(t)
 
     def step(t):
+        if backward:
+            return ops.scan_bwd(desc, t["s"], t["x"], t["dt"], t["A"], t["B"], t["C"], t.get("D"),
+                                t["ids"], t["dout"], ws=t["ws"], dgrad=t["out"])
         return ops.scan_fwd(desc, t["s"], t["x"], t["dt"], t["A"], t["B"], t["C"], t.get("D"),
                             t["ids"], conv_w=t.get("conv_w"), conv_state=t.get("conv_state"),
                             ws=t["ws"], out=t["out"])
 
     res = step(sets[0])
     torch.cuda.synchronize()
-    parity = parity_gate(name, p, res)
+    parity = parity_gate_bwd(p, res[1]) if backward else parity_gate(name, p, res)
 
     for k in range(args.warmup):
         step(sets[k % copies])
     torch.cuda.synchronize()
+    # events on the stream the library launches on (torch's current stream)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     t0 = time.perf_counter()
@@ -224,22 +294,37 @@ def main():
     ms_per_step = total_ms / args.steps
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     ch_tok = p.n_seqs * p.n_tokens * p.n_head * p.head_dim
-    avg_launch_ms = float(launch_ms.mean())
-    slots = valu_slots_per_channel_token(p) * ch_tok
-    alu_t = slots / (avg_launch_ms * 1e-3) / 1e12
-    hbm_gbs = step_bytes / (avg_launch_ms * 1e-3) / 1e9
-    alu_floor_us = slots / (VALU_PEAK_T * 1e12) * 1e6
-    hbm_floor_us = step_bytes / (HBM_PEAK_GBS * 1e9) * 1e6
-    if alu_floor_us >= hbm_floor_us:
-        roof = {"bound": "alu", "achieved": round(alu_t, 3), "peak": VALU_PEAK_T,
-                "unit": "T VALU-slots/s", "frac": round(alu_t / VALU_PEAK_T, 4)}
+    avg_s = float(launch_ms.mean()) * 1e-3
+    floors = {"hbm": step_bytes / (HBM_PEAK_GBS * 1e9)}
+    if uses_ssd(p) and not backward:
+        flops = ssd_mfma_flops(p)
+        floors["mfma"] = flops / (MFMA_BF16_PEAK_T * 1e12)
     else:
-        roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(hbm_gbs / HBM_PEAK_GBS, 4)}
-    roof.update({"traffic": None, "kernel": "selective_scan_fwd (all launches of one call)",
-                 "avg_launch_us": round(avg_launch_ms * 1e3, 3),
-                 "alu_floor_us": round(alu_floor_us, 2), "hbm_floor_us": round(hbm_floor_us, 2),
-                 "algorithmic_bytes": step_bytes, "valu_slots": int(slots)})
+        slots = valu_slots_per_channel_token(p, backward) * ch_tok
+        floors["alu"] = slots / (VALU_PEAK_T * 1e12)
+    bound = max(floors, key=floors.get)
+    if bound == "hbm":
+        ach = step_bytes / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    elif bound == "mfma":
+        ach = flops / avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_T,
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_T, 4)}
+    else:
+        ach = slots / avg_s / 1e12
+        roof = {"bound": "alu", "achieved": round(ach, 3), "peak": VALU_PEAK_T,
+                "unit": "T VALU-slots/s", "frac": round(ach / VALU_PEAK_T, 4)}
+    roof.update({"traffic": None,
+                 "kernel": f"{'selective_scan_bwd' if backward else 'selective_scan_fwd'} "
+                           "(all launches of one call)",
+                 "avg_launch_us": round(avg_s * 1e6, 3),
+                 "floors_us": {k: round(v * 1e6, 2) for k, v in floors.items()},
+                 "algorithmic_bytes": step_bytes})
+    if "alu" in floors:
+        roof["valu_slots"] = int(slots)
+    if "mfma" in floors:
+        roof["mfma_flops"] = int(flops)
     line = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
