@@ -36,4 +36,22 @@ __device__ __forceinline__ float softplus(float v) {
     return v > 20.0f ? v : log1pf(expf(v));
 }
 
+// DPP quad permute: lane q of each group of four lanes reads lane P<q>.
+template <int P0, int P1, int P2, int P3>
+__device__ __forceinline__ float quad_perm(float v) {
+    constexpr int ctrl = P0 | (P1 << 2) | (P2 << 4) | (P3 << 6);
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl,
+                                                                 0xF, 0xF, true));
+}
+template <int K>
+__device__ __forceinline__ float quad_bcast(float v) { return quad_perm<K, K, K, K>(v); }
+// lane q reads lane (q - R) mod 4
+template <int R>
+__device__ __forceinline__ float quad_rot(float v) {
+    return quad_perm<(4 - R) & 3, (5 - R) & 3, (6 - R) & 3, (7 - R) & 3>(v);
+}
+// lane q reads lane q ^ 1 / q ^ 2
+__device__ __forceinline__ float quad_xor1(float v) { return quad_perm<1, 0, 3, 2>(v); }
+__device__ __forceinline__ float quad_xor2(float v) { return quad_perm<2, 3, 0, 1>(v); }
+
 }  // namespace ssm

@@ -185,6 +185,9 @@ size_t fwd_workspace_bytes(const Shape& sh) {
 int launch_scan_fwd(const FwdArgs& a, hipStream_t stream) {
     const Shape& sh = a.sh;
     if (sh.S == 0 || sh.H * sh.P == 0) return SSM_OK;
+    // few (sequence, channel) rows and no explicit chunk: split time inside a workgroup
+    if (sh.chunk == 0 && sh.S * ((sh.d_inner() + 63) / 64) * 4 < 2048 && ts_supported(sh, a))
+        return launch_ts_fwd(a, stream);
     if (quad_supported(sh)) return launch_quad_fwd(a, stream);
     if (ssd_supported(sh, a)) return launch_ssd_fwd(a, stream);
     FwdKP kp;

@@ -60,24 +60,6 @@ struct QuadKP {
     int tiled;       // 1: aligned case, use quad_tiled
 };
 
-// DPP quad permute: lane q of each quad reads lane SEL(q).
-template <int P0, int P1, int P2, int P3>
-__device__ __forceinline__ float quad_perm(float v) {
-    constexpr int ctrl = P0 | (P1 << 2) | (P2 << 4) | (P3 << 6);
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl,
-                                                                 0xF, 0xF, true));
-}
-template <int K>
-__device__ __forceinline__ float quad_bcast(float v) { return quad_perm<K, K, K, K>(v); }
-// lane q reads lane (q - R) mod 4
-template <int R>
-__device__ __forceinline__ float quad_rot(float v) {
-    return quad_perm<(4 - R) & 3, (5 - R) & 3, (6 - R) & 3, (7 - R) & 3>(v);
-}
-// lane q reads lane q ^ 1 / q ^ 2
-__device__ __forceinline__ float quad_xor1(float v) { return quad_perm<1, 0, 3, 2>(v); }
-__device__ __forceinline__ float quad_xor2(float v) { return quad_perm<2, 3, 0, 1>(v); }
-
 template <typename T>
 __device__ __forceinline__ float ld(const T* p) { return to_f32(*p); }
 

@@ -77,6 +77,11 @@ bool quad_supported(const Shape& sh);
 size_t quad_workspace_bytes(const Shape& sh);
 int launch_quad_fwd(const FwdArgs& a, hipStream_t stream);
 
+// Mamba-1 forward, d_state 16, time split across the waves of a workgroup
+// (for batches with too few channels to fill the GPU otherwise).
+bool ts_supported(const Shape& sh, const FwdArgs& a);
+int launch_ts_fwd(const FwdArgs& a, hipStream_t stream);
+
 // Mamba-2 form (scalar A per head), bf16 io, no conv: chunked products on MFMA.
 bool ssd_supported(const Shape& sh, const FwdArgs& a);
 int launch_ssd_fwd(const FwdArgs& a, hipStream_t stream);

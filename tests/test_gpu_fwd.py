@@ -107,6 +107,17 @@ CASES = {
                          A_kind="uniform", io="bf16", bc_std=1 / np.sqrt(128)),
     "m2_N256_groups": dict(n_head=4, head_dim=4, d_state=256, n_group=2, d_conv=0,
                            a_per_state=False, A_kind="uniform", bc_std=1 / 16),
+    # d_inner a multiple of 16, few rows, no chunk given: the time-split path
+    # (16 channels per workgroup, tiles of 128 tokens)
+    "ts_f32_conv4_ragged_perm": dict(n_head=48, n_tokens=300, conv_state_std=1.0, n_state_rows=5,
+                                     ids="perm"),
+    "ts_bf16_conv3_softplus": dict(n_head=32, n_tokens=129, d_conv=3, dt_softplus=True,
+                                   dt_shift=0.0, io="bf16", conv_state_std=1.0),
+    "ts_conv2_noD_L128": dict(n_head=16, n_tokens=128, d_conv=2, has_D=False),
+    "ts_noconv_L1": dict(n_head=16, n_tokens=1, d_conv=0),
+    "ts_conv4_L2": dict(n_head=16, n_tokens=2, conv_state_std=1.0),
+    "ts_bf16_long": dict(n_seqs=2, n_head=32, n_tokens=1000, io="bf16"),
+    "ts_dup_ids_s4d": dict(n_head=64, n_tokens=200, n_state_rows=2, ids=np.array([1, 1, 0], np.int32)),
     # bf16, head_dim 32/64, d_state 64/128, no conv: the chunked MFMA (SSD) path
     "ssd_P64_N128_ragged_perm": dict(n_head=3, head_dim=64, d_state=128, n_tokens=200,
                                      **_M2, n_state_rows=5, ids="perm"),
@@ -140,18 +151,21 @@ def test_empty_inputs(gpu):
     assert r0.out.numel() == 0
 
 
-def test_dt_zero_gathers_state_rows_exactly(gpu):
+@pytest.mark.parametrize("n_head", [70, 32])
+def test_dt_zero_gathers_state_rows_exactly(gpu, n_head):
     """dt = 0: the final state of sequence i is row ids[i] of s, bit for bit."""
-    p = _small(9, d_conv=0, n_state_rows=6, ids=np.array([5, 2, 2], np.int32))
+    p = _small(9, d_conv=0, n_state_rows=6, ids=np.array([5, 2, 2], np.int32), n_head=n_head)
     p.t["dt"] = ssm_inputs._const(np.zeros_like(p.value("dt")), p.io)
-    s = (np.arange(6 * 70 * 16, dtype=np.float32).reshape(6, 70, 1, 16) + 1) * 0.25
+    s = (np.arange(6 * n_head * 16, dtype=np.float32).reshape(6, n_head, 1, 16) + 1) * 0.25
     p.t["s"] = ssm_inputs._const(s)
     d, r = run_fwd(p)
     np.testing.assert_array_equal(host(r.state), s[p.ids].astype(np.float64))
 
 
-def test_bad_id_gives_nan_rows_and_sets_flag(gpu):
-    p = _small(10, n_state_rows=3, ids=np.array([1, 3, 0], np.int32), conv_state_std=1.0)
+@pytest.mark.parametrize("n_head", [70, 32])
+def test_bad_id_gives_nan_rows_and_sets_flag(gpu, n_head):
+    p = _small(10, n_state_rows=3, ids=np.array([1, 3, 0], np.int32), conv_state_std=1.0,
+               n_head=n_head)
     t = device_inputs(p)
     ws = ops.workspace(desc_of(p), False)
     d, r = run_fwd(p, t=t, ws=ws)
