@@ -12,21 +12,34 @@
 //     y_t = sum_{s<=t} (C_t . B_s) exp(cum_t - cum_s) dt_s x_s      (intra-chunk)
 //         + exp(cum_t) C_t . h_in                                    (carried state)
 //         + D_h x_t
-// which are dense products: G = C B^T (Q x Q over the states), M = G o L with
-// L[t][s] = exp(cum_t - cum_s) dt_s for s <= t (0 above the diagonal),
-// Y = M X + diag(exp(cum)) (C h_in^T), and the state at the chunk end
-// h_out = exp(cum_last) h_in + (w o X)^T B with w_s = exp(cum_last - cum_s) dt_s.
-// This chunked form is derived here from the recurrence; it reaches the
-// sequential result up to rounding.  Every exponent is cum_t - cum_s with
-// s <= t, which is <= 0 for A <= 0, so no term overflows.
+// which are dense products: G = C B^T over the states, M = G o L with
+// L[t][s] = exp(cum_t - cum_s) dt_s for s <= t (0 above the diagonal), and
+// the state at the chunk end h_out = exp(cum_last) h_in + (w o X)^T B with
+// w_s = exp(cum_last - cum_s) dt_s.  This chunked form is derived here from
+// the recurrence; it reaches the sequential result up to rounding.  Every
+// exponent is cum_t - cum_s with s <= t, which is <= 0 for A <= 0.
 //
-// One workgroup (4 waves) runs one (sequence, head) through its chunks in
-// order, keeping the fp32 state [P][N] in MFMA accumulators.  Products run
-// on v_mfma_f32_16x16x32_bf16 (bf16 operands, fp32 accumulation); every
-// operand tile is read from LDS as one 16-byte load per lane from a
-// row-major tile whose k index is contiguous.  The chunk's x, B, C are
-// fetched into registers one chunk ahead and written to LDS (natural and
-// transposed copies) after the current chunk is done.
+// Work split.  One workgroup (8 waves) runs one (sequence, head) through its
+// 64-token chunks in order.  Wave w produces the y of tokens 16(w%4)..+15 of
+// each chunk for half of the channels, and keeps half of the state columns
+// of one 16-channel block (h^T [N/2][16]) in fp32 MFMA accumulators.  All
+// products run on v_mfma_f32_16x16x32_bf16 (bf16 operands, fp32
+// accumulation), computed transposed:
+//     G^T[s][t]   = B C^T          (A: B rows, B: C rows; natural LDS rows)
+//     M^T         = G^T o L^T      (in registers; only the causal tiles s <= t)
+//     Yd^T[p][t]  = X^T M^T        (A: x^T rows from LDS, B: M^T from registers)
+//     Yo^T[p][t]  = h C^T          (A: bf16 copy of h from LDS, B: C rows)
+//     h^T[n][p]  += B^T (w o X)    (A: B^T rows, B: x^T rows scaled by w)
+// An MFMA's accumulator gives each lane four consecutive rows of one column
+// of a 16x16 tile, while an operand wants eight k values of one row or
+// column.  Two tiles stacked along k give each lane rows {4g+r} and
+// {16+4g+r} (g = lane/16, r = 0..3); a contraction is unchanged when both
+// operands use the same order of k, so M^T is fed from registers with k in
+// that order and the x^T operand on the other side is read in the same order
+// (two 8-byte reads instead of one 16-byte read).  The state each wave
+// updates is written to LDS as bf16 at the start of the next chunk, where
+// every wave reads the channels it needs for the carried-state product.
+//
 #include "device_common.h"
 #include "ssm_internal.h"
 
@@ -34,11 +47,15 @@ namespace ssm {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kQ = 64;       // tokens per chunk
-constexpr int kPad = 8;      // bf16 elements of row padding (16 bytes): 2-way LDS bank use
-constexpr int kThreads = 256;
+constexpr int kQ = 64;        // tokens per chunk
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTP = kQ + 8;   // bf16 pitch of transposed rows (token axis): 36 dwords
 
 struct SsdKP {
     const float* s;
@@ -53,41 +70,52 @@ struct SsdKP {
     float* state_out;
     uint32_t* err;
     int L, H, G, R, hpg;
-    int has_D, softplus;
+    int has_D;
 };
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Operand fragment of a 16 x 32 (rows x k) block of a row-major bf16 tile
-// with row stride `stride` elements: lane l reads row r0 + l%16, k0 + 8*(l/16).
-__device__ __forceinline__ bf16x8 frag(const bf16_t* tile, int stride, int r0, int k0, int lane) {
-    return *reinterpret_cast<const bf16x8*>(tile + (r0 + (lane & 15)) * stride + k0 + 8 * (lane >> 4));
+__device__ __forceinline__ bf16x8 ld8(const bf16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ bf16x4 ld4(const bf16_t* p) { return *reinterpret_cast<const bf16x4*>(p); }
+__device__ __forceinline__ bf16x8 cat(const bf16x4& lo, const bf16x4& hi) {
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
-
-__device__ __forceinline__ float bfv(bf16_t v) { return to_f32(v); }
+__device__ __forceinline__ bf16x8 to_bf16x8(const f32x4& lo, const f32x4& hi) {
+    bf16x8 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        r[j] = (__bf16)lo[j];
+        r[4 + j] = (__bf16)hi[j];
+    }
+    return r;
+}
+__device__ __forceinline__ uint32_t lo16(uint32_t v) { return v & 0xffffu; }
+__device__ __forceinline__ uint32_t hi16(uint32_t v) { return v >> 16; }
 
 template <int P, int N, bool SOFTPLUS>
-__global__ __launch_bounds__(kThreads) void ssd_fwd(SsdKP p) {
-    static_assert(P % 16 == 0 && N % 32 == 0 && P <= 64 && N <= 128, "tile shapes");
-    constexpr int SN = N + kPad;    // row stride of tiles with k = state
-    constexpr int SQ = kQ + kPad;   // row stride of tiles with k = token
-    constexpr int PB = P / 16;      // 16-row blocks of channels
-    constexpr int NB = N / 16;      // 16-column blocks of states
-    __shared__ __attribute__((aligned(16))) bf16_t C_l[kQ * SN];   // [t][n]
-    __shared__ __attribute__((aligned(16))) bf16_t B_l[kQ * SN];   // [s][n]
-    __shared__ __attribute__((aligned(16))) bf16_t BT_l[N * SQ];   // [n][s]
-    __shared__ __attribute__((aligned(16))) bf16_t XT_l[P * SQ];   // [p][s]
-    __shared__ __attribute__((aligned(16))) bf16_t XwT_l[P * SQ];  // [p][s] = w_s x_s,p
-    __shared__ __attribute__((aligned(16))) bf16_t M_l[kQ * SQ];   // [t][s]
-    __shared__ __attribute__((aligned(16))) bf16_t H_l[P * SN];    // [p][n] state, bf16 copy
-    __shared__ float dt_l[kQ];
-    __shared__ float cum_l[4][kQ], ecum_l[4][kQ], w_l[4][kQ];      // per-wave copies
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void ssd_fwd(SsdKP p) {
+    static_assert((P == 32 || P == 64) && (N == 64 || N == 128), "tile shapes");
+    constexpr int PB = P / 16;      // 16-channel blocks
+    constexpr int NB = N / 16;      // state blocks
+    constexpr int NP = N + 8;       // bf16 pitch of natural B/C rows (state axis)
+    __shared__ __attribute__((aligned(16))) bf16_t C_l[kQ * NP];   // [t][n]
+    __shared__ __attribute__((aligned(16))) bf16_t B_l[kQ * NP];   // [s][n]
+    __shared__ __attribute__((aligned(16))) bf16_t BT_l[N * kTP];  // [n][s]
+    __shared__ __attribute__((aligned(16))) bf16_t XT_l[P * kTP];  // [p][s]
+    __shared__ __attribute__((aligned(16))) bf16_t H_l[P * NP];    // [p][n], state entering the chunk
+    __shared__ __attribute__((aligned(16))) float dt_l[kQ];
+    __shared__ __attribute__((aligned(16))) float cum_l[kQ];
+    __shared__ __attribute__((aligned(16))) float ecum_l[kQ];
+    __shared__ __attribute__((aligned(16))) float w_l[kQ];
+    __shared__ float elast_l;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
     const int hh = (int)(blockIdx.x % (unsigned)p.H), i = (int)(blockIdx.x / (unsigned)p.H);
-    const int g = hh / p.hpg;
+    const int grp = hh / p.hpg;
+    const int L = p.L;
     const float Ah = p.A[hh];
     const float Dh = p.has_D ? p.D[hh] : 0.0f;
     int r = p.ids[i];
@@ -96,201 +124,223 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd(SsdKP p) {
         r = 0;
         if (tid == 0) atomicOr(p.err, (uint32_t)SSM_DEVERR_IDS);
     }
+    // state role: wave w keeps tiles [NH*sh, NH*sh + NH) of channel block sp
+    constexpr int NH = NB / 2;
+    const bool owns = wave < 2 * PB;
+    const int sp = owns ? wave >> 1 : 0, sh = wave & 1;
+    const int pw = sp * 16;  // first channel of the state block
+    // y role: token block tb, channel blocks yp0 .. yp0 + YPW - 1
+    constexpr int YPW = PB / 2;
+    const int tb = wave & 3, yp0 = (wave >> 2) * YPW;
 
-    // M is zero above the diagonal for every chunk: clear it once
-    for (int e = tid; e < kQ * SQ; e += kThreads) M_l[e] = bf16_t(0);
-
-    // the state [P][N]: wave w owns channel block pb = w (if any), all NB state blocks
-    f32x4 hacc[NB];
-    const bool owns_state = wave < PB;
-    const float* s0 = p.s + (((int64_t)r * p.H + hh) * P) * N;
+    // state h^T[n][p]: tile j holds rows n = 16(NH*sh + j) + 4g + r, column p = pw + l16
+    f32x4 hacc[NH];
+    {
+        const float* s0 = p.s + (((int64_t)r * p.H + hh) * P + pw + l16) * N + NH * sh * 16;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int pp = wave * 16 + 4 * (lane >> 4) + k, n = nb * 16 + (lane & 15);
-            hacc[nb][k] = owns_state ? (bad ? __builtin_nanf("") : s0[pp * N + n]) : 0.0f;
+        for (int j = 0; j < NH; ++j) {
+            const float4 v = *reinterpret_cast<const float4*>(s0 + j * 16 + 4 * g4);
+            hacc[j] = f32x4{v.x, v.y, v.z, v.w};
+            if (bad) hacc[j] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
         }
     }
-    if (owns_state) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                H_l[(wave * 16 + 4 * (lane >> 4) + k) * SN + nb * 16 + (lane & 15)] = bf16_rne(hacc[nb][k]);
-    }
 
-    // staging of one chunk: x [kQ][P], B and C [kQ][N] (bf16), dt [kQ]
-    constexpr int XCH = kQ * P / 8, BCH = kQ * N / 8;   // 16-byte chunks
-    constexpr int XPER = (XCH + kThreads - 1) / kThreads, BPER = (BCH + kThreads - 1) / kThreads;
-    uint4 sx[XPER], sb[BPER], sc[BPER];
-    float sdt = 0.0f;
-    const int64_t tok_x = (int64_t)p.H * P;         // elements between tokens in x / y
-    const int64_t tok_bc = (int64_t)p.G * N;        // elements between tokens in B / C
-    const bf16_t* xg = p.x + ((int64_t)i * p.L * p.H + hh) * P;
-    const bf16_t* bg = p.B + ((int64_t)i * p.L * p.G + g) * N;
-    const bf16_t* cg = p.C + ((int64_t)i * p.L * p.G + g) * N;
+    // chunk-based descriptors: rows past the sequence end read as zero / drop stores
+    const int64_t xrow = (int64_t)p.H * P * 2;   // bytes between tokens of x / y
+    const int64_t brow = (int64_t)p.G * N * 2;   // bytes between tokens of B / C
+    const int64_t drow = (int64_t)p.H * 2;       // bytes between tokens of dt
+    const char* xg = reinterpret_cast<const char*>(p.x) + ((int64_t)i * L * p.H + hh) * P * 2;
+    const char* bg = reinterpret_cast<const char*>(p.B) + ((int64_t)i * L * p.G + grp) * N * 2;
+    const char* cg = reinterpret_cast<const char*>(p.C) + ((int64_t)i * L * p.G + grp) * N * 2;
+    const char* dg = reinterpret_cast<const char*>(p.dt) + ((int64_t)i * L * p.H + hh) * 2;
+    char* yg = reinterpret_cast<char*>(p.y) + ((int64_t)i * L * p.H + hh) * P * 2;
+    auto rsrc = [&](const char* base, int t0, int64_t row) {
+        const int rows = L - t0;
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base) + (int64_t)t0 * row, 0,
+                                                 rows > 0 ? (int)(rows * row) : 0, 0x00020000);
+    };
+
+    // staging roles: (token pair tp, octet) for x and B (transposed as token
+    // pairs); C by 16-byte chunks
+    const int tp = tid & 31, oct = tid >> 5;   // oct 0..15
+    constexpr int XO = P / 8;                  // x octets per token
+    constexpr int BO = N / 8;                  // B octets per token
+    constexpr int CPER = kQ * N / 8 / kThreads;
+    static_assert(CPER >= 1 && 32 * BO <= kThreads, "staging covers the chunk");
+    u32x4 sx[2], sb[2], sc[CPER];
+    uint32_t sdt = 0;
     auto load_chunk = [&](int t0) {
+        const auto rx = rsrc(xg, t0, xrow), rb = rsrc(bg, t0, brow), rc = rsrc(cg, t0, brow);
+        if (oct < XO) {
 #pragma unroll
-        for (int k = 0; k < XPER; ++k) {
-            const int e = tid + kThreads * k;
-            const int t = e / (P / 8), pc = e % (P / 8);
-            sx[k] = (e < XCH && t0 + t < p.L)
-                        ? *reinterpret_cast<const uint4*>(xg + (int64_t)(t0 + t) * tok_x + pc * 8)
-                        : make_uint4(0, 0, 0, 0);
+            for (int u = 0; u < 2; ++u)
+                sx[u] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)((2 * tp + u) * xrow) + oct * 16, 0, 0);
+        }
+        if (oct < BO) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                sb[u] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)((2 * tp + u) * brow) + oct * 16, 0, 0);
         }
 #pragma unroll
-        for (int k = 0; k < BPER; ++k) {
+        for (int k = 0; k < CPER; ++k) {
             const int e = tid + kThreads * k;
-            const int t = e / (N / 8), nc = e % (N / 8);
-            const bool ok = e < BCH && t0 + t < p.L;
-            sb[k] = ok ? *reinterpret_cast<const uint4*>(bg + (int64_t)(t0 + t) * tok_bc + nc * 8)
-                       : make_uint4(0, 0, 0, 0);
-            sc[k] = ok ? *reinterpret_cast<const uint4*>(cg + (int64_t)(t0 + t) * tok_bc + nc * 8)
-                       : make_uint4(0, 0, 0, 0);
+            const int t = e / (N / 8), part = e % (N / 8);
+            sc[k] = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(t * brow) + part * 16, 0, 0);
         }
-        if (tid < kQ) {
-            float v = (t0 + tid < p.L) ? bfv(p.dt[((int64_t)i * p.L + t0 + tid) * p.H + hh]) : 0.0f;
-            if constexpr (SOFTPLUS) v = (t0 + tid < p.L) ? softplus(v) : 0.0f;
-            sdt = v;
-        }
+        if (tid < kQ) sdt = __builtin_amdgcn_raw_buffer_load_b16(rsrc(dg, t0, drow), (int)(tid * drow), 0, 0);
     };
-    auto store_chunk = [&]() {
+    auto store_chunk = [&](int t0) {
+        if (oct < XO) {
 #pragma unroll
-        for (int k = 0; k < XPER; ++k) {
-            const int e = tid + kThreads * k;
-            if (e < XCH) {
-                const int t = e / (P / 8), pc = e % (P / 8);
-                const bf16_t* v = reinterpret_cast<const bf16_t*>(&sx[k]);
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t a = j & 1 ? hi16(sx[0][j >> 1]) : lo16(sx[0][j >> 1]);
+                const uint32_t b = j & 1 ? hi16(sx[1][j >> 1]) : lo16(sx[1][j >> 1]);
+                *reinterpret_cast<uint32_t*>(&XT_l[(oct * 8 + j) * kTP + 2 * tp]) = a | (b << 16);
+            }
+        }
+        if (oct < BO) {
+            *reinterpret_cast<u32x4*>(&B_l[(2 * tp) * NP + oct * 8]) = sb[0];
+            *reinterpret_cast<u32x4*>(&B_l[(2 * tp + 1) * NP + oct * 8]) = sb[1];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) XT_l[(pc * 8 + j) * SQ + t] = v[j];
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t a = j & 1 ? hi16(sb[0][j >> 1]) : lo16(sb[0][j >> 1]);
+                const uint32_t b = j & 1 ? hi16(sb[1][j >> 1]) : lo16(sb[1][j >> 1]);
+                *reinterpret_cast<uint32_t*>(&BT_l[(oct * 8 + j) * kTP + 2 * tp]) = a | (b << 16);
             }
         }
 #pragma unroll
-        for (int k = 0; k < BPER; ++k) {
+        for (int k = 0; k < CPER; ++k) {
             const int e = tid + kThreads * k;
-            if (e < BCH) {
-                const int t = e / (N / 8), nc = e % (N / 8);
-                *reinterpret_cast<uint4*>(&B_l[t * SN + nc * 8]) = sb[k];
-                *reinterpret_cast<uint4*>(&C_l[t * SN + nc * 8]) = sc[k];
-                const bf16_t* v = reinterpret_cast<const bf16_t*>(&sb[k]);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) BT_l[(nc * 8 + j) * SQ + t] = v[j];
-            }
+            const int t = e / (N / 8), part = e % (N / 8);
+            *reinterpret_cast<u32x4*>(&C_l[t * NP + part * 8]) = sc[k];
         }
-        if (tid < kQ) dt_l[tid] = sdt;
-    };
-
-    const int n_chunks = (p.L + kQ - 1) / kQ;
-    load_chunk(0);
-    store_chunk();
-    __syncthreads();
-    for (int ch = 0; ch < n_chunks; ++ch) {
-        const int t0 = ch * kQ;
-        if (ch + 1 < n_chunks) load_chunk(t0 + kQ);
-
-        // decays: every wave forms the chunk's cumulative log-decay itself (lane = token)
-        float e_last;
-        {
-            const float lt = dt_l[lane] * Ah;
-            float cum = lt;
+        if (wave == 0) {  // decays of the chunk, lane = token
+            float d = to_f32((bf16_t)sdt);
+            if constexpr (SOFTPLUS) d = softplus(d);
+            if (t0 + lane >= L) d = 0.0f;
+            float cum = d * Ah;
 #pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const float o = __shfl_up(cum, d, 64);
-                if (lane >= d) cum += o;
+            for (int k = 1; k < 64; k <<= 1) {
+                const float o = __shfl_up(cum, k, 64);
+                if (lane >= k) cum += o;
             }
             const float last = __shfl(cum, 63, 64);
-            cum_l[wave][lane] = cum;
-            ecum_l[wave][lane] = __expf(cum);
-            w_l[wave][lane] = __expf(last - cum) * dt_l[lane];
-            e_last = __expf(last);
+            dt_l[lane] = d;
+            cum_l[lane] = cum;
+            ecum_l[lane] = __expf(cum);
+            w_l[lane] = __expf(last - cum) * d;
+            if (lane == 0) elast_l = __expf(last);
         }
-        // the wave reads its own copies back across lanes: LDS serves one wave in order
-        __builtin_amdgcn_wave_barrier();
-        const float* cumw = cum_l[wave];
+        if (owns) {  // the state entering this chunk, as bf16 [p][n]
+#pragma unroll
+            for (int j = 0; j < NH; ++j) {
+                const f32x4 v = hacc[j];
+                const uint32_t lo = uint32_t(bf16_rne(v[0])) | (uint32_t(bf16_rne(v[1])) << 16);
+                const uint32_t hi = uint32_t(bf16_rne(v[2])) | (uint32_t(bf16_rne(v[3])) << 16);
+                *reinterpret_cast<u32x2*>(&H_l[(pw + l16) * NP + (NH * sh + j) * 16 + 4 * g4]) = u32x2{lo, hi};
+            }
+        }
+    };
 
-        // G = C B^T on the causal 16x16 tiles, then M = G o L into M_l
-        for (int tile = wave; tile < 10; tile += 4) {
-            // tiles (tb, sb) with sb <= tb, numbered row by row
-            const int tb = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
-            const int sb = tile - (tb * (tb + 1)) / 2;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < N; kk += 32)
-                acc = mfma(frag(C_l, SN, tb * 16, kk, lane), frag(B_l, SN, sb * 16, kk, lane), acc);
-            const int s = sb * 16 + (lane & 15);
-            const float cs = cumw[s], dts = dt_l[s];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int t = tb * 16 + 4 * (lane >> 4) + k;
-                const float m = s <= t ? acc[k] * __expf(cumw[t] - cs) * dts : 0.0f;
-                M_l[t * SQ + s] = bf16_rne(m);
-            }
-        }
-        // XwT = w o X (transposed), for the state update
-        for (int e = tid; e < P * kQ / 8; e += kThreads) {
-            const int pp = e / (kQ / 8), sc8 = (e % (kQ / 8)) * 8;
-            bf16x8 v = *reinterpret_cast<const bf16x8*>(&XT_l[pp * SQ + sc8]);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = (__bf16)((float)v[j] * w_l[wave][sc8 + j]);
-            *reinterpret_cast<bf16x8*>(&XwT_l[pp * SQ + sc8]) = v;
-        }
-        __syncthreads();
+    // y stores: lane (t = 16tb + l16, channels 16pb + 4g .. +3), one 8-byte store per channel block
+    const int yoff = (int)((tb * 16 + l16) * xrow) + 4 * g4 * 2;
 
-        // Y = M X + diag(exp(cum)) C H^T + D x: wave w computes channel block pb = w
-        if (owns_state) {
-            const int pb = wave;
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                f32x4 yd = {0.f, 0.f, 0.f, 0.f}, yo = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < (tb + 1) * 16; kk += 32)
-                    yd = mfma(frag(M_l, SQ, tb * 16, kk, lane), frag(XT_l, SQ, pb * 16, kk, lane), yd);
-#pragma unroll
-                for (int kk = 0; kk < N; kk += 32)
-                    yo = mfma(frag(C_l, SN, tb * 16, kk, lane), frag(H_l, SN, pb * 16, kk, lane), yo);
-                const int pp = pb * 16 + (lane & 15);
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int t = tb * 16 + 4 * (lane >> 4) + k;
-                    if (t0 + t < p.L) {
-                        const float xv = bfv(XT_l[pp * SQ + t]);
-                        const float yv = fmaf(Dh, xv, fmaf(ecum_l[wave][t], yo[k], yd[k]));
-                        p.y[((int64_t)i * p.L + t0 + t) * tok_x + (int64_t)hh * P + pp] = bf16_rne(yv);
-                    }
-                }
-            }
-            // state: h = exp(cum_last) h + (w o X)^T B
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                f32x4 a = hacc[nb];
-#pragma unroll
-                for (int k = 0; k < 4; ++k) a[k] *= e_last;
-#pragma unroll
-                for (int kk = 0; kk < kQ; kk += 32)
-                    a = mfma(frag(XwT_l, SQ, pb * 16, kk, lane), frag(BT_l, SQ, nb * 16, kk, lane), a);
-                hacc[nb] = a;
-            }
-        }
-        __syncthreads();  // every wave is done with this chunk's tiles and with H_l
-        if (owns_state) {
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    H_l[(wave * 16 + 4 * (lane >> 4) + k) * SN + nb * 16 + (lane & 15)] = bf16_rne(hacc[nb][k]);
-        }
-        if (ch + 1 < n_chunks) store_chunk();
+    const int n_chunks = (L + kQ - 1) / kQ;
+    load_chunk(0);
+    for (int ch = 0; ch < n_chunks; ++ch) {
+        const int t0 = ch * kQ;
+        __syncthreads();  // every wave is done with the previous chunk's tiles
+        store_chunk(t0);
         __syncthreads();
+        load_chunk(t0 + kQ);  // next chunk (past the end: reads zero, never used)
+
+        // this wave's 16 tokens: t = 16tb + l16 in every tile below
+        const int t = tb * 16 + l16;
+        const float cum_t = cum_l[t];
+        // M^T tiles (sb, tb), sb <= tb, in registers: rows s = 16sb + 4g + r, column t
+        f32x4 mt[4];
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) {
+            mt[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (sb > tb) continue;
+            f32x4 gacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < N / 32; ++kk)
+                gacc = mfma(ld8(&B_l[(sb * 16 + l16) * NP + kk * 32 + 8 * g4]),
+                            ld8(&C_l[t * NP + kk * 32 + 8 * g4]), gacc);
+            const float4 cs = *reinterpret_cast<const float4*>(&cum_l[sb * 16 + 4 * g4]);
+            const float4 ds = *reinterpret_cast<const float4*>(&dt_l[sb * 16 + 4 * g4]);
+            const float csv[4] = {cs.x, cs.y, cs.z, cs.w}, dsv[4] = {ds.x, ds.y, ds.z, ds.w};
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int s = sb * 16 + 4 * g4 + rr;
+                mt[sb][rr] = s <= t ? gacc[rr] * __expf(cum_t - csv[rr]) * dsv[rr] : 0.0f;
+            }
+        }
+        bf16x8 mb[2];
+        mb[0] = to_bf16x8(mt[0], mt[1]);
+        mb[1] = to_bf16x8(mt[2], mt[3]);
+        const float et = ecum_l[t];
+        const auto ry = rsrc(yg, t0, xrow);
+#pragma unroll
+        for (int q = 0; q < YPW; ++q) {
+            const int pb = yp0 + q;
+            const int prow = pb * 16 + l16;
+            // Yd^T = X^T M^T over s (k in stacked-tile order), Yo^T = h C^T over n
+            f32x4 yd = {0.f, 0.f, 0.f, 0.f}, yo = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                if (2 * kk > tb) continue;
+                const bf16_t* xr = &XT_l[prow * kTP + kk * 32 + 4 * g4];
+                yd = mfma(cat(ld4(xr), ld4(xr + 16)), mb[kk], yd);
+            }
+#pragma unroll
+            for (int kk = 0; kk < N / 32; ++kk)
+                yo = mfma(ld8(&H_l[prow * NP + kk * 32 + 8 * g4]), ld8(&C_l[t * NP + kk * 32 + 8 * g4]), yo);
+            // y[t][p] for p = 16pb + 4g + r: y = yd + exp(cum_t) yo + D x
+            uint32_t packed[2];
+#pragma unroll
+            for (int rr = 0; rr < 4; rr += 2) {
+                const int p0 = pb * 16 + 4 * g4 + rr;
+                const float x0 = to_f32(XT_l[p0 * kTP + t]), x1 = to_f32(XT_l[(p0 + 1) * kTP + t]);
+                const float y0 = fmaf(Dh, x0, fmaf(et, yo[rr], yd[rr]));
+                const float y1 = fmaf(Dh, x1, fmaf(et, yo[rr + 1], yd[rr + 1]));
+                packed[rr / 2] = uint32_t(bf16_rne(y0)) | (uint32_t(bf16_rne(y1)) << 16);
+            }
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{packed[0], packed[1]}, ry, yoff + pb * 32, 0, 0);
+        }
+
+        // state of this wave's block: h^T = exp(cum_last) h^T + B^T (w o X)
+        if (owns) {
+            const float e_last = elast_l;
+            bf16x8 xw[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x8 xv = ld8(&XT_l[(pw + l16) * kTP + kk * 32 + 8 * g4]);
+                const float4 w0 = *reinterpret_cast<const float4*>(&w_l[kk * 32 + 8 * g4]);
+                const float4 w1 = *reinterpret_cast<const float4*>(&w_l[kk * 32 + 8 * g4 + 4]);
+                const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+                for (int j = 0; j < 8; ++j) xw[kk][j] = (__bf16)((float)xv[j] * wv[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < NH; ++j) {
+                const int nb = NH * sh + j;
+                f32x4 a = hacc[j] * e_last;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+                    a = mfma(ld8(&BT_l[(nb * 16 + l16) * kTP + kk * 32 + 8 * g4]), xw[kk], a);
+                hacc[j] = a;
+            }
+        }
     }
 
-    if (owns_state) {
-        float* so = p.state_out + (((int64_t)i * p.H + hh) * P) * N;
+    if (owns) {
+        float* so = p.state_out + (((int64_t)i * p.H + hh) * P + pw + l16) * N + NH * sh * 16;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                so[(wave * 16 + 4 * (lane >> 4) + k) * N + nb * 16 + (lane & 15)] = hacc[nb][k];
+        for (int j = 0; j < NH; ++j)
+            *reinterpret_cast<float4*>(so + j * 16 + 4 * g4) =
+                make_float4(hacc[j][0], hacc[j][1], hacc[j][2], hacc[j][3]);
     }
 }
 
@@ -306,9 +356,12 @@ int launch_ssd_pn(const SsdKP& kp, int S, bool softplus, hipStream_t st) {
 
 bool ssd_supported(const Shape& sh, const FwdArgs& a) {
     auto al16 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; };
+    // per-sequence byte extents must fit the 31-bit offsets of the buffer descriptors
+    const int64_t lim = int64_t(1) << 31;
     return !sh.a_per_state && sh.io == SSM_BF16 && sh.K == 0 && (sh.P == 64 || sh.P == 32) &&
-           (sh.N == 128 || sh.N == 64) && al16(a.x) && al16(a.B) && al16(a.C) && sh.L > 0 &&
-           sh.S * sh.H < (int64_t(1) << 31);
+           (sh.N == 128 || sh.N == 64) && al16(a.x) && al16(a.B) && al16(a.C) && al16(a.s) &&
+           al16(a.state_out) && (reinterpret_cast<uintptr_t>(a.y) & 7) == 0 && sh.L > 0 &&
+           sh.S * sh.H < lim && sh.L * sh.H * sh.P * 2 < lim && sh.L * sh.G * sh.N * 2 < lim;
 }
 
 int launch_ssd_fwd(const FwdArgs& a, hipStream_t stream) {
@@ -321,8 +374,7 @@ int launch_ssd_fwd(const FwdArgs& a, hipStream_t stream) {
     kp.L = (int)sh.L; kp.H = (int)sh.H; kp.G = (int)sh.G; kp.R = (int)sh.R;
     kp.hpg = (int)(sh.H / sh.G);
     kp.has_D = (sh.flags & SSM_HAS_D) ? 1 : 0;
-    kp.softplus = (sh.flags & SSM_DT_SOFTPLUS) ? 1 : 0;
-    const bool sp = kp.softplus != 0;
+    const bool sp = (sh.flags & SSM_DT_SOFTPLUS) != 0;
     const int S = (int)sh.S;
     if (sh.P == 64 && sh.N == 128) return launch_ssd_pn<64, 128>(kp, S, sp, stream);
     if (sh.P == 64 && sh.N == 64) return launch_ssd_pn<64, 64>(kp, S, sp, stream);
