@@ -27,9 +27,15 @@
 // accumulation), computed transposed:
 //     G^T[s][t]   = B C^T          (A: B rows, B: C rows; natural LDS rows)
 //     M^T         = G^T o L^T      (in registers; only the causal tiles s <= t)
-//     Yd^T[p][t]  = X^T M^T        (A: x^T rows from LDS, B: M^T from registers)
+//     Yd^T[p][t]  = X^T M^T        (A: x columns, B: M^T from registers)
 //     Yo^T[p][t]  = h C^T          (A: bf16 copy of h from LDS, B: C rows)
-//     h^T[n][p]  += B^T (w o X)    (A: B^T rows, B: x^T rows scaled by w)
+//     h^T[n][p]  += B^T (w o X)    (A: B columns, B: x columns scaled by w)
+// Operands whose k index is the token (x and B columns) are read from the
+// natural row-major tiles with gfx950's transposing LDS read
+// (ds_read_b64_tr_b16): within each 16-lane group, lane i receives element
+// i%4 of the 8-byte blocks addressed by lanes 4k + i/4 (k = 0..3), so lanes
+// 4k+q addressing row s_k, columns 4q..4q+3 of a 16-column block give lane i
+// the column i of rows s_0..s_3.
 // An MFMA's accumulator gives each lane four consecutive rows of one column
 // of a 16x16 tile, while an operand wants eight k values of one row or
 // column.  Two tiles stacked along k give each lane rows {4g+r} and
@@ -51,11 +57,11 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kQ = 64;        // tokens per chunk
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kTP = kQ + 8;   // bf16 pitch of transposed rows (token axis): 36 dwords
 
 struct SsdKP {
     const float* s;
@@ -91,8 +97,29 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const f32x4& lo, const f32x4& hi) {
     }
     return r;
 }
-__device__ __forceinline__ uint32_t lo16(uint32_t v) { return v & 0xffffu; }
-__device__ __forceinline__ uint32_t hi16(uint32_t v) { return v >> 16; }
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_or_zero(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 ROW_MASK, 0xF, false));
+}
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts of 1, 2,
+// 4, 8 within each 16-lane row, then the row totals through row_bcast15/31.
+__device__ __forceinline__ float wave_incl_sum(float v) {
+    v += dpp_or_zero<0x111, 0xF>(v);  // row_shr:1
+    v += dpp_or_zero<0x112, 0xF>(v);  // row_shr:2
+    v += dpp_or_zero<0x114, 0xF>(v);  // row_shr:4
+    v += dpp_or_zero<0x118, 0xF>(v);  // row_shr:8
+    v += dpp_or_zero<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp_or_zero<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
+// transposing LDS read of this lane's 8-byte block (see the layout above)
+__device__ __forceinline__ bf16x4 ldtr(const bf16_t* p) {
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(p));
+    return __builtin_bit_cast(bf16x4, v);
+}
 
 template <int P, int N, bool SOFTPLUS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void ssd_fwd(SsdKP p) {
@@ -100,10 +127,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     constexpr int PB = P / 16;      // 16-channel blocks
     constexpr int NB = N / 16;      // state blocks
     constexpr int NP = N + 8;       // bf16 pitch of natural B/C rows (state axis)
+    constexpr int XP = P + 16;      // bf16 pitch of x rows: 8 dwords mod 32 banks for the transposing reads
     __shared__ __attribute__((aligned(16))) bf16_t C_l[kQ * NP];   // [t][n]
     __shared__ __attribute__((aligned(16))) bf16_t B_l[kQ * NP];   // [s][n]
-    __shared__ __attribute__((aligned(16))) bf16_t BT_l[N * kTP];  // [n][s]
-    __shared__ __attribute__((aligned(16))) bf16_t XT_l[P * kTP];  // [p][s]
+    __shared__ __attribute__((aligned(16))) bf16_t X_l[kQ * XP];   // [s][p]
     __shared__ __attribute__((aligned(16))) bf16_t H_l[P * NP];    // [p][n], state entering the chunk
     __shared__ __attribute__((aligned(16))) float dt_l[kQ];
     __shared__ __attribute__((aligned(16))) float cum_l[kQ];
@@ -160,71 +187,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                                                  rows > 0 ? (int)(rows * row) : 0, 0x00020000);
     };
 
-    // staging roles: (token pair tp, octet) for x and B (transposed as token
-    // pairs); C by 16-byte chunks
-    const int tp = tid & 31, oct = tid >> 5;   // oct 0..15
-    constexpr int XO = P / 8;                  // x octets per token
-    constexpr int BO = N / 8;                  // B octets per token
-    constexpr int CPER = kQ * N / 8 / kThreads;
-    static_assert(CPER >= 1 && 32 * BO <= kThreads, "staging covers the chunk");
-    u32x4 sx[2], sb[2], sc[CPER];
+    // staging: x, B, C rows by 16-byte chunks
+    constexpr int XCH = kQ * P / 8, BCH = kQ * N / 8;     // chunks per chunk-tile
+    constexpr int XPER = (XCH + kThreads - 1) / kThreads, BPER = BCH / kThreads;
+    static_assert(BPER >= 1 && BCH % kThreads == 0, "staging covers the chunk");
+    u32x4 sx[XPER], sb[BPER], sc[BPER];
     uint32_t sdt = 0;
     auto load_chunk = [&](int t0) {
         const auto rx = rsrc(xg, t0, xrow), rb = rsrc(bg, t0, brow), rc = rsrc(cg, t0, brow);
-        if (oct < XO) {
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
-                sx[u] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)((2 * tp + u) * xrow) + oct * 16, 0, 0);
-        }
-        if (oct < BO) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-                sb[u] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)((2 * tp + u) * brow) + oct * 16, 0, 0);
+        for (int k = 0; k < XPER; ++k) {
+            const int e = tid + kThreads * k;
+            if (e < XCH)
+                sx[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)((e / (P / 8)) * xrow) + (e % (P / 8)) * 16, 0, 0);
         }
 #pragma unroll
-        for (int k = 0; k < CPER; ++k) {
+        for (int k = 0; k < BPER; ++k) {
             const int e = tid + kThreads * k;
             const int t = e / (N / 8), part = e % (N / 8);
+            sb[k] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)(t * brow) + part * 16, 0, 0);
             sc[k] = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(t * brow) + part * 16, 0, 0);
         }
         if (tid < kQ) sdt = __builtin_amdgcn_raw_buffer_load_b16(rsrc(dg, t0, drow), (int)(tid * drow), 0, 0);
     };
     auto store_chunk = [&](int t0) {
-        if (oct < XO) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t a = j & 1 ? hi16(sx[0][j >> 1]) : lo16(sx[0][j >> 1]);
-                const uint32_t b = j & 1 ? hi16(sx[1][j >> 1]) : lo16(sx[1][j >> 1]);
-                *reinterpret_cast<uint32_t*>(&XT_l[(oct * 8 + j) * kTP + 2 * tp]) = a | (b << 16);
-            }
-        }
-        if (oct < BO) {
-            *reinterpret_cast<u32x4*>(&B_l[(2 * tp) * NP + oct * 8]) = sb[0];
-            *reinterpret_cast<u32x4*>(&B_l[(2 * tp + 1) * NP + oct * 8]) = sb[1];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t a = j & 1 ? hi16(sb[0][j >> 1]) : lo16(sb[0][j >> 1]);
-                const uint32_t b = j & 1 ? hi16(sb[1][j >> 1]) : lo16(sb[1][j >> 1]);
-                *reinterpret_cast<uint32_t*>(&BT_l[(oct * 8 + j) * kTP + 2 * tp]) = a | (b << 16);
-            }
+        for (int k = 0; k < XPER; ++k) {
+            const int e = tid + kThreads * k;
+            if (e < XCH) *reinterpret_cast<u32x4*>(&X_l[(e / (P / 8)) * XP + (e % (P / 8)) * 8]) = sx[k];
         }
 #pragma unroll
-        for (int k = 0; k < CPER; ++k) {
+        for (int k = 0; k < BPER; ++k) {
             const int e = tid + kThreads * k;
             const int t = e / (N / 8), part = e % (N / 8);
+            *reinterpret_cast<u32x4*>(&B_l[t * NP + part * 8]) = sb[k];
             *reinterpret_cast<u32x4*>(&C_l[t * NP + part * 8]) = sc[k];
         }
         if (wave == 0) {  // decays of the chunk, lane = token
             float d = to_f32((bf16_t)sdt);
             if constexpr (SOFTPLUS) d = softplus(d);
             if (t0 + lane >= L) d = 0.0f;
-            float cum = d * Ah;
-#pragma unroll
-            for (int k = 1; k < 64; k <<= 1) {
-                const float o = __shfl_up(cum, k, 64);
-                if (lane >= k) cum += o;
-            }
-            const float last = __shfl(cum, 63, 64);
+            const float cum = wave_incl_sum(d * Ah);
+            const float last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cum), 63));
             dt_l[lane] = d;
             cum_l[lane] = cum;
             ecum_l[lane] = __expf(cum);
@@ -291,20 +295,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 if (2 * kk > tb) continue;
-                const bf16_t* xr = &XT_l[prow * kTP + kk * 32 + 4 * g4];
-                yd = mfma(cat(ld4(xr), ld4(xr + 16)), mb[kk], yd);
+                // x column p = prow, rows s = 32kk + 4g + r and 32kk + 16 + 4g + r
+                const bf16_t* xr = &X_l[(kk * 32 + 4 * g4 + (l16 >> 2)) * XP + pb * 16 + 4 * (l16 & 3)];
+                yd = mfma(cat(ldtr(xr), ldtr(xr + 16 * XP)), mb[kk], yd);
             }
 #pragma unroll
             for (int kk = 0; kk < N / 32; ++kk)
                 yo = mfma(ld8(&H_l[prow * NP + kk * 32 + 8 * g4]), ld8(&C_l[t * NP + kk * 32 + 8 * g4]), yo);
             // y[t][p] for p = 16pb + 4g + r: y = yd + exp(cum_t) yo + D x
             uint32_t packed[2];
+            const bf16x4 xv = ld4(&X_l[t * XP + pb * 16 + 4 * g4]);
 #pragma unroll
             for (int rr = 0; rr < 4; rr += 2) {
-                const int p0 = pb * 16 + 4 * g4 + rr;
-                const float x0 = to_f32(XT_l[p0 * kTP + t]), x1 = to_f32(XT_l[(p0 + 1) * kTP + t]);
-                const float y0 = fmaf(Dh, x0, fmaf(et, yo[rr], yd[rr]));
-                const float y1 = fmaf(Dh, x1, fmaf(et, yo[rr + 1], yd[rr + 1]));
+                const float y0 = fmaf(Dh, (float)xv[rr], fmaf(et, yo[rr], yd[rr]));
+                const float y1 = fmaf(Dh, (float)xv[rr + 1], fmaf(et, yo[rr + 1], yd[rr + 1]));
                 packed[rr / 2] = uint32_t(bf16_rne(y0)) | (uint32_t(bf16_rne(y1)) << 16);
             }
             __builtin_amdgcn_raw_buffer_store_b64(u32x2{packed[0], packed[1]}, ry, yoff + pb * 32, 0, 0);
@@ -316,7 +320,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             bf16x8 xw[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 xv = ld8(&XT_l[(pw + l16) * kTP + kk * 32 + 8 * g4]);
+                // x column p = pw + l16, rows s = 32kk + 8g + j
+                const bf16_t* xr = &X_l[(kk * 32 + 8 * g4 + (l16 >> 2)) * XP + pw + 4 * (l16 & 3)];
+                const bf16x8 xv = cat(ldtr(xr), ldtr(xr + 4 * XP));
                 const float4 w0 = *reinterpret_cast<const float4*>(&w_l[kk * 32 + 8 * g4]);
                 const float4 w1 = *reinterpret_cast<const float4*>(&w_l[kk * 32 + 8 * g4 + 4]);
                 const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
@@ -328,8 +334,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                 const int nb = NH * sh + j;
                 f32x4 a = hacc[j] * e_last;
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-                    a = mfma(ld8(&BT_l[(nb * 16 + l16) * kTP + kk * 32 + 8 * g4]), xw[kk], a);
+                for (int kk = 0; kk < 2; ++kk) {
+                    // B column n = 16nb + l16, rows s = 32kk + 8g + j
+                    const bf16_t* br = &B_l[(kk * 32 + 8 * g4 + (l16 >> 2)) * NP + nb * 16 + 4 * (l16 & 3)];
+                    a = mfma(cat(ldtr(br), ldtr(br + 4 * NP)), xw[kk], a);
+                }
                 hacc[j] = a;
             }
         }
