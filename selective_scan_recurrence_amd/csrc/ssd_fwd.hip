@@ -20,14 +20,15 @@
 // exponent is cum_t - cum_s with s <= t, which is <= 0 for A <= 0.
 //
 // Work split.  One workgroup (8 waves) runs one (sequence, head) through its
-// 64-token chunks in order.  Wave w produces the y of tokens 16(w%4)..+15 of
-// each chunk for half of the channels, and keeps half of the state columns
+// 64-token chunks in order.  Each wave produces the y of one 16-token block
+// of each chunk for half of the channels, and keeps half of the state columns
 // of one 16-channel block (h^T [N/2][16]) in fp32 MFMA accumulators.  All
 // products run on v_mfma_f32_16x16x32_bf16 (bf16 operands, fp32
 // accumulation), computed transposed:
 //     G^T[s][t]   = B C^T          (A: B rows, B: C rows; natural LDS rows)
-//     M^T         = G^T o L^T      (in registers; only the causal tiles s <= t)
-//     Yd^T[p][t]  = X^T M^T        (A: x columns, B: M^T from registers)
+//     M           = G o L          (the 10 causal tiles, spread over the waves,
+//                                   written to LDS as bf16 rows [t][s])
+//     Yd^T[p][t]  = X^T M^T        (A: x columns, B: M rows)
 //     Yo^T[p][t]  = h C^T          (A: bf16 copy of h from LDS, B: C rows)
 //     h^T[n][p]  += B^T (w o X)    (A: B columns, B: x columns scaled by w)
 // Operands whose k index is the token (x and B columns) are read from the
@@ -36,15 +37,10 @@
 // i%4 of the 8-byte blocks addressed by lanes 4k + i/4 (k = 0..3), so lanes
 // 4k+q addressing row s_k, columns 4q..4q+3 of a 16-column block give lane i
 // the column i of rows s_0..s_3.
-// An MFMA's accumulator gives each lane four consecutive rows of one column
-// of a 16x16 tile, while an operand wants eight k values of one row or
-// column.  Two tiles stacked along k give each lane rows {4g+r} and
-// {16+4g+r} (g = lane/16, r = 0..3); a contraction is unchanged when both
-// operands use the same order of k, so M^T is fed from registers with k in
-// that order and the x^T operand on the other side is read in the same order
-// (two 8-byte reads instead of one 16-byte read).  The state each wave
-// updates is written to LDS as bf16 at the start of the next chunk, where
-// every wave reads the channels it needs for the carried-state product.
+// The state each wave updates is written to LDS as bf16 at the start of the
+// next chunk, where every wave reads the channels it needs for the
+// carried-state product.  Three barriers per chunk: chunk staged, M written,
+// chunk consumed.
 //
 #include "device_common.h"
 #include "ssm_internal.h"
@@ -132,6 +128,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     __shared__ __attribute__((aligned(16))) bf16_t B_l[kQ * NP];   // [s][n]
     __shared__ __attribute__((aligned(16))) bf16_t X_l[kQ * XP];   // [s][p]
     __shared__ __attribute__((aligned(16))) bf16_t H_l[P * NP];    // [p][n], state entering the chunk
+    constexpr int MP = kQ + 8;      // bf16 pitch of M rows
+    __shared__ __attribute__((aligned(16))) bf16_t M_l[kQ * MP];   // [t][s], causal (zero above the diagonal)
     __shared__ __attribute__((aligned(16))) float dt_l[kQ];
     __shared__ __attribute__((aligned(16))) float cum_l[kQ];
     __shared__ __attribute__((aligned(16))) float ecum_l[kQ];
@@ -249,6 +247,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     // y stores: lane (t = 16tb + l16, channels 16pb + 4g .. +3), one 8-byte store per channel block
     const int yoff = (int)((tb * 16 + l16) * xrow) + 4 * g4 * 2;
 
+    // M's tiles above the diagonal are never written: zero the whole tile once
+    for (int e = tid; e < kQ * MP / 2; e += kThreads) reinterpret_cast<uint32_t*>(M_l)[e] = 0u;
+
     const int n_chunks = (L + kQ - 1) / kQ;
     load_chunk(0);
     for (int ch = 0; ch < n_chunks; ++ch) {
@@ -258,57 +259,94 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         __syncthreads();
         load_chunk(t0 + kQ);  // next chunk (past the end: reads zero, never used)
 
-        // this wave's 16 tokens: t = 16tb + l16 in every tile below
-        const int t = tb * 16 + l16;
-        const float cum_t = cum_l[t];
-        // M^T tiles (sb, tb), sb <= tb, in registers: rows s = 16sb + 4g + r, column t
-        f32x4 mt[4];
+        // M = G o L on the 10 causal 16x16 tiles, to LDS as bf16.  Tile k (row by
+        // row: (tb,sb) = (0,0),(1,0),(1,1),(2,0),...) goes to wave k % 8: every
+        // wave has tile k = w, waves 0 and 1 also tile w + 8; their G products
+        // run interleaved.
+        {
+            const bool two = wave + kWaves < 10;
+            int mtb[2], msb[2];
 #pragma unroll
-        for (int sb = 0; sb < 4; ++sb) {
-            mt[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (sb > tb) continue;
-            f32x4 gacc = {0.f, 0.f, 0.f, 0.f};
+            for (int u = 0; u < 2; ++u) {
+                const int k = wave + kWaves * u;
+                mtb[u] = k < 1 ? 0 : k < 3 ? 1 : k < 6 ? 2 : 3;
+                msb[u] = k - mtb[u] * (mtb[u] + 1) / 2;
+                if (!two) { mtb[1] = mtb[0]; msb[1] = msb[0]; }
+            }
+            f32x4 gacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-            for (int kk = 0; kk < N / 32; ++kk)
-                gacc = mfma(ld8(&B_l[(sb * 16 + l16) * NP + kk * 32 + 8 * g4]),
-                            ld8(&C_l[t * NP + kk * 32 + 8 * g4]), gacc);
-            const float4 cs = *reinterpret_cast<const float4*>(&cum_l[sb * 16 + 4 * g4]);
-            const float4 ds = *reinterpret_cast<const float4*>(&dt_l[sb * 16 + 4 * g4]);
-            const float csv[4] = {cs.x, cs.y, cs.z, cs.w}, dsv[4] = {ds.x, ds.y, ds.z, ds.w};
+            for (int kk = 0; kk < N / 32; ++kk) {
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int s = sb * 16 + 4 * g4 + rr;
-                mt[sb][rr] = s <= t ? gacc[rr] * __expf(cum_t - csv[rr]) * dsv[rr] : 0.0f;
+                for (int u = 0; u < 2; ++u) {
+                    if (u == 1 && !two) continue;
+                    gacc[u] = mfma(ld8(&B_l[(msb[u] * 16 + l16) * NP + kk * 32 + 8 * g4]),
+                                   ld8(&C_l[(mtb[u] * 16 + l16) * NP + kk * 32 + 8 * g4]), gacc[u]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                if (u == 1 && !two) continue;
+                // G^T tile: column t, rows s = 16msb + 4g + r; exponents clamped to <= 0
+                // (above the diagonal the product is replaced by 0 anyway)
+                const int mt_t = mtb[u] * 16 + l16;
+                const float ct = cum_l[mt_t];
+                const float4 cs = *reinterpret_cast<const float4*>(&cum_l[msb[u] * 16 + 4 * g4]);
+                const float4 ds = *reinterpret_cast<const float4*>(&dt_l[msb[u] * 16 + 4 * g4]);
+                const float csv[4] = {cs.x, cs.y, cs.z, cs.w}, dsv[4] = {ds.x, ds.y, ds.z, ds.w};
+                float m[4];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int sidx = msb[u] * 16 + 4 * g4 + rr;
+                    const float v = gacc[u][rr] * __expf(fminf(ct - csv[rr], 0.0f)) * dsv[rr];
+                    m[rr] = sidx <= mt_t ? v : 0.0f;
+                }
+                const uint32_t lo = uint32_t(bf16_rne(m[0])) | (uint32_t(bf16_rne(m[1])) << 16);
+                const uint32_t hi = uint32_t(bf16_rne(m[2])) | (uint32_t(bf16_rne(m[3])) << 16);
+                *reinterpret_cast<u32x2*>(&M_l[mt_t * MP + msb[u] * 16 + 4 * g4]) = u32x2{lo, hi};
             }
         }
-        bf16x8 mb[2];
-        mb[0] = to_bf16x8(mt[0], mt[1]);
-        mb[1] = to_bf16x8(mt[2], mt[3]);
+        __syncthreads();
+
+        // this wave's 16 tokens: t = 16tb + l16 in every tile below
+        const int t = tb * 16 + l16;
         const float et = ecum_l[t];
         const auto ry = rsrc(yg, t0, xrow);
+        // Yd^T = X^T M^T over s, Yo^T = h C^T over n, for the wave's channel blocks
+        // (their MFMA chains interleaved; the M and C rows of token t are shared)
+        f32x4 yd[YPW], yo[YPW];
+#pragma unroll
+        for (int q = 0; q < YPW; ++q) {
+            yd[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+            yo[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            if (2 * kk > tb) continue;
+            const bf16x8 mrow = ld8(&M_l[t * MP + kk * 32 + 8 * g4]);
+#pragma unroll
+            for (int q = 0; q < YPW; ++q) {
+                // x column p = 16(yp0+q) + l16 over s = 32kk + 8g + j
+                const bf16_t* xr = &X_l[(kk * 32 + 8 * g4 + (l16 >> 2)) * XP + (yp0 + q) * 16 + 4 * (l16 & 3)];
+                yd[q] = mfma(cat(ldtr(xr), ldtr(xr + 4 * XP)), mrow, yd[q]);
+            }
+        }
+#pragma unroll
+        for (int kk = 0; kk < N / 32; ++kk) {
+            const bf16x8 crow = ld8(&C_l[t * NP + kk * 32 + 8 * g4]);
+#pragma unroll
+            for (int q = 0; q < YPW; ++q)
+                yo[q] = mfma(ld8(&H_l[((yp0 + q) * 16 + l16) * NP + kk * 32 + 8 * g4]), crow, yo[q]);
+        }
 #pragma unroll
         for (int q = 0; q < YPW; ++q) {
             const int pb = yp0 + q;
-            const int prow = pb * 16 + l16;
-            // Yd^T = X^T M^T over s (k in stacked-tile order), Yo^T = h C^T over n
-            f32x4 yd = {0.f, 0.f, 0.f, 0.f}, yo = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                if (2 * kk > tb) continue;
-                // x column p = prow, rows s = 32kk + 4g + r and 32kk + 16 + 4g + r
-                const bf16_t* xr = &X_l[(kk * 32 + 4 * g4 + (l16 >> 2)) * XP + pb * 16 + 4 * (l16 & 3)];
-                yd = mfma(cat(ldtr(xr), ldtr(xr + 16 * XP)), mb[kk], yd);
-            }
-#pragma unroll
-            for (int kk = 0; kk < N / 32; ++kk)
-                yo = mfma(ld8(&H_l[prow * NP + kk * 32 + 8 * g4]), ld8(&C_l[t * NP + kk * 32 + 8 * g4]), yo);
             // y[t][p] for p = 16pb + 4g + r: y = yd + exp(cum_t) yo + D x
             uint32_t packed[2];
             const bf16x4 xv = ld4(&X_l[t * XP + pb * 16 + 4 * g4]);
 #pragma unroll
             for (int rr = 0; rr < 4; rr += 2) {
-                const float y0 = fmaf(Dh, (float)xv[rr], fmaf(et, yo[rr], yd[rr]));
-                const float y1 = fmaf(Dh, (float)xv[rr + 1], fmaf(et, yo[rr + 1], yd[rr + 1]));
+                const float y0 = fmaf(Dh, (float)xv[rr], fmaf(et, yo[q][rr], yd[q][rr]));
+                const float y1 = fmaf(Dh, (float)xv[rr + 1], fmaf(et, yo[q][rr + 1], yd[q][rr + 1]));
                 packed[rr / 2] = uint32_t(bf16_rne(y0)) | (uint32_t(bf16_rne(y1)) << 16);
             }
             __builtin_amdgcn_raw_buffer_store_b64(u32x2{packed[0], packed[1]}, ry, yoff + pb * 32, 0, 0);
