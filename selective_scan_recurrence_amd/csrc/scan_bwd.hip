@@ -26,6 +26,8 @@
 // LDS, across channel blocks by kernel 3.  Kernel 3 also sums dA and dD over
 // sequences and gathers dh_0 into d_s by ids; every sum has a fixed order,
 // so results are bitwise repeatable.
+#include <type_traits>
+
 #include "device_common.h"
 #include "ssm_internal.h"
 
@@ -250,6 +252,267 @@ __global__ __launch_bounds__(kThreads) void bwd_rev(BwdKP p) {
     if (active && q == 0) p.dD_part[(int64_t)i * p.d_inner + c] = dD_acc;
 }
 
+// Fast path for d_state 16, 64 | d_inner and 16-byte aligned tensors.  Same
+// arithmetic and reduction order as bwd_rev; the next block's x, dt, dy, B, C
+// and checkpoint are loaded into registers while the current block runs and
+// written to the other half of a double-buffered LDS tile at its end (rows
+// are clamped to the sequence and the ones past its end are written as
+// zeros), so global-memory latency is hidden behind a block of work.
+template <typename T, bool SOFTPLUS>
+__global__ __launch_bounds__(kThreads) void bwd_fast(const BwdKP kp_arg) {
+    // lambdas below capture locals only (capturing the kernel argument would
+    // force it into scratch memory)
+    const BwdKP p = kp_arg;
+    constexpr int ES = (int)sizeof(T);
+    constexpr int CPR = kChan * ES / 16;        // 16-byte chunks per 64-channel row
+    constexpr int CHX = kBlk * CPR;             // chunks per x / dt / dy tile
+    constexpr int CPB = 16 * ES / 16;           // chunks per B / C row
+    constexpr int CHB = kBlk * CPB;             // chunks per B / C tile
+    constexpr int CHK = kChan * 16 * 4 / 16;    // chunks of the checkpoint tile (f32)
+    constexpr int H = kBlk / 2;                 // tokens per half block
+    __shared__ __attribute__((aligned(16))) T xs_l[2][kBlk * kChan];
+    __shared__ __attribute__((aligned(16))) T dts_l[2][kBlk * kChan];
+    __shared__ __attribute__((aligned(16))) T dys_l[2][kBlk * kChan];
+    __shared__ __attribute__((aligned(16))) T Bs_l[2][kBlk * 16];
+    __shared__ __attribute__((aligned(16))) T Cs_l[2][kBlk * 16];
+    // the checkpoint is read into registers right after the barrier that
+    // publishes it, so one buffer is enough (the next one is written after
+    // the following barrier)
+    __shared__ __attribute__((aligned(16))) float ck_l[kChan * 16];
+    // [token][wave][row][quad lane][dB 4 | dC 4]: sums over the row's four channels
+    __shared__ __attribute__((aligned(16))) float red_l[kBlk][4][4][4][8];
+
+    const int tid = threadIdx.x;
+    const int q = tid & 3;
+    const int cl = tid >> 2;            // channel within the block
+    const int wave = tid >> 6;
+    const int row = (tid >> 4) & 3;     // 16-lane row within the wave
+    const int lane_in_row = tid & 15;
+    const int cb = blockIdx.x, i = blockIdx.y;
+    const int c = cb * kChan + cl;
+    const int L = p.L, d_inner = p.d_inner;
+    const int64_t seq = (int64_t)i * L * d_inner;
+    const int rid = p.ids[i];
+    const bool bad = (rid < 0) | (rid >= p.R);  // unknown initial state: d_x, d_dt are NaN
+
+    float a2[4], An[4];
+    {
+        const float4 Av = *reinterpret_cast<const float4*>(p.A + (int64_t)c * 16 + 4 * q);
+        An[0] = Av.x; An[1] = Av.y; An[2] = Av.z; An[3] = Av.w;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) a2[s] = An[s] * kLog2e;
+    }
+    const float Dc = p.has_D ? p.D[c] : 0.0f;
+    float g[4], dA_acc[4] = {0.f, 0.f, 0.f, 0.f};
+    float dD_acc = 0.0f;
+    {
+        const float4 gv = *reinterpret_cast<const float4*>(p.dstate + ((int64_t)i * d_inner + c) * 16 + 4 * q);
+        g[0] = gv.x; g[1] = gv.y; g[2] = gv.z; g[3] = gv.w;
+    }
+
+    // staging: the chunks of x, dt, dy (rows of this block's 64 channels), B,
+    // C (rows of 16 states) and the checkpoint (64 channels x 16 states)
+    const char* xg = static_cast<const char*>(p.x) + (seq + (int64_t)cb * kChan) * ES;
+    const char* dg = static_cast<const char*>(p.dt) + (seq + (int64_t)cb * kChan) * ES;
+    const char* yg = static_cast<const char*>(p.dy) + (seq + (int64_t)cb * kChan) * ES;
+    const char* bg = static_cast<const char*>(p.B) + (int64_t)i * L * 16 * ES;
+    const char* cg = static_cast<const char*>(p.C) + (int64_t)i * L * 16 * ES;
+    const int64_t xrow = (int64_t)d_inner * ES;
+    const int n_blk = (L + kBlk - 1) / kBlk;
+    const float* ckpt = p.ckpt;
+    const int S = p.S;
+    float* d_x = p.d_x;
+    float* d_dt = p.d_dt;
+    // Slots: each thread stages at most NS 16-byte chunks per tile, every slot
+    // drawn from one or two arrays split at a wave boundary (so the choice of
+    // array is a select, not a lookup).  fp32: x, dt, dy (one chunk per
+    // thread each), B (threads 0-63) or C (64-127), checkpoint.  bf16: x
+    // (threads 0-127) or dt (128-255), dy (0-127) or B (128-159) or C
+    // (160-191), checkpoint.
+    constexpr int NS = ES == 4 ? 5 : 3;
+    static_assert(CHK == kThreads && (ES == 2 ? CHX == 128 && CHB == 32 : CHX == 256 && CHB == 64),
+                  "slot layout");
+    uint4 stg[NS];
+    // where slot k of this thread comes from: array id (0 x, 1 dt, 2 dy, 3 B, 4 C, 5 ckpt) and chunk
+    auto slot = [&](int k, int& arr, int& w) __attribute__((always_inline)) {
+        if constexpr (ES == 4) {
+            if (k < 3) { arr = k; w = tid; }
+            else if (k == 3) { arr = tid < 64 ? 3 : 4; w = tid & 63; }
+            else { arr = 5; w = tid; }
+        } else {
+            if (k == 0) { arr = tid < 128 ? 0 : 1; w = tid & 127; }
+            else if (k == 1) { arr = tid < 128 ? 2 : tid < 160 ? 3 : 4; w = tid < 128 ? tid : (tid - 128) & 31; }
+            else { arr = 5; w = tid; }
+        }
+    };
+    auto slot_used = [&](int k) __attribute__((always_inline)) {
+        return !(ES == 2 && k == 1 && tid >= 192) && !(ES == 4 && k == 3 && tid >= 128);
+    };
+    auto load_tile = [&](int b) __attribute__((always_inline)) {
+        const int bb = b < 0 ? 0 : b;
+        const int t0 = bb * kBlk;
+        const char* ckb = reinterpret_cast<const char*>(ckpt + (((int64_t)bb * S + i) * d_inner + cb * kChan) * 16);
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            if (!slot_used(k)) continue;
+            int arr, w;
+            slot(k, arr, w);
+            const char* src;
+            if (arr < 3) {
+                const int t = min(t0 + w / CPR, L - 1);
+                const char* base = arr == 0 ? xg : (arr == 1 ? dg : yg);
+                src = base + (int64_t)t * xrow + (w % CPR) * 16;
+            } else if (arr < 5) {
+                const int t = min(t0 + w / CPB, L - 1);
+                src = (arr == 3 ? bg : cg) + (int64_t)t * 16 * ES + (w % CPB) * 16;
+            } else {
+                src = ckb + w * 16;
+            }
+            stg[k] = *reinterpret_cast<const uint4*>(src);
+        }
+    };
+    auto store_tile = [&](int buf, int b) __attribute__((always_inline)) {
+        const int t0 = b * kBlk;
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            if (!slot_used(k)) continue;
+            int arr, w;
+            slot(k, arr, w);
+            char* dst;
+            bool ok = true;
+            if (arr < 3) {
+                ok = t0 + w / CPR < L;
+                T* tile = arr == 0 ? xs_l[buf] : (arr == 1 ? dts_l[buf] : dys_l[buf]);
+                dst = reinterpret_cast<char*>(tile) + w * 16;
+            } else if (arr < 5) {
+                ok = t0 + w / CPB < L;
+                dst = reinterpret_cast<char*>(arr == 3 ? Bs_l[buf] : Cs_l[buf]) + w * 16;
+            } else {
+                dst = reinterpret_cast<char*>(ck_l) + w * 16;
+            }
+            *reinterpret_cast<uint4*>(dst) = ok ? stg[k] : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto rowv = [&](const T* tile, int k) __attribute__((always_inline)) { return to_f32(tile[k * kChan + cl]); };
+    auto quad4 = [&](const T* tile, int k, float (&v)[4]) __attribute__((always_inline)) {
+        if constexpr (ES == 2) {
+            const uint2 w = *reinterpret_cast<const uint2*>(tile + k * 16 + 4 * q);
+            v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xffff0000u);
+            v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xffff0000u);
+        } else {
+            const float4 w = *reinterpret_cast<const float4*>(tile + k * 16 + 4 * q);
+            v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+        }
+    };
+
+    load_tile(n_blk - 1);
+    store_tile((n_blk - 1) & 1, n_blk - 1);
+    load_tile(n_blk - 2);
+    __syncthreads();
+    for (int b = n_blk - 1; b >= 0; --b) {
+        const int t0 = b * kBlk, buf = b & 1;
+        const int nk = min(kBlk, L - t0);
+        const T* xs = xs_l[buf];
+        const T* dts = dts_l[buf];
+        const T* dys = dys_l[buf];
+        const T* Bt = Bs_l[buf];
+        const T* Ct = Cs_l[buf];
+        float h0[4];
+        {
+            const float4 ck = *reinterpret_cast<const float4*>(&ck_l[cl * 16 + 4 * q]);
+            h0[0] = ck.x; h0[1] = ck.y; h0[2] = ck.z; h0[3] = ck.w;
+        }
+        auto dt_of = [&](int k) __attribute__((always_inline)) {
+            float dk = rowv(dts, k);
+            if constexpr (SOFTPLUS) dk = k < nk ? softplus(dk) : 0.0f;
+            return dk;
+        };
+        // recompute the block: decays a[k][s] and states h[k][s] (= h_{t0+k})
+        float a[kBlk][4], h[kBlk][4];
+#pragma unroll
+        for (int k = 0; k < kBlk; ++k) {
+            const float dk = dt_of(k), bk = dk * rowv(xs, k);
+            float Bq[4];
+            quad4(Bt, k, Bq);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                a[k][s] = fast_exp2(dk * a2[s]);
+                h[k][s] = fmaf(a[k][s], k == 0 ? h0[s] : h[k - 1][s], bk * Bq[s]);
+            }
+        }
+        // adjoint over the block, last token first
+#pragma unroll
+        for (int k = kBlk - 1; k >= 0; --k) {
+            const float dyk = rowv(dys, k);
+            const float draw = rowv(dts, k);
+            const float dk = SOFTPLUS ? (k < nk ? softplus(draw) : 0.0f) : draw;
+            const float uk = rowv(xs, k);
+            const float dtuk = dk * uk;
+            float Bq[4], Cq[4];
+            quad4(Bt, k, Bq);
+            quad4(Ct, k, Cq);
+            float S1 = 0.0f, S2 = 0.0f, dBp[4], dCp[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                g[s] = fmaf(Cq[s], dyk, g[s]);
+                dCp[s] = dyk * h[k][s];
+                S1 = fmaf(g[s], Bq[s], S1);
+                const float ga = g[s] * a[k][s];
+                const float qv = ga * (k == 0 ? h0[s] : h[k - 1][s]);
+                S2 = fmaf(qv, An[s], S2);
+                dA_acc[s] = fmaf(qv, dk, dA_acc[s]);
+                dBp[s] = g[s] * dtuk;
+                g[s] = ga;
+            }
+            S1 = quad_sum(S1);
+            S2 = quad_sum(S2);
+            if (q == 0 && k < nk) {
+                const int64_t idx = seq + (int64_t)(t0 + k) * d_inner + c;
+                float ddt = fmaf(uk, S1, S2);
+                if constexpr (SOFTPLUS) ddt *= 1.0f / (1.0f + expf(-draw));
+                d_x[idx] = bad ? __builtin_nanf("") : fmaf(Dc, dyk, dk * S1);
+                d_dt[idx] = bad ? __builtin_nanf("") : ddt;
+                dD_acc = fmaf(dyk, uk, dD_acc);
+            }
+            // sum the four channels of this 16-lane row (lanes 4j + q)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                dBp[s] = row_shr_add<8>(row_shr_add<4>(dBp[s]));
+                dCp[s] = row_shr_add<8>(row_shr_add<4>(dCp[s]));
+            }
+            if (lane_in_row >= 12) {
+                float* dst = &red_l[k][wave][row][q][0];
+                *reinterpret_cast<float4*>(dst) = make_float4(dBp[0], dBp[1], dBp[2], dBp[3]);
+                *reinterpret_cast<float4*>(dst + 4) = make_float4(dCp[0], dCp[1], dCp[2], dCp[3]);
+            }
+        }
+        __syncthreads();
+        // the block's channel sums: 16 tokens x (16 dB + 16 dC), 16 terms each, fixed order
+        for (int e = tid; e < kBlk * 32; e += kThreads) {
+            const int k = e / 32, m = e % 32;
+            if (k >= nk) continue;
+            const int which = m >> 4, n = m & 15, qq = n >> 2, s = n & 3;
+            float acc = 0.0f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc += red_l[k][w][r][qq][which * 4 + s];
+            p.dbc_part[(((int64_t)cb * p.S + i) * L + t0 + k) * 32 + m] = acc;
+        }
+        // next block's tiles into the other buffer; fetch the one after
+        if (b > 0) store_tile(buf ^ 1, b - 1);
+        load_tile(b - 2);
+        __syncthreads();
+    }
+    {
+        const int64_t row_i = ((int64_t)i * d_inner + c) * 16 + 4 * q;
+        *reinterpret_cast<float4*>(p.ds_part + row_i) = make_float4(g[0], g[1], g[2], g[3]);
+        *reinterpret_cast<float4*>(p.dA_part + row_i) = make_float4(dA_acc[0], dA_acc[1], dA_acc[2], dA_acc[3]);
+    }
+    // dD: lane q == 0 of each quad holds its channel's sum
+    if (q == 0) p.dD_part[(int64_t)i * d_inner + c] = dD_acc;
+}
+
 // d_B, d_C: sum of the channel-block partials in block order.
 __global__ __launch_bounds__(256) void bwd_reduce_bc(BwdKP p, float* d_B, float* d_C) {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -360,7 +623,18 @@ int launch_scan_bwd(const BwdArgs& a, hipStream_t stream) {
     if (rc) return rc;
     const dim3 grid((unsigned)kp.n_cb, (unsigned)sh.S);
     const bool bf = sh.io == SSM_BF16;
-    if (bf) {
+    auto al16 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; };
+    const bool fast = sh.N == 16 && sh.d_inner() % kChan == 0 && al16(a.x) && al16(a.dt) &&
+                      al16(a.dy) && al16(a.B) && al16(a.C) && al16(a.A) && al16(a.dstate);
+    if (fast) {
+        if (bf) {
+            if (kp.softplus) hipLaunchKernelGGL((bwd_fast<bf16_t, true>), grid, dim3(kThreads), 0, stream, kp);
+            else hipLaunchKernelGGL((bwd_fast<bf16_t, false>), grid, dim3(kThreads), 0, stream, kp);
+        } else {
+            if (kp.softplus) hipLaunchKernelGGL((bwd_fast<float, true>), grid, dim3(kThreads), 0, stream, kp);
+            else hipLaunchKernelGGL((bwd_fast<float, false>), grid, dim3(kThreads), 0, stream, kp);
+        }
+    } else if (bf) {
         if (kp.softplus) hipLaunchKernelGGL((bwd_rev<bf16_t, true>), grid, dim3(kThreads), 0, stream, kp);
         else hipLaunchKernelGGL((bwd_rev<bf16_t, false>), grid, dim3(kThreads), 0, stream, kp);
     } else {
