@@ -122,12 +122,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     static_assert((P == 32 || P == 64) && (N == 64 || N == 128), "tile shapes");
     constexpr int PB = P / 16;      // 16-channel blocks
     constexpr int NB = N / 16;      // state blocks
-    constexpr int NP = N + 8;       // bf16 pitch of natural B/C rows (state axis)
-    constexpr int XP = P + 16;      // bf16 pitch of x rows: 8 dwords mod 32 banks for the transposing reads
+    // LDS row pitches, from measured gfx950 throughput of each access pattern
+    // (row r read by lane 16g + r):
+    //   16-byte row reads run conflict-free at pitches of 8 (mod 16) dwords,
+    //   and at 1.7x the time otherwise;
+    //   transposing 8-byte reads (4 rows per 16-lane group) are fast at
+    //   most pitches except multiples of 32 dwords;
+    //   8-byte row writes are fastest at 2 (mod 4) dwords and 2x slower at
+    //   8 (mod 16).
+    // B and C are read as 16-byte rows on the hot loop (N + 16: 40 or 72
+    // dwords); H is written as 8-byte rows as often as it is read (N + 8);
+    // x is read transposed and written once (P + 8 = 36 dwords for P = 64).
+    constexpr int NP = N + 16;      // bf16 pitch of B/C rows (state axis)
+    constexpr int NPH = N + 8;      // bf16 pitch of the state rows
+    constexpr int XP = P == 64 ? P + 8 : P + 16;  // bf16 pitch of x rows
     __shared__ __attribute__((aligned(16))) bf16_t C_l[kQ * NP];   // [t][n]
     __shared__ __attribute__((aligned(16))) bf16_t B_l[kQ * NP];   // [s][n]
     __shared__ __attribute__((aligned(16))) bf16_t X_l[kQ * XP];   // [s][p]
-    __shared__ __attribute__((aligned(16))) bf16_t H_l[P * NP];    // [p][n], state entering the chunk
+    __shared__ __attribute__((aligned(16))) bf16_t H_l[P * NPH];   // [p][n], state entering the chunk
     constexpr int MP = kQ + 8;      // bf16 pitch of M rows
     __shared__ __attribute__((aligned(16))) bf16_t M_l[kQ * MP];   // [t][s], causal (zero above the diagonal)
     __shared__ __attribute__((aligned(16))) float dt_l[kQ];
@@ -239,7 +251,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                 const f32x4 v = hacc[j];
                 const uint32_t lo = uint32_t(bf16_rne(v[0])) | (uint32_t(bf16_rne(v[1])) << 16);
                 const uint32_t hi = uint32_t(bf16_rne(v[2])) | (uint32_t(bf16_rne(v[3])) << 16);
-                *reinterpret_cast<u32x2*>(&H_l[(pw + l16) * NP + (NH * sh + j) * 16 + 4 * g4]) = u32x2{lo, hi};
+                *reinterpret_cast<u32x2*>(&H_l[(pw + l16) * NPH + (NH * sh + j) * 16 + 4 * g4]) = u32x2{lo, hi};
             }
         }
     };
@@ -335,7 +347,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             const bf16x8 crow = ld8(&C_l[t * NP + kk * 32 + 8 * g4]);
 #pragma unroll
             for (int q = 0; q < YPW; ++q)
-                yo[q] = mfma(ld8(&H_l[((yp0 + q) * 16 + l16) * NP + kk * 32 + 8 * g4]), crow, yo[q]);
+                yo[q] = mfma(ld8(&H_l[((yp0 + q) * 16 + l16) * NPH + kk * 32 + 8 * g4]), crow, yo[q]);
         }
 #pragma unroll
         for (int q = 0; q < YPW; ++q) {
