@@ -253,11 +253,19 @@ __global__ __launch_bounds__(kThreads) void bwd_rev(BwdKP p) {
 }
 
 // Fast path for d_state 16, 64 | d_inner and 16-byte aligned tensors.  Same
-// arithmetic and reduction order as bwd_rev; the next block's x, dt, dy, B, C
-// and checkpoint are loaded into registers while the current block runs and
-// written to the other half of a double-buffered LDS tile at its end (rows
-// are clamped to the sequence and the ones past its end are written as
-// zeros), so global-memory latency is hidden behind a block of work.
+// arithmetic and reduction order as bwd_rev.
+//  - The next block's x, dt, dy, B, C and checkpoint are loaded into
+//    registers while the current block runs and written to the other half of
+//    a double-buffered LDS tile at its end, already as fp32 (rows past the
+//    sequence end as zeros): global-memory latency hides behind a block of
+//    work, and no LDS read in the block is followed by an unpack.
+//  - d_x and d_dt of the block are gathered in an LDS tile and leave as
+//    16-byte row stores once the block is done, after the loads of the tile
+//    after next (loads and stores share one completion counter, so the wait
+//    for those loads at the end of the next block never waits for these
+//    stores).
+//  - The products summed across channels (dB, dC) are formed without
+//    contraction so that each DPP row step is a single add.
 template <typename T, bool SOFTPLUS>
 __global__ __launch_bounds__(kThreads) void bwd_fast(const BwdKP kp_arg) {
     // lambdas below capture locals only (capturing the kernel argument would
@@ -269,18 +277,21 @@ __global__ __launch_bounds__(kThreads) void bwd_fast(const BwdKP kp_arg) {
     constexpr int CPB = 16 * ES / 16;           // chunks per B / C row
     constexpr int CHB = kBlk * CPB;             // chunks per B / C tile
     constexpr int CHK = kChan * 16 * 4 / 16;    // chunks of the checkpoint tile (f32)
-    constexpr int H = kBlk / 2;                 // tokens per half block
-    __shared__ __attribute__((aligned(16))) T xs_l[2][kBlk * kChan];
-    __shared__ __attribute__((aligned(16))) T dts_l[2][kBlk * kChan];
-    __shared__ __attribute__((aligned(16))) T dys_l[2][kBlk * kChan];
-    __shared__ __attribute__((aligned(16))) T Bs_l[2][kBlk * 16];
-    __shared__ __attribute__((aligned(16))) T Cs_l[2][kBlk * 16];
+    constexpr int VPC = 16 / ES;                // values per chunk
+    __shared__ __attribute__((aligned(16))) float xs_l[2][kBlk * kChan];
+    __shared__ __attribute__((aligned(16))) float dts_l[2][kBlk * kChan];
+    __shared__ __attribute__((aligned(16))) float dys_l[2][kBlk * kChan];
+    __shared__ __attribute__((aligned(16))) float Bs_l[2][kBlk * 16];
+    __shared__ __attribute__((aligned(16))) float Cs_l[2][kBlk * 16];
     // the checkpoint is read into registers right after the barrier that
     // publishes it, so one buffer is enough (the next one is written after
     // the following barrier)
     __shared__ __attribute__((aligned(16))) float ck_l[kChan * 16];
     // [token][wave][row][quad lane][dB 4 | dC 4]: sums over the row's four channels
     __shared__ __attribute__((aligned(16))) float red_l[kBlk][4][4][4][8];
+    // d_x and d_dt of the block, [token][channel]
+    __shared__ __attribute__((aligned(16))) float gx_l[kBlk * kChan];
+    __shared__ __attribute__((aligned(16))) float gdt_l[kBlk * kChan];
 
     const int tid = threadIdx.x;
     const int q = tid & 3;
@@ -321,8 +332,8 @@ __global__ __launch_bounds__(kThreads) void bwd_fast(const BwdKP kp_arg) {
     const int n_blk = (L + kBlk - 1) / kBlk;
     const float* ckpt = p.ckpt;
     const int S = p.S;
-    float* d_x = p.d_x;
-    float* d_dt = p.d_dt;
+    float* d_x = p.d_x + seq + (int64_t)cb * kChan;
+    float* d_dt = p.d_dt + seq + (int64_t)cb * kChan;
     // Slots: each thread stages at most NS 16-byte chunks per tile, every slot
     // drawn from one or two arrays split at a wave boundary (so the choice of
     // array is a select, not a lookup).  fp32: x, dt, dy (one chunk per
@@ -371,6 +382,22 @@ __global__ __launch_bounds__(kThreads) void bwd_fast(const BwdKP kp_arg) {
             stg[k] = *reinterpret_cast<const uint4*>(src);
         }
     };
+    // a staged chunk of io values into an fp32 tile (zeros for rows past the end)
+    auto put = [&](float* dst, const uint4& v, bool ok) __attribute__((always_inline)) {
+        if constexpr (ES == 2) {
+            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+            float f[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f[2 * e] = ok ? __uint_as_float(wv[e] << 16) : 0.0f;
+                f[2 * e + 1] = ok ? __uint_as_float(wv[e] & 0xffff0000u) : 0.0f;
+            }
+            *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
+            *reinterpret_cast<float4*>(dst + 4) = make_float4(f[4], f[5], f[6], f[7]);
+        } else {
+            *reinterpret_cast<uint4*>(dst) = ok ? v : make_uint4(0, 0, 0, 0);
+        }
+    };
     auto store_tile = [&](int buf, int b) __attribute__((always_inline)) {
         const int t0 = b * kBlk;
 #pragma unroll
@@ -378,31 +405,20 @@ __global__ __launch_bounds__(kThreads) void bwd_fast(const BwdKP kp_arg) {
             if (!slot_used(k)) continue;
             int arr, w;
             slot(k, arr, w);
-            char* dst;
-            bool ok = true;
             if (arr < 3) {
-                ok = t0 + w / CPR < L;
-                T* tile = arr == 0 ? xs_l[buf] : (arr == 1 ? dts_l[buf] : dys_l[buf]);
-                dst = reinterpret_cast<char*>(tile) + w * 16;
+                float* tile = arr == 0 ? xs_l[buf] : (arr == 1 ? dts_l[buf] : dys_l[buf]);
+                put(tile + w * VPC, stg[k], t0 + w / CPR < L);
             } else if (arr < 5) {
-                ok = t0 + w / CPB < L;
-                dst = reinterpret_cast<char*>(arr == 3 ? Bs_l[buf] : Cs_l[buf]) + w * 16;
+                put((arr == 3 ? Bs_l[buf] : Cs_l[buf]) + w * VPC, stg[k], t0 + w / CPB < L);
             } else {
-                dst = reinterpret_cast<char*>(ck_l) + w * 16;
+                *reinterpret_cast<uint4*>(ck_l + w * 4) = stg[k];
             }
-            *reinterpret_cast<uint4*>(dst) = ok ? stg[k] : make_uint4(0, 0, 0, 0);
         }
     };
-    auto rowv = [&](const T* tile, int k) __attribute__((always_inline)) { return to_f32(tile[k * kChan + cl]); };
-    auto quad4 = [&](const T* tile, int k, float (&v)[4]) __attribute__((always_inline)) {
-        if constexpr (ES == 2) {
-            const uint2 w = *reinterpret_cast<const uint2*>(tile + k * 16 + 4 * q);
-            v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xffff0000u);
-            v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xffff0000u);
-        } else {
-            const float4 w = *reinterpret_cast<const float4*>(tile + k * 16 + 4 * q);
-            v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
-        }
+    auto rowv = [&](const float* tile, int k) __attribute__((always_inline)) { return tile[k * kChan + cl]; };
+    auto quad4 = [&](const float* tile, int k, float (&v)[4]) __attribute__((always_inline)) {
+        const float4 w = *reinterpret_cast<const float4*>(tile + k * 16 + 4 * q);
+        v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
     };
 
     load_tile(n_blk - 1);
@@ -412,11 +428,11 @@ __global__ __launch_bounds__(kThreads) void bwd_fast(const BwdKP kp_arg) {
     for (int b = n_blk - 1; b >= 0; --b) {
         const int t0 = b * kBlk, buf = b & 1;
         const int nk = min(kBlk, L - t0);
-        const T* xs = xs_l[buf];
-        const T* dts = dts_l[buf];
-        const T* dys = dys_l[buf];
-        const T* Bt = Bs_l[buf];
-        const T* Ct = Cs_l[buf];
+        const float* xs = xs_l[buf];
+        const float* dts = dts_l[buf];
+        const float* dys = dys_l[buf];
+        const float* Bt = Bs_l[buf];
+        const float* Ct = Cs_l[buf];
         float h0[4];
         {
             const float4 ck = *reinterpret_cast<const float4*>(&ck_l[cl * 16 + 4 * q]);
@@ -443,6 +459,9 @@ __global__ __launch_bounds__(kThreads) void bwd_fast(const BwdKP kp_arg) {
         // adjoint over the block, last token first
 #pragma unroll
         for (int k = kBlk - 1; k >= 0; --k) {
+            // no contraction here: a product summed across lanes would otherwise be
+            // fused into the DPP add and formed twice
+#pragma clang fp contract(off)
             const float dyk = rowv(dys, k);
             const float draw = rowv(dts, k);
             const float dk = SOFTPLUS ? (k < nk ? softplus(draw) : 0.0f) : draw;
@@ -466,19 +485,21 @@ __global__ __launch_bounds__(kThreads) void bwd_fast(const BwdKP kp_arg) {
             }
             S1 = quad_sum(S1);
             S2 = quad_sum(S2);
-            if (q == 0 && k < nk) {
-                const int64_t idx = seq + (int64_t)(t0 + k) * d_inner + c;
+            if (q == 0) {
                 float ddt = fmaf(uk, S1, S2);
                 if constexpr (SOFTPLUS) ddt *= 1.0f / (1.0f + expf(-draw));
-                d_x[idx] = bad ? __builtin_nanf("") : fmaf(Dc, dyk, dk * S1);
-                d_dt[idx] = bad ? __builtin_nanf("") : ddt;
-                dD_acc = fmaf(dyk, uk, dD_acc);
+                gx_l[k * kChan + cl] = fmaf(Dc, dyk, dk * S1);
+                gdt_l[k * kChan + cl] = ddt;
+                if (k < nk) dD_acc = fmaf(dyk, uk, dD_acc);
             }
-            // sum the four channels of this 16-lane row (lanes 4j + q)
+            // sum the four channels of this 16-lane row (lanes 4j + q); the empty asm
+            // keeps the last add ahead of the branch below, where it stays fused
+            // with its DPP move
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 dBp[s] = row_shr_add<8>(row_shr_add<4>(dBp[s]));
                 dCp[s] = row_shr_add<8>(row_shr_add<4>(dCp[s]));
+                asm volatile("" : "+v"(dBp[s]), "+v"(dCp[s]));
             }
             if (lane_in_row >= 12) {
                 float* dst = &red_l[k][wave][row][q][0];
@@ -488,20 +509,44 @@ __global__ __launch_bounds__(kThreads) void bwd_fast(const BwdKP kp_arg) {
         }
         __syncthreads();
         // the block's channel sums: 16 tokens x (16 dB + 16 dC), 16 terms each, fixed order
-        for (int e = tid; e < kBlk * 32; e += kThreads) {
+        float bc[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int e = tid + kThreads * u;
             const int k = e / 32, m = e % 32;
-            if (k >= nk) continue;
             const int which = m >> 4, n = m & 15, qq = n >> 2, s = n & 3;
             float acc = 0.0f;
 #pragma unroll
             for (int w = 0; w < 4; ++w)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc += red_l[k][w][r][qq][which * 4 + s];
-            p.dbc_part[(((int64_t)cb * p.S + i) * L + t0 + k) * 32 + m] = acc;
+            bc[u] = acc;
         }
+        // the block's d_x / d_dt rows: thread -> token tid / 16, channels 4 (tid % 16) + 0..3
+        float4 gxv = *reinterpret_cast<const float4*>(&gx_l[tid * 4]);
+        float4 gdv = *reinterpret_cast<const float4*>(&gdt_l[tid * 4]);
         // next block's tiles into the other buffer; fetch the one after
         if (b > 0) store_tile(buf ^ 1, b - 1);
         load_tile(b - 2);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int e = tid + kThreads * u;
+            const int k = e / 32, m = e % 32;
+            if (k < nk) p.dbc_part[(((int64_t)cb * p.S + i) * L + t0 + k) * 32 + m] = bc[u];
+        }
+        {
+            const int k = tid >> 4;
+            if (bad) {
+                const float nan = __builtin_nanf("");
+                gxv = make_float4(nan, nan, nan, nan);
+                gdv = gxv;
+            }
+            if (k < nk) {
+                const int64_t off = (int64_t)(t0 + k) * d_inner + 4 * (tid & 15);
+                *reinterpret_cast<float4*>(d_x + off) = gxv;
+                *reinterpret_cast<float4*>(d_dt + off) = gdv;
+            }
+        }
         __syncthreads();
     }
     {
@@ -625,7 +670,8 @@ int launch_scan_bwd(const BwdArgs& a, hipStream_t stream) {
     const bool bf = sh.io == SSM_BF16;
     auto al16 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; };
     const bool fast = sh.N == 16 && sh.d_inner() % kChan == 0 && al16(a.x) && al16(a.dt) &&
-                      al16(a.dy) && al16(a.B) && al16(a.C) && al16(a.A) && al16(a.dstate);
+                      al16(a.dy) && al16(a.B) && al16(a.C) && al16(a.A) && al16(a.dstate) &&
+                      al16(a.d_x) && al16(a.d_dt);
     if (fast) {
         if (bf) {
             if (kp.softplus) hipLaunchKernelGGL((bwd_fast<bf16_t, true>), grid, dim3(kThreads), 0, stream, kp);
