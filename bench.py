@@ -106,8 +106,8 @@ COPY_FACTOR = {"fetch": 1.99993, "write": 1.00000}
 MEASURED_TRAFFIC = {
     "C1": {"sha256": "24d1fd524c88067dab34a3c7ba681f5ec38b6b2a65bef8a7ef795840bdcf8557", "fetch_kib": 34151.4, "write_kib": 33024.0},
     "C2": {"sha256": "24d1fd524c88067dab34a3c7ba681f5ec38b6b2a65bef8a7ef795840bdcf8557", "fetch_kib": 339338.3, "write_kib": 330240.0},
-    "C3": {"sha256": "f5e2d9f87c0bd08e4b2b8f1c670c3e860c9a68bbc97d7c6f68c1851c8eef1f23", "fetch_kib": 145151.0, "write_kib": 174081.0},
-    "C4": {"sha256": "791de295b4ba1e51629138beed7dc7d1bcff985abaf804fdc0bc846c7524086b", "fetch_kib": 1337402.2, "write_kib": 2306036.0},
+    "C3": {"sha256": "b0591ad1672f9c548339e541594127fcaa68e16a1916aa71e249cdc017a61ddb", "fetch_kib": 144438.3, "write_kib": 174081.6},
+    "C4": {"sha256": "e58840d56cd1aa4d080b772f47e4df7370b8081d06d18cde71ed1fd041605965", "fetch_kib": 1337163.3, "write_kib": 2306036.0},
 }
 KERNEL_SOURCES = {
     "C0": ("scan_fwd.hip", "scan_fwd_ts.hip", "scan_fwd_quad.hip", "device_common.h"),
