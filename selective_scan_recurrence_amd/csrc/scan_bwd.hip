@@ -17,7 +17,7 @@
 // and dD += dy_t u_t, dh_0 = g after the first token, scattered to row ids[i].
 //
 // Kernel 1 (scan_fwd_quad.hip, quad_ckpt) stores the state entering every
-// 16-token block.  Kernel 2 (bwd_rev) walks the blocks backwards: it stages
+// block of kCkpt (8) tokens.  Kernel 2 (bwd_rev) walks the blocks backwards: it stages
 // the block's inputs in LDS, recomputes the block's decays and states from
 // the checkpoint into registers, then runs the adjoint over the block.  The
 // layout is the forward's quad one: four lanes per channel, four states per
@@ -36,7 +36,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kChan = 64;  // channels per workgroup
-constexpr int kBlk = 16;   // tokens per block (checkpoint spacing)
+constexpr int kBlk = kCkpt;  // tokens per block (checkpoint spacing)
 
 struct BwdKP {
     const float* A;
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void bwd_rev(BwdKP p) {
             }
         }
         __syncthreads();
-        // the block's channel sums: 16 tokens x (16 dB + 16 dC), 16 terms each, fixed order
+        // the block's channel sums: kBlk tokens x (16 dB + 16 dC), 16 terms each, fixed order
         for (int e = tid; e < kBlk * 32; e += kThreads) {
             const int k = e / 32, m = e % 32;
             if (k >= nk) continue;
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void bwd_rev(BwdKP p) {
 //  - The products summed across channels (dB, dC) are formed without
 //    contraction so that each DPP row step is a single add.
 template <typename T, bool SOFTPLUS>
-__global__ __launch_bounds__(kThreads) void bwd_fast(const BwdKP kp_arg) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void bwd_fast(const BwdKP kp_arg) {
     // lambdas below capture locals only (capturing the kernel argument would
     // force it into scratch memory)
     const BwdKP p = kp_arg;
@@ -335,29 +335,28 @@ __global__ __launch_bounds__(kThreads) void bwd_fast(const BwdKP kp_arg) {
     float* d_x = p.d_x + seq + (int64_t)cb * kChan;
     float* d_dt = p.d_dt + seq + (int64_t)cb * kChan;
     // Slots: each thread stages at most NS 16-byte chunks per tile, every slot
-    // drawn from one or two arrays split at a wave boundary (so the choice of
-    // array is a select, not a lookup).  fp32: x, dt, dy (one chunk per
-    // thread each), B (threads 0-63) or C (64-127), checkpoint.  bf16: x
-    // (threads 0-127) or dt (128-255), dy (0-127) or B (128-159) or C
-    // (160-191), checkpoint.
-    constexpr int NS = ES == 4 ? 5 : 3;
-    static_assert(CHK == kThreads && (ES == 2 ? CHX == 128 && CHB == 32 : CHX == 256 && CHB == 64),
-                  "slot layout");
+    // drawn from arrays split at wave or 16-lane boundaries (so the choice of
+    // array is a select, not a lookup).  fp32: x (threads 0-127) or dt
+    // (128-255); dy (0-127) or B (128-159) or C (160-191); checkpoint.  bf16:
+    // x (wave 0) or dt (wave 1) or dy (wave 2) or B (192-207) or C (208-223);
+    // checkpoint.
+    constexpr int NS = ES == 4 ? 3 : 2;
+    static_assert(kBlk == 8 && CHK == kThreads &&
+                  (ES == 2 ? CHX == 64 && CHB == 16 : CHX == 128 && CHB == 32), "slot layout");
     uint4 stg[NS];
     // where slot k of this thread comes from: array id (0 x, 1 dt, 2 dy, 3 B, 4 C, 5 ckpt) and chunk
     auto slot = [&](int k, int& arr, int& w) __attribute__((always_inline)) {
         if constexpr (ES == 4) {
-            if (k < 3) { arr = k; w = tid; }
-            else if (k == 3) { arr = tid < 64 ? 3 : 4; w = tid & 63; }
-            else { arr = 5; w = tid; }
-        } else {
             if (k == 0) { arr = tid < 128 ? 0 : 1; w = tid & 127; }
             else if (k == 1) { arr = tid < 128 ? 2 : tid < 160 ? 3 : 4; w = tid < 128 ? tid : (tid - 128) & 31; }
+            else { arr = 5; w = tid; }
+        } else {
+            if (k == 0) { arr = tid < 192 ? (tid >> 6) : tid < 208 ? 3 : 4; w = tid < 192 ? (tid & 63) : (tid & 15); }
             else { arr = 5; w = tid; }
         }
     };
     auto slot_used = [&](int k) __attribute__((always_inline)) {
-        return !(ES == 2 && k == 1 && tid >= 192) && !(ES == 4 && k == 3 && tid >= 128);
+        return !(ES == 2 && k == 0 && tid >= 224) && !(ES == 4 && k == 1 && tid >= 192);
     };
     auto load_tile = [&](int b) __attribute__((always_inline)) {
         const int bb = b < 0 ? 0 : b;
@@ -508,10 +507,11 @@ __global__ __launch_bounds__(kThreads) void bwd_fast(const BwdKP kp_arg) {
             }
         }
         __syncthreads();
-        // the block's channel sums: 16 tokens x (16 dB + 16 dC), 16 terms each, fixed order
-        float bc[2];
+        // the block's channel sums: kBlk tokens x (16 dB + 16 dC), 16 terms each, fixed order
+        constexpr int NBC = kBlk * 32 / kThreads;  // channel sums per thread
+        float bc[NBC];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < NBC; ++u) {
             const int e = tid + kThreads * u;
             const int k = e / 32, m = e % 32;
             const int which = m >> 4, n = m & 15, qq = n >> 2, s = n & 3;
@@ -523,13 +523,15 @@ __global__ __launch_bounds__(kThreads) void bwd_fast(const BwdKP kp_arg) {
             bc[u] = acc;
         }
         // the block's d_x / d_dt rows: thread -> token tid / 16, channels 4 (tid % 16) + 0..3
-        float4 gxv = *reinterpret_cast<const float4*>(&gx_l[tid * 4]);
-        float4 gdv = *reinterpret_cast<const float4*>(&gdt_l[tid * 4]);
+        constexpr int NGX = kBlk * kChan / 4;  // 16-byte pieces of the d_x tile
+        const int tg = tid < NGX ? tid : 0;
+        float4 gxv = *reinterpret_cast<const float4*>(&gx_l[tg * 4]);
+        float4 gdv = *reinterpret_cast<const float4*>(&gdt_l[tg * 4]);
         // next block's tiles into the other buffer; fetch the one after
         if (b > 0) store_tile(buf ^ 1, b - 1);
         load_tile(b - 2);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < NBC; ++u) {
             const int e = tid + kThreads * u;
             const int k = e / 32, m = e % 32;
             if (k < nk) p.dbc_part[(((int64_t)cb * p.S + i) * L + t0 + k) * 32 + m] = bc[u];
@@ -541,7 +543,7 @@ __global__ __launch_bounds__(kThreads) void bwd_fast(const BwdKP kp_arg) {
                 gxv = make_float4(nan, nan, nan, nan);
                 gdv = gxv;
             }
-            if (k < nk) {
+            if (tid < NGX && k < nk) {
                 const int64_t off = (int64_t)(t0 + k) * d_inner + 4 * (tid & 15);
                 *reinterpret_cast<float4*>(d_x + off) = gxv;
                 *reinterpret_cast<float4*>(d_dt + off) = gdv;

@@ -65,7 +65,7 @@ __device__ __forceinline__ float ld(const T* p) { return to_f32(*p); }
 
 // The scan over tokens [t_begin, t_end) of one chunk.  MODE 0: end state
 // only (kernel 1); MODE 1: y, and the final state if this is the last chunk;
-// MODE 2: the state entering every 16-token block, for the backward pass.
+// MODE 2: the state entering every kCkpt-token block, for the backward pass.
 template <typename T, int K, int MODE>
 __device__ __forceinline__ void quad_chunk(const QuadKP& p, int i, int c_raw, int q,
                                            int t_begin, int t_end, float (&h)[4],
@@ -126,9 +126,9 @@ __device__ __forceinline__ void quad_chunk(const QuadKP& p, int i, int c_raw, in
         const int t0 = t_begin + 4 * g;
         const int tt0 = (4 * g) & (kTile - 1);
         const int buf = ((4 * g) / kTile) & 1;
-        if constexpr (MODE == 2) {  // state entering each 16-token block
-            if (((t0 - t_begin) & 15) == 0 && active) {
-                float* ck = p.agg + ((((int64_t)(t0 >> 4) * p.S + i) * p.d_inner + c) * 16 + 4 * q);
+        if constexpr (MODE == 2) {  // state entering each kCkpt-token block
+            if (((t0 - t_begin) & (kCkpt - 1)) == 0 && active) {
+                float* ck = p.agg + ((((int64_t)(t0 / kCkpt) * p.S + i) * p.d_inner + c) * 16 + 4 * q);
                 *reinterpret_cast<float4*>(ck) = make_float4(h[0], h[1], h[2], h[3]);
             }
         }
@@ -312,9 +312,9 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int cb, int q
     // One group of four tokens; FULL: every token of the group is < t_end.
     auto group = [&](int g, bool full_tile, int tb) {
         const int tt = 4 * g + q;  // owned row of this tile
-        if constexpr (MODE == 2) {  // state entering each 16-token block
-            if (((tb + 4 * g - t_begin) & 15) == 0) {
-                float* ck = p.agg + ((((int64_t)((tb + 4 * g) >> 4) * p.S + i) * p.d_inner + c) * 16 + 4 * q);
+        if constexpr (MODE == 2) {  // state entering each kCkpt-token block
+            if (((tb + 4 * g - t_begin) & (kCkpt - 1)) == 0) {
+                float* ck = p.agg + ((((int64_t)((tb + 4 * g) / kCkpt) * p.S + i) * p.d_inner + c) * 16 + 4 * q);
                 *reinterpret_cast<float4*>(ck) = make_float4(h[0], h[1], h[2], h[3]);
             }
         }
@@ -525,7 +525,7 @@ __global__ __launch_bounds__(kThreads) void quad_out(QuadKP p) {
     }
 }
 
-// Forward scan that stores the state entering every 16-token block to
+// Forward scan that stores the state entering every kCkpt-token block to
 // p.agg ([n_blocks][S][d_inner][16]); the backward pass recomputes each block
 // from it.
 template <typename T, bool TILED, bool SOFTPLUS>

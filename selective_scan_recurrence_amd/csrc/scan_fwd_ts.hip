@@ -175,7 +175,9 @@ __global__ __launch_bounds__(64 * J) void ts_fwd(TsKP p) {
                   "whole chunks per thread");
     constexpr int KA = NG == 1 ? CH_ARR / NT : 1;  // chunks per array per thread
     constexpr int NA = 4 / NG;                     // arrays per thread
-    const int grp = NG == 1 ? 0 : tid / CH_ARR;    // wave-uniform (CH_ARR is a multiple of 64)
+    // wave-uniform (CH_ARR is a multiple of 64); readfirstlane tells the compiler
+    // so, which keeps the buffer descriptors in scalar registers
+    const int grp = NG == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid / CH_ARR);
     const int te = NG == 1 ? tid : tid % CH_ARR;
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     u32x4 stg[NA][KA];

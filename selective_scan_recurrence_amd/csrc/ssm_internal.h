@@ -10,6 +10,10 @@
 
 namespace ssm {
 
+// Tokens between the states the forward stores for the backward (the backward's
+// block length).
+constexpr int kCkpt = 8;
+
 // Checked, expanded scan dimensions.
 struct Shape {
     int64_t S, L, H, P, N, G, R;  // seqs, tokens, heads, head_dim, d_state, groups, state rows
