@@ -241,7 +241,10 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int cb, int q
     const char* xg = static_cast<const char*>(p.x) + ((int64_t)i * p.L * p.d_inner + cb * 64) * ES;
     const char* dg = static_cast<const char*>(p.dt) + ((int64_t)i * p.L * p.d_inner + cb * 64) * ES;
     char* yg = static_cast<char*>(p.y) + ((int64_t)i * p.L * p.d_inner + cb * 64) * ES;
-    const char* bcg = static_cast<const char*>((tid >> 7) ? p.C : p.B) + (int64_t)i * p.L * 16 * ES;
+    // B for waves 0-1, C for waves 2-3 (readfirstlane: wave-uniform, so its
+    // buffer descriptor stays in scalar registers)
+    const int c_half = __builtin_amdgcn_readfirstlane(tid >> 7);
+    const char* bcg = static_cast<const char*>(c_half ? p.C : p.B) + (int64_t)i * p.L * 16 * ES;
     const float Dc = p.has_D ? p.D[c] : 0.0f;
 
     float w[4] = {0.f, 0.f, 0.f, 0.f};
@@ -261,35 +264,41 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int cb, int q
         }
     }
 
-    uint4 sx[2], sdt[2], sbc;
+    // Tile traffic goes through buffer descriptors based at the tile's first
+    // row and ending at t_end: rows past the end read as zero and stores past
+    // it are dropped, so no branch stands around a load or a store and the
+    // per-lane offsets stay the same on every tile.
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    auto rsrc = [&](const char* base, int tb, int64_t row_bytes) {
+        const int rows = min(t_end - tb, TT);
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base) + (int64_t)tb * row_bytes, 0,
+                                                 rows > 0 ? (int)(rows * row_bytes) : 0, 0x00020000);
+    };
+    int xoff[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int e = tid + kThreads * r;
+        xoff[r] = (int)((e / CPR) * row_stride) + (e % CPR) * 16;
+    }
+    const int bcoff = ((tid & (kThreads / 2 - 1)) / CPT) * 16 * ES + ((tid & (kThreads / 2 - 1)) % CPT) * 16;
+    u32x4 sx[2], sdt[2], sbc;
     auto load_tile = [&](int tb) {
+        const auto rx = rsrc(xg, tb, row_stride), rd = rsrc(dg, tb, row_stride);
+        const auto rb = rsrc(bcg, tb, 16 * ES);
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
-            const int e = tid + kThreads * r;
-            const int row = e / CPR, col = e % CPR;
-            const int t = tb + row;
-            if (t < t_end) {
-                sx[r] = *reinterpret_cast<const uint4*>(xg + (int64_t)t * row_stride + col * 16);
-                sdt[r] = *reinterpret_cast<const uint4*>(dg + (int64_t)t * row_stride + col * 16);
-            } else {
-                sx[r] = make_uint4(0, 0, 0, 0);
-                sdt[r] = make_uint4(0, 0, 0, 0);
-            }
+            sx[r] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[r], 0, 0);
+            sdt[r] = __builtin_amdgcn_raw_buffer_load_b128(rd, xoff[r], 0, 0);
         }
-        const int e = tid & (kThreads / 2 - 1);
-        const int t = tb + e / CPT;
-        if (t < t_end)
-            sbc = *reinterpret_cast<const uint4*>(bcg + ((int64_t)t * 16) * ES + (e % CPT) * 16);
-        else
-            sbc = make_uint4(0, 0, 0, 0);
+        sbc = __builtin_amdgcn_raw_buffer_load_b128(rb, bcoff, 0, 0);
     };
     auto store_tile = [&]() {
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
             const int e = tid + kThreads * r;
             const int row = e / CPR, col = e % CPR;
-            *reinterpret_cast<uint4*>(x_l + row * XS + col * 16) = sx[r];
-            *reinterpret_cast<uint4*>(dt_l + row * XS + col * 16) = sdt[r];
+            *reinterpret_cast<u32x4*>(x_l + row * XS + col * 16) = sx[r];
+            *reinterpret_cast<u32x4*>(dt_l + row * XS + col * 16) = sdt[r];
         }
         const int e = tid & (kThreads / 2 - 1);
         const int tok = e / CPT, part = e % CPT;
@@ -305,7 +314,7 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int cb, int q
             *reinterpret_cast<float4*>(dst + part * 8) = make_float4(f[0], f[1], f[2], f[3]);
             *reinterpret_cast<float4*>(dst + part * 8 + 4) = make_float4(f[4], f[5], f[6], f[7]);
         } else {
-            *reinterpret_cast<uint4*>(dst + part * 4) = sbc;
+            *reinterpret_cast<u32x4*>(dst + part * 4) = sbc;
         }
     };
 
@@ -388,7 +397,7 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int cb, int q
     for (int tile = 0; tile < n_tiles; ++tile) {
         const int tb = t_begin + tile * TT;
         const bool more = tile + 1 < n_tiles;
-        if (more) load_tile(tb + TT);
+        load_tile(tb + TT);  // past the end: zero rows, never staged
         if (tb + TT <= t_end) {
 #pragma unroll 2
             for (int g = 0; g < TT / 4; ++g) group(g, true, tb);
@@ -398,13 +407,13 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int cb, int q
         }
         __syncthreads();  // tile fully read (and y tile fully written)
         if constexpr (MODE == 1) {
+            const auto ry = rsrc(yg, tb, row_stride);
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
                 const int e = tid + kThreads * r;
                 const int row = e / CPR, col = e % CPR;
-                if (tb + row < t_end)
-                    *reinterpret_cast<uint4*>(yg + (int64_t)(tb + row) * row_stride + col * 16) =
-                        *reinterpret_cast<const uint4*>(y_l + row * XS + col * 16);
+                __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(y_l + row * XS + col * 16),
+                                                       ry, xoff[r], 0, 0);
             }
         }
         if (more) store_tile();
