@@ -104,10 +104,10 @@ def valu_slots_per_channel_token(p, backward=False) -> float:
 # kernel sources it was taken on; bench.py reports null once any of them changes.
 COPY_FACTOR = {"fetch": 1.99993, "write": 1.00000}
 MEASURED_TRAFFIC = {
-    "C1": {"sha256": "24d1fd524c88067dab34a3c7ba681f5ec38b6b2a65bef8a7ef795840bdcf8557", "fetch_kib": 34151.4, "write_kib": 33024.0},
-    "C2": {"sha256": "24d1fd524c88067dab34a3c7ba681f5ec38b6b2a65bef8a7ef795840bdcf8557", "fetch_kib": 339338.3, "write_kib": 330240.0},
+    "C1": {"sha256": "b54488bd1c4354444b1903423f99b869e566fd61179612657f748cdaf2dc0c37", "fetch_kib": 34152.3, "write_kib": 33024.0},
+    "C2": {"sha256": "b54488bd1c4354444b1903423f99b869e566fd61179612657f748cdaf2dc0c37", "fetch_kib": 339353.1, "write_kib": 330240.0},
     "C3": {"sha256": "b0591ad1672f9c548339e541594127fcaa68e16a1916aa71e249cdc017a61ddb", "fetch_kib": 144438.3, "write_kib": 174081.6},
-    "C4": {"sha256": "e58840d56cd1aa4d080b772f47e4df7370b8081d06d18cde71ed1fd041605965", "fetch_kib": 1337163.3, "write_kib": 2306036.0},
+    "C4": {"sha256": "2a19fd3700bb14b898a8f31d961c12501b1bdb0583c23b31fa03aca4474e50b7", "fetch_kib": 1665248.8, "write_kib": 2961396.0},
 }
 KERNEL_SOURCES = {
     "C0": ("scan_fwd.hip", "scan_fwd_ts.hip", "scan_fwd_quad.hip", "device_common.h"),

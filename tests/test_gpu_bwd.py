@@ -82,6 +82,12 @@ CASES = {
     "dstate_zero": dict(dstate_std=0.0),
     "aligned_bf16_tiled": dict(n_head=192, n_tokens=130, io="bf16"),
     "aligned_f32_tiled": dict(n_head=64, n_tokens=77),
+    # the prefetched path (64 | channels) around its 8-token block length
+    "aligned_L1": dict(n_head=64, n_tokens=1),
+    "aligned_L7_bf16_softplus": dict(n_head=64, n_tokens=7, io="bf16", dt_softplus=True, dt_shift=0.0),
+    "aligned_L8": dict(n_head=128, n_tokens=8),
+    "aligned_L9_bf16": dict(n_head=64, n_tokens=9, io="bf16"),
+    "aligned_L24_perm": dict(n_head=64, n_tokens=24, n_state_rows=5, ids="perm"),
 }
 
 
