@@ -77,6 +77,9 @@ def _load():
             lib.oracle_conv_fwd.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int64,
                                             ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
             lib.oracle_conv_fwd.restype = ctypes.c_int
+            lib.oracle_conv_bwd.argtypes = [P, P, P, P, P, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
+            lib.oracle_conv_bwd.restype = ctypes.c_int
             lib.oracle_threads_used.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int]
             lib.oracle_threads_used.restype = ctypes.c_int
             _lib = lib
@@ -190,6 +193,25 @@ def conv_fwd(sx, w, apply_silu=False):
     if rc:
         raise ValueError(f"oracle_conv_fwd failed ({rc})")
     return out
+
+
+def conv_bwd(sx, w, dout, apply_silu=False):
+    """Backward of ``conv_fwd`` (the ggmlR ssm_conv backward): sx [n_s][d_inner]
+    [d_conv-1+n_t], w [d_inner][d_conv], dout [n_s][n_t][d_inner] ->
+    (d_sx with the shape of sx, d_w with the shape of w)."""
+    sx, w, dout = _f64(sx), _f64(w), _f64(dout)
+    n_s, d_inner, length = sx.shape
+    K = w.shape[1]
+    n_t = length - (K - 1)
+    if n_t < 0 or w.shape[0] != d_inner or dout.shape != (n_s, n_t, d_inner):
+        raise ValueError("bad conv shapes")
+    d_sx = np.zeros_like(sx)
+    d_w = np.zeros_like(w)
+    rc = _load().oracle_conv_bwd(_ptr(sx), _ptr(w), _ptr(dout), _ptr(d_sx), _ptr(d_w), n_s, n_t,
+                                 d_inner, K, int(bool(apply_silu)))
+    if rc:
+        raise ValueError(f"oracle_conv_bwd failed ({rc})")
+    return d_sx, d_w
 
 
 def threads_used(n_head: int, n_threads: Optional[int] = None) -> int:

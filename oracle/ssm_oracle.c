@@ -19,6 +19,10 @@
  *    dL/dh_t = C^T dL/dy_t + A_bar dL/dh_{t+1}, with dL/dh_0 = A_bar dL/dh_1.
  *  - "mambazip mamba1/model.rs", accumulate_token_step_gradients: the
  *    per-element gradients of the selective step (dC, dB, d(u), d(dt), dA, dD).
+ *  - "ggmlR tests/testthat/test-ssm-rwkv.R", the ssm_conv backward block:
+ *    ggml_ssm_conv_back packs the gradient of sx then that of the conv
+ *    weights; its tests compare both with a central difference and give the
+ *    weight gradient of loss = sum(output) in closed form.
  *
  * Readings where the pages leave a step open (each also listed in the design
  * notes): dt is used as given unless the softplus flag is set; the initial
@@ -344,6 +348,43 @@ int oracle_conv_fwd(const double *sx, const double *w, double *out, int64_t n_s,
                 for (int64_t j = 0; j < d_conv; j++)
                     acc += sx[(s * d_inner + ch) * len + t + j] * w[ch * d_conv + j];
                 out[(s * n_t + t) * d_inner + ch] = apply_silu ? silu(acc) : acc;
+            }
+    return 0;
+}
+
+/* Backward of oracle_conv_fwd, the ggmlR extension's ssm_conv backward
+ * ("ggmlR tests/testthat/test-ssm-rwkv.R", the ssm_conv backward block:
+ * ggml_ssm_conv_back packs the gradient of sx followed by that of the
+ * weights).  With z_t = sum_j sx[t+j] w[j], out_t = z_t (or SiLU(z_t)) and
+ * the upstream gradient dout [n_s][n_t][d_inner]:
+ *   g_t   = dout_t, or dout_t * s(z_t) (1 + z_t (1 - s(z_t))) with the SiLU
+ *           (the derivative of z s(z), s the logistic function);
+ *   d_sx[tau] = sum over the (t, j) with t + j = tau of g_t w[j];
+ *   d_w[j]    = sum over sequences and t of g_t sx[t+j].
+ * d_sx has the layout of sx, d_w that of w. */
+int oracle_conv_bwd(const double *sx, const double *w, const double *dout, double *d_sx,
+                    double *d_w, int64_t n_s, int64_t n_t, int64_t d_inner, int32_t d_conv,
+                    int32_t apply_silu) {
+    if (!sx || !w || !dout || !d_sx || !d_w || n_s < 0 || n_t < 0 || d_inner < 1 || d_conv < 1)
+        return -1;
+    const int64_t len = d_conv - 1 + n_t;
+    memset(d_sx, 0, (size_t)(n_s * d_inner * len) * sizeof(double));
+    memset(d_w, 0, (size_t)(d_inner * d_conv) * sizeof(double));
+    for (int64_t s = 0; s < n_s; s++)
+        for (int64_t t = 0; t < n_t; t++)
+            for (int64_t ch = 0; ch < d_inner; ch++) {
+                const double *row = sx + (s * d_inner + ch) * len;
+                double g = dout[(s * n_t + t) * d_inner + ch];
+                if (apply_silu) {
+                    double z = 0.0;
+                    for (int64_t j = 0; j < d_conv; j++) z += row[t + j] * w[ch * d_conv + j];
+                    const double sg = sigmoid(z);
+                    g *= sg * (1.0 + z * (1.0 - sg));
+                }
+                for (int64_t j = 0; j < d_conv; j++) {
+                    d_sx[(s * d_inner + ch) * len + t + j] += g * w[ch * d_conv + j];
+                    d_w[ch * d_conv + j] += g * row[t + j];
+                }
             }
     return 0;
 }

@@ -34,6 +34,11 @@ MUTANTS = {
     "bwd_ds_to_sequence_row": ("J->d_s[((r * H + h) * P + p) * N + n] += g[n];",
                                "J->d_s[((i * H + h) * P + p) * N + n] += g[n];"),
     "bwd_softplus_chain_dropped": ("if (d->dt_softplus) ddt *= sigmoid(J->dt[(i * L + t) * H + h]);", ""),
+    "conv_bwd_tap_reversed": ("d_sx[(s * d_inner + ch) * len + t + j] += g * w[ch * d_conv + j];",
+                              "d_sx[(s * d_inner + ch) * len + t + j] += g * w[ch * d_conv + (d_conv - 1 - j)];"),
+    "conv_bwd_dw_window_shift": ("d_w[ch * d_conv + j] += g * row[t + j];",
+                                 "d_w[ch * d_conv + j] += g * row[t + d_conv - 1 - j];"),
+    "conv_bwd_silu_derivative_is_sigmoid": ("g *= sg * (1.0 + z * (1.0 - sg));", "g *= sg;"),
 }
 
 
@@ -48,7 +53,8 @@ def test_pins_catch_planted_mistake(name, tmp_path):
     subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-o", str(so), str(c_file),
                            "-lm", "-lpthread"])
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                        "tests/test_oracle_pins.py", "tests/test_oracle_bwd_pins.py"],
+                        "tests/test_oracle_pins.py", "tests/test_oracle_bwd_pins.py",
+                        "tests/test_oracle_conv_bwd_pins.py"],
                        cwd=ROOT, env=dict(os.environ, SSM_ORACLE_LIB=str(so)),
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
