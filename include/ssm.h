@@ -138,6 +138,33 @@ int ssm_conv_fwd(const void *sx, const float *w, void *out, int64_t n_s, int64_t
                  int64_t d_inner, int32_t d_conv, int32_t io_dtype, int32_t apply_silu,
                  ssm_stream_t stream);
 
+/* ssm_conv_bwd: backward of ssm_conv_fwd, the ggmlR extension's ssm_conv
+ * backward ("ggmlR tests/testthat/test-ssm-rwkv.R", the ssm_conv backward
+ * block; ggml_ssm_conv_back).  With z = sum_j sx[s][c][t + j] * w[c][j]:
+ *   g[s][t][c] = dout[s][t][c]                       (apply_silu == 0)
+ *   g[s][t][c] = dout[s][t][c] * d/dz (z * sigmoid(z))  (apply_silu != 0,
+ *                 at the pre-activation recomputed from sx and w)
+ *   d_sx[s][c][tau] = sum_j w[c][j] * g[s][tau - j][c]   (0 <= tau - j < n_t)
+ *   d_w[c][j]       = sum_{s,t} g[s][t][c] * sx[s][c][t + j]
+ *  - sx [n_s][d_inner][d_conv-1+n_t] has dtype io_dtype; w [d_inner][d_conv],
+ *    dout [n_s][n_t][d_inner] (the gradient of ssm_conv_fwd's out, e.g. the
+ *    d_x of selective_scan_bwd when the scan consumed that output) are f32.
+ *  - dgrad (f32, caller-owned) receives d_sx [n_s][d_inner][d_conv-1+n_t]
+ *    followed by d_w [d_inner][d_conv], the page's packed order; every
+ *    element is written.
+ *  - workspace (device, caller-owned, at least ssm_conv_bwd_workspace_bytes
+ *    bytes, 4-byte aligned; may be NULL when that is 0) holds per-tile
+ *    partial weight gradients; its contents need no initialisation.  d_w is
+ *    summed in a fixed order, so results repeat bitwise.
+ *  - sx and dout may be NULL when they have no elements (n_t = 0 for dout).
+ *  - Errors as ssm_conv_fwd, plus SSM_ERR_WORKSPACE for a short workspace;
+ *    nothing is launched on error.  Asynchronous on stream. */
+size_t ssm_conv_bwd_workspace_bytes(int64_t n_s, int64_t n_t, int64_t d_inner, int32_t d_conv);
+int ssm_conv_bwd(const void *sx, const float *w, const float *dout, float *dgrad, int64_t n_s,
+                 int64_t n_t, int64_t d_inner, int32_t d_conv, int32_t io_dtype,
+                 int32_t apply_silu, void *workspace, size_t workspace_bytes,
+                 ssm_stream_t stream);
+
 /* selective_scan_fwd: the scan over n_tokens tokens for every sequence.
  *  - Sequence i starts from state row ids[i] of s.  An id outside
  *    [0, n_state_rows) is not read: that sequence's y and state are written

@@ -20,7 +20,8 @@ SSM_DEVERR_IDS = 1
 
 EXPORTS = ("ssm_status_str", "ssm_version", "ssm_scan_out_bytes", "ssm_scan_state_offset_bytes",
            "ssm_scan_dgrad_layout", "ssm_scan_workspace_bytes", "ssm_conv_fwd",
-           "selective_scan_fwd", "selective_scan_bwd", "ssm_get_device_error")
+           "ssm_conv_bwd_workspace_bytes", "ssm_conv_bwd", "selective_scan_fwd",
+           "selective_scan_bwd", "ssm_get_device_error")
 
 
 class SsmError(RuntimeError):
@@ -66,6 +67,10 @@ def load():
         lib.ssm_scan_workspace_bytes.restype = SZ
         lib.ssm_conv_fwd.argtypes = [P, P, P, I64, I64, I64, I32, I32, I32, P]
         lib.ssm_conv_fwd.restype = ctypes.c_int
+        lib.ssm_conv_bwd_workspace_bytes.argtypes = [I64, I64, I64, I32]
+        lib.ssm_conv_bwd_workspace_bytes.restype = SZ
+        lib.ssm_conv_bwd.argtypes = [P, P, P, P, I64, I64, I64, I32, I32, I32, P, SZ, P]
+        lib.ssm_conv_bwd.restype = ctypes.c_int
         lib.selective_scan_fwd.argtypes = [D] + [P] * 13 + [SZ, P]
         lib.selective_scan_fwd.restype = ctypes.c_int
         lib.selective_scan_bwd.argtypes = [D] + [P] * 11 + [SZ, P]
@@ -130,6 +135,18 @@ def ssm_conv_fwd(sx, w, out, n_s, n_t, d_inner, d_conv, io_dtype, apply_silu, st
     rc = load().ssm_conv_fwd(_ptr(sx), _ptr(w), _ptr(out), int(n_s), int(n_t), int(d_inner),
                              int(d_conv), int(io_dtype), int(apply_silu), _stream(stream))
     return _check(rc, "ssm_conv_fwd")
+
+
+def ssm_conv_bwd_workspace_bytes(n_s, n_t, d_inner, d_conv) -> int:
+    return load().ssm_conv_bwd_workspace_bytes(int(n_s), int(n_t), int(d_inner), int(d_conv))
+
+
+def ssm_conv_bwd(sx, w, dout, dgrad, n_s, n_t, d_inner, d_conv, io_dtype, apply_silu, workspace,
+                 workspace_bytes, stream=None):
+    rc = load().ssm_conv_bwd(_ptr(sx), _ptr(w), _ptr(dout), _ptr(dgrad), int(n_s), int(n_t),
+                             int(d_inner), int(d_conv), int(io_dtype), int(apply_silu),
+                             _ptr(workspace), int(workspace_bytes), _stream(stream))
+    return _check(rc, "ssm_conv_bwd")
 
 
 def selective_scan_fwd(desc, s, x, dt, A, B, C, D, ids, conv_w, conv_state, out,

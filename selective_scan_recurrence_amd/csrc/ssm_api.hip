@@ -135,6 +135,35 @@ int ssm_conv_fwd(const void* sx, const float* w, void* out, int64_t n_s, int64_t
                            static_cast<hipStream_t>(stream));
 }
 
+size_t ssm_conv_bwd_workspace_bytes(int64_t n_s, int64_t n_t, int64_t d_inner, int32_t d_conv) {
+    if (n_s < 0 || n_t < 0 || d_inner < 1 || d_conv < 1 || d_conv > 8 || n_s > 65535) return 0;
+    int64_t len = d_conv - 1 + n_t, t1, t2;
+    if (!mul_ok(len, d_inner, &t1) || t1 > INT_MAX || !mul_ok(t1, n_s, &t2)) return 0;
+    return conv_bwd_workspace_bytes(n_s, n_t, d_inner, d_conv);
+}
+
+int ssm_conv_bwd(const void* sx, const float* w, const float* dout, float* dgrad, int64_t n_s,
+                 int64_t n_t, int64_t d_inner, int32_t d_conv, int32_t io_dtype, int32_t apply_silu,
+                 void* workspace, size_t workspace_bytes_, ssm_stream_t stream) {
+    if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
+    if (n_s < 0 || n_t < 0 || d_inner < 1 || d_conv < 1 || d_conv > 8) return SSM_ERR_SHAPE;
+    if (n_s > 65535) return SSM_ERR_SHAPE;
+    int64_t len = d_conv - 1 + n_t, t1, t2;
+    if (!mul_ok(len, d_inner, &t1) || t1 > INT_MAX || !mul_ok(t1, n_s, &t2)) return SSM_ERR_SHAPE;
+    if (!mul_ok(n_t, d_inner, &t1) || t1 > INT_MAX) return SSM_ERR_SHAPE;
+    // sx and dout may be NULL only when they have no elements
+    if (!w || !dgrad || (!sx && n_s * len > 0) || (!dout && n_s * n_t > 0)) return SSM_ERR_NULL;
+    const size_t need = conv_bwd_workspace_bytes(n_s, n_t, d_inner, d_conv);
+    if (need && !workspace) return SSM_ERR_NULL;
+    if (workspace_bytes_ < need) return SSM_ERR_WORKSPACE;
+    const size_t es = io_dtype == SSM_BF16 ? 2 : 4;
+    if (!aligned(sx, es) || !aligned(w, 4) || !aligned(dout, 4) || !aligned(dgrad, 4) ||
+        (need && !aligned(workspace, 4)))
+        return SSM_ERR_ALIGN;
+    return launch_conv_bwd(sx, w, dout, dgrad, n_s, n_t, d_inner, d_conv, io_dtype, apply_silu,
+                           workspace, static_cast<hipStream_t>(stream));
+}
+
 int selective_scan_fwd(const ssm_scan_desc* desc, const float* s, const void* x, const void* dt,
                        const float* A, const void* B, const void* C, const float* D,
                        const int32_t* ids, const float* conv_w, const float* conv_state,

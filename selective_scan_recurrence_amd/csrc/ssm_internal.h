@@ -98,5 +98,9 @@ int launch_scan_fwd(const FwdArgs& a, hipStream_t stream);
 int launch_scan_bwd(const BwdArgs& a, hipStream_t stream);
 int launch_conv_fwd(const void* sx, const float* w, void* out, int64_t n_s, int64_t n_t,
                     int64_t d_inner, int d_conv, int io, int apply_silu, hipStream_t stream);
+size_t conv_bwd_workspace_bytes(int64_t n_s, int64_t n_t, int64_t d_inner, int d_conv);
+int launch_conv_bwd(const void* sx, const float* w, const float* dout, float* dgrad, int64_t n_s,
+                    int64_t n_t, int64_t d_inner, int d_conv, int io, int apply_silu, void* ws,
+                    hipStream_t stream);
 
 }  // namespace ssm

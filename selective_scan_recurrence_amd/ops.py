@@ -105,3 +105,28 @@ def conv_fwd(sx: torch.Tensor, w: torch.Tensor, apply_silu=False, out=None, stre
         out = torch.empty(n_s, n_t, d_inner, dtype=sx.dtype, device=sx.device)
     B.ssm_conv_fwd(sx, w, out, n_s, n_t, d_inner, d_conv, io, int(bool(apply_silu)), stream)
     return out
+
+
+def conv_bwd_workspace(n_s, n_t, d_inner, d_conv, device="cuda") -> torch.Tensor:
+    n = B.ssm_conv_bwd_workspace_bytes(n_s, n_t, d_inner, d_conv)
+    return torch.empty(max(n, 4), dtype=torch.uint8, device=device)
+
+
+def conv_bwd(sx: torch.Tensor, w: torch.Tensor, dout: torch.Tensor, apply_silu=False, ws=None,
+             dgrad=None, stream=None):
+    """Backward of ``conv_fwd``: dout [n_s][n_t][d_inner] (f32) ->
+    (d_sx [n_s][d_inner][d_conv-1+n_t], d_w [d_inner][d_conv]), both f32
+    views of one packed buffer (d_sx then d_w)."""
+    n_s, d_inner, length = sx.shape
+    d_conv = w.shape[1]
+    n_t = length - (d_conv - 1)
+    io = B.SSM_BF16 if sx.dtype == torch.bfloat16 else B.SSM_F32
+    if ws is None:
+        ws = conv_bwd_workspace(n_s, n_t, d_inner, d_conv, sx.device)
+    if dgrad is None:
+        dgrad = torch.empty(n_s * d_inner * length + d_inner * d_conv, dtype=torch.float32,
+                            device=sx.device)
+    B.ssm_conv_bwd(sx, w, dout, dgrad, n_s, n_t, d_inner, d_conv, io, int(bool(apply_silu)), ws,
+                   ws.numel(), stream)
+    n_sx = n_s * d_inner * length
+    return dgrad[:n_sx].view(n_s, d_inner, length), dgrad[n_sx:n_sx + d_inner * d_conv].view(d_inner, d_conv)

@@ -188,3 +188,29 @@ def test_backward_unsupported_shapes_rejected_before_launch(kw):
         ssm.selective_scan_bwd(d, 256, 256, 256, 256, 256, 256, 256, 256, 256, 256, 256, ws,
                                stream=0)
     assert e.value.status == ssm.SSM_ERR_UNSUPPORTED
+
+
+def test_conv_bwd_argument_checks():
+    n_s, n_t, d_inner, K = 2, 5, 3, 4
+    need = ssm.ssm_conv_bwd_workspace_bytes(n_s, n_t, d_inner, K)
+    assert need == n_s * 1 * d_inner * K * 4          # one 128-position tile per sequence
+    assert ssm.ssm_conv_bwd_workspace_bytes(n_s, n_t, d_inner, 9) == 0
+    args = dict(n_s=n_s, n_t=n_t, d_inner=d_inner, d_conv=K, io_dtype=ssm.SSM_F32, apply_silu=1,
+                workspace=256, workspace_bytes=need, stream=0)
+    cases = [
+        (dict(sx=None), ssm.SSM_ERR_NULL),
+        (dict(dgrad=None), ssm.SSM_ERR_NULL),
+        (dict(workspace=None), ssm.SSM_ERR_NULL),
+        (dict(workspace_bytes=need - 4), ssm.SSM_ERR_WORKSPACE),
+        (dict(d_conv=9), ssm.SSM_ERR_SHAPE),
+        (dict(n_t=-1), ssm.SSM_ERR_SHAPE),
+        (dict(io_dtype=7), ssm.SSM_ERR_DTYPE),
+        (dict(dout=258), ssm.SSM_ERR_ALIGN),
+        (dict(sx=257, io_dtype=ssm.SSM_BF16), ssm.SSM_ERR_ALIGN),
+    ]
+    for over, status in cases:
+        a = dict(sx=256, w=256, dout=256, dgrad=256, **args)
+        a.update(over)
+        with pytest.raises(ssm.SsmError) as e:
+            ssm.ssm_conv_bwd(**a)
+        assert e.value.status == status, over
