@@ -46,6 +46,8 @@ WORKLOADS = {
     "C3": "Mamba-2 scan forward, 4x4096, 80 heads x 64, d_state 128, 1 group, bf16, "
           "fp32 state, permuted state ids",
     "C4": "Mamba-1 scan reverse-time backward of the 8x4096x5120 bf16 scan, fp32 grads",
+    "C5": "ssm_conv backward (conv + SiLU) of the 8x4096x5120 bf16 activations, d_conv 4, "
+          "fp32 gradients",
 }
 
 
@@ -115,6 +117,7 @@ KERNEL_SOURCES = {
     "C2": ("scan_fwd.hip", "scan_fwd_ts.hip", "scan_fwd_quad.hip", "device_common.h"),
     "C3": ("scan_fwd.hip", "ssd_fwd.hip", "device_common.h"),
     "C4": ("scan_bwd.hip", "scan_fwd_quad.hip", "device_common.h"),
+    "C5": ("conv_bwd.hip", "device_common.h"),
 }
 
 
@@ -278,6 +281,117 @@ def parity_gate_bwd(p, g):
             "1e-4 x rms (sums)"}
 
 
+def conv_bwd_bytes(c) -> int:
+    """sx read, dout read, d_sx written (each once), w and d_w."""
+    length = c.n_t + c.d_conv - 1
+    io = 2 if c.io == "bf16" else 4
+    return (c.n_s * c.d_inner * length * (io + 4) + c.n_s * c.n_t * c.d_inner * 4 +
+            2 * c.d_inner * c.d_conv * 4)
+
+
+def cpu_baseline_conv(c, min_seconds=10.0, max_reps=50):
+    """The float64 oracle's conv backward on the first 256 channels, repeated
+    until about min_seconds of CPU work."""
+    import oracle
+    ch = 256
+    sx, w, g = c.sx.value[:, :ch], c.w.value[:ch], c.dout.value[:, :, :ch]
+    reps, sec = 0, 0.0
+    while reps < max_reps and (reps == 0 or sec < min_seconds):
+        t0 = time.perf_counter()
+        oracle.conv_bwd(sx, w, g, apply_silu=c.apply_silu)
+        sec += time.perf_counter() - t0
+        reps += 1
+    per = sec / reps
+    gbs = conv_bwd_bytes(c) * ch / c.d_inner / per / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {ch} of {c.d_inner} channels, all sequences and tokens; {reps} repetitions",
+            "seconds": round(sec, 3), "cpu": platform.processor() or platform.machine(),
+            "nproc": os.cpu_count()}
+
+
+def main_conv_bwd(args):
+    import torch
+    import ssm_inputs
+    import oracle
+    from selective_scan_recurrence_amd import ops
+    import selective_scan_recurrence_amd as ssm
+
+    ssm.load()
+    dev = torch.device("cuda:0")
+    c = ssm_inputs.conv_config(args.config)
+    step_bytes = conv_bwd_bytes(c)
+    copies = max(2, math.ceil(3 * MALL_BYTES / step_bytes))
+    sets = []
+    for _ in range(copies):
+        t = {"sx": _dev(c.sx, dev), "w": _dev(c.w, dev), "dout": _dev(c.dout, dev),
+             "ws": ops.conv_bwd_workspace(c.n_s, c.n_t, c.d_inner, c.d_conv, dev)}
+        length = c.n_t + c.d_conv - 1
+        t["dgrad"] = torch.empty(c.n_s * c.d_inner * length + c.d_inner * c.d_conv,
+                                 dtype=torch.float32, device=dev)
+        sets.append(t)
+
+    def step(t):
+        return ops.conv_bwd(t["sx"], t["w"], t["dout"], apply_silu=c.apply_silu, ws=t["ws"],
+                            dgrad=t["dgrad"])
+
+    d_sx, d_w = step(sets[0])
+    torch.cuda.synchronize()
+    # parity gate: every element of sampled channels (each channel's gradients depend on it alone)
+    rng = np.random.default_rng(0xB5)
+    ch = np.unique(np.concatenate([[0, c.d_inner - 1], rng.choice(c.d_inner, 14, replace=False)]))
+    o_sx, o_w = oracle.conv_bwd(c.sx.value[:, ch], c.w.value[ch], c.dout.value[:, :, ch],
+                                apply_silu=c.apply_silu)
+    hs = torch.as_tensor(ch, device=dev)
+    for got_t, want, floor, what in ((d_sx.index_select(1, hs), o_sx, 1e-5, "d_sx"),
+                                     (d_w.index_select(0, hs), o_w, 1e-4, "d_w")):
+        got = got_t.double().cpu().numpy()
+        rms = float(np.sqrt(np.mean(want ** 2)))
+        bad = ~(np.abs(got - want) <= floor * rms + 1e-4 * np.abs(want))
+        if bad.any():
+            raise SystemExit(f"parity gate failed on {args.config} {what}: {int(bad.sum())} elements")
+    parity = {"checked_elements": int(o_sx.size + o_w.size), "rtol": 1e-4,
+              "atol": "1e-5 x rms (d_sx), 1e-4 x rms (d_w)"}
+
+    for k in range(args.warmup):
+        step(sets[k % copies])
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        starts[k].record()
+        step(sets[k % copies])
+        ends[k].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = np.array([s_.elapsed_time(e) for s_, e in zip(starts, ends)])
+    ms_per_step = starts[0].elapsed_time(ends[-1]) / args.steps
+    avg_s = float(launch_ms.mean()) * 1e-3
+    gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    ach = step_bytes / avg_s / 1e9
+    roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.config),
+            "traffic_unit": "HBM bytes per call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "kernel": "ssm_conv_bwd (all launches of one call)", "avg_launch_us": round(avg_s * 1e6, 3),
+            "floors_us": {"hbm": round(step_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2)},
+            "algorithmic_bytes": step_bytes}
+    line = {
+        "metric": "ssm_conv backward effective HBM GB/s (% of peak), 1 GPU", "value": round(gbs, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": c.io,
+        "data": "synthetic (seeded; distributions of the workload definition)",
+        "config": {"workload": f"{args.config}: {WORKLOADS[args.config]}", "n_seqs": c.n_s,
+                   "n_tokens": c.n_t, "d_inner": c.d_inner, "d_conv": c.d_conv,
+                   "apply_silu": c.apply_silu, "input_copies": copies},
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "roofline": roof, "parity": parity,
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_conv(c)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -297,6 +411,9 @@ def main():
 
     if args.copy_probe:
         copy_probe()
+        return
+    if args.config == "C5":
+        main_conv_bwd(args)
         return
     import torch
     import ssm_inputs

@@ -39,7 +39,7 @@ import numpy as np
 # Fixed stream index per tensor, so adding a tensor never shifts another's values.
 _STREAM = {
     "x": 1, "dt": 2, "A": 3, "B": 4, "C": 5, "D": 6, "conv_w": 7, "s": 8,
-    "ids": 9, "conv_state": 10, "dy": 11, "dstate": 12, "sx": 13, "probe": 14,
+    "ids": 9, "conv_state": 10, "dy": 11, "dstate": 12, "sx": 13, "probe": 14, "dout": 15,
 }
 
 
@@ -272,3 +272,22 @@ def config(name: str) -> ScanProblem:
 
 
 CONFIG_NAMES = ("C0", "C1", "C2", "C3", "C4")
+
+
+class ConvProblem:
+    """Inputs of the standalone conv backward (ssm_conv_bwd): sx
+    [n_s][d_inner][d_conv-1+n_t] (io dtype), w [d_inner][d_conv] (f32) and
+    the upstream gradient dout [n_s][n_t][d_inner] (f32)."""
+
+    def __init__(self, n_s, n_t, d_inner, d_conv, io, apply_silu, seed):
+        self.n_s, self.n_t, self.d_inner, self.d_conv = n_s, n_t, d_inner, d_conv
+        self.io, self.apply_silu, self.seed = io, apply_silu, seed
+        self.sx = _draw(seed, "sx", (n_s, d_inner, d_conv - 1 + n_t), io, _uniform(-1.0, 1.0))
+        self.w = _draw(seed, "conv_w", (d_inner, d_conv), "f32", _uniform(-0.5, 0.5))
+        self.dout = _draw(seed, "dout", (n_s, n_t, d_inner), "f32", _normal(1.0))
+
+
+def conv_config(name: str) -> ConvProblem:
+    if name == "C5":   # conv + SiLU backward of the C2 activations: 8 x 4096 x 5120, d_conv 4
+        return ConvProblem(8, 4096, 5120, 4, "bf16", True, 0xC5)
+    raise KeyError(name)
