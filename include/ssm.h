@@ -157,6 +157,9 @@ int ssm_conv_fwd(const void *sx, const float *w, void *out, int64_t n_s, int64_t
  *    partial weight gradients; its contents need no initialisation.  d_w is
  *    summed in a fixed order, so results repeat bitwise.
  *  - sx and dout may be NULL when they have no elements (n_t = 0 for dout).
+ *  - One sequence's tensors are addressed with 32-bit byte offsets:
+ *    (d_inner + 64) * (d_conv - 1 + n_t + 128) must not exceed 2^29 - 1, else
+ *    SSM_ERR_SHAPE.
  *  - Errors as ssm_conv_fwd, plus SSM_ERR_WORKSPACE for a short workspace;
  *    nothing is launched on error.  Asynchronous on stream. */
 size_t ssm_conv_bwd_workspace_bytes(int64_t n_s, int64_t n_t, int64_t d_inner, int32_t d_conv);

@@ -150,8 +150,9 @@ int ssm_conv_bwd(const void* sx, const float* w, const float* dout, float* dgrad
     if (n_s > 65535) return SSM_ERR_SHAPE;
     int64_t len = d_conv - 1 + n_t, t1, t2;
     if (!mul_ok(len, d_inner, &t1) || t1 > INT_MAX || !mul_ok(t1, n_s, &t2)) return SSM_ERR_SHAPE;
-    // per-sequence byte extents must fit the 31-bit offsets of the kernel's buffer descriptors
-    if (!mul_ok(n_t, d_inner, &t1) || t1 > (INT_MAX >> 2) || len > (INT_MAX >> 2)) return SSM_ERR_SHAPE;
+    // per-sequence byte extents, with a margin of one channel block and one
+    // tile and its staged rows, must fit the 31-bit offsets of the kernel's buffer descriptors
+    if (!mul_ok(len + 128, d_inner + 64, &t1) || t1 > (INT_MAX >> 2)) return SSM_ERR_SHAPE;
     // sx and dout may be NULL only when they have no elements
     if (!w || !dgrad || (!sx && n_s * len > 0) || (!dout && n_s * n_t > 0)) return SSM_ERR_NULL;
     const size_t need = conv_bwd_workspace_bytes(n_s, n_t, d_inner, d_conv);

@@ -193,7 +193,10 @@ def test_backward_unsupported_shapes_rejected_before_launch(kw):
 def test_conv_bwd_argument_checks():
     n_s, n_t, d_inner, K = 2, 5, 3, 4
     need = ssm.ssm_conv_bwd_workspace_bytes(n_s, n_t, d_inner, K)
-    assert need == n_s * 1 * d_inner * K * 4          # one 128-position tile per sequence
+    assert need == n_s * 1 * d_inner * K * 4          # one 64-position tile per sequence
+    # tiles of 64 positions of sx: 513 positions take 9, 512 take 8
+    assert ssm.ssm_conv_bwd_workspace_bytes(1, 510, d_inner, K) == 9 * d_inner * K * 4
+    assert ssm.ssm_conv_bwd_workspace_bytes(1, 509, d_inner, K) == 8 * d_inner * K * 4
     assert ssm.ssm_conv_bwd_workspace_bytes(n_s, n_t, d_inner, 9) == 0
     args = dict(n_s=n_s, n_t=n_t, d_inner=d_inner, d_conv=K, io_dtype=ssm.SSM_F32, apply_silu=1,
                 workspace=256, workspace_bytes=need, stream=0)
@@ -204,6 +207,7 @@ def test_conv_bwd_argument_checks():
         (dict(workspace_bytes=need - 4), ssm.SSM_ERR_WORKSPACE),
         (dict(d_conv=9), ssm.SSM_ERR_SHAPE),
         (dict(n_t=-1), ssm.SSM_ERR_SHAPE),
+        (dict(n_t=(1 << 29) // (d_inner + 64)), ssm.SSM_ERR_SHAPE),   # per-sequence 32-bit offsets
         (dict(io_dtype=7), ssm.SSM_ERR_DTYPE),
         (dict(dout=258), ssm.SSM_ERR_ALIGN),
         (dict(sx=257, io_dtype=ssm.SSM_BF16), ssm.SSM_ERR_ALIGN),

@@ -37,7 +37,7 @@ def _problem(seed, n_s, n_t, d_inner, K, io):
 @pytest.mark.parametrize("silu", [False, True])
 @pytest.mark.parametrize("K,n_t,d_inner,n_s", [
     (4, 5, 3, 2), (1, 7, 65, 1), (3, 127, 64, 2), (4, 128, 130, 1), (8, 129, 64, 2),
-    (4, 300, 200, 3), (2, 1, 1, 1)])
+    (4, 300, 200, 3), (2, 1, 1, 1), (5, 1100, 70, 2), (4, 1021, 64, 1)])
 def test_conv_bwd_parity(io, silu, K, n_t, d_inner, n_s):
     sx, w, g = _problem(K * 1000 + n_t + d_inner, n_s, n_t, d_inner, K, io)
     d_sx, d_w = ops.conv_bwd(dev(sx), dev(w), dev(g), apply_silu=silu)
