@@ -110,6 +110,7 @@ MEASURED_TRAFFIC = {
     "C2": {"sha256": "b54488bd1c4354444b1903423f99b869e566fd61179612657f748cdaf2dc0c37", "fetch_kib": 339353.1, "write_kib": 330240.0},
     "C3": {"sha256": "b0591ad1672f9c548339e541594127fcaa68e16a1916aa71e249cdc017a61ddb", "fetch_kib": 144438.3, "write_kib": 174081.6},
     "C4": {"sha256": "2a19fd3700bb14b898a8f31d961c12501b1bdb0583c23b31fa03aca4474e50b7", "fetch_kib": 1665248.8, "write_kib": 2961396.0},
+    "C5": {"sha256": "84a811e3d84aca510d566615083c4f313b721cec5e2ceaf515444d565e2f3171", "fetch_kib": 512933.0, "write_kib": 704396.3},
 }
 KERNEL_SOURCES = {
     "C0": ("scan_fwd.hip", "scan_fwd_ts.hip", "scan_fwd_quad.hip", "device_common.h"),
@@ -290,10 +291,10 @@ def conv_bwd_bytes(c) -> int:
 
 
 def cpu_baseline_conv(c, min_seconds=10.0, max_reps=50):
-    """The float64 oracle's conv backward on the first 256 channels, repeated
+    """The float64 oracle's conv backward on the first 1024 channels, repeated
     until about min_seconds of CPU work."""
     import oracle
-    ch = 256
+    ch = min(1024, c.d_inner)
     sx, w, g = c.sx.value[:, :ch], c.w.value[:ch], c.dout.value[:, :, :ch]
     reps, sec = 0, 0.0
     while reps < max_reps and (reps == 0 or sec < min_seconds):
