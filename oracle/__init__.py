@@ -80,6 +80,8 @@ def _load():
             lib.oracle_conv_bwd.argtypes = [P, P, P, P, P, ctypes.c_int64, ctypes.c_int64,
                                             ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
             lib.oracle_conv_bwd.restype = ctypes.c_int
+            lib.oracle_state_update.argtypes = [ctypes.POINTER(_Dims), P] + [P] * 13
+            lib.oracle_state_update.restype = ctypes.c_int
             lib.oracle_threads_used.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int]
             lib.oracle_threads_used.restype = ctypes.c_int
             _lib = lib
@@ -212,6 +214,40 @@ def conv_bwd(sx, w, dout, apply_silu=False):
     if rc:
         raise ValueError(f"oracle_conv_bwd failed ({rc})")
     return d_sx, d_w
+
+
+def state_update(s, x, dt, A, B, C, D, ids, *, dt_bias=None, z=None, conv_w=None,
+                 conv_state=None, dt_softplus=False, grp_of_head=None):
+    """One decode token of every sequence ("mambazip mamba1/model.rs",
+    forward_impl's single-token step).
+
+    Shapes (row-major): s [R][H][P][N]; x [S][H][P]; dt [S][H]; A [H][N] or [H];
+    B, C [S][G][N]; D [H] or None; ids [S]; dt_bias [H] or None; z [S][H][P]
+    or None; conv_w [H][K] with conv_state [R][H][K-1] (head_dim 1) or None.
+
+    Returns (y [S][H][P], new s, new conv_state or None); the inputs are not
+    modified.
+    """
+    s, x, dt, A, B, C, D = map(_f64, (s, x, dt, A, B, C, D))
+    dt_bias, z, conv_w, conv_state = map(_f64, (dt_bias, z, conv_w, conv_state))
+    s = s.copy()
+    conv_state = None if conv_state is None else conv_state.copy()
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    S, H, P = x.shape
+    R, N = s.shape[0], s.shape[3]
+    G = B.shape[1]
+    K = 0 if conv_w is None else conv_w.shape[1]
+    if K and conv_state is None:
+        raise ValueError("the decode conv needs a conv state")
+    grp = group_of_head(H, G) if grp_of_head is None else np.ascontiguousarray(grp_of_head, np.int64)
+    d = _dims(S, 1, H, P, N, G, R, A.ndim == 2, K, D is not None, dt_softplus)
+    y = np.zeros((S, H, P))
+    rc = _load().oracle_state_update(ctypes.byref(d), _ptr(grp), _ptr(s), _ptr(x), _ptr(dt),
+                                     _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                     _ptr(ids), _ptr(conv_w), _ptr(conv_state), _ptr(y))
+    if rc:
+        raise ValueError(f"oracle_state_update failed ({rc})")
+    return y, s, conv_state
 
 
 def threads_used(n_head: int, n_threads: Optional[int] = None) -> int:

@@ -23,6 +23,10 @@
  *    ggml_ssm_conv_back packs the gradient of sx then that of the conv
  *    weights; its tests compare both with a central difference and give the
  *    weight gradient of loss = sum(output) in closed form.
+ *  - "mambazip mamba1/model.rs", forward_impl's single-token step: the conv
+ *    window of the last d_conv-1 inputs plus the new one (depthwise_conv_step),
+ *    SiLU, dt = softplus(dt_raw + dt_bias), the in-place state update of
+ *    selective_scan_state16, and the output times SiLU(z).
  *
  * Readings where the pages leave a step open (each also listed in the design
  * notes): dt is used as given unless the softplus flag is set; the initial
@@ -386,5 +390,71 @@ int oracle_conv_bwd(const double *sx, const double *w, const double *dout, doubl
                     d_w[ch * d_conv + j] += g * row[t + j];
                 }
             }
+    return 0;
+}
+
+/* sum_j w[j] win[j] over the window of the K-1 previous inputs (oldest first)
+ * followed by the new one. */
+static double w_tap_sum(const double *w, const double *prev, double xin, int64_t K) {
+    double c = 0.0;
+    for (int64_t j = 0; j < K - 1; j++) c += w[j] * prev[j];
+    return c + w[K - 1] * xin;
+}
+
+/* One token of every sequence of a batch, updating states in place
+ * ("mambazip mamba1/model.rs", forward_impl's single-token step; the conv
+ * taps in ggml's order, the last weight on the newest input).  For sequence
+ * i, row r = ids[i], head h, channel p:
+ *   with d_conv = K > 0 (head_dim 1): win = conv_state[r][h][0..K-2] then
+ *     x[i][h]; c = sum_j w[h][j] win[j]; u = SiLU(c); conv_state[r][h] keeps
+ *     the last K-1 entries of win;  otherwise u = x[i][h][p];
+ *   d = dt[i][h] (+ dt_bias[h] when given), then softplus when asked;
+ *   s[r][h][p][n] = exp(d A) s[r][h][p][n] + d B[i][g][n] u   for every n;
+ *   y[i][h][p] = sum_n C[i][g][n] s[r][h][p][n] + D[h] u, times SiLU(z[i][h][p])
+ *     when z is given.
+ * Rows are updated in sequence order, so ids should be distinct (a repeated
+ * row would be stepped twice).  n_tokens in d is ignored (one token). */
+int oracle_state_update(const oracle_dims *d, const int64_t *grp_of_head, double *s,
+                        const double *x, const double *dt, const double *dt_bias,
+                        const double *A, const double *B, const double *C, const double *D,
+                        const double *z, const int32_t *ids, const double *conv_w,
+                        double *conv_state, double *y) {
+    int rc = check_dims(d, grp_of_head, ids);
+    if (rc) return rc;
+    if (!s || !x || !dt || !A || !B || !C || !y) return -1;
+    if (d->has_D && !D) return -1;
+    if (d->d_conv && (!conv_w || !conv_state)) return -1;
+    const int64_t H = d->n_head, P = d->head_dim, N = d->d_state, G = d->n_group, K = d->d_conv;
+    for (int64_t i = 0; i < d->n_seqs; i++) {
+        const int64_t r = ids[i];
+        for (int64_t h = 0; h < H; h++) {
+            const int64_t g = grp_of_head[h];
+            double dd = dt[i * H + h] + (dt_bias ? dt_bias[h] : 0.0);
+            if (d->dt_softplus) dd = softplus(dd);
+            for (int64_t p = 0; p < P; p++) {
+                double u;
+                if (K) {
+                    double *cs = conv_state + (r * H + h) * (K - 1);
+                    const double xin = x[i * H + h];
+                    double c = w_tap_sum(conv_w + h * K, cs, xin, K);
+                    for (int64_t j = 0; j + 1 < K - 1; j++) cs[j] = cs[j + 1];
+                    if (K > 1) cs[K - 2] = xin;
+                    u = silu(c);
+                } else {
+                    u = x[(i * H + h) * P + p];
+                }
+                double *st = s + ((r * H + h) * P + p) * N;
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; n++) {
+                    const double a = exp(dd * (d->a_per_state ? A[h * N + n] : A[h]));
+                    st[n] = a * st[n] + dd * B[(i * G + g) * N + n] * u;
+                    acc += C[(i * G + g) * N + n] * st[n];
+                }
+                if (d->has_D) acc += D[h] * u;
+                if (z) acc *= silu(z[(i * H + h) * P + p]);
+                y[(i * H + h) * P + p] = acc;
+            }
+        }
+    }
     return 0;
 }

@@ -39,6 +39,14 @@ MUTANTS = {
     "conv_bwd_dw_window_shift": ("d_w[ch * d_conv + j] += g * row[t + j];",
                                  "d_w[ch * d_conv + j] += g * row[t + d_conv - 1 - j];"),
     "conv_bwd_silu_derivative_is_sigmoid": ("g *= sg * (1.0 + z * (1.0 - sg));", "g *= sg;"),
+    "decode_ring_not_shifted": ("for (int64_t j = 0; j + 1 < K - 1; j++) cs[j] = cs[j + 1];", ""),
+    "decode_newest_tap_first": ("return c + w[K - 1] * xin;", "return c + w[0] * xin;"),
+    "decode_gate_is_sigmoid": ("if (z) acc *= silu(z[(i * H + h) * P + p]);",
+                               "if (z) acc *= sigmoid(z[(i * H + h) * P + p]);"),
+    "decode_bias_after_softplus": ("double dd = dt[i * H + h] + (dt_bias ? dt_bias[h] : 0.0);\n            if (d->dt_softplus) dd = softplus(dd);",
+                                   "double dd = dt[i * H + h];\n            if (d->dt_softplus) dd = softplus(dd);\n            dd += dt_bias ? dt_bias[h] : 0.0;"),
+    "decode_y_from_previous_state": ("st[n] = a * st[n] + dd * B[(i * G + g) * N + n] * u;\n                    acc += C[(i * G + g) * N + n] * st[n];",
+                                     "acc += C[(i * G + g) * N + n] * st[n];\n                    st[n] = a * st[n] + dd * B[(i * G + g) * N + n] * u;"),
 }
 
 
@@ -54,7 +62,7 @@ def test_pins_catch_planted_mistake(name, tmp_path):
                            "-lm", "-lpthread"])
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
                         "tests/test_oracle_pins.py", "tests/test_oracle_bwd_pins.py",
-                        "tests/test_oracle_conv_bwd_pins.py"],
+                        "tests/test_oracle_conv_bwd_pins.py", "tests/test_oracle_decode_pins.py"],
                        cwd=ROOT, env=dict(os.environ, SSM_ORACLE_LIB=str(so)),
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
