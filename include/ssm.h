@@ -205,6 +205,39 @@ int selective_scan_bwd(const ssm_scan_desc *desc, const float *s, const void *x,
                        const float *D, const int32_t *ids, const void *dout, float *dgrad,
                        void *workspace, size_t workspace_bytes, ssm_stream_t stream);
 
+/* selective_state_update: one decode token of every sequence of a batch,
+ * with the states updated in place ("mambazip mamba1/model.rs", forward_impl's
+ * single-token step: the conv window of depthwise_conv_step, SiLU,
+ * dt = softplus(dt_raw + dt_bias), the state update of selective_scan_state16,
+ * and the output times SiLU(z); the conv taps in ggml's order as in
+ * ssm_conv_fwd, the last weight on the newest input).  For sequence i with
+ * state row r = ids[i], head h, channel p:
+ *   u = SiLU(sum_j w[h][j] win[j]) with win = conv_state[r][h][0..K-2], x[i][h]
+ *       when d_conv = K > 0 (head_dim 1), after which conv_state[r][h] holds
+ *       the last K-1 entries of win; otherwise u = x[i][h][p];
+ *   d = dt[i][h] (+ dt_bias[h]), then softplus with SSM_DT_SOFTPLUS;
+ *   s[r][h][p][n] = exp(d A) s[r][h][p][n] + d B[i][g][n] u   (g = h / (n_head / n_group));
+ *   y[i][h][p] = (sum_n C[i][g][n] s[r][h][p][n] + D[h] u) * SiLU(z[i][h][p]).
+ *  - desc->n_tokens must be 1; chunk is ignored.  Shapes (row-major): s
+ *    [n_state_rows][n_head][head_dim][d_state] f32 (in/out); x, z, y
+ *    [n_seqs][n_head][head_dim] and dt [n_seqs][n_head] in io_dtype; B, C
+ *    [n_seqs][n_group][d_state] in io_dtype; A, D, dt_bias, conv_w as in
+ *    selective_scan_fwd (dt_bias [n_head] f32); conv_state
+ *    [n_state_rows][n_head][d_conv-1] f32 (in/out).
+ *  - dt_bias, z and err may be NULL; D may be NULL only without SSM_HAS_D;
+ *    conv_w and conv_state must be given when d_conv > 0.
+ *  - ids must be distinct: two sequences naming one row race on it.  An id
+ *    outside [0, n_state_rows) leaves every row untouched, writes that
+ *    sequence's y as NaN and, when err is given, sets SSM_DEVERR_IDS in *err
+ *    (a device word the caller owns and clears).
+ *  - Outputs must not alias inputs (s and conv_state are updated in place).
+ *  - No workspace.  Asynchronous on stream; nothing is launched on error. */
+int selective_state_update(const ssm_scan_desc *desc, float *s, const void *x, const void *dt,
+                           const float *dt_bias, const float *A, const void *B, const void *C,
+                           const float *D, const void *z, const int32_t *ids,
+                           const float *conv_w, float *conv_state, void *y, uint32_t *err,
+                           ssm_stream_t stream);
+
 /* Copies the device-error word of a workspace to *bits (synchronises the
  * stream; for tests and debugging, not for the hot path). */
 int ssm_get_device_error(const void *workspace, ssm_stream_t stream, uint32_t *bits);

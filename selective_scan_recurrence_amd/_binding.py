@@ -21,7 +21,7 @@ SSM_DEVERR_IDS = 1
 EXPORTS = ("ssm_status_str", "ssm_version", "ssm_scan_out_bytes", "ssm_scan_state_offset_bytes",
            "ssm_scan_dgrad_layout", "ssm_scan_workspace_bytes", "ssm_conv_fwd",
            "ssm_conv_bwd_workspace_bytes", "ssm_conv_bwd", "selective_scan_fwd",
-           "selective_scan_bwd", "ssm_get_device_error")
+           "selective_scan_bwd", "selective_state_update", "ssm_get_device_error")
 
 
 class SsmError(RuntimeError):
@@ -75,6 +75,8 @@ def load():
         lib.selective_scan_fwd.restype = ctypes.c_int
         lib.selective_scan_bwd.argtypes = [D] + [P] * 11 + [SZ, P]
         lib.selective_scan_bwd.restype = ctypes.c_int
+        lib.selective_state_update.argtypes = [D] + [P] * 15
+        lib.selective_state_update.restype = ctypes.c_int
         lib.ssm_get_device_error.argtypes = [P, P, ctypes.POINTER(ctypes.c_uint32)]
         lib.ssm_get_device_error.restype = ctypes.c_int
         _lib = lib
@@ -165,6 +167,15 @@ def selective_scan_bwd(desc, s, x, dt, A, B, C, D, ids, dout, dgrad, workspace,
                                    _ptr(dgrad), _ptr(workspace), int(workspace_bytes),
                                    _stream(stream))
     return _check(rc, "selective_scan_bwd")
+
+
+def selective_state_update(desc, s, x, dt, dt_bias, A, B, C, D, z, ids, conv_w, conv_state, y,
+                           err, stream=None):
+    rc = load().selective_state_update(ctypes.byref(desc), _ptr(s), _ptr(x), _ptr(dt),
+                                       _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                       _ptr(ids), _ptr(conv_w), _ptr(conv_state), _ptr(y),
+                                       _ptr(err), _stream(stream))
+    return _check(rc, "selective_state_update")
 
 
 def ssm_get_device_error(workspace, stream=None) -> int:

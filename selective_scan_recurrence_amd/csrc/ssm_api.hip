@@ -246,6 +246,37 @@ int selective_scan_bwd(const ssm_scan_desc* desc, const float* s, const void* x,
     return launch_scan_bwd(a, static_cast<hipStream_t>(stream));
 }
 
+int selective_state_update(const ssm_scan_desc* desc, float* s, const void* x, const void* dt,
+                           const float* dt_bias, const float* A, const void* B, const void* C,
+                           const float* D, const void* z, const int32_t* ids,
+                           const float* conv_w, float* conv_state, void* y, uint32_t* err,
+                           ssm_stream_t stream) {
+    Shape sh;
+    int rc = check_desc(desc, &sh);
+    if (rc) return rc;
+    if (sh.L != 1) return SSM_ERR_SHAPE;
+    int64_t rows;
+    if (!mul_ok(sh.S, sh.d_inner(), &rows) || rows > (int64_t)INT_MAX * 16) return SSM_ERR_SHAPE;
+    const bool has_seq = sh.S > 0;
+    if (!s || !A || (has_seq && (!x || !dt || !B || !C || !ids || !y))) return SSM_ERR_NULL;
+    if ((sh.flags & SSM_HAS_D) && !D) return SSM_ERR_NULL;
+    if (sh.K > 0 && (!conv_w || !conv_state)) return SSM_ERR_NULL;
+    const size_t es = sh.io_bytes();
+    if (!aligned(x, es) || !aligned(dt, es) || !aligned(B, es) || !aligned(C, es) ||
+        !aligned(z, es) || !aligned(y, es) || !aligned(s, 4) || !aligned(A, 4) ||
+        !aligned(ids, 4) || !aligned(D, 4) || !aligned(dt_bias, 4) || !aligned(conv_w, 4) ||
+        !aligned(conv_state, 4) || !aligned(err, 4))
+        return SSM_ERR_ALIGN;
+    DecodeArgs a;
+    a.sh = sh; a.s = s; a.x = x; a.dt = dt; a.dt_bias = dt_bias; a.A = A; a.B = B; a.C = C;
+    a.D = (sh.flags & SSM_HAS_D) ? D : nullptr;
+    a.z = z; a.ids = ids;
+    a.conv_w = sh.K ? conv_w : nullptr;
+    a.conv_state = sh.K ? conv_state : nullptr;
+    a.y = y; a.err = err;
+    return launch_state_update(a, static_cast<hipStream_t>(stream));
+}
+
 int ssm_get_device_error(const void* workspace, ssm_stream_t stream, uint32_t* bits) {
     if (!workspace || !bits) return SSM_ERR_NULL;
     hipStream_t st = static_cast<hipStream_t>(stream);

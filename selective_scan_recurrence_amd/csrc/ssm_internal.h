@@ -68,6 +68,24 @@ struct BwdArgs {
     size_t ws_bytes;
 };
 
+struct DecodeArgs {
+    Shape sh;              // n_tokens (L) is 1
+    float* s;              // state rows, updated in place
+    const void* x;
+    const void* dt;
+    const float* dt_bias;  // nullable
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;        // nullable
+    const void* z;         // nullable
+    const int32_t* ids;
+    const float* conv_w;   // with K > 0
+    float* conv_state;     // with K > 0, updated in place
+    void* y;
+    uint32_t* err;         // nullable device-error word
+};
+
 constexpr size_t kErrBytes = 256;  // the device-error word's slot at the workspace start
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -99,6 +117,7 @@ int launch_scan_bwd(const BwdArgs& a, hipStream_t stream);
 int launch_conv_fwd(const void* sx, const float* w, void* out, int64_t n_s, int64_t n_t,
                     int64_t d_inner, int d_conv, int io, int apply_silu, hipStream_t stream);
 size_t conv_bwd_workspace_bytes(int64_t n_s, int64_t n_t, int64_t d_inner, int d_conv);
+int launch_state_update(const DecodeArgs& a, hipStream_t stream);
 int launch_conv_bwd(const void* sx, const float* w, const float* dout, float* dgrad, int64_t n_s,
                     int64_t n_t, int64_t d_inner, int d_conv, int io, int apply_silu, void* ws,
                     hipStream_t stream);

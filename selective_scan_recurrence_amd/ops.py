@@ -130,3 +130,15 @@ def conv_bwd(sx: torch.Tensor, w: torch.Tensor, dout: torch.Tensor, apply_silu=F
                    ws.numel(), stream)
     n_sx = n_s * d_inner * length
     return dgrad[:n_sx].view(n_s, d_inner, length), dgrad[n_sx:n_sx + d_inner * d_conv].view(d_inner, d_conv)
+
+
+def state_update(desc, s, x, dt, A, Bm, Cm, D, ids, *, dt_bias=None, z=None, conv_w=None,
+                 conv_state=None, y=None, err=None, stream=None) -> torch.Tensor:
+    """One decode token of every sequence (selective_state_update): s and
+    conv_state are updated in place; returns y [n_seqs][n_head][head_dim]."""
+    if y is None:
+        y = torch.empty(desc.n_seqs, desc.n_head, desc.head_dim, dtype=TORCH_IO[desc.io_dtype],
+                        device=s.device)
+    B.selective_state_update(desc, s, x, dt, dt_bias, A, Bm, Cm, D, z, ids, conv_w, conv_state, y,
+                             err, stream)
+    return y

@@ -40,6 +40,7 @@ import numpy as np
 _STREAM = {
     "x": 1, "dt": 2, "A": 3, "B": 4, "C": 5, "D": 6, "conv_w": 7, "s": 8,
     "ids": 9, "conv_state": 10, "dy": 11, "dstate": 12, "sx": 13, "probe": 14, "dout": 15,
+    "dt_bias": 16, "z": 17,
 }
 
 
@@ -290,4 +291,35 @@ class ConvProblem:
 def conv_config(name: str) -> ConvProblem:
     if name == "C5":   # conv + SiLU backward of the C2 activations: 8 x 4096 x 5120, d_conv 4
         return ConvProblem(8, 4096, 5120, 4, "bf16", True, 0xC5)
+    raise KeyError(name)
+
+
+def make_decode_problem(*, with_z=False, dt_bias_range=None, **kw) -> ScanProblem:
+    """Operands of one decode step (selective_state_update): a one-token
+    problem of ``make_problem`` (x [S][1][H][P] is laid out as [S][H][P], B and
+    C as [S][G][N], dt as [S][H]), plus z ~ N(0,1) in the io dtype when
+    with_z, and dt_bias ~ U(dt_bias_range) per head when given."""
+    kw.setdefault("n_tokens", 1)
+    if kw["n_tokens"] != 1:
+        raise ValueError("a decode step has one token")
+    p = make_problem(**kw)
+    S, H, P = p.n_seqs, p.n_head, p.head_dim
+    seed = kw.get("seed", 0)
+    if with_z:
+        p.t["z"] = _draw(seed, "z", (S, H, P), p.io, _normal(1.0))
+    if dt_bias_range is not None:
+        p.t["dt_bias"] = _draw(seed, "dt_bias", (H,), "f32", _uniform(*dt_bias_range))
+    return p
+
+
+def decode_config(name: str) -> ScanProblem:
+    if name == "C6":   # Mamba-1 decode at the large layer: 256 sequences x 5120 channels, d_state 16
+        return make_decode_problem(n_seqs=256, n_head=5120, d_state=16, d_conv=4, io="bf16",
+                                   seed=0xC6, h0_std=0.1, conv_state_std=0.5, n_state_rows=256,
+                                   ids="perm", with_z=True)
+    if name == "C7":   # Mamba-2 decode at the C3 layer: 64 sequences x 80 heads x 64, d_state 128
+        return make_decode_problem(n_seqs=64, n_head=80, head_dim=64, d_state=128, n_group=1,
+                                   a_per_state=False, d_conv=0, io="bf16", seed=0xC7, h0_std=0.1,
+                                   n_state_rows=64, ids="perm", A_kind="uniform",
+                                   A_range=(1.0, 16.0), bc_std=1.0 / np.sqrt(128.0), with_z=True)
     raise KeyError(name)

@@ -218,3 +218,32 @@ def test_conv_bwd_argument_checks():
         with pytest.raises(ssm.SsmError) as e:
             ssm.ssm_conv_bwd(**a)
         assert e.value.status == status, over
+
+
+def test_state_update_argument_checks():
+    """selective_state_update rejects bad arguments on the host (no launch)."""
+    d = ops.make_desc(n_seqs=2, n_tokens=1, n_head=3, d_state=16, d_conv=4, n_state_rows=4)
+    base = dict(s=256, x=256, dt=256, dt_bias=None, A=256, B=256, C=256, D=256, z=None, ids=256,
+                conv_w=256, conv_state=256, y=256, err=None, stream=0)
+    cases = [
+        (dict(desc=ops.make_desc(n_seqs=2, n_tokens=2, n_head=3, d_state=16)), ssm.SSM_ERR_SHAPE),
+        (dict(desc=ops.make_desc(n_seqs=2, n_tokens=1, n_head=3, d_state=16, head_dim=2,
+                                 d_conv=4)), ssm.SSM_ERR_SHAPE),
+        (dict(s=None), ssm.SSM_ERR_NULL),
+        (dict(ids=None), ssm.SSM_ERR_NULL),
+        (dict(y=None), ssm.SSM_ERR_NULL),
+        (dict(conv_state=None), ssm.SSM_ERR_NULL),
+        (dict(conv_w=None), ssm.SSM_ERR_NULL),
+        (dict(D=None), ssm.SSM_ERR_NULL),
+        (dict(s=258), ssm.SSM_ERR_ALIGN),
+        (dict(z=257), ssm.SSM_ERR_ALIGN),
+        (dict(err=258), ssm.SSM_ERR_ALIGN),
+        (dict(desc=ops.make_desc(n_seqs=2, n_tokens=1, n_head=3, d_state=16, io=5)),
+         ssm.SSM_ERR_DTYPE),
+    ]
+    for over, status in cases:
+        a = dict(desc=d, **base)
+        a.update(over)
+        with pytest.raises(ssm.SsmError) as e:
+            ssm.selective_state_update(**a)
+        assert e.value.status == status, over
