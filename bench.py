@@ -48,6 +48,10 @@ WORKLOADS = {
     "C4": "Mamba-1 scan reverse-time backward of the 8x4096x5120 bf16 scan, fp32 grads",
     "C5": "ssm_conv backward (conv + SiLU) of the 8x4096x5120 bf16 activations, d_conv 4, "
           "fp32 gradients",
+    "C6": "Mamba-1 single-token decode step of 256 sequences at the 5120-channel layer, "
+          "d_state 16, d_conv 4, bf16 x/dt/B/C/z/y, fp32 states updated in place by permuted ids",
+    "C7": "Mamba-2 single-token decode step of 64 sequences at the 80 heads x 64 layer, "
+          "d_state 128, bf16 x/dt/B/C/z/y, fp32 states updated in place by permuted ids",
 }
 
 
@@ -119,6 +123,8 @@ KERNEL_SOURCES = {
     "C3": ("scan_fwd.hip", "ssd_fwd.hip", "device_common.h"),
     "C4": ("scan_bwd.hip", "scan_fwd_quad.hip", "device_common.h"),
     "C5": ("conv_bwd.hip", "device_common.h"),
+    "C6": ("decode.hip", "device_common.h"),
+    "C7": ("decode.hip", "device_common.h"),
 }
 
 
@@ -393,6 +399,135 @@ def main_conv_bwd(args):
     print(json.dumps(line), flush=True)
 
 
+def decode_bytes(p) -> int:
+    """One decode step: the named state rows (and conv-state rows) read and
+    written once, x/dt/z read and y written once, B/C and the per-head
+    parameters read once."""
+    io = 2 if p.io == "bf16" else 4
+    S, H, P, N, G, K = p.n_seqs, p.n_head, p.head_dim, p.d_state, p.n_group, p.d_conv
+    state = 2 * S * H * P * N * 4
+    conv = 2 * S * H * max(K - 1, 0) * 4
+    acts = S * H * P * io * (3 if p.value("z") is not None else 2) + S * H * io
+    bc = 2 * S * G * N * io
+    params = (H * N if p.a_per_state else H) * 4 + (H * 4 if p.has_D else 0) + H * K * 4 + S * 4
+    if p.value("dt_bias") is not None:
+        params += H * 4
+    return state + conv + acts + bc + params
+
+
+def cpu_baseline_decode(p, min_seconds=10.0, max_reps=200):
+    """The float64 oracle's decode step on the whole batch, repeated until
+    about min_seconds of CPU work."""
+    import oracle
+    S, H, P, N, G = p.n_seqs, p.n_head, p.head_dim, p.d_state, p.n_group
+    args = (p.value("s"), p.value("x").reshape(S, H, P), p.value("dt").reshape(S, H), p.value("A"),
+            p.value("B").reshape(S, G, N), p.value("C").reshape(S, G, N), p.value("D"), p.ids)
+    kw = dict(dt_bias=p.value("dt_bias"), z=p.value("z"),
+              conv_w=p.value("conv_w") if p.d_conv else None,
+              conv_state=p.value("conv_state") if p.d_conv else None, dt_softplus=p.dt_softplus)
+    reps, sec = 0, 0.0
+    while reps < max_reps and (reps == 0 or sec < min_seconds):
+        t0 = time.perf_counter()
+        oracle.state_update(*args, **kw)
+        sec += time.perf_counter() - t0
+        reps += 1
+    per = sec / reps
+    return {"value": round(decode_bytes(p) / per / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "sample": f"the whole batch; {reps} repetitions",
+            "seconds": round(sec, 3), "cpu": platform.processor() or platform.machine(),
+            "nproc": os.cpu_count()}
+
+
+def main_decode(args):
+    import torch
+    import ssm_inputs
+    import oracle
+    from selective_scan_recurrence_amd import ops
+    import selective_scan_recurrence_amd as ssm
+
+    ssm.load()
+    dev = torch.device("cuda:0")
+    p = ssm_inputs.decode_config(args.config)
+    S, H, P, N, G = p.n_seqs, p.n_head, p.head_dim, p.d_state, p.n_group
+    desc = ops.make_desc(n_seqs=S, n_tokens=1, n_head=H, head_dim=P, d_state=N, n_group=G,
+                         n_state_rows=p.n_state_rows, a_per_state=p.a_per_state, d_conv=p.d_conv,
+                         io=p.io, has_D=p.has_D, dt_softplus=p.dt_softplus)
+    step_bytes = decode_bytes(p)
+    copies = max(2, math.ceil(3 * MALL_BYTES / step_bytes))
+    sets = []
+    for _ in range(copies):
+        t = {k: _dev(s_, dev) for k, s_ in p.t.items()}
+        t["ids"] = torch.from_numpy(p.ids).to(dev)
+        t["y"] = torch.empty(S, H, P, dtype=ops.TORCH_IO[desc.io_dtype], device=dev)
+        sets.append(t)
+
+    def step(t):
+        return ops.state_update(desc, t["s"], t["x"], t["dt"], t["A"], t["B"], t["C"], t.get("D"),
+                                t["ids"], dt_bias=t.get("dt_bias"), z=t.get("z"),
+                                conv_w=t.get("conv_w"), conv_state=t.get("conv_state"), y=t["y"])
+
+    # parity gate on the first call: every element of y and of the state rows
+    y = step(sets[0])
+    torch.cuda.synchronize()
+    cs = p.value("conv_state") if p.d_conv else None
+    y_o, s_o, cs_o = oracle.state_update(
+        p.value("s"), p.value("x").reshape(S, H, P), p.value("dt").reshape(S, H), p.value("A"),
+        p.value("B").reshape(S, G, N), p.value("C").reshape(S, G, N), p.value("D"), p.ids,
+        dt_bias=p.value("dt_bias"), z=p.value("z"), conv_w=p.value("conv_w") if p.d_conv else None,
+        conv_state=cs, dt_softplus=p.dt_softplus)
+    rtol, atol = (2e-2, 1e-3) if p.io == "bf16" else (1e-4, 1e-5)
+    checks = [(y.double().cpu().numpy(), y_o, rtol, atol, "y"),
+              (sets[0]["s"].double().cpu().numpy(), s_o, 1e-4, 1e-5, "state")]
+    if p.d_conv:
+        checks.append((sets[0]["conv_state"].double().cpu().numpy(), cs_o, 0.0, 0.0, "conv state"))
+    for got, want, rt, at, what in checks:
+        bad = ~(np.abs(got - want) <= at + rt * np.abs(want))
+        if bad.any():
+            raise SystemExit(f"parity gate failed on {args.config} {what}: {int(bad.sum())} elements")
+    parity = {"checked_elements": int(sum(c[1].size for c in checks)), "rtol_y": rtol,
+              "atol_y": atol, "state": "rtol 1e-4, atol 1e-5", "conv_state": "exact"}
+
+    for k in range(args.warmup):
+        step(sets[k % copies])
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        starts[k].record()
+        step(sets[k % copies])
+        ends[k].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = np.array([s_.elapsed_time(e) for s_, e in zip(starts, ends)])
+    ms_per_step = starts[0].elapsed_time(ends[-1]) / args.steps
+    avg_s = float(launch_ms.mean()) * 1e-3
+    gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    ach = step_bytes / avg_s / 1e9
+    roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.config),
+            "traffic_unit": "HBM bytes per call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "kernel": "selective_state_update", "avg_launch_us": round(avg_s * 1e6, 3),
+            "floors_us": {"hbm": round(step_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2)},
+            "algorithmic_bytes": step_bytes}
+    line = {
+        "metric": "selective-scan decode step effective HBM GB/s (% of peak) + channel-tokens/s, 1 GPU",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": p.io,
+        "data": "synthetic (seeded; distributions of the workload definition)",
+        "config": {"workload": f"{args.config}: {WORKLOADS[args.config]}", "n_seqs": S,
+                   "n_head": H, "head_dim": P, "d_state": N, "d_conv": p.d_conv,
+                   "input_copies": copies},
+        "channel_tokens_per_s": round(S * H * P / (ms_per_step * 1e-3), 1),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "roofline": roof, "parity": parity,
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_decode(p)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -415,6 +550,9 @@ def main():
         return
     if args.config == "C5":
         main_conv_bwd(args)
+        return
+    if args.config in ("C6", "C7"):
+        main_decode(args)
         return
     import torch
     import ssm_inputs

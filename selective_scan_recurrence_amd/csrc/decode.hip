@@ -27,6 +27,7 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+
 struct DecodeKP {
     float* s;
     const void* x;
@@ -51,30 +52,41 @@ __device__ __forceinline__ float ld(const void* p, int64_t i) {
     return to_f32(static_cast<const T*>(p)[i]);
 }
 
-// The scan input u and the step d of row (i, h, p) whose state row is r; the
-// conv state is advanced by the row's lane `writer` only.
+// The scan input u and the step d of row (i, h, p) whose state row is r.
+// With the conv, win receives the K-1 conv-state values (oldest first) and
+// the new input, kept in registers (fixed trip counts) so that the window is
+// written back only after every load of the step has been issued.
+constexpr int kMaxWin = 8;
 template <typename T>
 __device__ __forceinline__ void row_inputs(const DecodeKP& k, int64_t i, int h, int p, int r,
-                                           bool writer, float& u, float& d) {
+                                           float& u, float& d, float (&win)[kMaxWin]) {
     d = ld<T>(k.dt, i * k.H + h) + (k.dt_bias ? k.dt_bias[h] : 0.0f);
     if (k.softplus) d = softplus(d);
     if (k.K) {
         // head_dim is 1 with the conv: the row is channel h
-        float* cs = k.conv_state + ((int64_t)r * k.H + h) * (k.K - 1);
+        const float* cs = k.conv_state + ((int64_t)r * k.H + h) * (k.K - 1);
         const float* w = k.conv_w + (int64_t)h * k.K;
+#pragma unroll
+        for (int j = 0; j < kMaxWin - 1; ++j) win[j] = j < k.K - 1 ? cs[j] : 0.0f;
         const float xin = ld<T>(k.x, i * k.H + h);
-        float c = w[k.K - 1] * xin;
-        for (int j = 0; j < k.K - 1; ++j) c = fmaf(w[j], cs[j], c);
-        // every lane of the row has read the window (same wave, earlier
-        // instructions) before the writer shifts it
-        if (writer) {
-            for (int j = 0; j + 1 < k.K - 1; ++j) cs[j] = cs[j + 1];
-            if (k.K > 1) cs[k.K - 2] = xin;
+        float c = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kMaxWin; ++j) {
+            if (j == k.K - 1) win[j] = xin;
+            if (j < k.K) c = fmaf(w[j], win[j], c);
         }
         u = silu(c);
     } else {
         u = ld<T>(k.x, (i * k.H + h) * (int64_t)k.P + p);
     }
+}
+
+// The conv state keeps the last K-1 entries of the window.
+__device__ __forceinline__ void shift_window(const DecodeKP& k, int h, int r, const float (&win)[kMaxWin]) {
+    float* cs = k.conv_state + ((int64_t)r * k.H + h) * (k.K - 1);
+#pragma unroll
+    for (int j = 0; j < kMaxWin - 1; ++j)
+        if (j < k.K - 1) cs[j] = win[j + 1];
 }
 
 template <typename T>
@@ -83,89 +95,179 @@ __device__ __forceinline__ void store_y(const DecodeKP& k, int64_t e, float v) {
     store_io(static_cast<T*>(k.y) + e, v);
 }
 
-// N = 16 * LPR: LPR lanes per row, 16 states per lane.
-template <typename T, int LPR>
-__global__ __launch_bounds__(256) void decode_rows16(DecodeKP k) {
-    const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t row = gt / LPR;
-    const int q = (int)(gt % LPR);
-    if (row >= k.n_rows) return;  // whole rows leave together (LPR divides 64)
-    const int hp = (int)(row % ((int64_t)k.H * k.P));
-    const int64_t i = row / ((int64_t)k.H * k.P);
-    const int h = hp / k.P, p = hp % k.P;
-    const int r = k.ids[i];
-    const int64_t e = row;  // y / z / x element of the row
-    if (r < 0 || r >= k.R) {
-        if (q == 0) {
-            store_io(static_cast<T*>(k.y) + e, __builtin_nanf(""));
-            if (k.err) atomicOr(k.err, (uint32_t)SSM_DEVERR_IDS);
-        }
-        return;
+// N = SPL * LPR: a row's states lie across LPR lanes, SPL each (4 or 16); with
+// SPL = 4 one 16-byte access per lane moves 1 KB of contiguous state per
+// wave, with SPL = 16 each lane reads 64 contiguous bytes.  Each lane
+// takes RPT rows, 64 / LPR rows apart, and issues every load of all of them
+// before any arithmetic.  The conv window of a row (Mamba-1 form) is spread
+// over the row's lanes too: lane q holds window entries q, q + LPR, ...
+// (the newest input last), the taps are summed across the lanes, and each
+// lane writes its own entries back one place down.  UNI: every row of a
+// lane has one sequence and one group, so B and C are read once.  A row with
+// a bad id is read at row 0 (in bounds) and never written.
+template <typename T, int SPL, int LPR, int RPT, bool UNI>
+__global__ __launch_bounds__(256) void decode_rows(DecodeKP k) {
+    constexpr int NQ = SPL / 4;                     // 16-byte state pieces per lane
+    constexpr int RW = 64 / LPR;                    // rows per wave instruction
+    constexpr int WPL = (kMaxWin + LPR - 1) / LPR;  // window entries per lane
+    const int lane = threadIdx.x & 63, q = lane % LPR;
+    const int64_t wbase = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (RPT * RW);
+    const int64_t hp_n = (int64_t)k.H * k.P;
+    int64_t rowv[RPT], iv[RPT];
+    int hv[RPT], pv[RPT], rv[RPT];
+    bool live[RPT], okv[RPT];
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+        rowv[j] = wbase + j * RW + lane / LPR;
+        live[j] = rowv[j] < k.n_rows;
+        const int64_t row = live[j] ? rowv[j] : 0;
+        iv[j] = row / hp_n;
+        // one sequence per wave: ids[i] through the scalar cache
+        if constexpr (UNI) iv[j] = __builtin_amdgcn_readfirstlane((int)iv[j]);
+        const int hp = (int)(row - iv[j] * hp_n);
+        hv[j] = hp / k.P;
+        pv[j] = hp - hv[j] * k.P;
     }
-    const int g = h / (k.H / k.G);
-    float u, d;
-    row_inputs<T>(k, i, h, p, r, q == 0, u, d);
-
-    constexpr int NS = 16;
-    float* st = k.s + (((int64_t)r * k.H + h) * k.P + p) * k.N + q * NS;
-    f32x4 sv[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) sv[m] = reinterpret_cast<const f32x4*>(st)[m];
-    float bv[NS], cv[NS], av[NS];
-    const int64_t bc = ((int64_t)i * k.G + g) * k.N + q * NS;
-    if constexpr (sizeof(T) == 2) {
+    for (int j = 0; j < RPT; ++j) {
+        const int r = k.ids[iv[j]];
+        okv[j] = live[j] && r >= 0 && r < k.R;
+        rv[j] = okv[j] ? r : 0;
+    }
+    // every load of every row
+    f32x4 sv[RPT][NQ];
+    float av[RPT][SPL], bv[RPT][SPL], cv[RPT][SPL], u[RPT], d[RPT], wv[RPT][WPL];
+    auto load_vals = [&](const void* base, int64_t off, float (&out)[SPL]) {
+        if constexpr (sizeof(T) == 2) {
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            const T* p = static_cast<const T*>(base) + off;
+            if constexpr (SPL == 4) {
+                const u32x2 v = *reinterpret_cast<const u32x2*>(p);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const u32x4 b4 = reinterpret_cast<const u32x4*>(static_cast<const T*>(k.B) + bc)[m];
-            const u32x4 c4 = reinterpret_cast<const u32x4*>(static_cast<const T*>(k.C) + bc)[m];
+                for (int w = 0; w < 2; ++w) {
+                    out[2 * w] = __uint_as_float(v[w] << 16);
+                    out[2 * w + 1] = __uint_as_float(v[w] & 0xFFFF0000u);
+                }
+            } else {
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                bv[8 * m + 2 * w] = __uint_as_float(b4[w] << 16);
-                bv[8 * m + 2 * w + 1] = __uint_as_float(b4[w] & 0xFFFF0000u);
-                cv[8 * m + 2 * w] = __uint_as_float(c4[w] << 16);
-                cv[8 * m + 2 * w + 1] = __uint_as_float(c4[w] & 0xFFFF0000u);
+                for (int m = 0; m < SPL / 8; ++m) {
+                    const u32x4 v = reinterpret_cast<const u32x4*>(p)[m];
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        out[8 * m + 2 * w] = __uint_as_float(v[w] << 16);
+                        out[8 * m + 2 * w + 1] = __uint_as_float(v[w] & 0xFFFF0000u);
+                    }
+                }
+            }
+        } else {
+            const float* p = static_cast<const float*>(base) + off;
+#pragma unroll
+            for (int m = 0; m < NQ; ++m) {
+                const f32x4 v = reinterpret_cast<const f32x4*>(p)[m];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) out[4 * m + w] = v[w];
             }
         }
-    } else {
+    };
+    auto load_bc = [&](int j) {
+        const int64_t bc = (iv[j] * k.G + hv[j] / (k.H / k.G)) * k.N + q * SPL;
+        load_vals(k.B, bc, bv[j]);
+        load_vals(k.C, bc, cv[j]);
+    };
+    if constexpr (UNI) load_bc(0);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const f32x4 b4 = reinterpret_cast<const f32x4*>(static_cast<const float*>(k.B) + bc)[m];
-            const f32x4 c4 = reinterpret_cast<const f32x4*>(static_cast<const float*>(k.C) + bc)[m];
+    for (int j = 0; j < RPT; ++j) {
+        const int h = hv[j];
+        const float* st = k.s + (((int64_t)rv[j] * k.H + h) * k.P + pv[j]) * k.N + q * SPL;
+#pragma unroll
+        for (int m = 0; m < NQ; ++m) sv[j][m] = reinterpret_cast<const f32x4*>(st)[m];
+        if constexpr (!UNI) load_bc(j);
+        if (k.a_per_state) {
+#pragma unroll
+            for (int m = 0; m < NQ; ++m) {
+                const f32x4 a4 = reinterpret_cast<const f32x4*>(k.A + (int64_t)h * k.N + q * SPL)[m];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) av[j][4 * m + w] = a4[w];
+            }
+        } else {
+            const float a = k.A[h];
+#pragma unroll
+            for (int w = 0; w < SPL; ++w) av[j][w] = a;
+        }
+        d[j] = ld<T>(k.dt, iv[j] * k.H + h) + (k.dt_bias ? k.dt_bias[h] : 0.0f);
+        if (k.softplus) d[j] = softplus(d[j]);
+        if (k.K) {
+            // head_dim 1: the row is channel h; window entry e < K-1 is the
+            // conv state, entry K-1 the new input
+            const float* cs = k.conv_state + ((int64_t)rv[j] * k.H + h) * (k.K - 1);
+            const float xin = ld<T>(k.x, iv[j] * k.H + h);
+#pragma unroll
+            for (int m = 0; m < WPL; ++m) {
+                const int e = q + m * LPR;
+                wv[j][m] = e < k.K - 1 ? cs[e] : (e == k.K - 1 ? xin : 0.0f);
+            }
+        } else {
+            u[j] = ld<T>(k.x, (iv[j] * k.H + h) * (int64_t)k.P + pv[j]);
+        }
+    }
+    if constexpr (UNI) {
+#pragma unroll
+        for (int j = 1; j < RPT; ++j)
+#pragma unroll
+            for (int w = 0; w < SPL; ++w) {
+                bv[j][w] = bv[0][w];
+                cv[j][w] = cv[0][w];
+            }
+    }
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+        const int h = hv[j];
+        if (k.K) {
+            float c = 0.0f;
+#pragma unroll
+            for (int m = 0; m < WPL; ++m) {
+                const int e = q + m * LPR;
+                if (e < k.K) c = fmaf(k.conv_w[(int64_t)h * k.K + e], wv[j][m], c);
+            }
+#pragma unroll
+            for (int o = 1; o < LPR; o <<= 1) c += __shfl_xor(c, o, LPR);
+            u[j] = silu(c);
+        }
+        const float du = d[j] * u[j], dl = d[j] * kLog2e;
+        float acc = 0.0f;
+#pragma unroll
+        for (int m = 0; m < NQ; ++m)
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                bv[4 * m + w] = b4[w];
-                cv[4 * m + w] = c4[w];
+                const int n = 4 * m + w;
+                const float hn = fmaf(fast_exp2(dl * av[j][n]), sv[j][m][w], du * bv[j][n]);
+                sv[j][m][w] = hn;
+                acc = fmaf(cv[j][n], hn, acc);
+            }
+#pragma unroll
+        for (int o = 1; o < LPR; o <<= 1) acc += __shfl_xor(acc, o, LPR);
+        if (okv[j]) {
+            float* st = k.s + (((int64_t)rv[j] * k.H + h) * k.P + pv[j]) * k.N + q * SPL;
+#pragma unroll
+            for (int m = 0; m < NQ; ++m) reinterpret_cast<f32x4*>(st)[m] = sv[j][m];
+            if (k.K) {
+                float* cs = k.conv_state + ((int64_t)rv[j] * k.H + h) * (k.K - 1);
+#pragma unroll
+                for (int m = 0; m < WPL; ++m) {
+                    const int e = q + m * LPR;
+                    if (e >= 1 && e < k.K) cs[e - 1] = wv[j][m];
+                }
+            }
+        }
+        if (q == 0 && live[j]) {
+            if (okv[j]) {
+                store_y<T>(k, rowv[j], acc + (k.D ? k.D[h] * u[j] : 0.0f));
+            } else {
+                store_io(static_cast<T*>(k.y) + rowv[j], __builtin_nanf(""));
+                if (k.err) atomicOr(k.err, (uint32_t)SSM_DEVERR_IDS);
             }
         }
     }
-    if (k.a_per_state) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const f32x4 a4 = reinterpret_cast<const f32x4*>(k.A + (int64_t)h * k.N + q * NS)[m];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) av[4 * m + w] = a4[w];
-        }
-    } else {
-        const float a = k.A[h];
-#pragma unroll
-        for (int n = 0; n < NS; ++n) av[n] = a;
-    }
-    const float du = d * u, dl = d * kLog2e;
-    float acc = 0.0f;
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const int n = 4 * m + w;
-            const float hn = fmaf(fast_exp2(dl * av[n]), sv[m][w], du * bv[n]);
-            sv[m][w] = hn;
-            acc = fmaf(cv[n], hn, acc);
-        }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) reinterpret_cast<f32x4*>(st)[m] = sv[m];
-#pragma unroll
-    for (int o = 1; o < LPR; o <<= 1) acc += __shfl_xor(acc, o, LPR);
-    if (q == 0) store_y<T>(k, e, acc + (k.D ? k.D[h] * u : 0.0f));
 }
 
 // Any N: one lane per row, states in a loop.
@@ -183,8 +285,9 @@ __global__ __launch_bounds__(256) void decode_rows_any(DecodeKP k) {
         return;
     }
     const int g = h / (k.H / k.G);
-    float u, d;
-    row_inputs<T>(k, i, h, p, r, true, u, d);
+    float u, d, win[kMaxWin];
+    row_inputs<T>(k, i, h, p, r, u, d, win);
+    if (k.K) shift_window(k, h, r, win);
     float* st = k.s + (((int64_t)r * k.H + h) * k.P + p) * k.N;
     const int64_t bc = ((int64_t)i * k.G + g) * k.N;
     const float du = d * u, dl = d * kLog2e;
@@ -212,24 +315,51 @@ int launch_state_update(const DecodeArgs& a, hipStream_t stream) {
     k.softplus = (sh.flags & SSM_DT_SOFTPLUS) ? 1 : 0;
     if (k.n_rows == 0) return SSM_OK;
     auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+    auto al8 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7) == 0; };
     const bool bf = sh.io == SSM_BF16;
-    const int lpr = (sh.N % 16 == 0 && sh.N <= 256) ? (int)(sh.N / 16) : 0;
-    const bool fast = lpr && (lpr & (lpr - 1)) == 0 && al16(a.s) && al16(a.B) && al16(a.C) &&
+    // 16 states per lane from d_state 64 up (Mamba-2 rows), else 4 per lane
+    const int spl = (sh.N >= 64 && sh.N % 16 == 0) ? 16 : 4;
+    const int lpr = sh.N % spl == 0 ? (int)(sh.N / spl) : 0;
+    const bool bc_al = bf ? (spl == 4 ? al8(a.B) && al8(a.C) : al16(a.B) && al16(a.C))
+                          : (al16(a.B) && al16(a.C));
+    const bool fast = lpr && lpr <= 64 && (lpr & (lpr - 1)) == 0 && al16(a.s) && bc_al &&
                       (!sh.a_per_state || al16(a.A));
     if (fast) {
-        const int64_t threads = k.n_rows * lpr;
-        const dim3 grid((unsigned)((threads + 255) / 256));
-        auto go = [&](auto lc) {
-            constexpr int LPR = decltype(lc)::value;
-            if (bf) hipLaunchKernelGGL((decode_rows16<bf16_t, LPR>), grid, dim3(256), 0, stream, k);
-            else hipLaunchKernelGGL((decode_rows16<float, LPR>), grid, dim3(256), 0, stream, k);
+        const int rpt = spl == 16 ? 1 : 2;  // rows per lane, as RPT below
+        const int64_t rows_per_wave = rpt * (64 / lpr);
+        const int64_t rows_per_block = 4 * rows_per_wave;
+        const dim3 grid((unsigned)((k.n_rows + rows_per_block - 1) / rows_per_block));
+        // one sequence per wave, and one group for a lane's rows
+        const bool uni = (sh.H * sh.P) % rows_per_wave == 0 && (sh.G == 1 || sh.P % rows_per_wave == 0);
+        auto go = [&](auto sc, auto lc) {
+            constexpr int SPL = decltype(sc)::value, LPR = decltype(lc)::value;
+            constexpr int RPT = SPL == 16 ? 1 : 2;
+            if (bf) {
+                if (uni) hipLaunchKernelGGL((decode_rows<bf16_t, SPL, LPR, RPT, true>), grid, dim3(256), 0, stream, k);
+                else hipLaunchKernelGGL((decode_rows<bf16_t, SPL, LPR, RPT, false>), grid, dim3(256), 0, stream, k);
+            } else {
+                if (uni) hipLaunchKernelGGL((decode_rows<float, SPL, LPR, RPT, true>), grid, dim3(256), 0, stream, k);
+                else hipLaunchKernelGGL((decode_rows<float, SPL, LPR, RPT, false>), grid, dim3(256), 0, stream, k);
+            }
         };
-        switch (lpr) {
-            case 1: go(std::integral_constant<int, 1>{}); break;
-            case 2: go(std::integral_constant<int, 2>{}); break;
-            case 4: go(std::integral_constant<int, 4>{}); break;
-            case 8: go(std::integral_constant<int, 8>{}); break;
-            default: go(std::integral_constant<int, 16>{}); break;
+        using I4 = std::integral_constant<int, 4>;
+        using I16 = std::integral_constant<int, 16>;
+        if (spl == 4) {
+            switch (lpr) {
+                case 1: go(I4{}, std::integral_constant<int, 1>{}); break;
+                case 2: go(I4{}, std::integral_constant<int, 2>{}); break;
+                case 4: go(I4{}, std::integral_constant<int, 4>{}); break;
+                case 8: go(I4{}, std::integral_constant<int, 8>{}); break;
+                case 16: go(I4{}, std::integral_constant<int, 16>{}); break;
+                case 32: go(I4{}, std::integral_constant<int, 32>{}); break;
+                default: go(I4{}, std::integral_constant<int, 64>{}); break;
+            }
+        } else {
+            switch (lpr) {
+                case 4: go(I16{}, std::integral_constant<int, 4>{}); break;
+                case 8: go(I16{}, std::integral_constant<int, 8>{}); break;
+                default: go(I16{}, std::integral_constant<int, 16>{}); break;
+            }
         }
     } else {
         const dim3 grid((unsigned)((k.n_rows + 255) / 256));
