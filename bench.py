@@ -115,6 +115,8 @@ MEASURED_TRAFFIC = {
     "C3": {"sha256": "b0591ad1672f9c548339e541594127fcaa68e16a1916aa71e249cdc017a61ddb", "fetch_kib": 144438.3, "write_kib": 174081.6},
     "C4": {"sha256": "2a19fd3700bb14b898a8f31d961c12501b1bdb0583c23b31fa03aca4474e50b7", "fetch_kib": 1665248.8, "write_kib": 2961396.0},
     "C5": {"sha256": "84a811e3d84aca510d566615083c4f313b721cec5e2ceaf515444d565e2f3171", "fetch_kib": 512933.0, "write_kib": 704396.3},
+    "C6": {"sha256": "5060521dce2d813674341dfe930be0831fe8c04182c13b450093e534a8b93fb8", "fetch_kib": 52854.2, "write_kib": 100233.3},
+    "C7": {"sha256": "5060521dce2d813674341dfe930be0831fe8c04182c13b450093e534a8b93fb8", "fetch_kib": 83418.7, "write_kib": 164482.0},
 }
 KERNEL_SOURCES = {
     "C0": ("scan_fwd.hip", "scan_fwd_ts.hip", "scan_fwd_quad.hip", "device_common.h"),
