@@ -636,6 +636,7 @@ bool bwd_supported(const Shape& sh) {
 }
 
 size_t bwd_workspace_bytes(const Shape& sh) {
+    if (ssd_bwd_supported(sh)) return ssd_bwd_workspace_bytes(sh);
     if (!bwd_supported(sh) || sh.S == 0 || sh.L == 0) return 0;
     return carve(sh, nullptr).total;
 }
@@ -644,6 +645,7 @@ int launch_quad_ckpt(const BwdArgs& a, float* ckpt, hipStream_t stream);
 
 int launch_scan_bwd(const BwdArgs& a, hipStream_t stream) {
     const Shape& sh = a.sh;
+    if (ssd_bwd_supported(sh)) return launch_ssd_bwd(a, stream);
     if (!bwd_supported(sh)) return SSM_ERR_UNSUPPORTED;
     const int64_t per_row = sh.d_inner() * sh.N;
     BwdKP kp = {};

@@ -70,6 +70,7 @@ struct SsdKP {
     const int32_t* ids;
     bf16_t* y;
     float* state_out;
+    bf16_t* ckpt;  // CKPT: [S][H][n_chunks][P][N], the state entering each chunk
     uint32_t* err;
     int L, H, G, R, hpg;
     int has_D;
@@ -117,7 +118,10 @@ __device__ __forceinline__ bf16x4 ldtr(const bf16_t* p) {
     return __builtin_bit_cast(bf16x4, v);
 }
 
-template <int P, int N, bool SOFTPLUS>
+// CKPT: the backward's recompute: no y, no final state; the state entering
+// every chunk is stored (as the bf16 the forward's carried-state product
+// reads) for the reverse pass.
+template <int P, int N, bool SOFTPLUS, bool CKPT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void ssd_fwd(SsdKP p) {
     static_assert((P == 32 || P == 64) && (N == 64 || N == 128), "tile shapes");
     constexpr int PB = P / 16;      // 16-channel blocks
@@ -197,6 +201,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                                                  rows > 0 ? (int)(rows * row) : 0, 0x00020000);
     };
 
+    const int n_chunks = (L + kQ - 1) / kQ;
     // staging: x, B, C rows by 16-byte chunks
     constexpr int XCH = kQ * P / 8, BCH = kQ * N / 8;     // chunks per chunk-tile
     constexpr int XPER = (XCH + kThreads - 1) / kThreads, BPER = BCH / kThreads;
@@ -216,7 +221,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             const int e = tid + kThreads * k;
             const int t = e / (N / 8), part = e % (N / 8);
             sb[k] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)(t * brow) + part * 16, 0, 0);
-            sc[k] = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(t * brow) + part * 16, 0, 0);
+            if constexpr (!CKPT) sc[k] = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(t * brow) + part * 16, 0, 0);
         }
         if (tid < kQ) sdt = __builtin_amdgcn_raw_buffer_load_b16(rsrc(dg, t0, drow), (int)(tid * drow), 0, 0);
     };
@@ -231,7 +236,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             const int e = tid + kThreads * k;
             const int t = e / (N / 8), part = e % (N / 8);
             *reinterpret_cast<u32x4*>(&B_l[t * NP + part * 8]) = sb[k];
-            *reinterpret_cast<u32x4*>(&C_l[t * NP + part * 8]) = sc[k];
+            if constexpr (!CKPT) *reinterpret_cast<u32x4*>(&C_l[t * NP + part * 8]) = sc[k];
         }
         if (wave == 0) {  // decays of the chunk, lane = token
             float d = to_f32((bf16_t)sdt);
@@ -252,6 +257,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                 const uint32_t lo = uint32_t(bf16_rne(v[0])) | (uint32_t(bf16_rne(v[1])) << 16);
                 const uint32_t hi = uint32_t(bf16_rne(v[2])) | (uint32_t(bf16_rne(v[3])) << 16);
                 *reinterpret_cast<u32x2*>(&H_l[(pw + l16) * NPH + (NH * sh + j) * 16 + 4 * g4]) = u32x2{lo, hi};
+                if constexpr (CKPT)
+                    *reinterpret_cast<u32x2*>(p.ckpt + (((((int64_t)i * p.H + hh) * n_chunks + t0 / kQ) * P + pw + l16) * N +
+                                                        (NH * sh + j) * 16 + 4 * g4)) = u32x2{lo, hi};
             }
         }
     };
@@ -262,7 +270,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     // M's tiles above the diagonal are never written: zero the whole tile once
     for (int e = tid; e < kQ * MP / 2; e += kThreads) reinterpret_cast<uint32_t*>(M_l)[e] = 0u;
 
-    const int n_chunks = (L + kQ - 1) / kQ;
     load_chunk(0);
     for (int ch = 0; ch < n_chunks; ++ch) {
         const int t0 = ch * kQ;
@@ -271,6 +278,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         __syncthreads();
         load_chunk(t0 + kQ);  // next chunk (past the end: reads zero, never used)
 
+        if constexpr (!CKPT) {
         // M = G o L on the 10 causal 16x16 tiles, to LDS as bf16.  Tile k (row by
         // row: (tb,sb) = (0,0),(1,0),(1,1),(2,0),...) goes to wave k % 8: every
         // wave has tile k = w, waves 0 and 1 also tile w + 8; their G products
@@ -364,6 +372,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             __builtin_amdgcn_raw_buffer_store_b64(u32x2{packed[0], packed[1]}, ry, yoff + pb * 32, 0, 0);
         }
 
+        }  // !CKPT
+
         // state of this wave's block: h^T = exp(cum_last) h^T + B^T (w o X)
         if (owns) {
             const float e_last = elast_l;
@@ -394,7 +404,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         }
     }
 
-    if (owns) {
+    if (owns && !CKPT) {
         float* so = p.state_out + (((int64_t)i * p.H + hh) * P + pw + l16) * N + NH * sh * 16;
 #pragma unroll
         for (int j = 0; j < NH; ++j)
@@ -403,11 +413,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
 }
 
-template <int P, int N>
+template <int P, int N, bool CKPT = false>
 int launch_ssd_pn(const SsdKP& kp, int S, bool softplus, hipStream_t st) {
     const dim3 grid((unsigned)((int64_t)kp.H * S));
-    if (softplus) hipLaunchKernelGGL((ssd_fwd<P, N, true>), grid, dim3(kThreads), 0, st, kp);
-    else hipLaunchKernelGGL((ssd_fwd<P, N, false>), grid, dim3(kThreads), 0, st, kp);
+    if (softplus) hipLaunchKernelGGL((ssd_fwd<P, N, true, CKPT>), grid, dim3(kThreads), 0, st, kp);
+    else hipLaunchKernelGGL((ssd_fwd<P, N, false, CKPT>), grid, dim3(kThreads), 0, st, kp);
     return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
@@ -429,6 +439,7 @@ int launch_ssd_fwd(const FwdArgs& a, hipStream_t stream) {
     kp.s = a.s; kp.x = static_cast<const bf16_t*>(a.x); kp.dt = static_cast<const bf16_t*>(a.dt);
     kp.A = a.A; kp.B = static_cast<const bf16_t*>(a.B); kp.C = static_cast<const bf16_t*>(a.C);
     kp.D = a.D; kp.ids = a.ids; kp.y = static_cast<bf16_t*>(a.y); kp.state_out = a.state_out;
+    kp.ckpt = nullptr;
     kp.err = a.err;
     kp.L = (int)sh.L; kp.H = (int)sh.H; kp.G = (int)sh.G; kp.R = (int)sh.R;
     kp.hpg = (int)(sh.H / sh.G);
@@ -439,6 +450,27 @@ int launch_ssd_fwd(const FwdArgs& a, hipStream_t stream) {
     if (sh.P == 64 && sh.N == 64) return launch_ssd_pn<64, 64>(kp, S, sp, stream);
     if (sh.P == 32 && sh.N == 128) return launch_ssd_pn<32, 128>(kp, S, sp, stream);
     if (sh.P == 32 && sh.N == 64) return launch_ssd_pn<32, 64>(kp, S, sp, stream);
+    return SSM_ERR_UNSUPPORTED;
+}
+
+// The backward's recompute: chunk-entry states of every (sequence, head) as
+// bf16 into ckpt [S][H][n_chunks][P][N].
+int launch_ssd_ckpt(const BwdArgs& a, bf16_t* ckpt, hipStream_t stream) {
+    const Shape& sh = a.sh;
+    SsdKP kp;
+    kp.s = a.s; kp.x = static_cast<const bf16_t*>(a.x); kp.dt = static_cast<const bf16_t*>(a.dt);
+    kp.A = a.A; kp.B = static_cast<const bf16_t*>(a.B); kp.C = static_cast<const bf16_t*>(a.C);
+    kp.D = a.D; kp.ids = a.ids; kp.y = nullptr; kp.state_out = nullptr; kp.ckpt = ckpt;
+    kp.err = a.err;
+    kp.L = (int)sh.L; kp.H = (int)sh.H; kp.G = (int)sh.G; kp.R = (int)sh.R;
+    kp.hpg = (int)(sh.H / sh.G);
+    kp.has_D = (sh.flags & SSM_HAS_D) ? 1 : 0;
+    const bool sp = (sh.flags & SSM_DT_SOFTPLUS) != 0;
+    const int S = (int)sh.S;
+    if (sh.P == 64 && sh.N == 128) return launch_ssd_pn<64, 128, true>(kp, S, sp, stream);
+    if (sh.P == 64 && sh.N == 64) return launch_ssd_pn<64, 64, true>(kp, S, sp, stream);
+    if (sh.P == 32 && sh.N == 128) return launch_ssd_pn<32, 128, true>(kp, S, sp, stream);
+    if (sh.P == 32 && sh.N == 64) return launch_ssd_pn<32, 64, true>(kp, S, sp, stream);
     return SSM_ERR_UNSUPPORTED;
 }
 

@@ -111,6 +111,12 @@ int launch_ssd_fwd(const FwdArgs& a, hipStream_t stream);
 // Backward: Mamba-1 form, d_state <= 16, one group, no fused conv.
 bool bwd_supported(const Shape& sh);
 
+// Backward of the Mamba-2 form (bf16 io, head_dim 32/64, d_state 64/128, no
+// conv): chunked products on MFMA.
+bool ssd_bwd_supported(const Shape& sh);
+size_t ssd_bwd_workspace_bytes(const Shape& sh);
+int launch_ssd_bwd(const BwdArgs& a, hipStream_t stream);
+
 // Returns SSM_OK, SSM_ERR_UNSUPPORTED, or SSM_ERR_HIP.
 int launch_scan_fwd(const FwdArgs& a, hipStream_t stream);
 int launch_scan_bwd(const BwdArgs& a, hipStream_t stream);

@@ -269,6 +269,10 @@ def config(name: str) -> ScanProblem:
                          io="bf16", seed=0xC2)
         add_dout(p, 0xC4)
         return p
+    if name == "C8":   # backward of the C3 Mamba-2 scan: C3's draws, dy ~ N(0,1), dstate = 0
+        p = config("C3")
+        add_dout(p, 0xC8)
+        return p
     raise KeyError(name)
 
 

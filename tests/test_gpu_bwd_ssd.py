@@ -1,0 +1,142 @@
+"""GPU parity of selective_scan_bwd for the Mamba-2 form (scalar A per head,
+B/C shared by the heads of a group; bf16 io), the chunked backward on MFMA,
+against the float64 oracle through the C ABI.
+
+Tolerance.  The products run with bf16 operands (x, dy, B, C as stored; the
+checkpointed state, the carried gradient and the M and Lm tiles rounded to
+bf16 once per chunk) and fp32 accumulation, as the forward's MFMA path does:
+each term carries a relative error of about 2^-8, and sums of many terms of
+either sign carry an absolute error that scales with their terms.  Every
+gradient is compared element by element with rtol 2e-2 and an absolute floor
+of 2e-2 x rms of the oracle's values (the bf16 tolerance the forward uses,
+with the floor of the channel/token sums)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ssm_inputs
+from selective_scan_recurrence_amd import ops
+from tests.gpu_util import desc_of, device_inputs, dev, host
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("d_x", "d_dt", "d_s", "d_A", "d_D", "d_B", "d_C")
+
+
+def _check(name, got, want, rtol=2e-2, floor=2e-2):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert got.shape == want.shape, (name, got.shape, want.shape)
+    rms = float(np.sqrt(np.mean(want ** 2))) if want.size else 0.0
+    atol = floor * max(rms, 1e-30)
+    err = np.abs(got - want)
+    bad = ~(err <= atol + rtol * np.abs(want))
+    if bad.any():
+        worst = np.unravel_index(np.argmax(err - atol - rtol * np.abs(want)), err.shape)
+        raise AssertionError(f"{name}: {int(bad.sum())}/{bad.size} outside (rms {rms:.3g}, atol {atol:.3g}); "
+                             f"worst at {worst}: got {got[worst]!r} want {want[worst]!r}")
+
+
+def _run(p, t=None):
+    t = t or device_inputs(p)
+    d = desc_of(p)
+    dout = torch.cat([t["dy"].reshape(-1).view(torch.uint8), t["dstate"].reshape(-1).view(torch.uint8)])
+    _, g = ops.scan_bwd(d, t["s"], t["x"], t["dt"], t["A"], t["B"], t["C"], t.get("D"), t["ids"], dout)
+    torch.cuda.synchronize()
+    return g
+
+
+def _problem(seed, **kw):
+    base = dict(n_seqs=2, n_tokens=200, n_head=4, head_dim=64, d_state=128, n_group=1,
+                a_per_state=False, d_conv=0, io="bf16", h0_std=0.1, ids="perm", n_state_rows=3,
+                A_kind="uniform", A_range=(1.0, 16.0), bc_std=1.0 / np.sqrt(128.0))
+    base.update(kw)
+    p = ssm_inputs.make_problem(seed=seed, **base)
+    ssm_inputs.add_dout(p, seed + 1)
+    return p
+
+
+CASES = {
+    "p64_n128_ragged": dict(),
+    "p32_n64_two_groups": dict(n_seqs=1, n_tokens=64, n_head=4, head_dim=32, d_state=64, n_group=2,
+                               n_state_rows=1, ids="identity", bc_std=0.125),
+    "p64_n64_softplus": dict(n_tokens=130, head_dim=64, d_state=64, n_group=2, dt_softplus=True,
+                             bc_std=0.125),
+    "p32_n128_one_token": dict(n_seqs=1, n_tokens=1, n_head=2, head_dim=32, n_state_rows=2),
+    "p64_n128_no_D_long": dict(n_seqs=1, n_tokens=333, n_head=2, has_D=False, n_state_rows=1,
+                               ids="identity"),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_ssd_bwd_parity(case):
+    p = _problem(101 + sorted(CASES).index(case), **CASES[case])
+    g = _run(p)
+    o = oracle.problem_bwd(p)
+    for k in GRADS:
+        if o.get(k) is None:
+            continue
+        _check(f"{case} {k}", host(g[k]), o[k])
+
+
+def test_ssd_bwd_dstate_seed():
+    """A nonzero upstream gradient of the final state enters the last chunk's carry."""
+    p = ssm_inputs.make_problem(n_seqs=2, n_tokens=150, n_head=3, head_dim=64, d_state=128,
+                                a_per_state=False, d_conv=0, io="bf16", seed=131, h0_std=0.1,
+                                ids="perm", n_state_rows=2, A_kind="uniform", A_range=(1.0, 16.0),
+                                bc_std=1.0 / np.sqrt(128.0))
+    ssm_inputs.add_dout(p, 132, dstate_std=1.0)
+    g = _run(p)
+    o = oracle.problem_bwd(p)
+    for k in GRADS:
+        _check(f"dstate {k}", host(g[k]), o[k])
+
+
+def test_ssd_bwd_bad_id():
+    """A sequence whose id is out of range: its d_x and d_dt are NaN, it adds
+    nothing to d_s, the error word is set; the other sequence is unaffected."""
+    p = _problem(141, n_seqs=2, n_tokens=70, n_head=2, n_state_rows=3)
+    t = device_inputs(p)
+    bad = p.ids.copy()
+    bad[1] = 7
+    t["ids"] = dev(bad)
+    d = desc_of(p)
+    dout = torch.cat([t["dy"].reshape(-1).view(torch.uint8), t["dstate"].reshape(-1).view(torch.uint8)])
+    ws = ops.workspace(d, True)
+    _, g = ops.scan_bwd(d, t["s"], t["x"], t["dt"], t["A"], t["B"], t["C"], t.get("D"), t["ids"], dout, ws=ws)
+    torch.cuda.synchronize()
+    import selective_scan_recurrence_amd as ssm
+    assert ssm.ssm_get_device_error(ws) & ssm.SSM_DEVERR_IDS
+    assert np.isnan(host(g["d_x"])[1]).all() and np.isnan(host(g["d_dt"])[1]).all()
+    # sequence 0 alone, from the oracle
+    q = _problem(141, n_seqs=2, n_tokens=70, n_head=2, n_state_rows=3)
+    o = oracle.scan_bwd(q.value("s"), q.value("x")[:1], q.value("dt")[:1], q.value("A"), q.value("B")[:1],
+                        q.value("C")[:1], q.value("D"), q.ids[:1], q.value("dy")[:1], q.value("dstate")[:1])
+    _check("bad-id d_x of the good sequence", host(g["d_x"])[0], o["d_x"][0])
+    ds = host(g["d_s"])
+    _check("bad-id d_s", ds, o["d_s"])
+
+
+def test_ssd_bwd_full_size_head_subset():
+    """The 4 x 4096 x 80 x 64 x 128 workload in the launch configuration bench.py
+    times, with dy zero outside three heads: every gradient (d_B and d_C, sums
+    over heads, included) then equals the oracle's on those three heads alone."""
+    p = ssm_inputs.config("C8")
+    heads = np.array([0, 37, 79])
+    dy_bits = p.t["dy"].bits.copy()
+    mask = np.zeros(p.n_head, bool)
+    mask[heads] = True
+    dy_bits[:, :, ~mask, :] = 0
+    p.t["dy"] = ssm_inputs.Stored(dy_bits, ssm_inputs.bf16_bits_to_f32(dy_bits), "bf16")
+    g = _run(p)
+    v = p.value
+    o = oracle.scan_bwd(v("s")[:, heads], v("x")[:, :, heads], v("dt")[:, :, heads], v("A")[heads],
+                        v("B"), v("C"), v("D")[heads], p.ids, v("dy")[:, :, heads], v("dstate")[:, heads])
+    _check("C8 d_x", host(g["d_x"])[:, :, heads], o["d_x"])
+    _check("C8 d_dt", host(g["d_dt"])[:, :, heads], o["d_dt"])
+    _check("C8 d_s", host(g["d_s"])[:, heads], o["d_s"])
+    _check("C8 d_A", host(g["d_A"])[heads], o["d_A"])
+    _check("C8 d_D", host(g["d_D"])[heads], o["d_D"])
+    _check("C8 d_B", host(g["d_B"]), o["d_B"])
+    _check("C8 d_C", host(g["d_C"]), o["d_C"])
