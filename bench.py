@@ -52,6 +52,8 @@ WORKLOADS = {
           "d_state 16, d_conv 4, bf16 x/dt/B/C/z/y, fp32 states updated in place by permuted ids",
     "C7": "Mamba-2 single-token decode step of 64 sequences at the 80 heads x 64 layer, "
           "d_state 128, bf16 x/dt/B/C/z/y, fp32 states updated in place by permuted ids",
+    "C8": "Mamba-2 scan reverse-time backward of the 4x4096, 80 heads x 64, d_state 128 bf16 scan, "
+          "fp32 grads",
 }
 
 
@@ -117,6 +119,7 @@ MEASURED_TRAFFIC = {
     "C5": {"sha256": "84a811e3d84aca510d566615083c4f313b721cec5e2ceaf515444d565e2f3171", "fetch_kib": 512933.0, "write_kib": 704396.3},
     "C6": {"sha256": "5060521dce2d813674341dfe930be0831fe8c04182c13b450093e534a8b93fb8", "fetch_kib": 52854.2, "write_kib": 100233.3},
     "C7": {"sha256": "5060521dce2d813674341dfe930be0831fe8c04182c13b450093e534a8b93fb8", "fetch_kib": 83418.7, "write_kib": 164482.0},
+    "C8": {"sha256": "6b78613da6a0a906f47e65dc905cae4c6386789adee41ad9e76b2b4caefc5d01", "fetch_kib": 762295.7, "write_kib": 2645552.8},
 }
 KERNEL_SOURCES = {
     "C0": ("scan_fwd.hip", "scan_fwd_ts.hip", "scan_fwd_quad.hip", "device_common.h"),
@@ -127,6 +130,7 @@ KERNEL_SOURCES = {
     "C5": ("conv_bwd.hip", "device_common.h"),
     "C6": ("decode.hip", "device_common.h"),
     "C7": ("decode.hip", "device_common.h"),
+    "C8": ("ssd_bwd.hip", "ssd_fwd.hip", "device_common.h"),
 }
 
 
@@ -172,6 +176,19 @@ def ssd_mfma_flops(p) -> int:
     chunks = -(-p.n_tokens // q)
     tri = q * (q + 1) // 2
     per = 2 * tri * p.d_state + 2 * tri * p.head_dim + 4 * q * p.d_state * p.head_dim
+    return int(p.n_seqs * p.n_head * chunks * per)
+
+
+def ssd_bwd_mfma_flops(p) -> int:
+    """Dense-product flops of the chunked Mamba-2 backward, per (sequence, head,
+    64-token chunk): S = C B^T and R = dY X^T on the causal tiles, M^T dY,
+    Lm B and Lm^T C on the causal tiles, and the four Q x N x P products
+    (B G^T, dY h_in, X G, the carry C^T dY), plus the recompute's state update."""
+    q = SSD_Q
+    chunks = -(-p.n_tokens // q)
+    tri = q * (q + 1) // 2
+    n, pd = p.d_state, p.head_dim
+    per = 2 * tri * (n + pd) + 2 * tri * pd + 4 * tri * n + 5 * 2 * q * n * pd
     return int(p.n_seqs * p.n_head * chunks * per)
 
 
@@ -237,7 +254,7 @@ def cpu_baseline(name, p, min_seconds=10.0, max_reps=50):
     args = (v("s")[:, heads], v("x")[:, :, heads], v("dt")[:, :, heads], v("A")[heads], v("B"),
             v("C"), v("D")[heads] if p.has_D else None, p.ids)
     grp = oracle.group_of_head(p.n_head, p.n_group)[heads]
-    backward = name == "C4"
+    backward = name in ("C4", "C8")
     extra = (v("dy")[:, :, heads], v("dstate")[:, heads]) if backward else ()
     reps, sec = 0, 0.0
     while reps < max_reps and (reps == 0 or sec < min_seconds):
@@ -259,10 +276,12 @@ def cpu_baseline(name, p, min_seconds=10.0, max_reps=50):
             "nproc": os.cpu_count()}
 
 
-def parity_gate_bwd(p, g):
-    """Backward: every token of sampled channels against the oracle, per-element
-    gradients with rtol 1e-4 and an absolute floor of 1e-5 x rms, channel and
-    token sums with a floor of 1e-4 x rms."""
+def parity_gate_bwd(name, p, g):
+    """Backward: every token of sampled channels (heads) against the oracle.
+    Mamba-1 (fp32 arithmetic): per-element gradients with rtol 1e-4 and an
+    absolute floor of 1e-5 x rms, channel and token sums with a floor of
+    1e-4 x rms.  Mamba-2 (bf16 MFMA operands): rtol 2e-2 and a floor of
+    2e-2 x rms for every gradient."""
     import torch
     import oracle
     rng = np.random.default_rng(0xB1)
@@ -273,21 +292,24 @@ def parity_gate_bwd(p, g):
                         v("dy")[:, :, heads], v("dstate")[:, heads],
                         grp_of_head=np.zeros(len(heads), np.int64))
     hs = torch.as_tensor(heads, device=g["d_x"].device)
-    picks = {"d_x": (g["d_x"].index_select(2, hs), 1e-5), "d_dt": (g["d_dt"].index_select(2, hs), 1e-5),
-             "d_A": (g["d_A"].index_select(0, hs), 1e-4), "d_s": (g["d_s"].index_select(1, hs), 1e-4)}
+    mfma = uses_ssd(p)
+    rtol = 2e-2 if mfma else 1e-4
+    fe, fs = (2e-2, 2e-2) if mfma else (1e-5, 1e-4)
+    picks = {"d_x": (g["d_x"].index_select(2, hs), fe), "d_dt": (g["d_dt"].index_select(2, hs), fe),
+             "d_A": (g["d_A"].index_select(0, hs), fs), "d_s": (g["d_s"].index_select(1, hs), fs)}
     if p.has_D:
-        picks["d_D"] = (g["d_D"].index_select(0, hs), 1e-4)
+        picks["d_D"] = (g["d_D"].index_select(0, hs), fs)
     checked = 0
     for k, (got_t, floor) in picks.items():
         got = got_t.double().cpu().numpy()
         want = o[k]
         rms = float(np.sqrt(np.mean(want ** 2))) if want.size else 0.0
-        bad = ~(np.abs(got - want) <= floor * rms + 1e-4 * np.abs(want))
+        bad = ~(np.abs(got - want) <= floor * rms + rtol * np.abs(want))
         if bad.any():
-            raise SystemExit(f"parity gate failed on C4 {k}: {int(bad.sum())} elements outside")
+            raise SystemExit(f"parity gate failed on {name} {k}: {int(bad.sum())} elements outside")
         checked += want.size
-    return {"checked_elements": int(checked), "rtol": 1e-4, "atol": "1e-5 x rms (per element), "
-            "1e-4 x rms (sums)"}
+    return {"checked_elements": int(checked), "rtol": rtol,
+            "atol": f"{fe:g} x rms (per element), {fs:g} x rms (sums)"}
 
 
 def conv_bwd_bytes(c) -> int:
@@ -564,7 +586,7 @@ def main():
     ssm.load()
     dev = torch.device("cuda:0")
     name = args.config
-    backward = name == "C4"
+    backward = name in ("C4", "C8")
     p = ssm_inputs.config(name)
     desc = ops.make_desc(n_seqs=p.n_seqs, n_tokens=p.n_tokens, n_head=p.n_head,
                          head_dim=p.head_dim, d_state=p.d_state, n_group=p.n_group,
@@ -596,7 +618,7 @@ def main():
 
     res = step(sets[0])
     torch.cuda.synchronize()
-    parity = parity_gate_bwd(p, res[1]) if backward else parity_gate(name, p, res)
+    parity = parity_gate_bwd(name, p, res[1]) if backward else parity_gate(name, p, res)
 
     for k in range(args.warmup):
         step(sets[k % copies])
@@ -618,8 +640,8 @@ def main():
     ch_tok = p.n_seqs * p.n_tokens * p.n_head * p.head_dim
     avg_s = float(launch_ms.mean()) * 1e-3
     floors = {"hbm": step_bytes / (HBM_PEAK_GBS * 1e9)}
-    if uses_ssd(p) and not backward:
-        flops = ssd_mfma_flops(p)
+    if uses_ssd(p):
+        flops = ssd_bwd_mfma_flops(p) if backward else ssd_mfma_flops(p)
         floors["mfma"] = flops / (MFMA_BF16_PEAK_T * 1e12)
     else:
         slots = valu_slots_per_channel_token(p, backward) * ch_tok

@@ -62,7 +62,7 @@ typedef enum {
     SSM_ERR_NULL = 1,        /* a required pointer is NULL */
     SSM_ERR_SHAPE = 2,       /* a dimension is out of range or inconsistent */
     SSM_ERR_DTYPE = 3,       /* unknown io dtype */
-    SSM_ERR_UNSUPPORTED = 4, /* a valid combination this build has no kernel for */
+    SSM_ERR_UNSUPPORTED = 4, /* a valid combination the library has no kernel for */
     SSM_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
     SSM_ERR_ALIGN = 6,       /* a pointer is not aligned to its element size (workspace: 256 B) */
     SSM_ERR_HIP = 7          /* a HIP launch reported an error */
@@ -193,12 +193,18 @@ int selective_scan_fwd(const ssm_scan_desc *desc, const float *s, const void *x,
  * sets SSM_DEVERR_IDS, adds nothing to d_s, and has its d_x and d_dt written
  * as NaN; sums it takes part in that depend on its initial state (d_A, d_C)
  * are NaN as well.
- * This build supports the Mamba-1 form with d_state <= 16 and one group;
- * other shapes return SSM_ERR_UNSUPPORTED.  The adjoint is the one of "kizzasi-model
+ * Supported: the Mamba-1 form with d_state <= 16 and one group, and the
+ * Mamba-2 form (A per head) with bf16 io, head_dim 32 or 64, d_state 64 or
+ * 128 and 16-byte aligned x, dout, B, C, s and dgrad; other shapes return
+ * SSM_ERR_UNSUPPORTED.  The adjoint is the one of "kizzasi-model
  * backprop_ssm.rs" (ssm_backward): dL/dh_{t-1} = a_t dL/dh_t + C_{t-1} dy_{t-1},
  * with the per-element terms of "mambazip mamba1/model.rs"
- * (accumulate_token_step_gradients).  Sums over channels and tokens are
- * taken in a fixed order: results are bitwise repeatable.
+ * (accumulate_token_step_gradients).  Mamba-1: sums over channels and tokens
+ * are taken in a fixed order, so results are bitwise repeatable.  Mamba-2:
+ * the products run on bf16 MFMA operands (the carried gradient and the
+ * checkpointed state as bf16 pairs) with fp32 accumulation, and d_B and d_C
+ * collect the heads of a group with fp32 atomic adds, whose order (and so
+ * their last bits) varies from run to run. 
  * workspace: ssm_scan_workspace_bytes(desc, 1) bytes, 256-byte aligned. */
 int selective_scan_bwd(const ssm_scan_desc *desc, const float *s, const void *x,
                        const void *dt, const float *A, const void *B, const void *C,
