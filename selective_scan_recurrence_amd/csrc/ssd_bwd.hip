@@ -31,11 +31,11 @@
 // Work split.  One workgroup (8 waves) runs one (sequence, head) through its
 // chunks from the last.  G^T [N][P] is held in fp32 MFMA accumulators by the
 // waves that own a 16-channel block and half of the states (as the forward
-// holds h^T); a bf16 copy of G and the checkpointed h_in are staged in LDS
-// (G as a bf16 value plus a bf16 remainder, so that the products that read it
-// keep about 16 significant bits of the carried gradient) with the chunk's
-// x, dy, B and C rows, the next (earlier) chunk's rows being
-// loaded meanwhile.  All products run on v_mfma_f32_16x16x32_bf16: operands
+// holds h^T).  G is staged in LDS as a bf16 value plus a bf16 remainder, so
+// that the products that read it keep about 16 significant bits of the
+// carried gradient, and so is the fp32 checkpoint of h_in (the decay
+// gradient multiplies its errors by A); with them the chunk's x, dy, B and C
+// rows, the next (earlier) chunk's rows being loaded meanwhile.  All products run on v_mfma_f32_16x16x32_bf16: operands
 // whose k index runs along a stored row come from 16-byte LDS row reads, the
 // others from the transposing read ds_read_b64_tr_b16 (as in the forward).
 // dB and dC, which every head of a group adds to, are accumulated with fp32
@@ -71,7 +71,7 @@ struct SsdBwdKP {
     const int32_t* ids;
     const bf16_t* dy;
     const float* dstate;
-    const bf16_t* ckpt;  // [S][H][n_chunks][P][N]: state entering each chunk
+    const float* ckpt;   // [S][H][n_chunks][P][N]: state entering each chunk
     float* d_x;
     float* d_dt;
     float* d_B;          // zeroed before; atomic adds
@@ -134,7 +134,8 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
     __shared__ __attribute__((aligned(16))) bf16_t Y_l[kQ * XP];    // dy
     __shared__ __attribute__((aligned(16))) bf16_t B_l[kQ * NP];
     __shared__ __attribute__((aligned(16))) bf16_t C_l[kQ * NP];
-    __shared__ __attribute__((aligned(16))) bf16_t H_l[P * NPH];    // h_in
+    __shared__ __attribute__((aligned(16))) bf16_t H_l[P * NPH];    // h_in as bf16 ...
+    __shared__ __attribute__((aligned(16))) bf16_t Hr_l[P * NPH];   // ... and its remainder
     __shared__ __attribute__((aligned(16))) bf16_t G_l[P * NPH];    // G as bf16 ...
     __shared__ __attribute__((aligned(16))) bf16_t Gr_l[P * NPH];   // ... and its remainder, G - G_l in bf16
     __shared__ __attribute__((aligned(16))) bf16_t M_l[kQ * MP];
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
     const char* dg = reinterpret_cast<const char*>(p.dt) + ((int64_t)i * L * p.H + hh) * 2;
     char* dxg = reinterpret_cast<char*>(p.d_x) + ((int64_t)i * L * p.H + hh) * P * 4;
     char* ddg = reinterpret_cast<char*>(p.d_dt) + ((int64_t)i * L * p.H + hh) * 4;
-    const bf16_t* ckg = p.ckpt + ((int64_t)i * p.H + hh) * p.n_chunks * (P * N);
+    const float* ckg = p.ckpt + ((int64_t)i * p.H + hh) * p.n_chunks * (P * N);
     auto rsrc = [&](const char* base, int t0, int64_t row) {
         // t0 < 0 (before the first chunk) gives an empty range
         const int rows = t0 < 0 ? 0 : L - t0;
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
     };
 
     // staging of a chunk: x, dy, B, C rows and the checkpoint, by 16-byte pieces
-    constexpr int XCH = kQ * P / 8, BCH = kQ * N / 8, HCH = P * N / 8;
+    constexpr int XCH = kQ * P / 8, BCH = kQ * N / 8, HCH = P * N / 4;  // HCH: 16-byte pieces of fp32
     constexpr int XPER = (XCH + kThreads - 1) / kThreads, BPER = BCH / kThreads;
     constexpr int HPER = (HCH + kThreads - 1) / kThreads;
     static_assert(BPER >= 1 && BCH % kThreads == 0, "staging covers the chunk");
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
         const auto rx = rsrc(xg, c < 0 ? -1 : t0, xrow), ry = rsrc(yg, c < 0 ? -1 : t0, xrow);
         const auto rb = rsrc(bg, c < 0 ? -1 : t0, brow), rc = rsrc(cg, c < 0 ? -1 : t0, brow);
         const auto rk = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<bf16_t*>(ckg) + (c < 0 ? 0 : (int64_t)c * (P * N)), 0, c < 0 ? 0 : P * N * 2, 0x00020000);
+            const_cast<float*>(ckg) + (c < 0 ? 0 : (int64_t)c * (P * N)), 0, c < 0 ? 0 : P * N * 4, 0x00020000);
 #pragma unroll
         for (int k = 0; k < XPER; ++k) {
             const int e = tid + kThreads * k;
@@ -241,8 +242,18 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
         }
 #pragma unroll
         for (int k = 0; k < HPER; ++k) {
-            const int e = tid + kThreads * k;  // 16-byte piece e of the [P][N] checkpoint
-            if (e < HCH) *reinterpret_cast<u32x4*>(&H_l[(e / (N / 8)) * NPH + (e % (N / 8)) * 8]) = sk[k];
+            const int e = tid + kThreads * k;  // 16-byte piece e (4 states) of the fp32 [P][N] checkpoint
+            if (e < HCH) {
+                float v[4], rem[4];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    v[rr] = __uint_as_float(sk[k][rr]);
+                    rem[rr] = v[rr] - to_f32(bf16_rne(v[rr]));
+                }
+                const int off = (e / (N / 4)) * NPH + (e % (N / 4)) * 4;
+                *reinterpret_cast<u32x2*>(&H_l[off]) = pack4(v[0], v[1], v[2], v[3]);
+                *reinterpret_cast<u32x2*>(&Hr_l[off]) = pack4(rem[0], rem[1], rem[2], rem[3]);
+            }
         }
         if (wave == 0) {  // decays of the chunk, lane = token
             dt_raw = to_f32((bf16_t)sdt);
@@ -374,9 +385,12 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
 #pragma unroll
             for (int j = 0; j < NH; ++j)
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr)
-                    gh = fmaf(gacc[j][rr], (float)*reinterpret_cast<const __bf16*>(
-                                               &H_l[(pw + l16) * NPH + (NH * sh + j) * 16 + 4 * g4 + rr]), gh);
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int off = (pw + l16) * NPH + (NH * sh + j) * 16 + 4 * g4 + rr;
+                    const float hv = (float)*reinterpret_cast<const __bf16*>(&H_l[off]) +
+                                     (float)*reinterpret_cast<const __bf16*>(&Hr_l[off]);
+                    gh = fmaf(gacc[j][rr], hv, gh);
+                }
             gh = wave_sum(gh);
             if (lane == 0) gh_l[wave] = gh;
         } else if (lane == 0) {
@@ -437,8 +451,11 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
                 const int nb = nb0 + j, n = nb * 16 + l16;
                 f32x4 c1 = {0.f, 0.f, 0.f, 0.f}, c2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kk = 0; kk < P / 32; ++kk)
-                    c1 = mfma(rowop(Y_l, XP, tb * 16, kk * 32), colop(H_l, NPH, nb * 16, kk * 32), c1);
+                for (int kk = 0; kk < P / 32; ++kk) {
+                    const bf16x8 yo8 = rowop(Y_l, XP, tb * 16, kk * 32);
+                    c1 = mfma(yo8, colop(H_l, NPH, nb * 16, kk * 32), c1);
+                    c1 = mfma(yo8, colop(Hr_l, NPH, nb * 16, kk * 32), c1);
+                }
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
                     if (2 * kk > tb) continue;  // every s of the block is after t
@@ -494,7 +511,8 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
         // (4) the carry: G^T [n][p] = exp(cum_last) G^T + C^T diag(exp(cum)) dY
         if (owns) {
             const float el = elast_l;
-            bf16x8 ye[2];
+            // dy exp(cum) as a bf16 pair, so that the carry keeps about 16 bits
+            bf16x8 ye[2], yr[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const bf16x8 yv = colop(Y_l, XP, pw, kk * 32);
@@ -502,14 +520,22 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
                 const float4 e1 = *reinterpret_cast<const float4*>(&ecum_l[kk * 32 + 8 * g4 + 4]);
                 const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
 #pragma unroll
-                for (int jj = 0; jj < 8; ++jj) ye[kk][jj] = (__bf16)((float)yv[jj] * ev[jj]);
+                for (int jj = 0; jj < 8; ++jj) {
+                    const float v = (float)yv[jj] * ev[jj];
+                    ye[kk][jj] = (__bf16)v;
+                    yr[kk][jj] = (__bf16)(v - (float)ye[kk][jj]);
+                }
             }
 #pragma unroll
             for (int j = 0; j < NH; ++j) {
                 const int nb = NH * sh + j;
                 f32x4 a = gacc[j] * el;
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) a = mfma(colop(C_l, NP, nb * 16, kk * 32), ye[kk], a);
+                for (int kk = 0; kk < 2; ++kk) {
+                    const bf16x8 co = colop(C_l, NP, nb * 16, kk * 32);
+                    a = mfma(co, ye[kk], a);
+                    a = mfma(co, yr[kk], a);
+                }
                 gacc[j] = a;
             }
         }
@@ -614,11 +640,11 @@ bool ssd_bwd_supported(const Shape& sh) {
 
 size_t ssd_bwd_workspace_bytes(const Shape& sh) {
     const int64_t n_chunks = (sh.L + kQ - 1) / kQ;
-    return align_up((size_t)(sh.S * sh.H * n_chunks * sh.P * sh.N) * 2, 256) +
+    return align_up((size_t)(sh.S * sh.H * n_chunks * sh.P * sh.N) * 4, 256) +
            align_up((size_t)(sh.S * sh.H * sh.P * sh.N) * 4, 256) + 2 * align_up((size_t)(sh.S * sh.H) * 4, 256);
 }
 
-int launch_ssd_ckpt(const BwdArgs& a, bf16_t* ckpt, hipStream_t stream);
+int launch_ssd_ckpt(const BwdArgs& a, float* ckpt, hipStream_t stream);
 
 int launch_ssd_bwd(const BwdArgs& a, hipStream_t stream) {
     const Shape& sh = a.sh;
@@ -628,8 +654,8 @@ int launch_ssd_bwd(const BwdArgs& a, hipStream_t stream) {
         return SSM_ERR_UNSUPPORTED;
     const int64_t n_chunks = (sh.L + kQ - 1) / kQ;
     char* w = a.ws;
-    bf16_t* ckpt = reinterpret_cast<bf16_t*>(w);
-    w += align_up((size_t)(sh.S * sh.H * n_chunks * sh.P * sh.N) * 2, 256);
+    float* ckpt = reinterpret_cast<float*>(w);
+    w += align_up((size_t)(sh.S * sh.H * n_chunks * sh.P * sh.N) * 4, 256);
     float* ds_part = reinterpret_cast<float*>(w);
     w += align_up((size_t)(sh.S * sh.H * sh.P * sh.N) * 4, 256);
     float* dA_part = reinterpret_cast<float*>(w);

@@ -70,7 +70,7 @@ struct SsdKP {
     const int32_t* ids;
     bf16_t* y;
     float* state_out;
-    bf16_t* ckpt;  // CKPT: [S][H][n_chunks][P][N], the state entering each chunk
+    float* ckpt;   // CKPT: [S][H][n_chunks][P][N], the state entering each chunk
     uint32_t* err;
     int L, H, G, R, hpg;
     int has_D;
@@ -118,9 +118,8 @@ __device__ __forceinline__ bf16x4 ldtr(const bf16_t* p) {
     return __builtin_bit_cast(bf16x4, v);
 }
 
-// CKPT: the backward's recompute: no y, no final state; the state entering
-// every chunk is stored (as the bf16 the forward's carried-state product
-// reads) for the reverse pass.
+// CKPT: the backward's recompute: no y, no final state; the fp32 state
+// entering every chunk is stored for the reverse pass.
 template <int P, int N, bool SOFTPLUS, bool CKPT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void ssd_fwd(SsdKP p) {
     static_assert((P == 32 || P == 64) && (N == 64 || N == 128), "tile shapes");
@@ -258,8 +257,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                 const uint32_t hi = uint32_t(bf16_rne(v[2])) | (uint32_t(bf16_rne(v[3])) << 16);
                 *reinterpret_cast<u32x2*>(&H_l[(pw + l16) * NPH + (NH * sh + j) * 16 + 4 * g4]) = u32x2{lo, hi};
                 if constexpr (CKPT)
-                    *reinterpret_cast<u32x2*>(p.ckpt + (((((int64_t)i * p.H + hh) * n_chunks + t0 / kQ) * P + pw + l16) * N +
-                                                        (NH * sh + j) * 16 + 4 * g4)) = u32x2{lo, hi};
+                    *reinterpret_cast<f32x4*>(p.ckpt + (((((int64_t)i * p.H + hh) * n_chunks + t0 / kQ) * P + pw + l16) * N +
+                                                        (NH * sh + j) * 16 + 4 * g4)) = v;
             }
         }
     };
@@ -453,9 +452,9 @@ int launch_ssd_fwd(const FwdArgs& a, hipStream_t stream) {
     return SSM_ERR_UNSUPPORTED;
 }
 
-// The backward's recompute: chunk-entry states of every (sequence, head) as
-// bf16 into ckpt [S][H][n_chunks][P][N].
-int launch_ssd_ckpt(const BwdArgs& a, bf16_t* ckpt, hipStream_t stream) {
+// The backward's recompute: chunk-entry states of every (sequence, head)
+// into ckpt [S][H][n_chunks][P][N].
+int launch_ssd_ckpt(const BwdArgs& a, float* ckpt, hipStream_t stream) {
     const Shape& sh = a.sh;
     SsdKP kp;
     kp.s = a.s; kp.x = static_cast<const bf16_t*>(a.x); kp.dt = static_cast<const bf16_t*>(a.dt);
