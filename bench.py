@@ -114,12 +114,12 @@ COPY_FACTOR = {"fetch": 1.99993, "write": 1.00000}
 MEASURED_TRAFFIC = {
     "C1": {"sha256": "b54488bd1c4354444b1903423f99b869e566fd61179612657f748cdaf2dc0c37", "fetch_kib": 34152.3, "write_kib": 33024.0},
     "C2": {"sha256": "b54488bd1c4354444b1903423f99b869e566fd61179612657f748cdaf2dc0c37", "fetch_kib": 339353.1, "write_kib": 330240.0},
-    "C3": {"sha256": "b0591ad1672f9c548339e541594127fcaa68e16a1916aa71e249cdc017a61ddb", "fetch_kib": 144438.3, "write_kib": 174081.6},
+    "C3": {"sha256": "73711f6479978241a44d920238fa836895f3e59fc28c6b86144d4a2e39e186cc", "fetch_kib": 144487.6, "write_kib": 174082.0},
     "C4": {"sha256": "2a19fd3700bb14b898a8f31d961c12501b1bdb0583c23b31fa03aca4474e50b7", "fetch_kib": 1665248.8, "write_kib": 2961396.0},
     "C5": {"sha256": "84a811e3d84aca510d566615083c4f313b721cec5e2ceaf515444d565e2f3171", "fetch_kib": 512933.0, "write_kib": 704396.3},
     "C6": {"sha256": "5060521dce2d813674341dfe930be0831fe8c04182c13b450093e534a8b93fb8", "fetch_kib": 52854.2, "write_kib": 100233.3},
     "C7": {"sha256": "5060521dce2d813674341dfe930be0831fe8c04182c13b450093e534a8b93fb8", "fetch_kib": 83418.7, "write_kib": 164482.0},
-    "C8": {"sha256": "6b78613da6a0a906f47e65dc905cae4c6386789adee41ad9e76b2b4caefc5d01", "fetch_kib": 762295.7, "write_kib": 2645552.8},
+    "C8": {"sha256": "239e0d39855c5cd174deaef0b68e44799016a86043553d49c61ea37eb38162f0", "fetch_kib": 682656.1, "write_kib": 2370216.4},
 }
 KERNEL_SOURCES = {
     "C0": ("scan_fwd.hip", "scan_fwd_ts.hip", "scan_fwd_quad.hip", "device_common.h"),

@@ -314,7 +314,6 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
         __syncthreads();  // every wave is done with the later chunk's tiles and partial sums
         store_chunk(t0);
         __syncthreads();
-        load_chunk(ch - 1);
 
         // (1) the causal 16x16 tiles of S^T = B C^T and R^T = X dY^T: M, Lm and
         // the sums of Z.  Tile k (row by row: (tb,sb) = (0,0),(1,0),(1,1),...)
@@ -446,6 +445,13 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
             float yo[4] = {0.f, 0.f, 0.f, 0.f}, uu[4] = {0.f, 0.f, 0.f, 0.f};
             float* dCg = p.d_C + ((int64_t)i * L * p.G + grp) * N;
             float* dBg = p.d_B + ((int64_t)i * L * p.G + grp) * N;
+            // the lane's four tokens t = 16 tb + 4 g4 + rr (and s, the same block)
+            const float4 et4 = *reinterpret_cast<const float4*>(&ecum_l[tb * 16 + 4 * g4]);
+            const float4 ws4 = *reinterpret_cast<const float4*>(&w_l[tb * 16 + 4 * g4]);
+            const float et[4] = {et4.x, et4.y, et4.z, et4.w}, wsv[4] = {ws4.x, ws4.y, ws4.z, ws4.w};
+            // C[t][n] and B[s][n] of the lane's four rows at column n: one
+            // transposing read each (lanes 4k + q address row 4 g4 + k)
+            const int trow = (tb * 16 + 4 * g4 + (l16 >> 2)) * NP + 4 * (l16 & 3);
 #pragma unroll
             for (int j = 0; j < NPW; ++j) {
                 const int nb = nb0 + j, n = nb * 16 + l16;
@@ -461,12 +467,13 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
                     if (2 * kk > tb) continue;  // every s of the block is after t
                     c2 = mfma(rowop(Lm_l, MP, tb * 16, kk * 32), colop(B_l, NP, nb * 16, kk * 32), c2);
                 }
+                const bf16x4 cn = ldtr(&C_l[trow + nb * 16]);
                 // lane: t = 16 tb + 4 g4 + rr, n
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
                     const int t = tb * 16 + 4 * g4 + rr;
-                    const float off = ecum_l[t] * c1[rr];
-                    yo[rr] = fmaf(off, (float)*reinterpret_cast<const __bf16*>(&C_l[t * NP + n]), yo[rr]);
+                    const float off = et[rr] * c1[rr];
+                    yo[rr] = fmaf(off, (float)cn[rr], yo[rr]);
                     if (t0 + t < L) unsafeAtomicAdd(dCg + (int64_t)(t0 + t) * p.G * N + n, off + c2[rr]);
                 }
                 f32x4 b1 = {0.f, 0.f, 0.f, 0.f}, b2 = {0.f, 0.f, 0.f, 0.f};
@@ -482,12 +489,13 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
                     b2 = mfma(xo, colop(G_l, NPH, nb * 16, kk * 32), b2);
                     b2 = mfma(xo, colop(Gr_l, NPH, nb * 16, kk * 32), b2);
                 }
+                const bf16x4 bn = ldtr(&B_l[trow + nb * 16]);
                 // lane: s = 16 sb + 4 g4 + rr, n
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
                     const int s = sb * 16 + 4 * g4 + rr;
-                    uu[rr] = fmaf(b2[rr], (float)*reinterpret_cast<const __bf16*>(&B_l[s * NP + n]), uu[rr]);
-                    if (t0 + s < L) unsafeAtomicAdd(dBg + (int64_t)(t0 + s) * p.G * N + n, fmaf(w_l[s], b2[rr], b1[rr]));
+                    uu[rr] = fmaf(b2[rr], (float)bn[rr], uu[rr]);
+                    if (t0 + s < L) unsafeAtomicAdd(dBg + (int64_t)(t0 + s) * p.G * N + n, fmaf(wsv[rr], b2[rr], b1[rr]));
                 }
             }
             // sums over this wave's n (the 16 lanes of a group)
@@ -507,6 +515,10 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
                 *reinterpret_cast<float4*>(&u_l[half][tb * 16 + 4 * g4]) = make_float4(uu[0], uu[1], uu[2], uu[3]);
             }
         }
+
+        // the earlier chunk's loads, issued only here: held from the staging
+        // barrier on, their registers spilled through the products above
+        load_chunk(ch - 1);
 
         // (4) the carry: G^T [n][p] = exp(cum_last) G^T + C^T diag(exp(cum)) dY
         if (owns) {
