@@ -54,6 +54,9 @@ WORKLOADS = {
           "d_state 128, bf16 x/dt/B/C/z/y, fp32 states updated in place by permuted ids",
     "C8": "Mamba-2 scan reverse-time backward of the 4x4096, 80 heads x 64, d_state 128 bf16 scan, "
           "fp32 grads",
+    "C9": "Mamba-1 fused conv+SiLU+scan forward of 8 packed sequences of mixed lengths (32768 "
+          "tokens) at the 5120-channel layer, d_state 16, d_conv 4, with dt bias + softplus and the "
+          "SiLU(z) output gate, bf16 x/dt/B/C/z/y, fp32 state/A/D",
 }
 
 
@@ -125,6 +128,7 @@ KERNEL_SOURCES = {
     "C0": ("scan_fwd.hip", "scan_fwd_ts.hip", "scan_fwd_quad.hip", "device_common.h"),
     "C1": ("scan_fwd.hip", "scan_fwd_ts.hip", "scan_fwd_quad.hip", "device_common.h"),
     "C2": ("scan_fwd.hip", "scan_fwd_ts.hip", "scan_fwd_quad.hip", "device_common.h"),
+    "C9": ("scan_fwd.hip", "scan_fwd_quad.hip", "device_common.h"),
     "C3": ("scan_fwd.hip", "ssd_fwd.hip", "device_common.h"),
     "C4": ("scan_bwd.hip", "scan_fwd_quad.hip", "device_common.h"),
     "C5": ("conv_bwd.hip", "device_common.h"),
@@ -552,6 +556,165 @@ def main_decode(args):
     print(json.dumps(line), flush=True)
 
 
+def varlen_bytes(p) -> int:
+    """Each input read once, each output written once, over the packed token axis."""
+    io = 2 if p.io == "bf16" else 4
+    T, S, H, N, K = p.total_tokens, p.n_seqs, p.n_head, p.d_state, p.d_conv
+    x = y = z = T * H * io
+    dt = T * H * io
+    bc = 2 * T * N * io
+    params = (H * N + H + H * K + H) * 4           # A, D, conv_w, dt_bias
+    states = 2 * S * H * N * 4 + 2 * S * H * (K - 1) * 4   # state and conv state, in and out
+    return x + y + z + dt + bc + params + states + S * 4 + (S + 1) * 4
+
+
+def valu_slots_ext(p) -> float:
+    """valu_slots_per_channel_token plus the extras per channel-token: the
+    bias (add), softplus (exp, log: 2 transcendentals and 3 slots) and the
+    gate SiLU(z) * y (mul, exp, add, rcp, mul)."""
+    return valu_slots_per_channel_token(p) + 1 + (3 + 2 * TRANS_COST) + (3 + 2 * TRANS_COST)
+
+
+def _oracle_ext_heads(p, heads):
+    import oracle
+    v = lambda n: None if p.value(n) is None else p.value(n).astype(np.float64)
+    pk = lambda n: v(n)[0][:, heads]
+    return oracle.scan_fwd_ext(v("s")[:, heads], pk("x"), pk("dt"), v("A")[heads], v("B")[0], v("C")[0],
+                               v("D")[heads], p.ids, cu_seqlens=p.cu_seqlens,
+                               dt_bias=v("dt_bias")[heads], z=pk("z"), conv_w=v("conv_w")[heads],
+                               conv_state=v("conv_state")[:, heads], dt_softplus=p.dt_softplus,
+                               n_threads=oracle.default_threads())
+
+
+def main_varlen(args):
+    """C9: the fused forward over packed sequences of mixed lengths with the
+    dt bias and the z gate (selective_scan_fwd_ext)."""
+    import torch
+    import oracle
+    import ssm_inputs
+    from selective_scan_recurrence_amd import ops
+    import selective_scan_recurrence_amd as ssm
+
+    ssm.load()
+    dev = torch.device("cuda:0")
+    name = args.config
+    p = ssm_inputs.varlen_config(name)
+    desc = ops.make_desc(n_seqs=p.n_seqs, n_tokens=p.n_tokens, n_head=p.n_head, d_state=p.d_state,
+                         n_state_rows=p.n_state_rows, d_conv=p.d_conv,
+                         chunk=0 if args.chunk is None else args.chunk, io=p.io, has_D=p.has_D,
+                         dt_softplus=p.dt_softplus)
+    step_bytes = varlen_bytes(p)
+    copies = max(2, math.ceil(3 * MALL_BYTES / step_bytes))
+    sets = []
+    for _ in range(copies):
+        t = {k: _dev(s, dev) for k, s in p.t.items()}
+        t["ids"] = torch.from_numpy(p.ids).to(dev)
+        t["cu"] = torch.from_numpy(p.cu_seqlens).to(dev)
+        t["ws"] = ops.workspace(desc, False, dev)
+        t["out"] = torch.empty(ssm.ssm_scan_ext_out_bytes(desc, ssm.make_ext(cu_seqlens=1, total_tokens=p.total_tokens))[0],
+                               dtype=torch.uint8, device=dev)
+        t["cso"] = torch.empty(p.n_seqs, p.n_head, p.d_conv - 1, dtype=torch.float32, device=dev)
+        sets.append(t)
+
+    def step(t):
+        return ops.scan_fwd_ext(desc, t["s"], t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["ids"],
+                                dt_bias=t["dt_bias"], z=t["z"], cu_seqlens=t["cu"],
+                                total_tokens=p.total_tokens, conv_w=t["conv_w"],
+                                conv_state=t["conv_state"], want_conv_state=True, ws=t["ws"], out=t["out"])
+
+    res = step(sets[0])
+    torch.cuda.synchronize()
+    # parity gate: every token of sampled channels against the oracle
+    rng = np.random.default_rng(0xB9)
+    heads = np.unique(np.concatenate([[0, p.n_head - 1], rng.choice(p.n_head, 8, replace=False)]))
+    y_o, st_o, cs_o = _oracle_ext_heads(p, heads)
+    hs = torch.as_tensor(heads, device=dev)
+    rtol, atol = 2e-2, 1e-3
+    # y's absolute floor scales with |SiLU(z)|: the gate multiplies an fp32 y
+    # that carries the ungated error
+    zg = p.value("z")[0][:, heads].astype(np.float64)
+    gate = np.maximum(1.0, np.abs(zg / (1.0 + np.exp(-zg))))
+    checked = 0
+    for got, want, what, sc in ((res.y.index_select(1, hs), y_o, "y", gate),
+                                (res.state.index_select(1, hs), st_o, "state", 1.0),
+                                (res.conv_state.index_select(1, hs), cs_o, "conv_state", 1.0)):
+        g = got.double().cpu().numpy()
+        bad = ~(np.abs(g - want) <= atol * sc + rtol * np.abs(want))
+        if bad.any():
+            raise SystemExit(f"parity gate failed on {name} {what}: {int(bad.sum())} elements outside "
+                             f"rtol={rtol} atol={atol}")
+        checked += want.size
+    if ssm.ssm_get_device_error(sets[0]["ws"]):
+        raise SystemExit(f"{name}: device error word set")
+    parity = {"checked_elements": int(checked), "rtol": rtol, "atol": atol,
+              "atol_y": "1e-3 x max(1, |SiLU(z)|)"}
+
+    for k in range(args.warmup):
+        step(sets[k % copies])
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        starts[k].record()
+        step(sets[k % copies])
+        ends[k].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    ms_per_step = starts[0].elapsed_time(ends[-1]) / args.steps
+    avg_s = float(launch_ms.mean()) * 1e-3
+    gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    ch_tok = p.total_tokens * p.n_head
+    slots = valu_slots_ext(p) * ch_tok
+    floors = {"hbm": step_bytes / (HBM_PEAK_GBS * 1e9), "alu": slots / (VALU_PEAK_T * 1e12)}
+    if floors["alu"] >= floors["hbm"]:
+        ach = slots / avg_s / 1e12
+        roof = {"bound": "alu", "achieved": round(ach, 3), "peak": VALU_PEAK_T, "unit": "T VALU-slots/s",
+                "frac": round(ach / VALU_PEAK_T, 4)}
+    else:
+        ach = step_bytes / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    roof.update({"traffic": measured_traffic(name),
+                 "traffic_unit": "HBM bytes per call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                 "kernel": "selective_scan_fwd_ext (all launches of one call)",
+                 "avg_launch_us": round(avg_s * 1e6, 3),
+                 "floors_us": {k: round(v * 1e6, 2) for k, v in floors.items()},
+                 "algorithmic_bytes": step_bytes, "valu_slots": int(slots)})
+    lengths = np.diff(p.cu_seqlens).tolist()
+    line = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; distributions of the workload definition)",
+        "config": {"workload": f"{name}: {WORKLOADS[name]}", "n_seqs": p.n_seqs,
+                   "total_tokens": p.total_tokens, "lengths": lengths, "n_head": p.n_head,
+                   "d_state": p.d_state, "d_conv": p.d_conv, "chunk": desc.chunk,
+                   "input_copies": copies},
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "channel_tokens_per_s": round(ch_tok / (ms_per_step * 1e-3), 1),
+        "roofline": roof, "parity": parity, "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        n = 1024
+        sub = np.arange(n)
+        reps, sec = 0, 0.0
+        while reps < 50 and (reps == 0 or sec < 10.0):
+            t1 = time.perf_counter()
+            _oracle_ext_heads(p, sub)
+            sec += time.perf_counter() - t1
+            reps += 1
+        per = sec / reps
+        line["cpu_baseline"] = {
+            "value": round(step_bytes * n / p.n_head / per / 1e9, 4), "unit": "GB/s",
+            "cores": oracle.threads_used(n, oracle.default_threads()), "kind": "oracle",
+            "sample": f"first {n} of {p.n_head} channels, all sequences and tokens; {reps} repetitions",
+            "seconds": round(sec, 3), "channel_tokens_per_s": round(p.total_tokens * n / per, 1),
+            "cpu": platform.processor() or platform.machine(), "nproc": os.cpu_count()}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -577,6 +740,9 @@ def main():
         return
     if args.config in ("C6", "C7"):
         main_decode(args)
+        return
+    if args.config == "C9":
+        main_varlen(args)
         return
     import torch
     import ssm_inputs

@@ -77,7 +77,10 @@ enum {
 };
 
 /* Device-side error bits, read back with ssm_get_device_error(). */
-enum { SSM_DEVERR_IDS = 1u /* an ids[i] was outside [0, n_state_rows) */ };
+enum {
+    SSM_DEVERR_IDS = 1u,     /* an ids[i] was outside [0, n_state_rows) */
+    SSM_DEVERR_SEQLENS = 2u  /* a cu_seqlens span was invalid (selective_scan_fwd_ext) */
+};
 
 typedef struct ssm_scan_desc {
     int64_t n_seqs;       /* sequences (>= 0)                                  */
@@ -184,6 +187,55 @@ int selective_scan_fwd(const ssm_scan_desc *desc, const float *s, const void *x,
                        const float *D, const int32_t *ids, const float *conv_w,
                        const float *conv_state, void *out, float *conv_state_out,
                        void *workspace, size_t workspace_bytes, ssm_stream_t stream);
+
+/* Extras of selective_scan_fwd_ext.  Every pointer may be NULL (feature off).
+ *  - dt_bias [n_head] f32: added to dt before softplus, as the step of
+ *    "mambazip mamba1/model.rs" (forward_impl) does: dt = softplus(dt_raw +
+ *    dt_bias) with SSM_DT_SOFTPLUS, dt_raw + dt_bias without it.
+ *  - z, shaped like x in io dtype: the output gate of that step,
+ *    y = (sum_n C h + D u) * SiLU(z), applied before y is rounded to io.
+ *  - cu_seqlens [n_seqs + 1] int32, DEVICE: variable-length sequences packed
+ *    along one token axis.  Sequence i is tokens cu_seqlens[i] ..
+ *    cu_seqlens[i+1]-1 and starts from state row ids[i] (and conv_state row
+ *    ids[i]), as the flattened sequences of the ggmlR page's RWKV shapes
+ *    start a fresh state at each sequence; lengths may differ and may be 0.
+ *    x, z, y are then [total_tokens][n_head][head_dim], dt [total_tokens]
+ *    [n_head], B and C [total_tokens][n_group][d_state], and desc->n_tokens
+ *    is an upper bound on every length (it sizes chunking and workspace).
+ *    A span with cu_seqlens[i] < 0, cu_seqlens[i+1] < cu_seqlens[i],
+ *    cu_seqlens[i+1] > total_tokens or a length above desc->n_tokens is not
+ *    scanned: its final state is written as NaN, its y rows are left as they
+ *    were, and SSM_DEVERR_SEQLENS is set.
+ *  - total_tokens: with cu_seqlens, the length of the packed token axis
+ *    (>= 0); without, it must be 0 and the layout is that of
+ *    selective_scan_fwd. */
+typedef struct ssm_scan_ext {
+    const float *dt_bias;
+    const void *z;
+    const int32_t *cu_seqlens;
+    int64_t total_tokens;
+} ssm_scan_ext;
+
+/* Size of the packed result of selective_scan_fwd_ext: y (total_tokens x
+ * n_head x head_dim io elements with cu_seqlens, else as ssm_scan_out_bytes)
+ * followed by the n_seqs final states in f32.  *state_offset (may be NULL)
+ * receives the state block's byte offset.  Returns 0 if desc or ext is
+ * invalid (ext may be NULL: no extras). */
+size_t ssm_scan_ext_out_bytes(const ssm_scan_desc *desc, const ssm_scan_ext *ext,
+                              size_t *state_offset);
+
+/* selective_scan_fwd_ext: selective_scan_fwd with the extras above (ext may
+ * be NULL, which equals selective_scan_fwd).  Same arguments, checks and
+ * workspace (ssm_scan_workspace_bytes(desc, 0)); z must be aligned like x.
+ * Kernels: every shape selective_scan_fwd runs, with the extras fused into
+ * the scan (dt_bias where dt is read, the gate where y is written, the
+ * spans in each workgroup's token range). */
+int selective_scan_fwd_ext(const ssm_scan_desc *desc, const ssm_scan_ext *ext, const float *s,
+                           const void *x, const void *dt, const float *A, const void *B,
+                           const void *C, const float *D, const int32_t *ids,
+                           const float *conv_w, const float *conv_state, void *out,
+                           float *conv_state_out, void *workspace, size_t workspace_bytes,
+                           ssm_stream_t stream);
 
 /* selective_scan_bwd: reverse-time adjoint of selective_scan_fwd without the
  * fused conv (d_conv must be 0).  dout is packed like the forward result

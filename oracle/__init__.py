@@ -16,7 +16,13 @@ Where the pages leave a step open this oracle takes these readings:
     state is written to row i of the state block (sequence order);
   * dt is used as given; ``dt_softplus`` applies softplus with the
     threshold-20 form of "mambazip mamba1/model.rs" (softplus);
-  * with the fused conv, D multiplies the scan input u = SiLU(conv(x)).
+  * with the fused conv, D multiplies the scan input u = SiLU(conv(x));
+  * ``scan_fwd_ext``: the dt bias is added to the raw dt before softplus and
+    the gate multiplies the whole y (C.h + D.u) by SiLU(z), as the decode step
+    of "mambazip mamba1/model.rs" (forward_impl) does per token; sequences
+    packed on one token axis (the ggmlR page's RWKV shapes, equal lengths
+    there) may have different lengths, given as offsets cu_seqlens, and each
+    starts from its own state and conv-state row.
 """
 from __future__ import annotations
 
@@ -150,6 +156,56 @@ def scan_fwd(s, x, dt, A, B, C, D, ids, *, conv_w=None, conv_state=None,
                              n_threads or default_threads())
     if rc:
         raise ValueError(f"oracle_scan_fwd failed ({rc})")
+    return y, st, cso
+
+
+def _silu(z):
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def scan_fwd_ext(s, x, dt, A, B, C, D, ids, *, cu_seqlens=None, dt_bias=None, z=None,
+                 conv_w=None, conv_state=None, dt_softplus=False, grp_of_head=None,
+                 n_threads: Optional[int] = None):
+    """``scan_fwd`` with the extras of the per-token step of "mambazip
+    mamba1/model.rs" (forward_impl): dt = dt_raw + dt_bias before softplus, and
+    y = (C.h + D.u) * SiLU(z); and with sequences packed on one token axis (the
+    ggmlR page's RWKV shapes start a fresh state at every sequence), sequence i
+    being tokens cu_seqlens[i] .. cu_seqlens[i+1]-1.
+
+    Without cu_seqlens the shapes are those of ``scan_fwd``.  With it: x and z
+    [T][H][P], dt [T][H], B and C [T][G][N], and y comes back as [T][H][P];
+    each sequence is ``scan_fwd`` over its own tokens from state row ids[i]
+    (conv-state row ids[i]).  dt_bias [H] or None; z like x or None.
+
+    Returns (y, state [S][H][P][N], conv_state_out [S][H][K-1] or None).
+    """
+    dt = _f64(dt)
+    if dt_bias is not None:
+        dt = dt + _f64(dt_bias)  # broadcast over the head axis, the last one of dt
+    kw = dict(conv_w=conv_w, conv_state=conv_state, dt_softplus=dt_softplus,
+              grp_of_head=grp_of_head, n_threads=n_threads)
+    if cu_seqlens is None:
+        y, st, cso = scan_fwd(s, x, dt, A, B, C, D, ids, **kw)
+    else:
+        x, B, C = _f64(x), _f64(B), _f64(C)
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+        n_seqs = len(cu) - 1
+        H, P, N = x.shape[1], x.shape[2], np.asarray(s).shape[3]
+        K = 0 if conv_w is None else np.asarray(conv_w).shape[1]
+        y = np.zeros(x.shape)
+        st = np.zeros((n_seqs, H, P, N))
+        cso = np.zeros((n_seqs, H, max(K - 1, 0))) if K else None
+        for i in range(n_seqs):
+            a, b = int(cu[i]), int(cu[i + 1])
+            yi, si, ci = scan_fwd(s, x[None, a:b], dt[None, a:b], A, B[None, a:b], C[None, a:b], D,
+                                  np.asarray(ids)[i:i + 1], **kw)
+            y[a:b] = yi[0]
+            st[i] = si[0]
+            if K:
+                cso[i] = ci[0]
+    if z is not None:
+        y = y * _silu(_f64(z))
     return y, st, cso
 
 

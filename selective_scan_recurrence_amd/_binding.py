@@ -8,6 +8,7 @@ from __future__ import annotations
 import ctypes
 import os
 import threading
+from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libssm.so")
@@ -16,12 +17,13 @@ SSM_OK, SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_DTYPE, SSM_ERR_UNSUPPORTED, \
     SSM_ERR_WORKSPACE, SSM_ERR_ALIGN, SSM_ERR_HIP = range(8)
 SSM_F32, SSM_BF16 = 0, 1
 SSM_HAS_D, SSM_DT_SOFTPLUS = 1, 2
-SSM_DEVERR_IDS = 1
+SSM_DEVERR_IDS, SSM_DEVERR_SEQLENS = 1, 2
 
 EXPORTS = ("ssm_status_str", "ssm_version", "ssm_scan_out_bytes", "ssm_scan_state_offset_bytes",
            "ssm_scan_dgrad_layout", "ssm_scan_workspace_bytes", "ssm_conv_fwd",
            "ssm_conv_bwd_workspace_bytes", "ssm_conv_bwd", "selective_scan_fwd",
-           "selective_scan_bwd", "selective_state_update", "ssm_get_device_error")
+           "selective_scan_bwd", "selective_state_update", "ssm_get_device_error",
+           "ssm_scan_ext_out_bytes", "selective_scan_fwd_ext")
 
 
 class SsmError(RuntimeError):
@@ -38,6 +40,11 @@ class SsmScanDesc(ctypes.Structure):
                 ("d_conv", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("io_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
                 ("reserved", ctypes.c_uint32)]
+
+
+class SsmScanExt(ctypes.Structure):
+    _fields_ = [("dt_bias", ctypes.c_void_p), ("z", ctypes.c_void_p),
+                ("cu_seqlens", ctypes.c_void_p), ("total_tokens", ctypes.c_int64)]
 
 
 _lib = None
@@ -77,6 +84,11 @@ def load():
         lib.selective_scan_bwd.restype = ctypes.c_int
         lib.selective_state_update.argtypes = [D] + [P] * 15
         lib.selective_state_update.restype = ctypes.c_int
+        E = ctypes.POINTER(SsmScanExt)
+        lib.ssm_scan_ext_out_bytes.argtypes = [D, E, ctypes.POINTER(SZ)]
+        lib.ssm_scan_ext_out_bytes.restype = SZ
+        lib.selective_scan_fwd_ext.argtypes = [D, E] + [P] * 13 + [SZ, P]
+        lib.selective_scan_fwd_ext.restype = ctypes.c_int
         lib.ssm_get_device_error.argtypes = [P, P, ctypes.POINTER(ctypes.c_uint32)]
         lib.ssm_get_device_error.restype = ctypes.c_int
         _lib = lib
@@ -158,6 +170,28 @@ def selective_scan_fwd(desc, s, x, dt, A, B, C, D, ids, conv_w, conv_state, out,
                                    _ptr(conv_state), _ptr(out), _ptr(conv_state_out),
                                    _ptr(workspace), int(workspace_bytes), _stream(stream))
     return _check(rc, "selective_scan_fwd")
+
+
+def make_ext(dt_bias=None, z=None, cu_seqlens=None, total_tokens=0) -> SsmScanExt:
+    return SsmScanExt(_ptr(dt_bias), _ptr(z), _ptr(cu_seqlens), int(total_tokens))
+
+
+def ssm_scan_ext_out_bytes(desc: SsmScanDesc, ext: Optional[SsmScanExt]):
+    """(total bytes, state block offset); (0, 0) if invalid."""
+    off = ctypes.c_size_t(0)
+    n = load().ssm_scan_ext_out_bytes(ctypes.byref(desc), None if ext is None else ctypes.byref(ext),
+                                      ctypes.byref(off))
+    return int(n), int(off.value)
+
+
+def selective_scan_fwd_ext(desc, ext, s, x, dt, A, B, C, D, ids, conv_w, conv_state, out,
+                           conv_state_out, workspace, workspace_bytes, stream=None):
+    rc = load().selective_scan_fwd_ext(ctypes.byref(desc), None if ext is None else ctypes.byref(ext),
+                                       _ptr(s), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                                       _ptr(D), _ptr(ids), _ptr(conv_w), _ptr(conv_state),
+                                       _ptr(out), _ptr(conv_state_out), _ptr(workspace),
+                                       int(workspace_bytes), _stream(stream))
+    return _check(rc, "selective_scan_fwd_ext")
 
 
 def selective_scan_bwd(desc, s, x, dt, A, B, C, D, ids, dout, dgrad, workspace,

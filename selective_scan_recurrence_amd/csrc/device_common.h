@@ -31,9 +31,42 @@ __device__ __forceinline__ float silu(float c) {
     return c * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-c * kLog2e));
 }
 
-// softplus with the threshold-20 branch of "mambazip mamba1/model.rs" (softplus).
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// softplus with the threshold-20 branch of "mambazip mamba1/model.rs"
+// (softplus): v above 20, else log(1 + e^v), on the transcendental unit.
+// With w = e^v (v_exp_f32) and u = 1 + w rounded, log(1 + w) is taken as
+// log(u) * w / (u - 1), which cancels the rounding error of u (Goldberg,
+// "What Every Computer Scientist Should Know About Floating-Point
+// Arithmetic", Theorem 4); when u rounds to 1 the result is w itself.  The
+// error is a few ulp of the result for every v.
 __device__ __forceinline__ float softplus(float v) {
-    return v > 20.0f ? v : log1pf(expf(v));
+    if (v > 20.0f) return v;
+    const float w = __builtin_amdgcn_exp2f(v * kLog2e);
+    const float u = 1.0f + w;
+    return u == 1.0f ? w : __builtin_amdgcn_logf(u) * kLn2 * (w * __builtin_amdgcn_rcpf(u - 1.0f));
+}
+
+// logistic(v) = 1 / (1 + e^-v), the derivative of softplus, with the hardware
+// exponential and reciprocal.
+__device__ __forceinline__ float sigmoid(float v) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v * kLog2e));
+}
+
+// Token range of sequence i: [t0, t0 + len) of the token axis.  Without
+// spans (cu null) every sequence has L tokens at i*L.  With spans, one that
+// is negative, reversed, past T or longer than L is taken as empty and
+// reported through bad.
+struct SeqSpan {
+    int64_t t0;
+    int len;
+    bool bad;
+};
+__device__ __forceinline__ SeqSpan seq_span(const int32_t* cu, int i, int L, int64_t T) {
+    if (!cu) return SeqSpan{(int64_t)i * L, L, false};
+    const int a = cu[i], b = cu[i + 1];
+    const bool bad = a < 0 || b < a || (int64_t)b > T || b - a > L;
+    return SeqSpan{bad ? 0 : (int64_t)a, bad ? 0 : b - a, bad};
 }
 
 // DPP quad permute: lane q of each group of four lanes reads lane P<q>.

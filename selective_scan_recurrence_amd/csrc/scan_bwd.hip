@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void bwd_rev(BwdKP p) {
             if (q == 0 && active && k < nk) {
                 const int64_t idx = seq + (int64_t)(t0 + k) * p.d_inner + c;
                 float ddt = fmaf(uk, S1, S2);
-                if constexpr (SOFTPLUS) ddt *= 1.0f / (1.0f + expf(-draw));
+                if constexpr (SOFTPLUS) ddt *= sigmoid(draw);
                 p.d_x[idx] = bad ? __builtin_nanf("") : fmaf(Dc, dyk, dk * S1);
                 p.d_dt[idx] = bad ? __builtin_nanf("") : ddt;
                 dD_acc = fmaf(dyk, uk, dD_acc);
@@ -486,7 +486,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             S2 = quad_sum(S2);
             if (q == 0) {
                 float ddt = fmaf(uk, S1, S2);
-                if constexpr (SOFTPLUS) ddt *= 1.0f / (1.0f + expf(-draw));
+                if constexpr (SOFTPLUS) ddt *= sigmoid(draw);
                 gx_l[k * kChan + cl] = fmaf(Dc, dyk, dk * S1);
                 gdt_l[k * kChan + cl] = ddt;
                 if (k < nk) dD_acc = fmaf(dyk, uk, dD_acc);

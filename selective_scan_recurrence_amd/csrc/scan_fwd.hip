@@ -9,6 +9,9 @@
 // With the fused conv (head_dim 1), the lane also keeps the last d_conv-1
 // inputs of its channel and forms u = SiLU(sum_j w[j] x[t-K+1+j]) on the fly
 // (tap K-1 on the newest input, as in the ggmlR ssm_conv reference).
+// The extras of the decode step of that model page (dt bias before softplus,
+// y times SiLU(z)) and variable-length spans of a packed token axis are
+// taken here as well.
 #include "device_common.h"
 #include "ssm_internal.h"
 
@@ -30,6 +33,10 @@ struct FwdKP {
     float* state_out;
     float* conv_state_out;
     uint32_t* err;
+    const float* dt_bias;  // [H] or null
+    const void* z;         // like x, or null
+    const int32_t* cu;     // [S+1] spans, or null
+    int64_t T;             // tokens on the packed axis
     int L, H, P, N, G, R, d_inner, heads_per_group;
     int has_D, softplus;
 };
@@ -52,12 +59,16 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_rows(FwdKP p) {
     const int n0 = j * kNPL;
 
     int r = p.ids[i];
-    const bool bad = (r < 0) | (r >= p.R);
+    const SeqSpan sp = seq_span(p.cu, i, p.L, p.T);
+    const bool bad_id = (r < 0) | (r >= p.R);
+    const bool bad = bad_id | sp.bad;
     if (bad) {
         r = 0;
-        if (threadIdx.x == 0) atomicOr(p.err, (uint32_t)SSM_DEVERR_IDS);
+        if (threadIdx.x == 0 && blockIdx.x == 0)
+            atomicOr(p.err, (bad_id ? (uint32_t)SSM_DEVERR_IDS : 0u) | (sp.bad ? (uint32_t)SSM_DEVERR_SEQLENS : 0u));
     }
     const float nan = __builtin_nanf("");
+    const float dtb = p.dt_bias ? p.dt_bias[h] : 0.0f;
 
     float hs[kNPL], a2[kNPL];
     const float* srow = p.s + (((int64_t)r * p.H + h) * p.P + pp) * p.N;
@@ -80,16 +91,17 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_rows(FwdKP p) {
                          : (p.conv_state ? p.conv_state[((int64_t)r * p.H + h) * (K - 1) + q] : 0.0f);
     }
 
-    const T* xs = static_cast<const T*>(p.x) + (int64_t)i * p.L * p.d_inner + c;
-    const T* dts = static_cast<const T*>(p.dt) + (int64_t)i * p.L * p.H + h;
-    const T* Bs = static_cast<const T*>(p.B) + ((int64_t)i * p.L * p.G + g) * p.N + n0;
-    const T* Cs = static_cast<const T*>(p.C) + ((int64_t)i * p.L * p.G + g) * p.N + n0;
-    T* ys = static_cast<T*>(p.y) + (int64_t)i * p.L * p.d_inner + c;
+    const T* xs = static_cast<const T*>(p.x) + sp.t0 * p.d_inner + c;
+    const T* dts = static_cast<const T*>(p.dt) + sp.t0 * p.H + h;
+    const T* Bs = static_cast<const T*>(p.B) + (sp.t0 * p.G + g) * p.N + n0;
+    const T* Cs = static_cast<const T*>(p.C) + (sp.t0 * p.G + g) * p.N + n0;
+    T* ys = static_cast<T*>(p.y) + sp.t0 * p.d_inner + c;
+    const T* zs = p.z ? static_cast<const T*>(p.z) + sp.t0 * p.d_inner + c : nullptr;
     const int bc_stride = p.G * p.N;
 
-    for (int t = 0; t < p.L; ++t) {
+    for (int t = 0; t < sp.len; ++t) {
         const float xv = to_f32(xs[(int64_t)t * p.d_inner]);
-        float dtv = to_f32(dts[(int64_t)t * p.H]);
+        float dtv = to_f32(dts[(int64_t)t * p.H]) + dtb;
         if (p.softplus) dtv = softplus(dtv);
         float u;
         if constexpr (K > 0) {
@@ -118,7 +130,11 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_rows(FwdKP p) {
         }
 #pragma unroll
         for (int m = LPR / 2; m >= 1; m /= 2) yv += __shfl_xor(yv, m, LPR);
-        if (active && j == 0) store_io(ys + (int64_t)t * p.d_inner, fmaf(Dh, u, yv));
+        if (active && j == 0) {
+            float yo = fmaf(Dh, u, yv);
+            if (zs) yo *= silu(to_f32(zs[(int64_t)t * p.d_inner]));
+            store_io(ys + (int64_t)t * p.d_inner, yo);
+        }
     }
 
     if (active) {
@@ -186,7 +202,8 @@ int launch_scan_fwd(const FwdArgs& a, hipStream_t stream) {
     const Shape& sh = a.sh;
     if (sh.S == 0 || sh.H * sh.P == 0) return SSM_OK;
     // few (sequence, channel) rows and no explicit chunk: split time inside a workgroup
-    if (sh.chunk == 0 && sh.S * ((sh.d_inner() + 63) / 64) * 4 < 2048 && ts_supported(sh, a))
+    if (!a.has_ext() && sh.chunk == 0 && sh.S * ((sh.d_inner() + 63) / 64) * 4 < 2048 &&
+        ts_supported(sh, a))
         return launch_ts_fwd(a, stream);
     if (quad_supported(sh)) return launch_quad_fwd(a, stream);
     if (ssd_supported(sh, a)) return launch_ssd_fwd(a, stream);
@@ -194,6 +211,7 @@ int launch_scan_fwd(const FwdArgs& a, hipStream_t stream) {
     kp.s = a.s; kp.x = a.x; kp.dt = a.dt; kp.A = a.A; kp.B = a.B; kp.C = a.C; kp.D = a.D;
     kp.ids = a.ids; kp.conv_w = a.conv_w; kp.conv_state = a.conv_state;
     kp.y = a.y; kp.state_out = a.state_out; kp.conv_state_out = a.conv_state_out; kp.err = a.err;
+    kp.dt_bias = a.dt_bias; kp.z = a.z; kp.cu = a.cu; kp.T = a.T;
     kp.L = (int)sh.L; kp.H = (int)sh.H; kp.P = (int)sh.P; kp.N = (int)sh.N; kp.G = (int)sh.G;
     kp.R = (int)sh.R; kp.d_inner = (int)sh.d_inner(); kp.heads_per_group = (int)(sh.H / sh.G);
     kp.has_D = (sh.flags & SSM_HAS_D) ? 1 : 0;

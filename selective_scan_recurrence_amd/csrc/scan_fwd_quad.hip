@@ -24,6 +24,13 @@
 // (a, b) o (a', b') = (a a', a' b + b') ("kizzasi-model backprop_ssm.rs",
 // associative scan); kernel 3 re-scans every chunk from its carried-in state
 // and writes y and the final state.
+//
+// Extras (selective_scan_fwd_ext).  The dt bias is added where dt is read,
+// before softplus; the gate y * SiLU(z) is applied where y is written (in the
+// tiled variant on the 16-byte rows that leave LDS, with z read along the
+// same rows).  With spans on a packed token axis every workgroup takes its
+// sequence's first token and length; a chunk past the end of its sequence
+// is empty, which the carry treats as the identity.
 #include "device_common.h"
 #include "ssm_internal.h"
 
@@ -53,6 +60,10 @@ struct QuadKP {
     float* agg;      // [n_chunks-1][S][d_inner][16] chunk end states (kernel 1)
     float* dtsum;    // [n_chunks-1][S][d_inner]     chunk dt sums    (kernel 1)
     float* hin;      // [n_chunks][S][d_inner][16]   carried-in states (kernel 2)
+    const float* dt_bias;  // [d_inner] or null
+    const void* z;         // like x, or null
+    const int32_t* cu;     // [S+1] spans, or null
+    int64_t T;             // tokens on the packed axis
     int L, d_inner, N, R, S;
     int chunk_len;   // multiple of 4
     int n_chunks;
@@ -67,20 +78,22 @@ __device__ __forceinline__ float ld(const T* p) { return to_f32(*p); }
 // only (kernel 1); MODE 1: y, and the final state if this is the last chunk;
 // MODE 2: the state entering every kCkpt-token block, for the backward pass.
 template <typename T, int K, int MODE>
-__device__ __forceinline__ void quad_chunk(const QuadKP& p, int i, int c_raw, int q,
+__device__ __forceinline__ void quad_chunk(const QuadKP& p, int i, int64_t tok0, int c_raw, int q,
                                            int t_begin, int t_end, float (&h)[4],
                                            const float (&a2)[4], float& dt_acc, bool active,
                                            bool bad) {
     __shared__ __attribute__((aligned(16))) float B_l[2][kTile][16];
     __shared__ __attribute__((aligned(16))) float C_l[2][kTile][16];
     const int c = active ? c_raw : p.d_inner - 1;
-    const int64_t seq_x = (int64_t)i * p.L * p.d_inner;
+    const int64_t seq_x = tok0 * p.d_inner;
     const T* xs = static_cast<const T*>(p.x) + seq_x + c;
     const T* dts = static_cast<const T*>(p.dt) + seq_x + c;
     T* ys = static_cast<T*>(p.y) + seq_x + c;
-    const T* Bg = static_cast<const T*>(p.B) + (int64_t)i * p.L * p.N;
-    const T* Cg = static_cast<const T*>(p.C) + (int64_t)i * p.L * p.N;
+    const T* zs = p.z ? static_cast<const T*>(p.z) + seq_x + c : nullptr;
+    const T* Bg = static_cast<const T*>(p.B) + tok0 * p.N;
+    const T* Cg = static_cast<const T*>(p.C) + tok0 * p.N;
     const float Dc = p.has_D ? p.D[c] : 0.0f;
+    const float dtb = p.dt_bias ? p.dt_bias[c] : 0.0f;
 
     float w[4] = {0.f, 0.f, 0.f, 0.f};
     float xp = 0.0f;  // the owner's input one group back (token t_begin - 4 + q)
@@ -141,6 +154,7 @@ __device__ __forceinline__ void quad_chunk(const QuadKP& p, int i, int c_raw, in
             x_nx = ld(xs + (int64_t)t_next * p.d_inner);
             dt_nx = ld(dts + (int64_t)t_next * p.d_inner);
         }
+        dtv += dtb;
         if (p.softplus) dtv = softplus(dtv);
         float u;
         if constexpr (K > 0) {
@@ -196,7 +210,11 @@ __device__ __forceinline__ void quad_chunk(const QuadKP& p, int i, int c_raw, in
             const bool hi1 = (q & 1) != 0;
             const float keep = hi1 ? r1 : r0, send = hi1 ? r0 : r1;
             const float yv = keep + quad_xor1(send);
-            if (active && own_ok) store_io(ys + (int64_t)(t0 + q) * p.d_inner, fmaf(Dc, u, yv));
+            if (active && own_ok) {
+                float yo = fmaf(Dc, u, yv);
+                if (zs) yo *= silu(ld(zs + (int64_t)(t0 + q) * p.d_inner));
+                store_io(ys + (int64_t)(t0 + q) * p.d_inner, yo);
+            }
         }
         if (tt0 == kTile - 4) __syncthreads();  // next tile staged; this one fully read
     }
@@ -217,8 +235,8 @@ struct TileCfg<bf16_t> { static constexpr int TT = 64; };
 template <>
 struct TileCfg<float> { static constexpr int TT = 32; };
 
-template <typename T, int K, int MODE, bool SOFTPLUS>
-__device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int cb, int q, int cl,
+template <typename T, int K, int MODE, bool SOFTPLUS, bool GATE = false>
+__device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int64_t tok0, int cb, int q, int cl,
                                            int t_begin, int t_end, float (&h)[4],
                                            const float (&a2)[4], float& dt_acc, bool bad) {
     constexpr int TT = TileCfg<T>::TT;
@@ -231,21 +249,27 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int cb, int q
     static_assert(TT * CPT == kThreads / 2, "one B or C chunk per thread per tile");
     __shared__ __attribute__((aligned(16))) char x_l[TT * XS];
     __shared__ __attribute__((aligned(16))) char dt_l[TT * XS];
-    __shared__ __attribute__((aligned(16))) char y_l[MODE == 1 ? TT * XS : 16];
+    // y tile; with the gate and bf16 io the owners' y stays fp32 (row stride
+    // XSF) so that y * SiLU(z) is rounded to bf16 once
+    constexpr bool YF = GATE && ES == 2;
+    constexpr int XSF = 64 * 4 + 32;
+    __shared__ __attribute__((aligned(16))) char y_l[MODE == 1 ? (YF ? TT * XSF : TT * XS) : 16];
     __shared__ __attribute__((aligned(16))) float B_l[TT][16];
     __shared__ __attribute__((aligned(16))) float C_l[TT][16];
 
     const int tid = threadIdx.x;
     const int c = cb * 64 + cl;
     const int64_t row_stride = (int64_t)p.d_inner * ES;  // bytes between token rows
-    const char* xg = static_cast<const char*>(p.x) + ((int64_t)i * p.L * p.d_inner + cb * 64) * ES;
-    const char* dg = static_cast<const char*>(p.dt) + ((int64_t)i * p.L * p.d_inner + cb * 64) * ES;
-    char* yg = static_cast<char*>(p.y) + ((int64_t)i * p.L * p.d_inner + cb * 64) * ES;
+    const char* xg = static_cast<const char*>(p.x) + (tok0 * p.d_inner + cb * 64) * ES;
+    const char* dg = static_cast<const char*>(p.dt) + (tok0 * p.d_inner + cb * 64) * ES;
+    char* yg = static_cast<char*>(p.y) + (tok0 * p.d_inner + cb * 64) * ES;
+    const char* zg = static_cast<const char*>(p.z) + (tok0 * p.d_inner + cb * 64) * ES;  // GATE only
     // B for waves 0-1, C for waves 2-3 (readfirstlane: wave-uniform, so its
     // buffer descriptor stays in scalar registers)
     const int c_half = __builtin_amdgcn_readfirstlane(tid >> 7);
-    const char* bcg = static_cast<const char*>(c_half ? p.C : p.B) + (int64_t)i * p.L * 16 * ES;
+    const char* bcg = static_cast<const char*>(c_half ? p.C : p.B) + tok0 * 16 * ES;
     const float Dc = p.has_D ? p.D[c] : 0.0f;
+    const float dtb = p.dt_bias ? p.dt_bias[c] : 0.0f;
 
     float w[4] = {0.f, 0.f, 0.f, 0.f};
     float xp = 0.0f;
@@ -329,7 +353,7 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int cb, int q
         }
         const bool own_ok = full_tile || (tb + tt < t_end);
         const float xc = to_f32(*reinterpret_cast<const T*>(x_l + tt * XS + cl * ES));
-        float dtv = to_f32(*reinterpret_cast<const T*>(dt_l + tt * XS + cl * ES));
+        float dtv = to_f32(*reinterpret_cast<const T*>(dt_l + tt * XS + cl * ES)) + dtb;
         if constexpr (SOFTPLUS) dtv = softplus(dtv);
         float u;
         if constexpr (K > 0) {
@@ -383,7 +407,9 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int cb, int q
             const bool hi1 = (q & 1) != 0;
             const float keep = hi1 ? r1 : r0, send = hi1 ? r0 : r1;
             const float yv = fmaf(Dc, u, keep + quad_xor1(send));
-            if constexpr (ES == 2)
+            if constexpr (YF)
+                *reinterpret_cast<float*>(y_l + tt * XSF + cl * 4) = yv;
+            else if constexpr (ES == 2)
                 *reinterpret_cast<bf16_t*>(y_l + tt * XS + cl * ES) = bf16_rne(yv);
             else
                 *reinterpret_cast<float*>(y_l + tt * XS + cl * ES) = yv;
@@ -397,6 +423,14 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int cb, int q
     for (int tile = 0; tile < n_tiles; ++tile) {
         const int tb = t_begin + tile * TT;
         const bool more = tile + 1 < n_tiles;
+        // the gate's z rows of this tile, issued before the next tile's loads
+        // so that waiting for them does not wait for those
+        u32x4 sz[2];
+        if constexpr (GATE && MODE == 1) {
+            const auto rz = rsrc(zg, tb, row_stride);
+#pragma unroll
+            for (int r = 0; r < 2; ++r) sz[r] = __builtin_amdgcn_raw_buffer_load_b128(rz, xoff[r], 0, 0);
+        }
         load_tile(tb + TT);  // past the end: zero rows, never staged
         if (tb + TT <= t_end) {
 #pragma unroll 2
@@ -412,8 +446,26 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int cb, int q
             for (int r = 0; r < 2; ++r) {
                 const int e = tid + kThreads * r;
                 const int row = e / CPR, col = e % CPR;
-                __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(y_l + row * XS + col * 16),
-                                                       ry, xoff[r], 0, 0);
+                u32x4 yv;
+                if constexpr (YF) {  // 8 fp32 y of the row times SiLU(z), rounded once
+                    const float4 ya = *reinterpret_cast<const float4*>(y_l + row * XSF + col * 32);
+                    const float4 yb = *reinterpret_cast<const float4*>(y_l + row * XSF + col * 32 + 16);
+                    const float yf[8] = {ya.x, ya.y, ya.z, ya.w, yb.x, yb.y, yb.z, yb.w};
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const float z0 = __uint_as_float(sz[r][k] << 16), z1 = __uint_as_float(sz[r][k] & 0xffff0000u);
+                        yv[k] = uint32_t(bf16_rne(yf[2 * k] * silu(z0))) |
+                                (uint32_t(bf16_rne(yf[2 * k + 1] * silu(z1))) << 16);
+                    }
+                } else {
+                    yv = *reinterpret_cast<const u32x4*>(y_l + row * XS + col * 16);
+                    if constexpr (GATE) {  // fp32 io: y * SiLU(z)
+#pragma unroll
+                        for (int k = 0; k < 4; ++k)
+                            yv[k] = __float_as_uint(__uint_as_float(yv[k]) * silu(__uint_as_float(sz[r][k])));
+                    }
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(yv, ry, xoff[r], 0, 0);
             }
         }
         if (more) store_tile();
@@ -430,7 +482,8 @@ __global__ __launch_bounds__(kThreads) void quad_agg(QuadKP p) {
     const int i = blockIdx.y;
     const int chunk = blockIdx.z;  // 0 .. n_chunks-2
     int r = p.ids[i];
-    const bool bad = (r < 0) | (r >= p.R);
+    const SeqSpan sp = seq_span(p.cu, i, p.L, p.T);
+    const bool bad = (r < 0) | (r >= p.R) | sp.bad;
     float h[4], a2[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -442,11 +495,13 @@ __global__ __launch_bounds__(kThreads) void quad_agg(QuadKP p) {
     }
     float dt_acc = 0.0f;
     const int t_begin = chunk * p.chunk_len;
-    const int t_end = min(p.L, t_begin + p.chunk_len);
-    if constexpr (TILED)
-        quad_tiled<T, K, 0, SOFTPLUS>(p, i, blockIdx.x, q, threadIdx.x >> 2, t_begin, t_end, h, a2, dt_acc, bad);
-    else
-        quad_chunk<T, K, 0>(p, i, c_raw, q, t_begin, t_end, h, a2, dt_acc, active, bad);
+    const int t_end = min(sp.len, t_begin + p.chunk_len);
+    if (t_begin < t_end) {  // workgroup-uniform: a chunk past the sequence's end is empty
+        if constexpr (TILED)
+            quad_tiled<T, K, 0, SOFTPLUS>(p, i, sp.t0, blockIdx.x, q, threadIdx.x >> 2, t_begin, t_end, h, a2, dt_acc, bad);
+        else
+            quad_chunk<T, K, 0>(p, i, sp.t0, c_raw, q, t_begin, t_end, h, a2, dt_acc, active, bad);
+    }
     if (active) {
         const int64_t row = ((int64_t)chunk * p.S + i) * p.d_inner + c;
 #pragma unroll
@@ -478,7 +533,7 @@ __global__ __launch_bounds__(256) void quad_carry(QuadKP p) {
     }
 }
 
-template <typename T, int K, bool TILED, bool SOFTPLUS>
+template <typename T, int K, bool TILED, bool SOFTPLUS, bool GATE>
 __global__ __launch_bounds__(kThreads) void quad_out(QuadKP p) {
     const int q = threadIdx.x & 3;
     const int c_raw = blockIdx.x * kChanPerBlock + (threadIdx.x >> 2);
@@ -487,10 +542,13 @@ __global__ __launch_bounds__(kThreads) void quad_out(QuadKP p) {
     const int i = blockIdx.y;
     const int chunk = blockIdx.z;
     int r = p.ids[i];
-    const bool bad = (r < 0) | (r >= p.R);
+    const SeqSpan sp = seq_span(p.cu, i, p.L, p.T);
+    const bool bad_id = (r < 0) | (r >= p.R);
+    const bool bad = bad_id | sp.bad;
     if (bad) {
         r = 0;
-        if (threadIdx.x == 0 && chunk == 0) atomicOr(p.err, (uint32_t)SSM_DEVERR_IDS);
+        if (threadIdx.x == 0 && chunk == 0)
+            atomicOr(p.err, (bad_id ? (uint32_t)SSM_DEVERR_IDS : 0u) | (sp.bad ? (uint32_t)SSM_DEVERR_SEQLENS : 0u));
     }
     float h[4], a2[4];
     const int64_t rows = (int64_t)p.S * p.d_inner;
@@ -506,11 +564,14 @@ __global__ __launch_bounds__(kThreads) void quad_out(QuadKP p) {
     }
     float dt_acc = 0.0f;
     const int t_begin = chunk * p.chunk_len;
-    const int t_end = min(p.L, t_begin + p.chunk_len);
-    if constexpr (TILED)
-        quad_tiled<T, K, 1, SOFTPLUS>(p, i, blockIdx.x, q, threadIdx.x >> 2, t_begin, t_end, h, a2, dt_acc, bad);
-    else
-        quad_chunk<T, K, 1>(p, i, c_raw, q, t_begin, t_end, h, a2, dt_acc, active, bad);
+    const int t_end = min(sp.len, t_begin + p.chunk_len);
+    if (t_begin < t_end) {  // workgroup-uniform
+        if constexpr (TILED)
+            quad_tiled<T, K, 1, SOFTPLUS, GATE>(p, i, sp.t0, blockIdx.x, q, threadIdx.x >> 2, t_begin, t_end, h, a2,
+                                                dt_acc, bad);
+        else
+            quad_chunk<T, K, 1>(p, i, sp.t0, c_raw, q, t_begin, t_end, h, a2, dt_acc, active, bad);
+    }
     if (active && chunk == p.n_chunks - 1) {
         float* so = p.state_out + ((int64_t)i * p.d_inner + c) * p.N;
 #pragma unroll
@@ -518,11 +579,11 @@ __global__ __launch_bounds__(kThreads) void quad_out(QuadKP p) {
             if (4 * q + s < p.N) so[4 * q + s] = h[s];
         if constexpr (K > 1) {
             if (p.conv_state_out && q == 0) {
-                const T* xs = static_cast<const T*>(p.x) + (int64_t)i * p.L * p.d_inner + c;
+                const T* xs = static_cast<const T*>(p.x) + sp.t0 * p.d_inner + c;
                 float* co = p.conv_state_out + ((int64_t)i * p.d_inner + c) * (K - 1);
 #pragma unroll
                 for (int j = 0; j < K - 1; ++j) {
-                    const int tau = p.L - (K - 1) + j;
+                    const int tau = sp.len - (K - 1) + j;
                     float v;
                     if (tau >= 0) v = ld(xs + (int64_t)tau * p.d_inner);
                     else if (bad) v = __builtin_nanf("");
@@ -557,12 +618,13 @@ __global__ __launch_bounds__(kThreads) void quad_ckpt(QuadKP p) {
     }
     float dt_acc = 0.0f;
     if constexpr (TILED)
-        quad_tiled<T, 0, 2, SOFTPLUS>(p, i, blockIdx.x, q, threadIdx.x >> 2, 0, p.L, h, a2, dt_acc, bad);
+        quad_tiled<T, 0, 2, SOFTPLUS>(p, i, (int64_t)i * p.L, blockIdx.x, q, threadIdx.x >> 2, 0, p.L, h, a2, dt_acc,
+                                      bad);
     else
-        quad_chunk<T, 0, 2>(p, i, c_raw, q, 0, p.L, h, a2, dt_acc, active, bad);
+        quad_chunk<T, 0, 2>(p, i, (int64_t)i * p.L, c_raw, q, 0, p.L, h, a2, dt_acc, active, bad);
 }
 
-template <typename T, int K, bool TILED, bool SOFTPLUS>
+template <typename T, int K, bool TILED, bool SOFTPLUS, bool GATE = false>
 int launch_quad_t(const QuadKP& kp, hipStream_t st) {
     const dim3 block(kThreads);
     const unsigned cblocks = (unsigned)((kp.d_inner + kChanPerBlock - 1) / kChanPerBlock);
@@ -572,15 +634,19 @@ int launch_quad_t(const QuadKP& kp, hipStream_t st) {
         const int64_t threads = (int64_t)kp.S * kp.d_inner * 16;
         hipLaunchKernelGGL(quad_carry, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, kp);
     }
-    hipLaunchKernelGGL((quad_out<T, K, TILED, SOFTPLUS>), dim3(cblocks, kp.S, kp.n_chunks), block, 0, st, kp);
+    hipLaunchKernelGGL((quad_out<T, K, TILED, SOFTPLUS, GATE>), dim3(cblocks, kp.S, kp.n_chunks), block, 0, st, kp);
     return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
 template <typename T, int K>
 int launch_quad(const QuadKP& kp, hipStream_t st) {
-    if (kp.tiled)
+    if (kp.tiled) {
+        if (kp.z)
+            return kp.softplus ? launch_quad_t<T, K, true, true, true>(kp, st)
+                               : launch_quad_t<T, K, true, false, true>(kp, st);
         return kp.softplus ? launch_quad_t<T, K, true, true>(kp, st)
                            : launch_quad_t<T, K, true, false>(kp, st);
+    }
     return launch_quad_t<T, K, false, false>(kp, st);
 }
 
@@ -616,6 +682,7 @@ size_t quad_workspace_bytes(const Shape& sh) {
 int launch_quad_ckpt(const BwdArgs& a, float* ckpt, hipStream_t stream) {
     const Shape& sh = a.sh;
     QuadKP kp = {};
+    kp.T = sh.S * sh.L;
     kp.s = a.s; kp.x = a.x; kp.dt = a.dt; kp.A = a.A; kp.B = a.B; kp.C = a.C; kp.D = nullptr;
     kp.ids = a.ids; kp.err = a.err; kp.agg = ckpt;
     kp.L = (int)sh.L; kp.d_inner = (int)sh.d_inner(); kp.N = (int)sh.N; kp.R = (int)sh.R;
@@ -651,6 +718,7 @@ int launch_quad_fwd(const FwdArgs& a, hipStream_t stream) {
     kp.s = a.s; kp.x = a.x; kp.dt = a.dt; kp.A = a.A; kp.B = a.B; kp.C = a.C; kp.D = a.D;
     kp.ids = a.ids; kp.conv_w = a.conv_w; kp.conv_state = a.conv_state; kp.y = a.y;
     kp.state_out = a.state_out; kp.conv_state_out = a.conv_state_out; kp.err = a.err;
+    kp.dt_bias = a.dt_bias; kp.z = a.z; kp.cu = a.cu; kp.T = a.T;
     kp.L = (int)sh.L; kp.d_inner = (int)sh.d_inner(); kp.N = (int)sh.N; kp.R = (int)sh.R;
     kp.S = (int)sh.S;
     kp.has_D = (sh.flags & SSM_HAS_D) ? 1 : 0;
@@ -658,7 +726,7 @@ int launch_quad_fwd(const FwdArgs& a, hipStream_t stream) {
     const int es = sh.io_bytes();
     auto al16 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; };
     kp.tiled = (sh.N == 16 && sh.d_inner() % 64 == 0 && al16(a.x) && al16(a.dt) && al16(a.B) &&
-                al16(a.C) && al16(a.y)) ? 1 : 0;
+                al16(a.C) && al16(a.y) && al16(a.z)) ? 1 : 0;
     const int tile = es == 2 ? 64 : 32;
     int len = pick_chunk(sh);
     if (len == 0 || len >= sh.L) len = (int)((sh.L + 3) / 4 * 4);

@@ -572,7 +572,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
             const float suf = lane63(pre) - pre + dcum;
             const float wp = __expf(cum_l[kQ - 1] - cum_l[t]);
             float ddt = fmaf(Ah, suf, fmaf(wp, uu, zc));
-            if constexpr (SOFTPLUS) ddt *= 1.0f / (1.0f + __expf(-dt_raw));
+            if constexpr (SOFTPLUS) ddt *= sigmoid(dt_raw);
             if (bad) ddt = __builtin_nanf("");
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ddt), rsrc(ddg, t0, drow4), (int)(t * drow4), 0, 0);
             dA_acc += wave_sum(dcum * sdt_pre);

@@ -72,6 +72,10 @@ struct SsdKP {
     float* state_out;
     float* ckpt;   // CKPT: [S][H][n_chunks][P][N], the state entering each chunk
     uint32_t* err;
+    const float* dt_bias;  // [H] or null
+    const bf16_t* z;       // like x (GATE), or null
+    const int32_t* cu;     // [S+1] spans on the packed token axis, or null
+    int64_t T;             // tokens on the packed axis
     int L, H, G, R, hpg;
     int has_D;
 };
@@ -120,7 +124,7 @@ __device__ __forceinline__ bf16x4 ldtr(const bf16_t* p) {
 
 // CKPT: the backward's recompute: no y, no final state; the fp32 state
 // entering every chunk is stored for the reverse pass.
-template <int P, int N, bool SOFTPLUS, bool CKPT>
+template <int P, int N, bool SOFTPLUS, bool CKPT, bool GATE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void ssd_fwd(SsdKP p) {
     static_assert((P == 32 || P == 64) && (N == 64 || N == 128), "tile shapes");
     constexpr int PB = P / 16;      // 16-channel blocks
@@ -155,14 +159,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int l16 = lane & 15, g4 = lane >> 4;
     const int hh = (int)(blockIdx.x % (unsigned)p.H), i = (int)(blockIdx.x / (unsigned)p.H);
     const int grp = hh / p.hpg;
-    const int L = p.L;
+    // this sequence's tokens: [t0, t0 + L) of the token axis
+    const SeqSpan span = seq_span(p.cu, i, p.L, p.T);
+    const int L = span.len;
     const float Ah = p.A[hh];
     const float Dh = p.has_D ? p.D[hh] : 0.0f;
+    const float dtb = p.dt_bias ? p.dt_bias[hh] : 0.0f;
     int r = p.ids[i];
-    const bool bad = (r < 0) | (r >= p.R);
+    const bool bad_id = (r < 0) | (r >= p.R);
+    const bool bad = bad_id | span.bad;
     if (bad) {
         r = 0;
-        if (tid == 0) atomicOr(p.err, (uint32_t)SSM_DEVERR_IDS);
+        if (tid == 0)
+            atomicOr(p.err, (bad_id ? (uint32_t)SSM_DEVERR_IDS : 0u) | (span.bad ? (uint32_t)SSM_DEVERR_SEQLENS : 0u));
     }
     // state role: wave w keeps tiles [NH*sh, NH*sh + NH) of channel block sp
     constexpr int NH = NB / 2;
@@ -189,11 +198,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int64_t xrow = (int64_t)p.H * P * 2;   // bytes between tokens of x / y
     const int64_t brow = (int64_t)p.G * N * 2;   // bytes between tokens of B / C
     const int64_t drow = (int64_t)p.H * 2;       // bytes between tokens of dt
-    const char* xg = reinterpret_cast<const char*>(p.x) + ((int64_t)i * L * p.H + hh) * P * 2;
-    const char* bg = reinterpret_cast<const char*>(p.B) + ((int64_t)i * L * p.G + grp) * N * 2;
-    const char* cg = reinterpret_cast<const char*>(p.C) + ((int64_t)i * L * p.G + grp) * N * 2;
-    const char* dg = reinterpret_cast<const char*>(p.dt) + ((int64_t)i * L * p.H + hh) * 2;
-    char* yg = reinterpret_cast<char*>(p.y) + ((int64_t)i * L * p.H + hh) * P * 2;
+    const int64_t tok0 = span.t0;
+    const char* xg = reinterpret_cast<const char*>(p.x) + (tok0 * p.H + hh) * P * 2;
+    const char* bg = reinterpret_cast<const char*>(p.B) + (tok0 * p.G + grp) * N * 2;
+    const char* cg = reinterpret_cast<const char*>(p.C) + (tok0 * p.G + grp) * N * 2;
+    const char* dg = reinterpret_cast<const char*>(p.dt) + (tok0 * p.H + hh) * 2;
+    char* yg = reinterpret_cast<char*>(p.y) + (tok0 * p.H + hh) * P * 2;
+    const char* zg = reinterpret_cast<const char*>(p.z) + (tok0 * p.H + hh) * P * 2;  // GATE only
     auto rsrc = [&](const char* base, int t0, int64_t row) {
         const int rows = L - t0;
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base) + (int64_t)t0 * row, 0,
@@ -238,7 +249,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             if constexpr (!CKPT) *reinterpret_cast<u32x4*>(&C_l[t * NP + part * 8]) = sc[k];
         }
         if (wave == 0) {  // decays of the chunk, lane = token
-            float d = to_f32((bf16_t)sdt);
+            float d = to_f32((bf16_t)sdt) + dtb;
             if constexpr (SOFTPLUS) d = softplus(d);
             if (t0 + lane >= L) d = 0.0f;
             const float cum = wave_incl_sum(d * Ah);
@@ -275,6 +286,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         __syncthreads();  // every wave is done with the previous chunk's tiles
         store_chunk(t0);
         __syncthreads();
+        // the gate's z at this lane's y positions, issued before the next
+        // chunk's loads so that waiting for them does not wait for those
+        u32x2 zv[GATE ? PB / 2 : 1];
+        if constexpr (GATE && !CKPT) {
+            const auto rz = rsrc(zg, t0, xrow);
+#pragma unroll
+            for (int q = 0; q < PB / 2; ++q)
+                zv[q] = __builtin_amdgcn_raw_buffer_load_b64(rz, yoff + ((wave >> 2) * (PB / 2) + q) * 32, 0, 0);
+        }
         load_chunk(t0 + kQ);  // next chunk (past the end: reads zero, never used)
 
         if constexpr (!CKPT) {
@@ -364,8 +384,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             const bf16x4 xv = ld4(&X_l[t * XP + pb * 16 + 4 * g4]);
 #pragma unroll
             for (int rr = 0; rr < 4; rr += 2) {
-                const float y0 = fmaf(Dh, (float)xv[rr], fmaf(et, yo[q][rr], yd[q][rr]));
-                const float y1 = fmaf(Dh, (float)xv[rr + 1], fmaf(et, yo[q][rr + 1], yd[q][rr + 1]));
+                float y0 = fmaf(Dh, (float)xv[rr], fmaf(et, yo[q][rr], yd[q][rr]));
+                float y1 = fmaf(Dh, (float)xv[rr + 1], fmaf(et, yo[q][rr + 1], yd[q][rr + 1]));
+                if constexpr (GATE) {  // y * SiLU(z), rounded once
+                    const uint32_t zw = zv[q][rr / 2];
+                    y0 *= silu(__uint_as_float(zw << 16));
+                    y1 *= silu(__uint_as_float(zw & 0xffff0000u));
+                }
                 packed[rr / 2] = uint32_t(bf16_rne(y0)) | (uint32_t(bf16_rne(y1)) << 16);
             }
             __builtin_amdgcn_raw_buffer_store_b64(u32x2{packed[0], packed[1]}, ry, yoff + pb * 32, 0, 0);
@@ -415,8 +440,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 template <int P, int N, bool CKPT = false>
 int launch_ssd_pn(const SsdKP& kp, int S, bool softplus, hipStream_t st) {
     const dim3 grid((unsigned)((int64_t)kp.H * S));
-    if (softplus) hipLaunchKernelGGL((ssd_fwd<P, N, true, CKPT>), grid, dim3(kThreads), 0, st, kp);
-    else hipLaunchKernelGGL((ssd_fwd<P, N, false, CKPT>), grid, dim3(kThreads), 0, st, kp);
+    if (kp.z && !CKPT) {
+        if (softplus) hipLaunchKernelGGL((ssd_fwd<P, N, true, CKPT, true>), grid, dim3(kThreads), 0, st, kp);
+        else hipLaunchKernelGGL((ssd_fwd<P, N, false, CKPT, true>), grid, dim3(kThreads), 0, st, kp);
+    } else {
+        if (softplus) hipLaunchKernelGGL((ssd_fwd<P, N, true, CKPT, false>), grid, dim3(kThreads), 0, st, kp);
+        else hipLaunchKernelGGL((ssd_fwd<P, N, false, CKPT, false>), grid, dim3(kThreads), 0, st, kp);
+    }
     return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
@@ -428,7 +458,8 @@ bool ssd_supported(const Shape& sh, const FwdArgs& a) {
     const int64_t lim = int64_t(1) << 31;
     return !sh.a_per_state && sh.io == SSM_BF16 && sh.K == 0 && (sh.P == 64 || sh.P == 32) &&
            (sh.N == 128 || sh.N == 64) && al16(a.x) && al16(a.B) && al16(a.C) && al16(a.s) &&
-           al16(a.state_out) && (reinterpret_cast<uintptr_t>(a.y) & 7) == 0 && sh.L > 0 &&
+           al16(a.state_out) && (reinterpret_cast<uintptr_t>(a.y) & 7) == 0 &&
+           (reinterpret_cast<uintptr_t>(a.z) & 7) == 0 && sh.L > 0 &&
            sh.S * sh.H < lim && sh.L * sh.H * sh.P * 2 < lim && sh.L * sh.G * sh.N * 2 < lim;
 }
 
@@ -440,6 +471,7 @@ int launch_ssd_fwd(const FwdArgs& a, hipStream_t stream) {
     kp.D = a.D; kp.ids = a.ids; kp.y = static_cast<bf16_t*>(a.y); kp.state_out = a.state_out;
     kp.ckpt = nullptr;
     kp.err = a.err;
+    kp.dt_bias = a.dt_bias; kp.z = static_cast<const bf16_t*>(a.z); kp.cu = a.cu; kp.T = a.T;
     kp.L = (int)sh.L; kp.H = (int)sh.H; kp.G = (int)sh.G; kp.R = (int)sh.R;
     kp.hpg = (int)(sh.H / sh.G);
     kp.has_D = (sh.flags & SSM_HAS_D) ? 1 : 0;
@@ -461,6 +493,7 @@ int launch_ssd_ckpt(const BwdArgs& a, float* ckpt, hipStream_t stream) {
     kp.A = a.A; kp.B = static_cast<const bf16_t*>(a.B); kp.C = static_cast<const bf16_t*>(a.C);
     kp.D = a.D; kp.ids = a.ids; kp.y = nullptr; kp.state_out = nullptr; kp.ckpt = ckpt;
     kp.err = a.err;
+    kp.dt_bias = nullptr; kp.z = nullptr; kp.cu = nullptr; kp.T = sh.S * sh.L;
     kp.L = (int)sh.L; kp.H = (int)sh.H; kp.G = (int)sh.G; kp.R = (int)sh.R;
     kp.hpg = (int)(sh.H / sh.G);
     kp.has_D = (sh.flags & SSM_HAS_D) ? 1 : 0;

@@ -166,17 +166,38 @@ int ssm_conv_bwd(const void* sx, const float* w, const float* dout, float* dgrad
                            workspace, static_cast<hipStream_t>(stream));
 }
 
-int selective_scan_fwd(const ssm_scan_desc* desc, const float* s, const void* x, const void* dt,
-                       const float* A, const void* B, const void* C, const float* D,
-                       const int32_t* ids, const float* conv_w, const float* conv_state,
-                       void* out, float* conv_state_out, void* workspace, size_t workspace_bytes_,
-                       ssm_stream_t stream) {
+}  // extern "C"
+
+namespace ssm {
+namespace {
+
+// Checks the extras against the descriptor and gives the packed token count.
+int check_ext(const Shape& sh, const ssm_scan_ext* ext, int64_t* T) {
+    *T = sh.S * sh.L;
+    if (!ext) return SSM_OK;
+    if (!ext->cu_seqlens) return ext->total_tokens == 0 ? SSM_OK : SSM_ERR_SHAPE;
+    int64_t t1, t2;
+    if (ext->total_tokens < 0 || !mul_ok(ext->total_tokens, sh.d_inner(), &t1) ||
+        !mul_ok(t1, 4, &t2) || !mul_ok(ext->total_tokens, sh.G * sh.N * 4, &t2))
+        return SSM_ERR_SHAPE;
+    *T = ext->total_tokens;
+    return SSM_OK;
+}
+
+int fwd_impl(const ssm_scan_desc* desc, const ssm_scan_ext* ext, const float* s, const void* x,
+             const void* dt, const float* A, const void* B, const void* C, const float* D,
+             const int32_t* ids, const float* conv_w, const float* conv_state, void* out,
+             float* conv_state_out, void* workspace, size_t workspace_bytes_, hipStream_t stream) {
     Shape sh;
     int rc = check_desc(desc, &sh);
     if (rc) return rc;
     if (sh.S > 65535) return SSM_ERR_SHAPE;  // grid y
+    int64_t T;
+    if ((rc = check_ext(sh, ext, &T))) return rc;
+    const int32_t* cu = ext ? ext->cu_seqlens : nullptr;
+    const void* z = ext ? ext->z : nullptr;
     // a pointer may be NULL only when its tensor has no elements
-    const bool has_x = sh.nelem_x() > 0, has_bc = sh.nelem_BC() > 0, has_seq = sh.S > 0;
+    const bool has_x = T * sh.d_inner() > 0, has_bc = T * sh.G * sh.N > 0, has_seq = sh.S > 0;
     if (!s || !A || !workspace || (has_x && (!x || !dt)) || (has_bc && (!B || !C)) ||
         (has_seq && (!ids || !out)))
         return SSM_ERR_NULL;
@@ -188,9 +209,10 @@ int selective_scan_fwd(const ssm_scan_desc* desc, const float* s, const void* x,
         !aligned(out, es) || !aligned(s, 4) || !aligned(A, 4) || !aligned(ids, 4) ||
         (D && !aligned(D, 4)) || (conv_w && !aligned(conv_w, 4)) ||
         (conv_state && !aligned(conv_state, 4)) || (conv_state_out && !aligned(conv_state_out, 4)) ||
-        !aligned(workspace, 256))
+        !aligned(workspace, 256) || !aligned(z, es) || (ext && !aligned(ext->dt_bias, 4)) ||
+        !aligned(cu, 4))
         return SSM_ERR_ALIGN;
-    char* state_block = static_cast<char*>(out) + state_offset(sh);
+    char* state_block = static_cast<char*>(out) + (size_t)(T * sh.d_inner()) * es;
     if (!aligned(state_block, 4)) return SSM_ERR_ALIGN;
     FwdArgs a;
     a.sh = sh; a.s = s; a.x = x; a.dt = dt; a.A = A; a.B = B; a.C = C;
@@ -201,7 +223,45 @@ int selective_scan_fwd(const ssm_scan_desc* desc, const float* s, const void* x,
     a.err = static_cast<uint32_t*>(workspace);
     a.ws = static_cast<char*>(workspace) + kErrBytes;
     a.ws_bytes = workspace_bytes_ - kErrBytes;
-    return launch_scan_fwd(a, static_cast<hipStream_t>(stream));
+    a.dt_bias = ext ? ext->dt_bias : nullptr;
+    a.z = z;
+    a.cu = cu;
+    a.T = T;
+    return launch_scan_fwd(a, stream);
+}
+
+}  // namespace
+}  // namespace ssm
+
+extern "C" {
+
+int selective_scan_fwd(const ssm_scan_desc* desc, const float* s, const void* x, const void* dt,
+                       const float* A, const void* B, const void* C, const float* D,
+                       const int32_t* ids, const float* conv_w, const float* conv_state,
+                       void* out, float* conv_state_out, void* workspace, size_t workspace_bytes_,
+                       ssm_stream_t stream) {
+    return fwd_impl(desc, nullptr, s, x, dt, A, B, C, D, ids, conv_w, conv_state, out,
+                    conv_state_out, workspace, workspace_bytes_, static_cast<hipStream_t>(stream));
+}
+
+size_t ssm_scan_ext_out_bytes(const ssm_scan_desc* desc, const ssm_scan_ext* ext,
+                              size_t* state_offset_) {
+    Shape sh;
+    int64_t T;
+    if (check_desc(desc, &sh) != SSM_OK || check_ext(sh, ext, &T) != SSM_OK) return 0;
+    const size_t off = (size_t)(T * sh.d_inner()) * sh.io_bytes();
+    if (state_offset_) *state_offset_ = off;
+    return off + (size_t)sh.nelem_state() * 4;
+}
+
+int selective_scan_fwd_ext(const ssm_scan_desc* desc, const ssm_scan_ext* ext, const float* s,
+                           const void* x, const void* dt, const float* A, const void* B,
+                           const void* C, const float* D, const int32_t* ids,
+                           const float* conv_w, const float* conv_state, void* out,
+                           float* conv_state_out, void* workspace, size_t workspace_bytes_,
+                           ssm_stream_t stream) {
+    return fwd_impl(desc, ext, s, x, dt, A, B, C, D, ids, conv_w, conv_state, out,
+                    conv_state_out, workspace, workspace_bytes_, static_cast<hipStream_t>(stream));
 }
 
 int selective_scan_bwd(const ssm_scan_desc* desc, const float* s, const void* x, const void* dt,

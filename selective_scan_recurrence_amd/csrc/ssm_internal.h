@@ -48,6 +48,12 @@ struct FwdArgs {
     uint32_t* err;         // device-error word (workspace)
     char* ws;              // workspace after the error word
     size_t ws_bytes;
+    // extras (selective_scan_fwd_ext); all null / S*L for the plain call
+    const float* dt_bias;
+    const void* z;
+    const int32_t* cu;     // [S+1] spans on the packed token axis, or null
+    int64_t T;             // tokens on the packed axis (S*L without cu)
+    bool has_ext() const { return dt_bias || z || cu; }
 };
 
 struct BwdArgs {

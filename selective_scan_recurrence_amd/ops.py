@@ -67,6 +67,35 @@ def scan_fwd(desc, s, x, dt, A, Bm, Cm, D, ids, conv_w=None, conv_state=None,
     return FwdResult(out, y, st, cso)
 
 
+def scan_fwd_ext(desc, s, x, dt, A, Bm, Cm, D, ids, *, dt_bias=None, z=None, cu_seqlens=None,
+                 total_tokens=0, conv_w=None, conv_state=None, want_conv_state=False, ws=None,
+                 out=None, stream=None) -> FwdResult:
+    """selective_scan_fwd_ext.  With cu_seqlens (int32 device [n_seqs+1]) the
+    token axis is packed: y is returned as [total_tokens][n_head][head_dim]."""
+    ext = B.make_ext(dt_bias, z, cu_seqlens, total_tokens if cu_seqlens is not None else 0)
+    total, off = B.ssm_scan_ext_out_bytes(desc, ext)
+    if total == 0:
+        raise B.SsmError(B.SSM_ERR_SHAPE, "ssm_scan_ext_out_bytes")
+    if out is None:
+        out = torch.empty(total, dtype=torch.uint8, device=x.device)
+    cso = None
+    if want_conv_state and desc.d_conv > 1:
+        cso = torch.empty(desc.n_seqs, desc.n_head, desc.d_conv - 1, dtype=torch.float32,
+                          device=x.device)
+    if ws is None:
+        ws = workspace(desc, False, x.device)
+    B.selective_scan_fwd_ext(desc, ext, s, x, dt, A, Bm, Cm, D, ids, conv_w, conv_state, out, cso,
+                             ws, ws.numel(), stream)
+    io = TORCH_IO[desc.io_dtype]
+    H, P = desc.n_head, desc.head_dim
+    n_tok = total_tokens if cu_seqlens is not None else desc.n_seqs * desc.n_tokens
+    y = out[:off].view(io)[:n_tok * H * P].view(n_tok, H, P)
+    if cu_seqlens is None:
+        y = y.view(desc.n_seqs, desc.n_tokens, H, P)
+    st = out[off:].view(torch.float32).view(desc.n_seqs, H, P, desc.d_state)
+    return FwdResult(out, y, st, cso)
+
+
 def split_dgrad(desc: B.SsmScanDesc, dgrad: torch.Tensor) -> dict:
     total, offs = B.ssm_scan_dgrad_layout(desc)
     S, L, H, P, N, G, R = (desc.n_seqs, desc.n_tokens, desc.n_head, desc.head_dim,

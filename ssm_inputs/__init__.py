@@ -40,7 +40,7 @@ import numpy as np
 _STREAM = {
     "x": 1, "dt": 2, "A": 3, "B": 4, "C": 5, "D": 6, "conv_w": 7, "s": 8,
     "ids": 9, "conv_state": 10, "dy": 11, "dstate": 12, "sx": 13, "probe": 14, "dout": 15,
-    "dt_bias": 16, "z": 17,
+    "dt_bias": 16, "z": 17, "lengths": 18,
 }
 
 
@@ -314,6 +314,52 @@ def make_decode_problem(*, with_z=False, dt_bias_range=None, **kw) -> ScanProble
     if dt_bias_range is not None:
         p.t["dt_bias"] = _draw(seed, "dt_bias", (H,), "f32", _uniform(*dt_bias_range))
     return p
+
+
+def make_varlen_problem(*, lengths, n_state_rows=None, ids="perm", with_z=False,
+                        dt_bias_range=None, seed=0, **kw) -> ScanProblem:
+    """Sequences of the given lengths packed on one token axis: one draw of
+    ``make_problem`` with a single sequence of sum(lengths) tokens (its x
+    [1][T][H][P] is the packed [T][H][P], and so on), n_seqs set to the
+    number of lengths, n_tokens to the longest, cu_seqlens the offsets; plus
+    z ~ N(0,1) in the io dtype when with_z and dt_bias ~ U(dt_bias_range)
+    per head when given."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    S, T = len(lengths), int(lengths.sum())
+    R = S if n_state_rows is None else n_state_rows
+    if isinstance(ids, str):
+        idv = (np.arange(S) if ids == "identity" else _rng(seed, "ids").permutation(R)[:S])
+    else:
+        idv = ids
+    p = make_problem(n_seqs=1, n_tokens=T, n_state_rows=R, ids=np.asarray(idv, np.int32), seed=seed,
+                     **kw)
+    p.n_seqs, p.n_tokens = S, int(lengths.max()) if S else 0
+    p.cu_seqlens = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    p.total_tokens = T
+    if with_z:
+        p.t["z"] = _draw(seed, "z", (1, T, p.n_head, p.head_dim), p.io, _normal(1.0))
+    if dt_bias_range is not None:
+        p.t["dt_bias"] = _draw(seed, "dt_bias", (p.n_head,), "f32", _uniform(*dt_bias_range))
+    return p
+
+
+def length_mix(n_seqs: int, total: int, seed: int, lo=0.25, hi=1.75) -> np.ndarray:
+    """n_seqs lengths summing to total: U(lo, hi) times the mean length, rounded
+    (a seeded mix of short and long sequences, most not multiples of 64)."""
+    w = _rng(seed, "lengths").uniform(lo, hi, n_seqs)
+    L = np.floor(w / w.sum() * total).astype(np.int64)
+    L[-1] += total - L.sum()
+    return L
+
+
+def varlen_config(name: str) -> ScanProblem:
+    if name == "C9":   # the C2 layer as one packed batch: 8 sequences of a length mix summing to
+        # 8 x 4096 tokens, 5120 channels, d_state 16, d_conv 4, bf16; dt bias, softplus, z gate
+        lengths = length_mix(8, 8 * 4096, 0xC9)
+        return make_varlen_problem(lengths=lengths, n_head=5120, d_state=16, d_conv=4, io="bf16",
+                                   seed=0xC9, h0_std=0.1, conv_state_std=0.5, dt_softplus=True,
+                                   with_z=True, dt_bias_range=(-3.0, -1.0))
+    raise KeyError(name)
 
 
 def decode_config(name: str) -> ScanProblem:

@@ -247,3 +247,34 @@ def test_state_update_argument_checks():
         with pytest.raises(ssm.SsmError) as e:
             ssm.selective_state_update(**a)
         assert e.value.status == status, over
+
+
+def test_scan_fwd_ext_argument_checks():
+    """selective_scan_fwd_ext rejects bad extras on the host (no launch), and
+    sizes its packed result from total_tokens when spans are given."""
+    d = ops.make_desc(n_seqs=2, n_tokens=8, n_head=64, d_state=16, d_conv=4, io="bf16")
+    ws_bytes = ssm.ssm_scan_workspace_bytes(d, 0)
+    base = dict(s=256, x=256, dt=256, A=256, B=256, C=256, D=256, ids=256, conv_w=256,
+                conv_state=None, out=256, conv_state_out=None, workspace=256,
+                workspace_bytes=ws_bytes, stream=0)
+    E = ssm.make_ext
+    cases = [
+        (E(total_tokens=5), ssm.SSM_ERR_SHAPE),                       # a count without spans
+        (E(cu_seqlens=256, total_tokens=-1), ssm.SSM_ERR_SHAPE),
+        (E(z=257), ssm.SSM_ERR_ALIGN),                                # z aligned like x (2 bytes)
+        (E(dt_bias=258), ssm.SSM_ERR_ALIGN),
+        (E(cu_seqlens=258, total_tokens=4), ssm.SSM_ERR_ALIGN),
+    ]
+    for ext, status in cases:
+        with pytest.raises(ssm.SsmError) as e:
+            ssm.selective_scan_fwd_ext(d, ext, **base)
+        assert e.value.status == status, (ext.z, ext.dt_bias, ext.total_tokens)
+    with pytest.raises(ssm.SsmError) as e:
+        ssm.selective_scan_fwd_ext(d, E(cu_seqlens=256, total_tokens=3), **dict(base, workspace_bytes=0))
+    assert e.value.status == ssm.SSM_ERR_WORKSPACE
+    # sizes: y of total_tokens rows then n_seqs states
+    n, off = ssm.ssm_scan_ext_out_bytes(d, E(cu_seqlens=256, total_tokens=13))
+    assert off == 13 * 64 * 2 and n == off + 2 * 64 * 16 * 4
+    assert ssm.ssm_scan_ext_out_bytes(d, None) == (ssm.ssm_scan_out_bytes(d),
+                                                   ssm.ssm_scan_state_offset_bytes(d))
+    assert ssm.ssm_scan_ext_out_bytes(d, E(total_tokens=3)) == (0, 0)
