@@ -115,14 +115,15 @@ def valu_slots_per_channel_token(p, backward=False) -> float:
 # kernel sources it was taken on; bench.py reports null once any of them changes.
 COPY_FACTOR = {"fetch": 1.99993, "write": 1.00000}
 MEASURED_TRAFFIC = {
-    "C1": {"sha256": "b54488bd1c4354444b1903423f99b869e566fd61179612657f748cdaf2dc0c37", "fetch_kib": 34152.3, "write_kib": 33024.0},
-    "C2": {"sha256": "b54488bd1c4354444b1903423f99b869e566fd61179612657f748cdaf2dc0c37", "fetch_kib": 339353.1, "write_kib": 330240.0},
-    "C3": {"sha256": "73711f6479978241a44d920238fa836895f3e59fc28c6b86144d4a2e39e186cc", "fetch_kib": 144487.6, "write_kib": 174082.0},
-    "C4": {"sha256": "2a19fd3700bb14b898a8f31d961c12501b1bdb0583c23b31fa03aca4474e50b7", "fetch_kib": 1665248.8, "write_kib": 2961396.0},
-    "C5": {"sha256": "84a811e3d84aca510d566615083c4f313b721cec5e2ceaf515444d565e2f3171", "fetch_kib": 512933.0, "write_kib": 704396.3},
-    "C6": {"sha256": "5060521dce2d813674341dfe930be0831fe8c04182c13b450093e534a8b93fb8", "fetch_kib": 52854.2, "write_kib": 100233.3},
-    "C7": {"sha256": "5060521dce2d813674341dfe930be0831fe8c04182c13b450093e534a8b93fb8", "fetch_kib": 83418.7, "write_kib": 164482.0},
-    "C8": {"sha256": "239e0d39855c5cd174deaef0b68e44799016a86043553d49c61ea37eb38162f0", "fetch_kib": 682656.1, "write_kib": 2370216.4},
+    "C1": {"sha256": "4218716b5642d1132f49b5ca41e6c4d8b5d55f9b5b36521e7cd087e5efe84b63", "fetch_kib": 34152.8, "write_kib": 33024.0},
+    "C2": {"sha256": "4218716b5642d1132f49b5ca41e6c4d8b5d55f9b5b36521e7cd087e5efe84b63", "fetch_kib": 339354.0, "write_kib": 330240.0},
+    "C3": {"sha256": "b361281832b24d2c5fa3bed6c1adaa6dadd6ce25471c2aded6e156b2cc16cbd6", "fetch_kib": 142741.0, "write_kib": 174081.0},
+    "C4": {"sha256": "dd18f7a60ce21f038f90f17eb1da7da86124d0b03b67e7302e282072df6b3181", "fetch_kib": 1665316.9, "write_kib": 2961396.0},
+    "C5": {"sha256": "19d21d3c16653649e1d9cac38de168171b782e33178b052b1b50c035b9a95dd5", "fetch_kib": 512936.3, "write_kib": 704342.2},
+    "C6": {"sha256": "fefd2284eb86a0bce2f08280980fbc69fc554eef99b5ec7621fddf1b67c6921a", "fetch_kib": 52837.7, "write_kib": 100230.0},
+    "C7": {"sha256": "fefd2284eb86a0bce2f08280980fbc69fc554eef99b5ec7621fddf1b67c6921a", "fetch_kib": 83414.4, "write_kib": 164482.1},
+    "C8": {"sha256": "e17c27a243ebd3f9b3414f1a08bdca51ddbc2cca792ed119a5b5ce51ab8ad89c", "fetch_kib": 681539.8, "write_kib": 2369653.5},
+    "C9": {"sha256": "856c2b90a5a1872964550d0184eae879db27307310394725b0eaea81e7700484", "fetch_kib": 505345.6, "write_kib": 330720.0},
 }
 KERNEL_SOURCES = {
     "C0": ("scan_fwd.hip", "scan_fwd_ts.hip", "scan_fwd_quad.hip", "device_common.h"),
