@@ -115,8 +115,8 @@ def valu_slots_per_channel_token(p, backward=False) -> float:
 # kernel sources it was taken on; bench.py reports null once any of them changes.
 COPY_FACTOR = {"fetch": 1.99993, "write": 1.00000}
 MEASURED_TRAFFIC = {
-    "C1": {"sha256": "4218716b5642d1132f49b5ca41e6c4d8b5d55f9b5b36521e7cd087e5efe84b63", "fetch_kib": 34152.8, "write_kib": 33024.0},
-    "C2": {"sha256": "4218716b5642d1132f49b5ca41e6c4d8b5d55f9b5b36521e7cd087e5efe84b63", "fetch_kib": 339354.0, "write_kib": 330240.0},
+    "C1": {"sha256": "16e6eeef9848c1dfb8bcc0084e2262cc3353987d0d4939a7359568a52b206b8f", "fetch_kib": 34140.6, "write_kib": 33024.0},
+    "C2": {"sha256": "16e6eeef9848c1dfb8bcc0084e2262cc3353987d0d4939a7359568a52b206b8f", "fetch_kib": 339350.8, "write_kib": 330240.0},
     "C3": {"sha256": "b361281832b24d2c5fa3bed6c1adaa6dadd6ce25471c2aded6e156b2cc16cbd6", "fetch_kib": 142741.0, "write_kib": 174081.0},
     "C4": {"sha256": "dd18f7a60ce21f038f90f17eb1da7da86124d0b03b67e7302e282072df6b3181", "fetch_kib": 1665316.9, "write_kib": 2961396.0},
     "C5": {"sha256": "19d21d3c16653649e1d9cac38de168171b782e33178b052b1b50c035b9a95dd5", "fetch_kib": 512936.3, "write_kib": 704342.2},
