@@ -391,18 +391,7 @@ def main_conv_bwd(args):
     for k in range(args.warmup):
         step(sets[k % copies])
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        starts[k].record()
-        step(sets[k % copies])
-        ends[k].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = np.array([s_.elapsed_time(e) for s_, e in zip(starts, ends)])
-    ms_per_step = starts[0].elapsed_time(ends[-1]) / args.steps
-    avg_s = float(launch_ms.mean()) * 1e-3
+    ms_per_step, avg_s, wall = timed_steps(torch, step, sets, copies, args.steps)
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     ach = step_bytes / avg_s / 1e9
     roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -519,18 +508,7 @@ def main_decode(args):
     for k in range(args.warmup):
         step(sets[k % copies])
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        starts[k].record()
-        step(sets[k % copies])
-        ends[k].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = np.array([s_.elapsed_time(e) for s_, e in zip(starts, ends)])
-    ms_per_step = starts[0].elapsed_time(ends[-1]) / args.steps
-    avg_s = float(launch_ms.mean()) * 1e-3
+    ms_per_step, avg_s, wall = timed_steps(torch, step, sets, copies, args.steps)
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     ach = step_bytes / avg_s / 1e9
     roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -555,6 +533,38 @@ def main_decode(args):
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_decode(p)
     print(json.dumps(line), flush=True)
+
+
+EVENT_STRIDE = 8  # every 8th call of the timed region gets its own pair of events
+
+
+def timed_steps(torch, step, sets, copies, steps):
+    """Times exactly `steps` calls of step(sets[k % copies]).  Two events on
+    the library's stream (torch's current stream) bracket the whole region and
+    give ms per step; every EVENT_STRIDE-th call is also bracketed by its own
+    pair, and the mean of those is the average launch duration.  A pair on
+    every call would add its own cost (about 7 us on a 60 us call) to the
+    region.  Returns (ms_per_step, average launch seconds, wall seconds)."""
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(0, steps, EVENT_STRIDE)]
+    t0 = time.perf_counter()
+    t_begin.record()
+    for k in range(steps):
+        if k % EVENT_STRIDE == 0:
+            a, b = pairs[k // EVENT_STRIDE]
+            a.record()
+            step(sets[k % copies])
+            b.record()
+        else:
+            step(sets[k % copies])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = t_begin.elapsed_time(t_end) / steps
+    avg_s = float(np.mean([a.elapsed_time(b) for a, b in pairs])) * 1e-3
+    return ms_per_step, avg_s, wall
 
 
 def varlen_bytes(p) -> int:
@@ -653,18 +663,7 @@ def main_varlen(args):
     for k in range(args.warmup):
         step(sets[k % copies])
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        starts[k].record()
-        step(sets[k % copies])
-        ends[k].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
-    ms_per_step = starts[0].elapsed_time(ends[-1]) / args.steps
-    avg_s = float(launch_ms.mean()) * 1e-3
+    ms_per_step, avg_s, wall = timed_steps(torch, step, sets, copies, args.steps)
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     ch_tok = p.total_tokens * p.n_head
     slots = valu_slots_ext(p) * ch_tok
@@ -790,22 +789,9 @@ def main():
     for k in range(args.warmup):
         step(sets[k % copies])
     torch.cuda.synchronize()
-    # events on the stream the library launches on (torch's current stream)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        starts[k].record()
-        step(sets[k % copies])
-        ends[k].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
-    total_ms = starts[0].elapsed_time(ends[-1])
-    ms_per_step = total_ms / args.steps
+    ms_per_step, avg_s, wall = timed_steps(torch, step, sets, copies, args.steps)
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     ch_tok = p.n_seqs * p.n_tokens * p.n_head * p.head_dim
-    avg_s = float(launch_ms.mean()) * 1e-3
     floors = {"hbm": step_bytes / (HBM_PEAK_GBS * 1e9)}
     if uses_ssd(p):
         flops = ssd_bwd_mfma_flops(p) if backward else ssd_mfma_flops(p)
