@@ -211,3 +211,41 @@ def test_varlen_full_size_sampled():
     assert_close(host(r.state)[:, heads], st, "bf16", "C9 state")
     assert_close(host(r.conv_state)[:, heads], cso, p.io, "C9 conv_state")
     assert ssm.ssm_get_device_error(ws) == 0
+
+
+@pytest.mark.parametrize("name", ["quad_tiled_bf16", "ssd_bf16", "rows_m2_f32"])
+def test_all_sequences_empty(name):
+    """total_tokens = 0 (every span empty, x/dt/B/C/z/y absent): each final state is
+    its gathered state row and each conv state its conv-state row; no error."""
+    p = _problem(name, lengths=[0, 0, 0], seed=0x96)
+    t = device_inputs(p)
+    d = desc_of(p)
+    d.n_tokens = 8                        # a positive bound; every span is empty
+    ws = ops.workspace(d, False)
+    x = torch.empty(0, device="cuda")
+    r = ops.scan_fwd_ext(d, t["s"], x, x, t["A"], x, x, t.get("D"), t["ids"],
+                         dt_bias=t.get("dt_bias"), cu_seqlens=dev(p.cu_seqlens), total_tokens=0,
+                         conv_w=t.get("conv_w"), conv_state=t.get("conv_state"), want_conv_state=True,
+                         ws=ws)
+    torch.cuda.synchronize()
+    assert r.y.numel() == 0
+    np.testing.assert_array_equal(host(r.state), p.value("s")[p.ids].astype(np.float64))
+    if p.d_conv > 1:
+        np.testing.assert_array_equal(host(r.conv_state), p.value("conv_state")[p.ids].astype(np.float64))
+    assert ssm.ssm_get_device_error(ws) == 0
+
+
+def test_no_sequences():
+    """n_seqs = 0 with spans: nothing is launched and the call succeeds."""
+    d = ops.make_desc(n_seqs=0, n_tokens=8, n_head=64, d_state=16, d_conv=4, io="bf16", n_state_rows=1)
+    e = torch.empty(0, device="cuda")
+    s = torch.zeros(64 * 16, device="cuda")
+    A = torch.zeros(64 * 16, device="cuda")
+    D = torch.zeros(64, device="cuda")
+    w = torch.zeros(64 * 4, device="cuda")
+    cu = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ids = torch.zeros(0, dtype=torch.int32, device="cuda")
+    ws = ops.workspace(d, False)
+    ssm.selective_scan_fwd_ext(d, ssm.make_ext(cu_seqlens=cu, total_tokens=0), s, e, e, A, e, e, D, ids,
+                               w, None, e, None, ws, ws.numel(), None)
+    torch.cuda.synchronize()
