@@ -66,6 +66,12 @@ CASES = {
     "p32_n128_one_token": dict(n_seqs=1, n_tokens=1, n_head=2, head_dim=32, n_state_rows=2),
     "p64_n128_no_D_long": dict(n_seqs=1, n_tokens=333, n_head=2, has_D=False, n_state_rows=1,
                                ids="identity"),
+    # two sequences start from one state row: their d_s contributions add up
+    "p64_n128_dup_ids": dict(n_seqs=3, n_tokens=97, n_head=2, n_state_rows=2,
+                             ids=np.array([1, 1, 0], np.int32)),
+    # four heads share each of two groups, softplus on, several chunks and a ragged tail
+    "p32_n128_groups_softplus": dict(n_seqs=2, n_tokens=200, n_head=8, head_dim=32, n_group=2,
+                                     dt_softplus=True, n_state_rows=3),
 }
 
 
