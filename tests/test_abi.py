@@ -278,3 +278,29 @@ def test_scan_fwd_ext_argument_checks():
     assert ssm.ssm_scan_ext_out_bytes(d, None) == (ssm.ssm_scan_out_bytes(d),
                                                    ssm.ssm_scan_state_offset_bytes(d))
     assert ssm.ssm_scan_ext_out_bytes(d, E(total_tokens=3)) == (0, 0)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """The binding has no fallback: a package copy without libssm.so raises on
+    load() and on the first compute call, naming the missing library."""
+    import shutil
+    import subprocess
+    import sys
+    src = os.path.dirname(ssm.__file__)
+    dst = tmp_path / "selective_scan_recurrence_amd"
+    dst.mkdir()
+    for f in os.listdir(src):
+        if f.endswith(".py"):
+            shutil.copy(os.path.join(src, f), dst / f)
+    code = ("import selective_scan_recurrence_amd as m\n"
+            "for call in (m.load, lambda: m.ssm_version()):\n"
+            "    try:\n"
+            "        call()\n"
+            "    except RuntimeError as e:\n"
+            "        assert 'libssm.so' in str(e) and 'not built' in str(e), e\n"
+            "    else:\n"
+            "        raise SystemExit('no error without the library')\n"
+            "print('raised')\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=tmp_path, capture_output=True, text=True,
+                       timeout=120, env={**os.environ, "PYTHONPATH": str(tmp_path)})
+    assert r.returncode == 0 and "raised" in r.stdout, r.stdout + r.stderr
