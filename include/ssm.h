@@ -197,8 +197,8 @@ int selective_scan_fwd(const ssm_scan_desc *desc, const float *s, const void *x,
  *  - cu_seqlens [n_seqs + 1] int32, DEVICE: variable-length sequences packed
  *    along one token axis.  Sequence i is tokens cu_seqlens[i] ..
  *    cu_seqlens[i+1]-1 and starts from state row ids[i] (and conv_state row
- *    ids[i]), as the flattened sequences of the ggmlR page's RWKV shapes
- *    start a fresh state at each sequence; lengths may differ and may be 0.
+ *    ids[i]), as the flattened sequences of "ggmlR tests/testthat/test-ssm-rwkv.R"
+ *    (its RWKV-6/7 shapes) start a fresh state at each sequence; lengths may differ and may be 0.
  *    x, z, y are then [total_tokens][n_head][head_dim], dt [total_tokens]
  *    [n_head], B and C [total_tokens][n_group][d_state], and desc->n_tokens
  *    is an upper bound on every length (it sizes chunking and workspace).

@@ -20,8 +20,8 @@ Where the pages leave a step open this oracle takes these readings:
   * ``scan_fwd_ext``: the dt bias is added to the raw dt before softplus and
     the gate multiplies the whole y (C.h + D.u) by SiLU(z), as the decode step
     of "mambazip mamba1/model.rs" (forward_impl) does per token; sequences
-    packed on one token axis (the ggmlR page's RWKV shapes, equal lengths
-    there) may have different lengths, given as offsets cu_seqlens, and each
+    packed on one token axis (the RWKV-6/7 shapes of "ggmlR
+    tests/testthat/test-ssm-rwkv.R", equal lengths there) may have different lengths, given as offsets cu_seqlens, and each
     starts from its own state and conv-state row.
 """
 from __future__ import annotations
@@ -170,7 +170,8 @@ def scan_fwd_ext(s, x, dt, A, B, C, D, ids, *, cu_seqlens=None, dt_bias=None, z=
     """``scan_fwd`` with the extras of the per-token step of "mambazip
     mamba1/model.rs" (forward_impl): dt = dt_raw + dt_bias before softplus, and
     y = (C.h + D.u) * SiLU(z); and with sequences packed on one token axis (the
-    ggmlR page's RWKV shapes start a fresh state at every sequence), sequence i
+    RWKV-6/7 shapes of "ggmlR tests/testthat/test-ssm-rwkv.R" start a fresh
+    state at every sequence), sequence i
     being tokens cu_seqlens[i] .. cu_seqlens[i+1]-1.
 
     Without cu_seqlens the shapes are those of ``scan_fwd``.  With it: x and z

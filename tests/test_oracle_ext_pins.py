@@ -1,7 +1,7 @@
 """Pins for the oracle's forward extras (``oracle.scan_fwd_ext``): the dt bias
 and SiLU(z) gate of the per-token step of "mambazip mamba1/model.rs"
-(forward_impl), and sequences packed on one token axis (the ggmlR page's RWKV
-shapes, generalised to per-sequence lengths).  Each is checked against the
+(forward_impl), and sequences packed on one token axis (the RWKV-6/7 shapes of "ggmlR
+tests/testthat/test-ssm-rwkv.R", generalised to per-sequence lengths).  Each is checked against the
 separately pinned equal-length scan, invariants of the recurrence, or exact
 special cases -- never against its own formula retyped.  Each test names the
 mistake it would catch.  CPU only.
