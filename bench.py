@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the selective-scan hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C2]
 
 One step is one selective_scan_fwd call (Mamba-1 form: gather of the initial
 state by ids, causal depthwise conv + SiLU fused into the scan, the scan with
@@ -275,10 +275,19 @@ def cpu_baseline(name, p, min_seconds=10.0, max_reps=50):
     frac = len(heads) / p.n_head
     gbs = algorithmic_bytes(p, backward) * frac / per / 1e9
     ch_tok = p.n_seqs * p.n_tokens * len(heads) * p.head_dim / per
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": oracle.threads_used(len(heads), threads),
-            "kind": "oracle", "sample": f"{sample}; {reps} repetitions", "seconds": round(sec, 3),
-            "channel_tokens_per_s": round(ch_tok, 1), "cpu": platform.processor() or platform.machine(),
-            "nproc": os.cpu_count()}
+    out = {"value": round(gbs, 4), "unit": "GB/s", "cores": oracle.threads_used(len(heads), threads),
+           "kind": "oracle", "sample": f"{sample}; {reps} repetitions", "seconds": round(sec, 3),
+           "channel_tokens_per_s": round(ch_tok, 1), "cpu": platform.processor() or platform.machine(),
+           "nproc": os.cpu_count()}
+    if name in ("C0", "C1"):  # the same workload on one thread
+        t0 = time.perf_counter()
+        oracle.scan_fwd(*args, conv_w=v("conv_w")[heads] if p.d_conv else None, grp_of_head=grp,
+                        n_threads=1)
+        one = time.perf_counter() - t0
+        out["one_thread"] = {"value": round(algorithmic_bytes(p) / one / 1e9, 4), "unit": "GB/s",
+                             "seconds": round(one, 3),
+                             "channel_tokens_per_s": round(p.n_seqs * p.n_tokens * p.n_head / one, 1)}
+    return out
 
 
 def parity_gate_bwd(name, p, g):
@@ -391,13 +400,15 @@ def main_conv_bwd(args):
     for k in range(args.warmup):
         step(sets[k % copies])
     torch.cuda.synchronize()
-    ms_per_step, avg_s, wall = timed_steps(torch, step, sets, copies, args.steps)
+    ms_per_step, wall = timed_steps(torch, step, sets, copies, args.steps)
+    spread = call_distribution(torch, step, sets, copies)
+    avg_s = ms_per_step * 1e-3  # the timed region's mean call duration
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     ach = step_bytes / avg_s / 1e9
     roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.config),
             "traffic_unit": "HBM bytes per call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-            "kernel": "ssm_conv_bwd (all launches of one call)", "avg_launch_us": round(avg_s * 1e6, 3),
+            "kernel": "ssm_conv_bwd (all launches of one call)", "call_us": round(avg_s * 1e6, 3), "call_spread": spread,
             "floors_us": {"hbm": round(step_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2)},
             "algorithmic_bytes": step_bytes}
     line = {
@@ -508,13 +519,15 @@ def main_decode(args):
     for k in range(args.warmup):
         step(sets[k % copies])
     torch.cuda.synchronize()
-    ms_per_step, avg_s, wall = timed_steps(torch, step, sets, copies, args.steps)
+    ms_per_step, wall = timed_steps(torch, step, sets, copies, args.steps)
+    spread = call_distribution(torch, step, sets, copies)
+    avg_s = ms_per_step * 1e-3  # the timed region's mean call duration
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     ach = step_bytes / avg_s / 1e9
     roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.config),
             "traffic_unit": "HBM bytes per call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-            "kernel": "selective_state_update", "avg_launch_us": round(avg_s * 1e6, 3),
+            "kernel": "selective_state_update", "call_us": round(avg_s * 1e6, 3), "call_spread": spread,
             "floors_us": {"hbm": round(step_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2)},
             "algorithmic_bytes": step_bytes}
     line = {
@@ -535,36 +548,38 @@ def main_decode(args):
     print(json.dumps(line), flush=True)
 
 
-EVENT_STRIDE = 8  # every 8th call of the timed region gets its own pair of events
-
-
 def timed_steps(torch, step, sets, copies, steps):
-    """Times exactly `steps` calls of step(sets[k % copies]).  Two events on
-    the library's stream (torch's current stream) bracket the whole region and
-    give ms per step; every EVENT_STRIDE-th call is also bracketed by its own
-    pair, and the mean of those is the average launch duration.  A pair on
-    every call would add its own cost (about 7 us on a 60 us call) to the
-    region.  Returns (ms_per_step, average launch seconds, wall seconds)."""
+    """Times exactly `steps` calls of step(sets[k % copies]), queued back to
+    back: two events on the library's stream (torch's current stream)
+    bracket the whole region.  Returns (ms per step, wall seconds)."""
     t_begin = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(0, steps, EVENT_STRIDE)]
     t0 = time.perf_counter()
     t_begin.record()
     for k in range(steps):
-        if k % EVENT_STRIDE == 0:
-            a, b = pairs[k // EVENT_STRIDE]
-            a.record()
-            step(sets[k % copies])
-            b.record()
-        else:
-            step(sets[k % copies])
+        step(sets[k % copies])
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = t_begin.elapsed_time(t_end) / steps
-    avg_s = float(np.mean([a.elapsed_time(b) for a, b in pairs])) * 1e-3
-    return ms_per_step, avg_s, wall
+    return t_begin.elapsed_time(t_end) / steps, wall
+
+
+def call_distribution(torch, step, sets, copies, n=30):
+    """A separate pass after the timed region: n calls, each bracketed by its
+    own pair of events, for the spread of single-call durations (median,
+    p10, p90, in us).  An event pair adds a few us of its own to each call,
+    so these figures sit slightly above the timed region's mean."""
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(n)]
+    for k, (a, b) in enumerate(pairs):
+        a.record()
+        step(sets[k % copies])
+        b.record()
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in pairs])
+    return {"median_us": round(float(np.median(us)), 3), "p10_us": round(float(np.percentile(us, 10)), 3),
+            "p90_us": round(float(np.percentile(us, 90)), 3), "calls": n,
+            "how": "one event pair per call, separate pass after the timed region"}
 
 
 def varlen_bytes(p) -> int:
@@ -663,7 +678,9 @@ def main_varlen(args):
     for k in range(args.warmup):
         step(sets[k % copies])
     torch.cuda.synchronize()
-    ms_per_step, avg_s, wall = timed_steps(torch, step, sets, copies, args.steps)
+    ms_per_step, wall = timed_steps(torch, step, sets, copies, args.steps)
+    spread = call_distribution(torch, step, sets, copies)
+    avg_s = ms_per_step * 1e-3  # the timed region's mean call duration
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     ch_tok = p.total_tokens * p.n_head
     slots = valu_slots_ext(p) * ch_tok
@@ -679,7 +696,7 @@ def main_varlen(args):
     roof.update({"traffic": measured_traffic(name),
                  "traffic_unit": "HBM bytes per call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                  "kernel": "selective_scan_fwd_ext (all launches of one call)",
-                 "avg_launch_us": round(avg_s * 1e6, 3),
+                 "call_us": round(avg_s * 1e6, 3), "call_spread": spread,
                  "floors_us": {k: round(v * 1e6, 2) for k, v in floors.items()},
                  "algorithmic_bytes": step_bytes, "valu_slots": int(slots)})
     lengths = np.diff(p.cu_seqlens).tolist()
@@ -720,7 +737,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="C1", choices=sorted(WORKLOADS))
+    ap.add_argument("--config", default="C2", choices=sorted(WORKLOADS))
     ap.add_argument("--chunk", type=int, default=None, help="override the time chunk (tokens)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -789,7 +806,9 @@ def main():
     for k in range(args.warmup):
         step(sets[k % copies])
     torch.cuda.synchronize()
-    ms_per_step, avg_s, wall = timed_steps(torch, step, sets, copies, args.steps)
+    ms_per_step, wall = timed_steps(torch, step, sets, copies, args.steps)
+    spread = call_distribution(torch, step, sets, copies)
+    avg_s = ms_per_step * 1e-3  # the timed region's mean call duration
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     ch_tok = p.n_seqs * p.n_tokens * p.n_head * p.head_dim
     floors = {"hbm": step_bytes / (HBM_PEAK_GBS * 1e9)}
@@ -815,7 +834,7 @@ def main():
     roof.update({"traffic": measured_traffic(name), "traffic_unit": "HBM bytes per call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                  "kernel": f"{'selective_scan_bwd' if backward else 'selective_scan_fwd'} "
                            "(all launches of one call)",
-                 "avg_launch_us": round(avg_s * 1e6, 3),
+                 "call_us": round(avg_s * 1e6, 3), "call_spread": spread,
                  "floors_us": {k: round(v * 1e6, 2) for k, v in floors.items()},
                  "algorithmic_bytes": step_bytes})
     if "alu" in floors:
@@ -831,7 +850,7 @@ def main():
         "config": {"workload": f"{name}: {WORKLOADS[name]}", "n_seqs": p.n_seqs,
                    "n_tokens": p.n_tokens, "n_head": p.n_head, "head_dim": p.head_dim,
                    "d_state": p.d_state, "n_group": p.n_group, "d_conv": p.d_conv,
-                   "chunk": desc.chunk, "input_copies": copies},
+                   "chunk": SSD_Q if uses_ssd(p) else desc.chunk, "input_copies": copies},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "channel_tokens_per_s": round(ch_tok / (ms_per_step * 1e-3), 1),
         "roofline": roof,

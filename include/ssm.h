@@ -237,6 +237,17 @@ int selective_scan_fwd_ext(const ssm_scan_desc *desc, const ssm_scan_ext *ext, c
                            float *conv_state_out, void *workspace, size_t workspace_bytes,
                            ssm_stream_t stream);
 
+/* ssm_scan_fwd_plan: the kernel family a selective_scan_fwd(_ext) call with
+ * this descriptor and extras (ext may be NULL; only which of its pointers
+ * are non-NULL matters) would run, taking every tensor as present and
+ * 256-byte aligned: "none" (nothing to compute), "time_split" (few
+ * (sequence, channel) rows: tokens split across the waves of a workgroup),
+ * "quad" or "quad_chunked" (the Mamba-1 form, d_state <= 16, without or with
+ * time chunks), "ssd" (the Mamba-2 form on MFMA) or "rows" (every other
+ * shape).  NULL if the descriptor or ext is invalid.  Host only; reads no
+ * device memory.  For profiling and tests. */
+const char *ssm_scan_fwd_plan(const ssm_scan_desc *desc, const ssm_scan_ext *ext);
+
 /* selective_scan_bwd: reverse-time adjoint of selective_scan_fwd without the
  * fused conv (d_conv must be 0).  dout is packed like the forward result
  * (dy in io, then dstate in f32).  dgrad receives the packed f32 gradient

@@ -10,6 +10,6 @@ from ._binding import (  # noqa: F401
     SSM_DEVERR_SEQLENS, SSM_HAS_D, SSM_OK, SsmError, SsmScanDesc, SsmScanExt, load, make_ext, selective_scan_bwd, selective_scan_fwd,
     selective_scan_fwd_ext, selective_state_update, ssm_scan_ext_out_bytes,
     ssm_conv_bwd, ssm_conv_bwd_workspace_bytes, ssm_conv_fwd, ssm_get_device_error,
-    ssm_scan_dgrad_layout, ssm_scan_out_bytes,
+    ssm_scan_dgrad_layout, ssm_scan_fwd_plan, ssm_scan_out_bytes,
     ssm_scan_state_offset_bytes, ssm_scan_workspace_bytes, ssm_status_str, ssm_version,
 )

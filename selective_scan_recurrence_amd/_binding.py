@@ -23,7 +23,7 @@ EXPORTS = ("ssm_status_str", "ssm_version", "ssm_scan_out_bytes", "ssm_scan_stat
            "ssm_scan_dgrad_layout", "ssm_scan_workspace_bytes", "ssm_conv_fwd",
            "ssm_conv_bwd_workspace_bytes", "ssm_conv_bwd", "selective_scan_fwd",
            "selective_scan_bwd", "selective_state_update", "ssm_get_device_error",
-           "ssm_scan_ext_out_bytes", "selective_scan_fwd_ext")
+           "ssm_scan_ext_out_bytes", "selective_scan_fwd_ext", "ssm_scan_fwd_plan")
 
 
 class SsmError(RuntimeError):
@@ -89,6 +89,8 @@ def load():
         lib.ssm_scan_ext_out_bytes.restype = SZ
         lib.selective_scan_fwd_ext.argtypes = [D, E] + [P] * 13 + [SZ, P]
         lib.selective_scan_fwd_ext.restype = ctypes.c_int
+        lib.ssm_scan_fwd_plan.argtypes = [D, E]
+        lib.ssm_scan_fwd_plan.restype = ctypes.c_char_p
         lib.ssm_get_device_error.argtypes = [P, P, ctypes.POINTER(ctypes.c_uint32)]
         lib.ssm_get_device_error.restype = ctypes.c_int
         _lib = lib
@@ -182,6 +184,12 @@ def ssm_scan_ext_out_bytes(desc: SsmScanDesc, ext: Optional[SsmScanExt]):
     n = load().ssm_scan_ext_out_bytes(ctypes.byref(desc), None if ext is None else ctypes.byref(ext),
                                       ctypes.byref(off))
     return int(n), int(off.value)
+
+
+def ssm_scan_fwd_plan(desc: SsmScanDesc, ext: Optional[SsmScanExt] = None) -> Optional[str]:
+    """The forward's kernel family for this descriptor (None if invalid)."""
+    r = load().ssm_scan_fwd_plan(ctypes.byref(desc), None if ext is None else ctypes.byref(ext))
+    return None if r is None else r.decode()
 
 
 def selective_scan_fwd_ext(desc, ext, s, x, dt, A, B, C, D, ids, conv_w, conv_state, out,

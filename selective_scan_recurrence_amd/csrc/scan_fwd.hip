@@ -198,15 +198,27 @@ size_t fwd_workspace_bytes(const Shape& sh) {
     return quad_supported(sh) ? quad_workspace_bytes(sh) : 0;
 }
 
-int launch_scan_fwd(const FwdArgs& a, hipStream_t stream) {
+FwdPath fwd_path(const FwdArgs& a) {
     const Shape& sh = a.sh;
-    if (sh.S == 0 || sh.H * sh.P == 0) return SSM_OK;
+    if (sh.S == 0 || sh.H * sh.P == 0) return FwdPath::kNone;
     // few (sequence, channel) rows and no explicit chunk: split time inside a workgroup
     if (!a.has_ext() && sh.chunk == 0 && sh.S * ((sh.d_inner() + 63) / 64) * 4 < 2048 &&
         ts_supported(sh, a))
-        return launch_ts_fwd(a, stream);
-    if (quad_supported(sh)) return launch_quad_fwd(a, stream);
-    if (ssd_supported(sh, a)) return launch_ssd_fwd(a, stream);
+        return FwdPath::kTimeSplit;
+    if (quad_supported(sh)) return FwdPath::kQuad;
+    if (ssd_supported(sh, a)) return FwdPath::kSsd;
+    return FwdPath::kRows;
+}
+
+int launch_scan_fwd(const FwdArgs& a, hipStream_t stream) {
+    const Shape& sh = a.sh;
+    switch (fwd_path(a)) {
+        case FwdPath::kNone: return SSM_OK;
+        case FwdPath::kTimeSplit: return launch_ts_fwd(a, stream);
+        case FwdPath::kQuad: return launch_quad_fwd(a, stream);
+        case FwdPath::kSsd: return launch_ssd_fwd(a, stream);
+        case FwdPath::kRows: break;
+    }
     FwdKP kp;
     kp.s = a.s; kp.x = a.x; kp.dt = a.dt; kp.A = a.A; kp.B = a.B; kp.C = a.C; kp.D = a.D;
     kp.ids = a.ids; kp.conv_w = a.conv_w; kp.conv_state = a.conv_state;

@@ -692,7 +692,7 @@ int launch_quad_ckpt(const BwdArgs& a, float* ckpt, hipStream_t stream) {
     auto al16 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; };
     // the tiled path also stages y; the checkpoint pass writes none, so only inputs matter
     kp.tiled = (sh.N == 16 && sh.d_inner() % 64 == 0 && al16(a.x) && al16(a.dt) && al16(a.B) &&
-                al16(a.C)) ? 1 : 0;
+                al16(a.C) && sh.d_inner() * 4 * 64 < (int64_t(1) << 31)) ? 1 : 0;
     kp.chunk_len = (int)sh.L;
     kp.n_chunks = 1;
     const dim3 grid((unsigned)((kp.d_inner + kChanPerBlock - 1) / kChanPerBlock), (unsigned)sh.S);
@@ -725,8 +725,10 @@ int launch_quad_fwd(const FwdArgs& a, hipStream_t stream) {
     kp.softplus = (sh.flags & SSM_DT_SOFTPLUS) ? 1 : 0;
     const int es = sh.io_bytes();
     auto al16 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; };
+    // one tile's rows of x/dt/y must fit the 31-bit sizes of a buffer descriptor
     kp.tiled = (sh.N == 16 && sh.d_inner() % 64 == 0 && al16(a.x) && al16(a.dt) && al16(a.B) &&
-                al16(a.C) && al16(a.y) && al16(a.z)) ? 1 : 0;
+                al16(a.C) && al16(a.y) && al16(a.z) &&
+                sh.d_inner() * 4 * 64 < (int64_t(1) << 31)) ? 1 : 0;
     const int tile = es == 2 ? 64 : 32;
     int len = pick_chunk(sh);
     if (len == 0 || len >= sh.L) len = (int)((sh.L + 3) / 4 * 4);

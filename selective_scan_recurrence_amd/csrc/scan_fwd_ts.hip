@@ -162,9 +162,12 @@ __global__ __launch_bounds__(64 * J) void ts_fwd(TsKP p) {
     const char* bg = static_cast<const char*>(p.B) + (int64_t)i * L * 16 * ES;
     const char* cg = static_cast<const char*>(p.C) + (int64_t)i * L * 16 * ES;
     char* yg = static_cast<char*>(p.y) + ((int64_t)i * L * d_inner + c0) * ES;
-    const int xrow = d_inner * ES;  // bytes between token rows of x, dt, y (< 2^31)
+    const int xrow = d_inner * ES;  // bytes between token rows of x, dt, y (bounded on the host)
+    // a descriptor spans at most the TT rows of one tile (the loads and y
+    // stores through it never reach further), so its size stays below 2^31
+    // however long the sequence is
     auto rsrc = [&](const char* base, int tb, int row_bytes) {
-        const int rows = L - tb;
+        const int rows = min(L - tb, TT);
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base) + (int64_t)tb * row_bytes, 0,
                                                  rows > 0 ? rows * row_bytes : 0, 0x00020000);
     };
@@ -383,7 +386,10 @@ bool ts_supported(const Shape& sh, const FwdArgs& a) {
     return sh.a_per_state && sh.P == 1 && sh.N == 16 && sh.G == 1 &&
            (sh.K == 0 || sh.K == 2 || sh.K == 3 || sh.K == 4) && sh.d_inner() % kCh == 0 &&
            al16(a.x) && al16(a.dt) && al16(a.B) && al16(a.C) && al16(a.y) && al16(a.A) &&
-           al16(a.s) && al16(a.state_out) && sh.S * (sh.d_inner() / kCh) < (int64_t(1) << 31);
+           al16(a.s) && al16(a.state_out) && sh.S * (sh.d_inner() / kCh) < (int64_t(1) << 31) &&
+           // one tile's rows of x/dt/y (kJ * kSub tokens plus the descriptor's
+           // reach) must fit the 31-bit byte sizes and offsets of a descriptor
+           sh.d_inner() * sh.io_bytes() * (kJ * kSub + kHalo + 1) < (int64_t(1) << 31);
 }
 
 int launch_ts_fwd(const FwdArgs& a, hipStream_t stream) {

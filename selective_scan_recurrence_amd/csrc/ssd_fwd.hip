@@ -20,27 +20,38 @@
 // exponent is cum_t - cum_s with s <= t, which is <= 0 for A <= 0.
 //
 // Work split.  One workgroup (8 waves) runs one (sequence, head) through its
-// 64-token chunks in order.  Each wave produces the y of one 16-token block
-// of each chunk for half of the channels, and keeps half of the state columns
-// of one 16-channel block (h^T [N/2][16]) in fp32 MFMA accumulators.  All
-// products run on v_mfma_f32_16x16x32_bf16 (bf16 operands, fp32
-// accumulation), computed transposed:
+// 64-token chunks in order.  With NS = 8 / (P/16) waves per 16-channel block,
+// wave w = (channel block w / NS, part w % NS) keeps the states
+// [part*N/NS, (part+1)*N/NS) of its channel block (h^T, fp32) in MFMA
+// accumulators and produces the y of its channel block for the token blocks
+// [part*4/NS, (part+1)*4/NS) of every chunk.  All products run on
+// v_mfma_f32_16x16x32_bf16 (bf16 operands, fp32 accumulation), computed
+// transposed:
 //     G^T[s][t]   = B C^T          (A: B rows, B: C rows; natural LDS rows)
 //     M           = G o L          (the 10 causal tiles, spread over the waves,
 //                                   written to LDS as bf16 rows [t][s])
 //     Yd^T[p][t]  = X^T M^T        (A: x columns, B: M rows)
-//     Yo^T[p][t]  = h C^T          (A: bf16 copy of h from LDS, B: C rows)
+//     Yo^T[p][t]  = h C^T          (A: the wave's own fp32 state, taken from
+//                                   its accumulators as a bf16 pair hi + lo,
+//                                   B: C rows; summed over its state part)
 //     h^T[n][p]  += B^T (w o X)    (A: B columns, B: x columns scaled by w)
+// The carried-state product needs every state of a channel, so each wave
+// forms it over its own part of the states for all 64 tokens and hands the
+// partial sums of the other waves' token blocks to them through LDS.  The
+// state enters that product as hi + lo, about 16 significant bits, so y's
+// error does not grow with the size of the state.  Within a 32-wide k block
+// the MFMA pairs A and B by the k slot a lane supplies, so the slots may map
+// to any state as long as both operands use the same map: lane 16g + i holds
+// states 16j + 4g + r (r = 0..3) of accumulator tile j, and reads C at the
+// same states.
 // Operands whose k index is the token (x and B columns) are read from the
 // natural row-major tiles with gfx950's transposing LDS read
 // (ds_read_b64_tr_b16): within each 16-lane group, lane i receives element
 // i%4 of the 8-byte blocks addressed by lanes 4k + i/4 (k = 0..3), so lanes
 // 4k+q addressing row s_k, columns 4q..4q+3 of a 16-column block give lane i
 // the column i of rows s_0..s_3.
-// The state each wave updates is written to LDS as bf16 at the start of the
-// next chunk, where every wave reads the channels it needs for the
-// carried-state product.  Three barriers per chunk: chunk staged, M written,
-// chunk consumed.
+// Three barriers per chunk: chunk staged; M and the partial carried-state
+// sums written; chunk consumed.
 //
 #include "device_common.h"
 #include "ssm_internal.h"
@@ -138,15 +149,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     //   8-byte row writes are fastest at 2 (mod 4) dwords and 2x slower at
     //   8 (mod 16).
     // B and C are read as 16-byte rows on the hot loop (N + 16: 40 or 72
-    // dwords); H is written as 8-byte rows as often as it is read (N + 8);
-    // x is read transposed and written once (P + 8 = 36 dwords for P = 64).
+    // dwords); x is read transposed and written once (P + 8 = 36 dwords for
+    // P = 64).
     constexpr int NP = N + 16;      // bf16 pitch of B/C rows (state axis)
-    constexpr int NPH = N + 8;      // bf16 pitch of the state rows
     constexpr int XP = P == 64 ? P + 8 : P + 16;  // bf16 pitch of x rows
+    constexpr int NS = 8 / PB;      // waves per channel block (state parts)
+    constexpr int NW = N / NS;      // states per wave
+    constexpr int NH = NW / 16;     // accumulator tiles per wave
+    constexpr int NKB = (NW + 31) / 32;  // 32-state k blocks of the carried-state product
+    constexpr int TBW = 4 / NS;     // 16-token blocks of y per wave
+    static_assert(NS * PB == kWaves && NH >= 1 && TBW >= 1, "wave roles");
     __shared__ __attribute__((aligned(16))) bf16_t C_l[kQ * NP];   // [t][n]
     __shared__ __attribute__((aligned(16))) bf16_t B_l[kQ * NP];   // [s][n]
     __shared__ __attribute__((aligned(16))) bf16_t X_l[kQ * XP];   // [s][p]
-    __shared__ __attribute__((aligned(16))) bf16_t H_l[P * NPH];   // [p][n], state entering the chunk
+    // partial carried-state sums for the other parts' token blocks:
+    // [channel block][receiving part][sender slot][block][lane] x 4 floats
+    __shared__ __attribute__((aligned(16))) f32x4 Yx_l[PB * NS * (NS > 1 ? NS - 1 : 1) * TBW * 64];
     constexpr int MP = kQ + 8;      // bf16 pitch of M rows
     __shared__ __attribute__((aligned(16))) bf16_t M_l[kQ * MP];   // [t][s], causal (zero above the diagonal)
     __shared__ __attribute__((aligned(16))) float dt_l[kQ];
@@ -173,14 +191,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         if (tid == 0)
             atomicOr(p.err, (bad_id ? (uint32_t)SSM_DEVERR_IDS : 0u) | (span.bad ? (uint32_t)SSM_DEVERR_SEQLENS : 0u));
     }
-    // state role: wave w keeps tiles [NH*sh, NH*sh + NH) of channel block sp
-    constexpr int NH = NB / 2;
-    const bool owns = wave < 2 * PB;
-    const int sp = owns ? wave >> 1 : 0, sh = wave & 1;
-    const int pw = sp * 16;  // first channel of the state block
-    // y role: token block tb, channel blocks yp0 .. yp0 + YPW - 1
-    constexpr int YPW = PB / 2;
-    const int tb = wave & 3, yp0 = (wave >> 2) * YPW;
+    // wave w: channel block sp, state part sh (tiles [NH*sh, NH*sh + NH) of
+    // 16 states), y token blocks [TBW*sh, TBW*sh + TBW)
+    const int sp = wave / NS, sh = wave % NS;
+    const int pw = sp * 16;  // first channel of the block
+    static_assert(NB == NS * NH, "state parts cover the states");
 
     // state h^T[n][p]: tile j holds rows n = 16(NH*sh + j) + 4g + r, column p = pw + l16
     f32x4 hacc[NH];
@@ -260,22 +275,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             w_l[lane] = __expf(last - cum) * d;
             if (lane == 0) elast_l = __expf(last);
         }
-        if (owns) {  // the state entering this chunk, as bf16 [p][n]
+        if constexpr (CKPT) {  // the fp32 state entering this chunk
 #pragma unroll
-            for (int j = 0; j < NH; ++j) {
-                const f32x4 v = hacc[j];
-                const uint32_t lo = uint32_t(bf16_rne(v[0])) | (uint32_t(bf16_rne(v[1])) << 16);
-                const uint32_t hi = uint32_t(bf16_rne(v[2])) | (uint32_t(bf16_rne(v[3])) << 16);
-                *reinterpret_cast<u32x2*>(&H_l[(pw + l16) * NPH + (NH * sh + j) * 16 + 4 * g4]) = u32x2{lo, hi};
-                if constexpr (CKPT)
-                    *reinterpret_cast<f32x4*>(p.ckpt + (((((int64_t)i * p.H + hh) * n_chunks + t0 / kQ) * P + pw + l16) * N +
-                                                        (NH * sh + j) * 16 + 4 * g4)) = v;
-            }
+            for (int j = 0; j < NH; ++j)
+                *reinterpret_cast<f32x4*>(p.ckpt + (((((int64_t)i * p.H + hh) * n_chunks + t0 / kQ) * P + pw + l16) * N +
+                                                    (NH * sh + j) * 16 + 4 * g4)) = hacc[j];
         }
     };
 
-    // y stores: lane (t = 16tb + l16, channels 16pb + 4g .. +3), one 8-byte store per channel block
-    const int yoff = (int)((tb * 16 + l16) * xrow) + 4 * g4 * 2;
+    // y stores: lane (t = 16tb + l16, channels pw + 4g .. +3), one 8-byte store per token block
+    auto yoff = [&](int tb) { return (int)((tb * 16 + l16) * xrow) + (pw + 4 * g4) * 2; };
 
     // M's tiles above the diagonal are never written: zero the whole tile once
     for (int e = tid; e < kQ * MP / 2; e += kThreads) reinterpret_cast<uint32_t*>(M_l)[e] = 0u;
@@ -288,12 +297,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         __syncthreads();
         // the gate's z at this lane's y positions, issued before the next
         // chunk's loads so that waiting for them does not wait for those
-        u32x2 zv[GATE ? PB / 2 : 1];
+        u32x2 zv[GATE ? TBW : 1];
         if constexpr (GATE && !CKPT) {
             const auto rz = rsrc(zg, t0, xrow);
 #pragma unroll
-            for (int q = 0; q < PB / 2; ++q)
-                zv[q] = __builtin_amdgcn_raw_buffer_load_b64(rz, yoff + ((wave >> 2) * (PB / 2) + q) * 32, 0, 0);
+            for (int q = 0; q < TBW; ++q)
+                zv[q] = __builtin_amdgcn_raw_buffer_load_b64(rz, yoff(TBW * sh + q), 0, 0);
         }
         load_chunk(t0 + kQ);  // next chunk (past the end: reads zero, never used)
 
@@ -344,48 +353,84 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                 *reinterpret_cast<u32x2*>(&M_l[mt_t * MP + msb[u] * 16 + 4 * g4]) = u32x2{lo, hi};
             }
         }
-        __syncthreads();
-
-        // this wave's 16 tokens: t = 16tb + l16 in every tile below
-        const int t = tb * 16 + l16;
-        const float et = ecum_l[t];
-        const auto ry = rsrc(yg, t0, xrow);
-        // Yd^T = X^T M^T over s, Yo^T = h C^T over n, for the wave's channel blocks
-        // (their MFMA chains interleaved; the M and C rows of token t are shared)
-        f32x4 yd[YPW], yo[YPW];
+        // carried-state product over this wave's state part, for all four token
+        // blocks: A = the state as bf16 hi + lo from the accumulators, B = C at
+        // the same states (see the header); the other parts' blocks go to LDS
+        f32x4 yo[4];
+        {
+            bf16x8 ahi[NKB], alo[NKB];
 #pragma unroll
-        for (int q = 0; q < YPW; ++q) {
-            yd[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-            yo[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+            for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            if (2 * kk > tb) continue;
-            const bf16x8 mrow = ld8(&M_l[t * MP + kk * 32 + 8 * g4]);
+                for (int e = 0; e < 8; ++e) {
+                    const int j = 2 * kb + (e >> 2);
+                    const float v = j < NH ? hacc[j][e & 3] : 0.0f;
+                    const __bf16 hi = (__bf16)v;
+                    ahi[kb][e] = hi;
+                    alo[kb][e] = (__bf16)(v - (float)hi);
+                }
+            }
 #pragma unroll
-            for (int q = 0; q < YPW; ++q) {
-                // x column p = 16(yp0+q) + l16 over s = 32kk + 8g + j
-                const bf16_t* xr = &X_l[(kk * 32 + 8 * g4 + (l16 >> 2)) * XP + (yp0 + q) * 16 + 4 * (l16 & 3)];
-                yd[q] = mfma(cat(ldtr(xr), ldtr(xr + 4 * XP)), mrow, yd[q]);
+            for (int tbk = 0; tbk < 4; ++tbk) {
+                yo[tbk] = f32x4{0.f, 0.f, 0.f, 0.f};
+                const bf16_t* crow = &C_l[(tbk * 16 + l16) * NP + NW * sh + 4 * g4];
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    const bf16x4 c0 = ld4(crow + 32 * kb);
+                    const bf16x4 c1 = 2 * kb + 1 < NH ? ld4(crow + 32 * kb + 16) : bf16x4{0, 0, 0, 0};
+                    const bf16x8 cop = cat(c0, c1);
+                    yo[tbk] = mfma(ahi[kb], cop, yo[tbk]);
+                    yo[tbk] = mfma(alo[kb], cop, yo[tbk]);
+                }
             }
         }
+        if constexpr (NS > 1) {
 #pragma unroll
-        for (int kk = 0; kk < N / 32; ++kk) {
-            const bf16x8 crow = ld8(&C_l[t * NP + kk * 32 + 8 * g4]);
+            for (int tbk = 0; tbk < 4; ++tbk) {
+                const int dst = tbk / TBW;
+                if (dst == sh) continue;
+                const int slot = (sh - dst - 1 + NS) % NS;  // 0 .. NS-2
+                Yx_l[(((sp * NS + dst) * (NS - 1) + slot) * TBW + tbk % TBW) * 64 + lane] = yo[tbk];
+            }
+        }
+        __syncthreads();
+
+        const auto ry = rsrc(yg, t0, xrow);
+        // Yd^T = X^T M^T over s for the wave's token blocks (x columns of its
+        // channel block, shared by the blocks)
+        bf16x8 xcol[2];
 #pragma unroll
-            for (int q = 0; q < YPW; ++q)
-                yo[q] = mfma(ld8(&H_l[((yp0 + q) * 16 + l16) * NPH + kk * 32 + 8 * g4]), crow, yo[q]);
+        for (int kk = 0; kk < 2; ++kk) {
+            const bf16_t* xr = &X_l[(kk * 32 + 8 * g4 + (l16 >> 2)) * XP + pw + 4 * (l16 & 3)];
+            xcol[kk] = cat(ldtr(xr), ldtr(xr + 4 * XP));
         }
 #pragma unroll
-        for (int q = 0; q < YPW; ++q) {
-            const int pb = yp0 + q;
-            // y[t][p] for p = 16pb + 4g + r: y = yd + exp(cum_t) yo + D x
+        for (int q = 0; q < TBW; ++q) {
+            const int tb = TBW * sh + q;
+            const int t = tb * 16 + l16;
+            f32x4 yd = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                if (2 * kk > tb) continue;
+                yd = mfma(xcol[kk], ld8(&M_l[t * MP + kk * 32 + 8 * g4]), yd);
+            }
+            f32x4 yot = yo[0];  // yo[tb], selected with constant indices
+#pragma unroll
+            for (int k = 1; k < 4; ++k)
+                if (k == tb) yot = yo[k];
+            if constexpr (NS > 1) {
+#pragma unroll
+                for (int slot = 0; slot < NS - 1; ++slot)
+                    yot += Yx_l[(((sp * NS + sh) * (NS - 1) + slot) * TBW + q) * 64 + lane];
+            }
+            const float et = ecum_l[t];
+            // y[t][p] for p = pw + 4g + r: y = yd + exp(cum_t) yo + D x
             uint32_t packed[2];
-            const bf16x4 xv = ld4(&X_l[t * XP + pb * 16 + 4 * g4]);
+            const bf16x4 xv = ld4(&X_l[t * XP + pw + 4 * g4]);
 #pragma unroll
             for (int rr = 0; rr < 4; rr += 2) {
-                float y0 = fmaf(Dh, (float)xv[rr], fmaf(et, yo[q][rr], yd[q][rr]));
-                float y1 = fmaf(Dh, (float)xv[rr + 1], fmaf(et, yo[q][rr + 1], yd[q][rr + 1]));
+                float y0 = fmaf(Dh, (float)xv[rr], fmaf(et, yot[rr], yd[rr]));
+                float y1 = fmaf(Dh, (float)xv[rr + 1], fmaf(et, yot[rr + 1], yd[rr + 1]));
                 if constexpr (GATE) {  // y * SiLU(z), rounded once
                     const uint32_t zw = zv[q][rr / 2];
                     y0 *= silu(__uint_as_float(zw << 16));
@@ -393,13 +438,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                 }
                 packed[rr / 2] = uint32_t(bf16_rne(y0)) | (uint32_t(bf16_rne(y1)) << 16);
             }
-            __builtin_amdgcn_raw_buffer_store_b64(u32x2{packed[0], packed[1]}, ry, yoff + pb * 32, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{packed[0], packed[1]}, ry, yoff(tb), 0, 0);
         }
 
         }  // !CKPT
 
         // state of this wave's block: h^T = exp(cum_last) h^T + B^T (w o X)
-        if (owns) {
+        {
             const float e_last = elast_l;
             bf16x8 xw[2];
 #pragma unroll
@@ -428,7 +473,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         }
     }
 
-    if (owns && !CKPT) {
+    if (!CKPT) {
         float* so = p.state_out + (((int64_t)i * p.H + hh) * P + pw + l16) * N + NH * sh * 16;
 #pragma unroll
         for (int j = 0; j < NH; ++j)

@@ -254,6 +254,36 @@ size_t ssm_scan_ext_out_bytes(const ssm_scan_desc* desc, const ssm_scan_ext* ext
     return off + (size_t)sh.nelem_state() * 4;
 }
 
+const char* ssm_scan_fwd_plan(const ssm_scan_desc* desc, const ssm_scan_ext* ext) {
+    Shape sh;
+    int64_t T;
+    if (check_desc(desc, &sh) != SSM_OK || check_ext(sh, ext, &T) != SSM_OK) return nullptr;
+    // every tensor taken as present and 256-byte aligned
+    static char dummy[256] __attribute__((aligned(256)));
+    void* pp = dummy;
+    FwdArgs a = {};
+    a.sh = sh;
+    a.s = a.A = a.D = a.conv_w = a.conv_state = static_cast<const float*>(pp);
+    a.x = a.dt = a.B = a.C = pp;
+    a.ids = static_cast<const int32_t*>(pp);
+    a.y = pp;
+    a.state_out = a.conv_state_out = static_cast<float*>(pp);
+    a.T = T;
+    if (ext) {
+        a.dt_bias = ext->dt_bias ? static_cast<const float*>(pp) : nullptr;
+        a.z = ext->z ? pp : nullptr;
+        a.cu = ext->cu_seqlens ? static_cast<const int32_t*>(pp) : nullptr;
+    }
+    switch (fwd_path(a)) {
+        case FwdPath::kNone: return "none";
+        case FwdPath::kTimeSplit: return "time_split";
+        case FwdPath::kQuad: return fwd_workspace_bytes(sh) > 0 ? "quad_chunked" : "quad";
+        case FwdPath::kSsd: return "ssd";
+        case FwdPath::kRows: return "rows";
+    }
+    return nullptr;
+}
+
 int selective_scan_fwd_ext(const ssm_scan_desc* desc, const ssm_scan_ext* ext, const float* s,
                            const void* x, const void* dt, const float* A, const void* B,
                            const void* C, const float* D, const int32_t* ids,

@@ -123,6 +123,10 @@ bool ssd_bwd_supported(const Shape& sh);
 size_t ssd_bwd_workspace_bytes(const Shape& sh);
 int launch_ssd_bwd(const BwdArgs& a, hipStream_t stream);
 
+// The forward's kernel family for a call (host-side decision only).
+enum class FwdPath { kNone, kTimeSplit, kQuad, kSsd, kRows };
+FwdPath fwd_path(const FwdArgs& a);
+
 // Returns SSM_OK, SSM_ERR_UNSUPPORTED, or SSM_ERR_HIP.
 int launch_scan_fwd(const FwdArgs& a, hipStream_t stream);
 int launch_scan_bwd(const BwdArgs& a, hipStream_t stream);

@@ -304,3 +304,46 @@ def test_missing_library_fails_loudly(tmp_path):
     r = subprocess.run([sys.executable, "-c", code], cwd=tmp_path, capture_output=True, text=True,
                        timeout=120, env={**os.environ, "PYTHONPATH": str(tmp_path)})
     assert r.returncode == 0 and "raised" in r.stdout, r.stdout + r.stderr
+
+
+@pytest.mark.parametrize("kw,want", [
+    # the benchmark layers
+    (dict(n_seqs=8, n_tokens=2048, n_head=512, head_dim=1, d_state=16, a_per_state=True, d_conv=4),
+     "time_split"),
+    (dict(n_seqs=8, n_tokens=4096, n_head=5120, head_dim=1, d_state=16, a_per_state=True, d_conv=4,
+          io="bf16"), "quad"),
+    (dict(n_seqs=4, n_tokens=4096, n_head=80, head_dim=64, d_state=128, io="bf16"), "ssd"),
+    # an explicit chunk on the Mamba-1 form asks for the chunked quad kernels
+    (dict(n_seqs=8, n_tokens=2048, n_head=512, head_dim=1, d_state=16, a_per_state=True, d_conv=4,
+          chunk=256), "quad_chunked"),
+    # shapes no specialised kernel takes
+    (dict(n_seqs=2, n_tokens=8, n_head=3, head_dim=2, d_state=4), "rows"),
+    (dict(n_seqs=2, n_tokens=8, n_head=64, head_dim=1, d_state=32, a_per_state=True), "rows"),
+    (dict(n_seqs=0, n_tokens=8, n_head=64, head_dim=1, d_state=16, a_per_state=True,
+          n_state_rows=1), "none"),
+    # one long f32 sequence of 8192 channels: the time-split kernel, whose
+    # buffer descriptors span one 128-token tile (8192 x 4 x 128 bytes), not
+    # the 2^32 bytes of the whole sequence
+    (dict(n_seqs=1, n_tokens=131072, n_head=8192, head_dim=1, d_state=16, a_per_state=True,
+          d_conv=4), "time_split"),
+    # a tile of 4M f32 channels no longer fits a descriptor's 31-bit size: the
+    # time-split kernel declines it (the quad kernel's 64-token tiles still fit)
+    (dict(n_seqs=1, n_tokens=1, n_head=1 << 22, head_dim=1, d_state=16, a_per_state=True,
+          d_conv=4), "quad"),
+])
+def test_forward_plan(kw, want):
+    """Which kernel family a forward call runs is decided on the host from the
+    descriptor alone (and the alignment of the tensors, here 256 bytes)."""
+    base = dict(a_per_state=False, io="f32")
+    base.update(kw)
+    assert ssm.ssm_scan_fwd_plan(ops.make_desc(**base)) == want
+
+
+def test_forward_plan_with_extras_and_invalid():
+    d = ops.make_desc(n_seqs=8, n_tokens=2048, n_head=512, d_state=16, d_conv=4)
+    # extras never take the time-split kernel: with this few rows the quad
+    # kernels split time into chunks instead
+    assert ssm.ssm_scan_fwd_plan(d, ssm.make_ext(cu_seqlens=1, total_tokens=100)) == "quad_chunked"
+    bad = ops.make_desc(n_seqs=2, n_tokens=8, n_head=3, head_dim=2, d_state=4)
+    bad.d_state = 0
+    assert ssm.ssm_scan_fwd_plan(bad) is None

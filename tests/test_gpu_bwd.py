@@ -98,30 +98,48 @@ def test_backward_edge_case_parity(gpu, case):
     _compare_all(p, g, case)
 
 
-def test_backward_full_size_c4_sampled(gpu):
-    """C4 (8 x 4096 x 5120, bf16 inputs): every token of sampled channels for
-    the per-channel gradients, and every channel of one sequence for d_B/d_C."""
+@pytest.fixture(scope="module")
+def c4_result(gpu):
+    """C4 (the backward of the 8 x 4096 x 5120 bf16 scan) run once on the GPU;
+    the per-sequence tests below add their oracle shares of the sums over
+    sequences (d_A, d_D, d_s) into `partial`."""
     p = ssm_inputs.config("C4")
     g = _run_bwd(p)
+    return {"p": p, "g": g, "partial": {}}
+
+
+def _c4_oracle_seq(p, seq):
     v = p.value
-    rng = np.random.default_rng(0xC4)
-    heads = np.unique(np.concatenate([[0, p.n_head - 1], rng.choice(p.n_head, 40, replace=False)]))
-    o = oracle.scan_bwd(v("s")[:, heads], v("x")[:, :, heads], v("dt")[:, :, heads], v("A")[heads],
-                        v("B"), v("C"), v("D")[heads], p.ids, v("dy")[:, :, heads],
-                        v("dstate")[:, heads], grp_of_head=np.zeros(len(heads), np.int64))
-    hs = torch.as_tensor(heads, device="cuda")
-    _check("C4 d_x", host(g["d_x"].index_select(2, hs)), o["d_x"], 1e-5)
-    _check("C4 d_dt", host(g["d_dt"].index_select(2, hs)), o["d_dt"], 1e-5)
-    _check("C4 d_A", host(g["d_A"].index_select(0, hs)), o["d_A"], 1e-4)
-    _check("C4 d_D", host(g["d_D"].index_select(0, hs)), o["d_D"], 1e-4)
-    _check("C4 d_s", host(g["d_s"].index_select(1, hs)), o["d_s"], 1e-4)
-    # one sequence, all channels: the channel sums
-    i = int(rng.integers(p.n_seqs))
-    sl = slice(i, i + 1)
-    o1 = oracle.scan_bwd(v("s"), v("x")[sl], v("dt")[sl], v("A"), v("B")[sl], v("C")[sl], v("D"),
-                         p.ids[sl], v("dy")[sl], v("dstate")[sl])
-    _check("C4 d_B (one sequence)", host(g["d_B"][sl]), o1["d_B"], 1e-4)
-    _check("C4 d_C (one sequence)", host(g["d_C"][sl]), o1["d_C"], 1e-4)
+    sl = slice(seq, seq + 1)
+    return oracle.scan_bwd(v("s"), v("x")[sl], v("dt")[sl], v("A"), v("B")[sl], v("C")[sl], v("D"),
+                           p.ids[sl], v("dy")[sl], v("dstate")[sl])
+
+
+@pytest.mark.parametrize("seq", range(8))
+def test_backward_c4_full_size_every_channel(c4_result, seq):
+    """Every channel and token of one sequence of C4: d_x, d_dt and that
+    sequence's rows of d_B and d_C against the oracle run on the sequence
+    alone."""
+    p, g = c4_result["p"], c4_result["g"]
+    o = _c4_oracle_seq(p, seq)
+    sl = slice(seq, seq + 1)
+    for k, floor in (("d_x", 1e-5), ("d_dt", 1e-5), ("d_B", 1e-4), ("d_C", 1e-4)):
+        _check(f"C4 sequence {seq} {k}", host(g[k][sl]), o[k], floor)
+    c4_result["partial"][seq] = {k: o[k] for k in ("d_A", "d_D", "d_s")}
+
+
+def test_backward_c4_full_size_sums_over_sequences(c4_result):
+    """d_A, d_D and d_s of C4 (sums over all 8 sequences) against the sum of
+    the per-sequence oracle gradients (any sequence not done above is run
+    here)."""
+    p, g, part = c4_result["p"], c4_result["g"], c4_result["partial"]
+    for seq in range(p.n_seqs):
+        if seq not in part:
+            o = _c4_oracle_seq(p, seq)
+            part[seq] = {k: o[k] for k in ("d_A", "d_D", "d_s")}
+    for k in ("d_A", "d_D", "d_s"):
+        want = sum(part[seq][k] for seq in range(p.n_seqs))
+        _check(f"C4 {k}", host(g[k]), want, 1e-4)
     for k in ("d_x", "d_dt", "d_B", "d_C"):
         assert bool(torch.isfinite(g[k]).all()), k
 

@@ -49,12 +49,11 @@ def _draw(k):
 @pytest.mark.parametrize("k", range(N_CASES))
 def test_random_shape(k):
     form, io, kw, varlen, lengths, ex = _draw(k)
-    h0 = 0.1 if form == "m2" else 0.3
     # dt is a positive step: a bias that could drive dt_raw + bias below zero is
     # drawn only when softplus follows it
     bias_range = ((-1.0, 0.5) if ex["softplus"] else (0.0, 0.5)) if ex["bias"] else None
     p = ssm_inputs.make_varlen_problem(lengths=lengths, n_state_rows=len(lengths) + 1, seed=2000 + k, io=io,
-                                       h0_std=h0, with_z=ex["with_z"], dt_softplus=ex["softplus"],
+                                       h0_std=0.3, with_z=ex["with_z"], dt_softplus=ex["softplus"],
                                        dt_bias_range=bias_range, **kw)
     what = f"case {k}: {form} {io} {kw} varlen={varlen} lengths={list(lengths)} {ex}"
     t = device_inputs(p)
@@ -84,5 +83,5 @@ def test_random_shape(k):
     bad = ~(err <= atol * scale + rtol * np.abs(y))
     assert not bad.any(), f"{what}: y {int(bad.sum())}/{bad.size} outside"
     assert_close(host(r.state), st, "f32" if io == "f32" else "bf16", f"{what}: state")
-    if p.d_conv > 1:
-        assert_close(host(r.conv_state), cs, io, f"{what}: conv state")
+    if p.d_conv > 1:  # a copy of inputs: exact
+        np.testing.assert_array_equal(host(r.conv_state), cs, err_msg=f"{what}: conv state")

@@ -33,40 +33,38 @@ def _fwd(p, **over):
 
 
 # --------------------------------------------------------------------------
-# Depthwise conv: the brute force written out in R on the ggmlR page
-# ("ggml_ssm_conv matches a depthwise convolution computed in R"): flat
-# column-major vectors, 1-based indices, out[ch, t] = sum_j sx[t+j-1, ch] c[j, ch].
+# Depthwise conv ("ggmlR tests/testthat/test-ssm-rwkv.R", the ssm_conv test
+# against a convolution computed in R): each output channel is the valid
+# cross-correlation of that channel's input row (the d_conv-1 earlier inputs
+# followed by the tokens) with that channel's taps, so the last tap meets
+# the newest input.  numpy's correlate computes it channel by channel.
 # Catches: reversed tap order, an off-by-one in the window, a transposed layout.
 # --------------------------------------------------------------------------
-def _r_style_conv(sx_v, c_v, d_conv, d_inner, n_t, n_s):
-    length = d_conv - 1 + n_t
-    ref = np.zeros(d_inner * n_t * n_s)
-    for s in range(1, n_s + 1):
-        for ch in range(1, d_inner + 1):
-            for t in range(1, n_t + 1):
-                acc = 0.0
-                for j in range(1, d_conv + 1):
-                    acc += sx_v[(s - 1) * d_inner * length + (ch - 1) * length + (t + j - 1) - 1] * \
-                           c_v[(ch - 1) * d_conv + j - 1]
-                ref[(s - 1) * d_inner * n_t + (t - 1) * d_inner + ch - 1] = acc
-    return ref
+def _depthwise_reference(sx, w):
+    """sx [n_s][d_inner][d_conv-1+n_t], w [d_inner][d_conv] -> [n_s][n_t][d_inner]."""
+    n_s, d_inner, _ = sx.shape
+    out = np.stack([np.stack([np.correlate(sx[s, ch], w[ch], mode="valid") for ch in range(d_inner)],
+                             axis=-1) for s in range(n_s)])
+    return out
 
 
-@pytest.mark.parametrize("d_conv,d_inner,n_t,n_s", [(3, 2, 4, 1), (4, 3, 5, 2), (1, 2, 3, 1)])
-def test_conv_matches_page_brute_force(d_conv, d_inner, n_t, n_s):
-    rng = np.random.default_rng(11)
-    length = d_conv - 1 + n_t
-    sx_v = rng.uniform(-1, 1, length * d_inner * n_s)
-    c_v = rng.uniform(-1, 1, d_conv * d_inner)
-    sx = sx_v.reshape(n_s, d_inner, length)   # ne [len, d_inner, n_s]
-    w = c_v.reshape(d_inner, d_conv)          # ne [d_conv, d_inner]
+@pytest.mark.parametrize("d_conv,d_inner,n_t,n_s", [(3, 5, 6, 2), (4, 3, 9, 1), (1, 2, 3, 1),
+                                                    (2, 4, 1, 3)])
+def test_conv_matches_depthwise_correlation(d_conv, d_inner, n_t, n_s):
+    rng = np.random.default_rng(0x2C0)
+    sx = rng.uniform(-1, 1, (n_s, d_inner, d_conv - 1 + n_t))
+    w = rng.uniform(-1, 1, (d_inner, d_conv))
     got = oracle.conv_fwd(sx, w)
-    assert got.shape == (n_s, n_t, d_inner)   # ne [d_inner, n_t, n_s]
-    np.testing.assert_allclose(got.ravel(), _r_style_conv(sx_v, c_v, d_conv, d_inner, n_t, n_s),
-                               rtol=1e-14, atol=1e-15)
+    assert got.shape == (n_s, n_t, d_inner)
+    np.testing.assert_allclose(got, _depthwise_reference(sx, w), rtol=1e-14, atol=1e-15)
+    # a single unit tap at position j picks the input j places after the window start
+    for j in range(d_conv):
+        e = np.zeros((d_inner, d_conv))
+        e[:, j] = 1.0
+        np.testing.assert_array_equal(oracle.conv_fwd(sx, e),
+                                      np.transpose(sx[:, :, j:j + n_t], (0, 2, 1)))
     got_silu = oracle.conv_fwd(sx, w, apply_silu=True)
-    pre = got.ravel()
-    np.testing.assert_allclose(got_silu.ravel(), pre * expit(pre), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(got_silu, got * expit(got), rtol=1e-13, atol=1e-15)
 
 
 def test_fused_conv_silu_feeds_scan():
@@ -82,7 +80,7 @@ def test_fused_conv_silu_feeds_scan():
     x = x[..., 0]
     for i, r in enumerate(p.ids):
         sx = np.concatenate([cs[r], x[i].T], axis=1)[None]    # [1][H][K-1+L]
-        pre = _r_style_conv(sx.ravel(), w.ravel(), 4, 3, 7, 1).reshape(7, 3)
+        pre = _depthwise_reference(sx, w)[0]
         np.testing.assert_allclose(y[i, :, :, 0], pre * expit(pre), rtol=1e-13, atol=1e-15)
         # conv_state_out: the last K-1 inputs, oldest first
         np.testing.assert_array_equal(cso[i], sx[0][:, -3:])
