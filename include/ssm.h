@@ -188,6 +188,28 @@ int selective_scan_fwd(const ssm_scan_desc *desc, const float *s, const void *x,
                        const float *conv_state, void *out, float *conv_state_out,
                        void *workspace, size_t workspace_bytes, ssm_stream_t stream);
 
+/* selective_scan_fwd_static: selective_scan_fwd for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It takes no workspace: its scratch (the
+ * time-chunk carries of the chunked kernels and the device-error word) is a
+ * 32 MiB array of static device memory inside the library, which each GPU
+ * holds from the first call on it until the process ends.  It calls no
+ * hipMalloc, hipFree or other allocating routine.
+ *  - Arguments, results and kernels are those of selective_scan_fwd.
+ *  - err (nullable): a caller-owned device word that receives the
+ *    SSM_DEVERR_* bits (set, never cleared); without it they are dropped.
+ *  - A call whose ssm_scan_workspace_bytes(desc, 0) exceeds 32 MiB returns
+ *    SSM_ERR_WORKSPACE before anything is launched.
+ *  - Every call on one GPU shares that GPU's scratch: calls that overlap in
+ *    time on one GPU (on different streams, or from several host threads
+ *    without ordering) race on it.  Calls queued on one stream are ordered
+ *    and safe.  Nothing in the scratch needs to start at zero. */
+int selective_scan_fwd_static(const ssm_scan_desc *desc, const float *s, const void *x,
+                              const void *dt, const float *A, const void *B, const void *C,
+                              const float *D, const int32_t *ids, const float *conv_w,
+                              const float *conv_state, void *out, float *conv_state_out,
+                              uint32_t *err, ssm_stream_t stream);
+
 /* Extras of selective_scan_fwd_ext.  Every pointer may be NULL (feature off).
  *  - dt_bias [n_head] f32: added to dt before softplus, as the step of
  *    "mambazip mamba1/model.rs" (forward_impl) does: dt = softplus(dt_raw +

@@ -23,7 +23,8 @@ EXPORTS = ("ssm_status_str", "ssm_version", "ssm_scan_out_bytes", "ssm_scan_stat
            "ssm_scan_dgrad_layout", "ssm_scan_workspace_bytes", "ssm_conv_fwd",
            "ssm_conv_bwd_workspace_bytes", "ssm_conv_bwd", "selective_scan_fwd",
            "selective_scan_bwd", "selective_state_update", "ssm_get_device_error",
-           "ssm_scan_ext_out_bytes", "selective_scan_fwd_ext", "ssm_scan_fwd_plan")
+           "ssm_scan_ext_out_bytes", "selective_scan_fwd_ext", "ssm_scan_fwd_plan",
+           "selective_scan_fwd_static")
 
 
 class SsmError(RuntimeError):
@@ -89,6 +90,8 @@ def load():
         lib.ssm_scan_ext_out_bytes.restype = SZ
         lib.selective_scan_fwd_ext.argtypes = [D, E] + [P] * 13 + [SZ, P]
         lib.selective_scan_fwd_ext.restype = ctypes.c_int
+        lib.selective_scan_fwd_static.argtypes = [D] + [P] * 13 + [P]
+        lib.selective_scan_fwd_static.restype = ctypes.c_int
         lib.ssm_scan_fwd_plan.argtypes = [D, E]
         lib.ssm_scan_fwd_plan.restype = ctypes.c_char_p
         lib.ssm_get_device_error.argtypes = [P, P, ctypes.POINTER(ctypes.c_uint32)]
@@ -172,6 +175,15 @@ def selective_scan_fwd(desc, s, x, dt, A, B, C, D, ids, conv_w, conv_state, out,
                                    _ptr(conv_state), _ptr(out), _ptr(conv_state_out),
                                    _ptr(workspace), int(workspace_bytes), _stream(stream))
     return _check(rc, "selective_scan_fwd")
+
+
+def selective_scan_fwd_static(desc, s, x, dt, A, B, C, D, ids, conv_w, conv_state, out,
+                              conv_state_out, err=None, stream=None):
+    rc = load().selective_scan_fwd_static(ctypes.byref(desc), _ptr(s), _ptr(x), _ptr(dt), _ptr(A),
+                                          _ptr(B), _ptr(C), _ptr(D), _ptr(ids), _ptr(conv_w),
+                                          _ptr(conv_state), _ptr(out), _ptr(conv_state_out),
+                                          _ptr(err), _stream(stream))
+    return _check(rc, "selective_scan_fwd_static")
 
 
 def make_ext(dt_bias=None, z=None, cu_seqlens=None, total_tokens=0) -> SsmScanExt:

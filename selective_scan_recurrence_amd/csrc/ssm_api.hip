@@ -4,6 +4,8 @@
 #include <limits.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "ssm_internal.h"
 
 namespace ssm {
@@ -187,7 +189,8 @@ int check_ext(const Shape& sh, const ssm_scan_ext* ext, int64_t* T) {
 int fwd_impl(const ssm_scan_desc* desc, const ssm_scan_ext* ext, const float* s, const void* x,
              const void* dt, const float* A, const void* B, const void* C, const float* D,
              const int32_t* ids, const float* conv_w, const float* conv_state, void* out,
-             float* conv_state_out, void* workspace, size_t workspace_bytes_, hipStream_t stream) {
+             float* conv_state_out, void* workspace, size_t workspace_bytes_, hipStream_t stream,
+             uint32_t* err_word = nullptr) {
     Shape sh;
     int rc = check_desc(desc, &sh);
     if (rc) return rc;
@@ -210,7 +213,7 @@ int fwd_impl(const ssm_scan_desc* desc, const ssm_scan_ext* ext, const float* s,
         (D && !aligned(D, 4)) || (conv_w && !aligned(conv_w, 4)) ||
         (conv_state && !aligned(conv_state, 4)) || (conv_state_out && !aligned(conv_state_out, 4)) ||
         !aligned(workspace, 256) || !aligned(z, es) || (ext && !aligned(ext->dt_bias, 4)) ||
-        !aligned(cu, 4))
+        !aligned(cu, 4) || !aligned(err_word, 4))
         return SSM_ERR_ALIGN;
     char* state_block = static_cast<char*>(out) + (size_t)(T * sh.d_inner()) * es;
     if (!aligned(state_block, 4)) return SSM_ERR_ALIGN;
@@ -220,7 +223,7 @@ int fwd_impl(const ssm_scan_desc* desc, const ssm_scan_ext* ext, const float* s,
     a.ids = ids; a.conv_w = sh.K ? conv_w : nullptr; a.conv_state = sh.K ? conv_state : nullptr;
     a.y = out; a.state_out = reinterpret_cast<float*>(state_block);
     a.conv_state_out = sh.K ? conv_state_out : nullptr;
-    a.err = static_cast<uint32_t*>(workspace);
+    a.err = err_word ? err_word : static_cast<uint32_t*>(workspace);
     a.ws = static_cast<char*>(workspace) + kErrBytes;
     a.ws_bytes = workspace_bytes_ - kErrBytes;
     a.dt_bias = ext ? ext->dt_bias : nullptr;
@@ -230,10 +233,53 @@ int fwd_impl(const ssm_scan_desc* desc, const ssm_scan_ext* ext, const float* s,
     return launch_scan_fwd(a, stream);
 }
 
+// Device scratch of selective_scan_fwd_static: a file-scope array each GPU
+// holds for the life of the process.  Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in for the symbol): the
+// device address comes from hipGetSymbolAddress, looked up once per device
+// with that device current, and is kept in static_scratch_ptr.
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+static __device__ __attribute__((aligned(256))) char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex static_scratch_mu;
+void* static_scratch_ptr[kMaxDevices] = {};
+
+int static_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SSM_ERR_HIP;
+    std::lock_guard<std::mutex> lock(static_scratch_mu);
+    if (!static_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SSM_ERR_HIP;
+        static_scratch_ptr[dev] = ptr;
+    }
+    *out = static_scratch_ptr[dev];
+    return SSM_OK;
+}
+
 }  // namespace
 }  // namespace ssm
 
 extern "C" {
+
+int selective_scan_fwd_static(const ssm_scan_desc* desc, const float* s, const void* x,
+                              const void* dt, const float* A, const void* B, const void* C,
+                              const float* D, const int32_t* ids, const float* conv_w,
+                              const float* conv_state, void* out, float* conv_state_out,
+                              uint32_t* err, ssm_stream_t stream) {
+    Shape sh;
+    int rc = check_desc(desc, &sh);
+    if (rc) return rc;
+    // the call's workspace must fit the static scratch; checked before any HIP call
+    const size_t need = workspace_bytes(sh, 0);
+    if (need > kStaticScratchBytes) return SSM_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if ((rc = static_scratch(&ws))) return rc;
+    // without a caller's error word, the bits go to the scratch's own word (never read)
+    return fwd_impl(desc, nullptr, s, x, dt, A, B, C, D, ids, conv_w, conv_state, out,
+                    conv_state_out, ws, kStaticScratchBytes, static_cast<hipStream_t>(stream), err);
+}
 
 int selective_scan_fwd(const ssm_scan_desc* desc, const float* s, const void* x, const void* dt,
                        const float* A, const void* B, const void* C, const float* D,
