@@ -78,7 +78,7 @@ def _load():
             P = ctypes.c_void_p
             lib.oracle_scan_fwd.argtypes = [ctypes.POINTER(_Dims), P] + [P] * 13 + [ctypes.c_int]
             lib.oracle_scan_fwd.restype = ctypes.c_int
-            lib.oracle_scan_bwd.argtypes = [ctypes.POINTER(_Dims), P] + [P] * 17 + [ctypes.c_int]
+            lib.oracle_scan_bwd.argtypes = [ctypes.POINTER(_Dims), P] + [P] * 21 + [ctypes.c_int]
             lib.oracle_scan_bwd.restype = ctypes.c_int
             lib.oracle_conv_fwd.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int64,
                                             ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
@@ -210,28 +210,37 @@ def scan_fwd_ext(s, x, dt, A, B, C, D, ids, *, cu_seqlens=None, dt_bias=None, z=
     return y, st, cso
 
 
-def scan_bwd(s, x, dt, A, B, C, D, ids, dy, dstate, *, dt_softplus=False,
-             grp_of_head=None, n_threads: Optional[int] = None):
-    """Reverse-time adjoint of ``scan_fwd`` without the fused conv.
+def scan_bwd(s, x, dt, A, B, C, D, ids, dy, dstate, *, conv_w=None, conv_state=None,
+             dt_softplus=False, grp_of_head=None, n_threads: Optional[int] = None):
+    """Reverse-time adjoint of ``scan_fwd``.
 
-    Returns a dict with d_s, d_x, d_dt, d_A, d_B, d_C and d_D (None without D).
+    Returns a dict with d_s, d_x, d_dt, d_A, d_B, d_C and d_D (None without D);
+    with the fused conv (conv_w [H][K], head_dim 1; conv_state [R][H][K-1] or
+    None for zeros) d_x is the gradient of the pre-conv input and the dict
+    also holds d_conv_w [H][K] and d_conv_state [R][H][K-1].
     """
     s, x, dt, A, B, C, D, dy, dstate = map(_f64, (s, x, dt, A, B, C, D, dy, dstate))
+    conv_w, conv_state = _f64(conv_w), _f64(conv_state)
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     S, L, H, P = x.shape
     R, N = s.shape[0], s.shape[3]
     G = B.shape[2]
+    K = 0 if conv_w is None else conv_w.shape[1]
     grp = group_of_head(H, G) if grp_of_head is None else np.ascontiguousarray(grp_of_head, np.int64)
-    d = _dims(S, L, H, P, N, G, R, A.ndim == 2, 0, D is not None, dt_softplus)
+    d = _dims(S, L, H, P, N, G, R, A.ndim == 2, K, D is not None, dt_softplus)
     out = dict(d_s=np.zeros_like(s), d_x=np.zeros_like(x), d_dt=np.zeros_like(dt),
                d_A=np.zeros_like(A), d_B=np.zeros_like(B), d_C=np.zeros_like(C),
-               d_D=None if D is None else np.zeros_like(D))
+               d_D=None if D is None else np.zeros_like(D),
+               d_conv_w=np.zeros((H, K)) if K else None,
+               d_conv_state=np.zeros((R, H, K - 1)) if K else None)
     lib = _load()
     rc = lib.oracle_scan_bwd(ctypes.byref(d), _ptr(grp), _ptr(s), _ptr(x), _ptr(dt), _ptr(A),
-                             _ptr(B), _ptr(C), _ptr(D), _ptr(ids), _ptr(dy), _ptr(dstate),
+                             _ptr(B), _ptr(C), _ptr(D), _ptr(ids), _ptr(conv_w), _ptr(conv_state),
+                             _ptr(dy), _ptr(dstate),
                              _ptr(out["d_s"]), _ptr(out["d_x"]), _ptr(out["d_dt"]),
                              _ptr(out["d_A"]), _ptr(out["d_B"]), _ptr(out["d_C"]),
-                             _ptr(out["d_D"]), n_threads or default_threads())
+                             _ptr(out["d_D"]), _ptr(out["d_conv_w"]), _ptr(out["d_conv_state"]),
+                             n_threads or default_threads())
     if rc:
         raise ValueError(f"oracle_scan_bwd failed ({rc})")
     return out
@@ -324,4 +333,6 @@ def problem_fwd(prob, n_threads=None):
 def problem_bwd(prob, n_threads=None):
     v = prob.value
     return scan_bwd(v("s"), v("x"), v("dt"), v("A"), v("B"), v("C"), v("D"), prob.ids,
-                    v("dy"), v("dstate"), dt_softplus=prob.dt_softplus, n_threads=n_threads)
+                    v("dy"), v("dstate"), conv_w=v("conv_w") if prob.d_conv else None,
+                    conv_state=v("conv_state") if prob.d_conv else None,
+                    dt_softplus=prob.dt_softplus, n_threads=n_threads)

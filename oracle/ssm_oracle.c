@@ -23,6 +23,11 @@
  *    ggml_ssm_conv_back packs the gradient of sx then that of the conv
  *    weights; its tests compare both with a central difference and give the
  *    weight gradient of loss = sum(output) in closed form.
+ *  - The backward of the fused conv + SiLU is the chain rule through the
+ *    forward above (the d_conv-1 conv-state inputs, then the tokens; SiLU's
+ *    derivative sigma(c)(1 + c(1 - sigma(c))); each tap's adjoint), in the
+ *    order the ggmlR page's ssm_conv backward block fixes for the
+ *    standalone op: the gradient of the inputs, then of the conv weights.
  *  - "mambazip mamba1/model.rs", forward_impl's single-token step: the conv
  *    window of the last d_conv-1 inputs plus the new one (depthwise_conv_step),
  *    SiLU, dt = softplus(dt_raw + dt_bias), the in-place state update of
@@ -60,7 +65,7 @@ typedef struct {
     double *y, *state_out, *conv_state_out;
     /* backward inputs / outputs */
     const double *dy, *dstate;
-    double *d_s, *d_x, *d_dt, *d_A, *d_D;
+    double *d_s, *d_x, *d_dt, *d_A, *d_D, *d_conv_w, *d_conv_state;
     double *dB_part, *dC_part; /* [n_threads][n_seqs][L][G][N] */
     int n_threads;
     int tid;
@@ -75,19 +80,29 @@ static double silu(double c) { return c / (1.0 + exp(-c)); }
  * conv (Mamba-1 form only, head_dim 1): the causal depthwise conv over the
  * sequence x[i][.][h] preceded by the d_conv-1 conv-state values (zeros when
  * no conv state is given), then SiLU.  win holds those d_conv-1 values. */
+/* Input tau of the conv of sequence i, head h: tau < 0 reads the conv state. */
+static double conv_in(const job_t *J, int64_t i, int64_t tau, int64_t h, const double *win) {
+    const oracle_dims *d = J->d;
+    return tau < 0 ? win[tau + d->d_conv - 1] : J->x[(i * d->n_tokens + tau) * d->n_head + h];
+}
+
+/* The conv's output (SiLU's argument) at token t. */
+static double conv_pre(const job_t *J, int64_t i, int64_t t, int64_t h, const double *win) {
+    const int64_t K = J->d->d_conv;
+    double c = 0.0;
+    for (int64_t j = 0; j < K; j++) {
+        int64_t tau = t - (K - 1) + j; /* tap j reads input tau; tap K-1 the newest */
+        c += J->conv_w[h * K + j] * conv_in(J, i, tau, h, win);
+    }
+    return c;
+}
+
 static double scan_input(const job_t *J, int64_t i, int64_t t, int64_t h, int64_t p,
                          const double *win) {
     const oracle_dims *d = J->d;
     const int64_t L = d->n_tokens, H = d->n_head, P = d->head_dim;
     if (!d->d_conv) return J->x[((i * L + t) * H + h) * P + p];
-    const int64_t K = d->d_conv;
-    double c = 0.0;
-    for (int64_t j = 0; j < K; j++) {
-        int64_t tau = t - (K - 1) + j; /* tap j reads input tau; tap K-1 the newest */
-        double xv = tau < 0 ? win[tau + K - 1] : J->x[(i * L + tau) * H + h];
-        c += J->conv_w[h * K + j] * xv;
-    }
-    return silu(c);
+    return silu(conv_pre(J, i, t, h, win));
 }
 
 static double dt_at(const job_t *J, int64_t i, int64_t t, int64_t h) {
@@ -146,10 +161,11 @@ static void forward_head(const job_t *J, int64_t h, double *st, double *win) {
 
 /* Backward of one head: recompute the states h_{-1..L-1} of each row, then
  * run the adjoint recurrence from the last token to the first. */
-static void backward_head(const job_t *J, int64_t h, double *hs, double *g) {
+static void backward_head(const job_t *J, int64_t h, double *hs, double *g, double *du_t,
+                          double *win) {
     const oracle_dims *d = J->d;
     const int64_t L = d->n_tokens, H = d->n_head, P = d->head_dim, N = d->d_state,
-                  G = d->n_group;
+                  G = d->n_group, K = d->d_conv;
     const int64_t grp = J->grp_of_head[h];
     double *dB = J->dB_part + (int64_t)J->tid * d->n_seqs * L * G * N;
     double *dC = J->dC_part + (int64_t)J->tid * d->n_seqs * L * G * N;
@@ -159,8 +175,9 @@ static void backward_head(const job_t *J, int64_t h, double *hs, double *g) {
         for (int64_t p = 0; p < P; p++) {
             /* hs[(t+1)*N + n] = h_t[n]; hs[0..N) = initial state */
             for (int64_t n = 0; n < N; n++) hs[n] = J->s[((r * H + h) * P + p) * N + n];
+            if (K) load_window(J, r, h, win);
             for (int64_t t = 0; t < L; t++) {
-                const double u = J->x[((i * L + t) * H + h) * P + p];
+                const double u = scan_input(J, i, t, h, p, win);
                 const double dtv = dt_at(J, i, t, h);
                 const double *Bt = J->B + ((i * L + t) * G + grp) * N;
                 for (int64_t n = 0; n < N; n++)
@@ -170,7 +187,7 @@ static void backward_head(const job_t *J, int64_t h, double *hs, double *g) {
             /* g = dL/dh_t, seeded with the upstream gradient of the final state */
             for (int64_t n = 0; n < N; n++) g[n] = J->dstate[((i * H + h) * P + p) * N + n];
             for (int64_t t = L - 1; t >= 0; t--) {
-                const double u = J->x[((i * L + t) * H + h) * P + p];
+                const double u = scan_input(J, i, t, h, p, win);
                 const double dtv = dt_at(J, i, t, h);
                 const double dyt = J->dy[((i * L + t) * H + h) * P + p];
                 const double *Bt = J->B + ((i * L + t) * G + grp) * N;
@@ -196,9 +213,34 @@ static void backward_head(const job_t *J, int64_t h, double *hs, double *g) {
                 }
                 if (d->dt_softplus) ddt *= sigmoid(J->dt[(i * L + t) * H + h]);
                 J->d_dt[(i * L + t) * H + h] += ddt;
-                J->d_x[((i * L + t) * H + h) * P + p] = du;
+                if (K) du_t[t] = du;  /* dL/du_t; the conv adjoint follows */
+                else J->d_x[((i * L + t) * H + h) * P + p] = du;
             }
             for (int64_t n = 0; n < N; n++) J->d_s[((r * H + h) * P + p) * N + n] += g[n];
+            if (K) {
+                /* u_t = SiLU(c_t): dL/dc_t = dL/du_t sigma(c_t) (1 + c_t (1 - sigma(c_t))) */
+                for (int64_t t = 0; t < L; t++) {
+                    const double c = conv_pre(J, i, t, h, win);
+                    const double sg = sigmoid(c);
+                    du_t[t] *= sg * (1.0 + c * (1.0 - sg));
+                }
+                /* c_t = sum_j w[j] in(t - (K-1) + j): input tau feeds tokens tau + K-1 - j */
+                for (int64_t tau = -(K - 1); tau < L; tau++) {
+                    double gin = 0.0;
+                    for (int64_t j = 0; j < K; j++) {
+                        const int64_t t = tau + (K - 1) - j;
+                        if (t >= 0 && t < L) gin += J->conv_w[h * K + j] * du_t[t];
+                    }
+                    if (tau >= 0) J->d_x[(i * L + tau) * H + h] = gin;
+                    else J->d_conv_state[(r * H + h) * (K - 1) + tau + K - 1] += gin;
+                }
+                for (int64_t j = 0; j < K; j++) {
+                    double gw = 0.0;
+                    for (int64_t t = 0; t < L; t++)
+                        gw += du_t[t] * conv_in(J, i, t - (K - 1) + j, h, win);
+                    J->d_conv_w[h * K + j] += gw;
+                }
+            }
         }
     }
     if (d->has_D) J->d_D[h] += dD_h;
@@ -208,22 +250,29 @@ static void *worker(void *arg) {
     job_t *J = (job_t *)arg;
     const oracle_dims *d = J->d;
     const int64_t N = d->d_state, L = d->n_tokens;
-    double *buf = NULL, *buf2 = NULL;
+    double *buf = NULL, *buf2 = NULL, *buf3 = NULL;
+    double *win = (double *)malloc(sizeof(double) * (size_t)(d->d_conv > 1 ? d->d_conv : 1));
     if (J->backward) {
         buf = (double *)malloc(sizeof(double) * (size_t)((L + 1) * N));
         buf2 = (double *)malloc(sizeof(double) * (size_t)N);
+        buf3 = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
     } else {
         buf = (double *)malloc(sizeof(double) * (size_t)N);
-        buf2 = (double *)malloc(sizeof(double) * (size_t)(d->d_conv > 1 ? d->d_conv : 1));
+        buf2 = buf3 = (double *)malloc(sizeof(double));
     }
-    if (!buf || !buf2) { free(buf); free(buf2); return (void *)1; }
+    if (!buf || !buf2 || !buf3 || !win) {
+        free(buf); free(buf2); if (J->backward) free(buf3); free(win);
+        return (void *)1;
+    }
     /* static partition of heads: thread tid takes heads tid, tid+T, ... */
     for (int64_t h = J->tid; h < d->n_head; h += J->n_threads) {
-        if (J->backward) backward_head(J, h, buf, buf2);
-        else forward_head(J, h, buf, buf2);
+        if (J->backward) backward_head(J, h, buf, buf2, buf3, win);
+        else forward_head(J, h, buf, win);
     }
     free(buf);
     free(buf2);
+    if (J->backward) free(buf3);
+    free(win);
     return NULL;
 }
 
@@ -290,23 +339,27 @@ int oracle_scan_fwd(const oracle_dims *d, const int64_t *grp_of_head, const doub
     return run_jobs(&J, n_threads);
 }
 
-/* Backward (no fused conv: x is the scan input).  Outputs are overwritten:
- * d_s [n_state_rows][H][P][N] (rows not referenced by ids are zero, repeated
- * ids accumulate), d_x like x, d_dt like dt, d_A like A, d_B/d_C like B/C,
- * d_D [H] (only when has_D). */
+/* Backward.  Outputs are overwritten: d_s [n_state_rows][H][P][N] (rows not
+ * referenced by ids are zero, repeated ids accumulate), d_x like x (with the
+ * fused conv: the gradient of the pre-conv input x), d_dt like dt, d_A like
+ * A, d_B/d_C like B/C, d_D [H] (only when has_D); with the fused conv also
+ * d_conv_w [H][K] and d_conv_state [n_state_rows][H][K-1] (the gradient of
+ * the gathered conv-state inputs, scattered to rows ids[i]; conv_state may
+ * be NULL for zeros). */
 int oracle_scan_bwd(const oracle_dims *d, const int64_t *grp_of_head, const double *s,
                     const double *x, const double *dt, const double *A, const double *B,
                     const double *C, const double *D, const int32_t *ids,
+                    const double *conv_w, const double *conv_state,
                     const double *dy, const double *dstate, double *d_s, double *d_x,
                     double *d_dt, double *d_A, double *d_B, double *d_C, double *d_D,
-                    int n_threads) {
+                    double *d_conv_w, double *d_conv_state, int n_threads) {
     int rc = check_dims(d, grp_of_head, ids);
     if (rc) return rc;
-    if (d->d_conv) return -3;
     if (!s || !x || !dt || !A || !B || !C || !dy || !dstate || !d_s || !d_x || !d_dt ||
         !d_A || !d_B || !d_C)
         return -1;
     if (d->has_D && (!D || !d_D)) return -1;
+    if (d->d_conv && (!conv_w || !d_conv_w || !d_conv_state)) return -1;
     const int64_t H = d->n_head, P = d->head_dim, N = d->d_state, L = d->n_tokens,
                   G = d->n_group, S = d->n_seqs;
     memset(d_s, 0, sizeof(double) * (size_t)(d->n_state_rows * H * P * N));
@@ -314,6 +367,10 @@ int oracle_scan_bwd(const oracle_dims *d, const int64_t *grp_of_head, const doub
     memset(d_dt, 0, sizeof(double) * (size_t)(S * L * H));
     memset(d_A, 0, sizeof(double) * (size_t)(d->a_per_state ? H * N : H));
     if (d->has_D) memset(d_D, 0, sizeof(double) * (size_t)H);
+    if (d->d_conv) {
+        memset(d_conv_w, 0, sizeof(double) * (size_t)(H * d->d_conv));
+        memset(d_conv_state, 0, sizeof(double) * (size_t)(d->n_state_rows * H * (d->d_conv - 1)));
+    }
     int T = oracle_threads_used(d, n_threads);
     const size_t part = (size_t)(S * L * G * N);
     double *dBp = (double *)calloc(part * (size_t)T, sizeof(double));
@@ -323,7 +380,9 @@ int oracle_scan_bwd(const oracle_dims *d, const int64_t *grp_of_head, const doub
     memset(&J, 0, sizeof J);
     J.d = d; J.grp_of_head = grp_of_head; J.s = s; J.x = x; J.dt = dt; J.A = A;
     J.B = B; J.C = C; J.D = D; J.ids = ids; J.dy = dy; J.dstate = dstate;
+    J.conv_w = conv_w; J.conv_state = conv_state;
     J.d_s = d_s; J.d_x = d_x; J.d_dt = d_dt; J.d_A = d_A; J.d_D = d_D;
+    J.d_conv_w = d_conv_w; J.d_conv_state = d_conv_state;
     J.dB_part = dBp; J.dC_part = dCp; J.backward = 1;
     rc = run_jobs(&J, T);
     /* fixed-order reduction of the per-thread partial sums */

@@ -39,6 +39,15 @@ MUTANTS = {
     "conv_bwd_dw_window_shift": ("d_w[ch * d_conv + j] += g * row[t + j];",
                                  "d_w[ch * d_conv + j] += g * row[t + d_conv - 1 - j];"),
     "conv_bwd_silu_derivative_is_sigmoid": ("g *= sg * (1.0 + z * (1.0 - sg));", "g *= sg;"),
+    "fused_bwd_silu_derivative_is_sigmoid": ("du_t[t] *= sg * (1.0 + c * (1.0 - sg));",
+                                             "du_t[t] *= sg;"),
+    "fused_bwd_tap_reversed": ("if (t >= 0 && t < L) gin += J->conv_w[h * K + j] * du_t[t];",
+                               "if (t >= 0 && t < L) gin += J->conv_w[h * K + (K - 1 - j)] * du_t[t];"),
+    "fused_bwd_conv_state_to_sequence_row": (
+        "else J->d_conv_state[(r * H + h) * (K - 1) + tau + K - 1] += gin;",
+        "else J->d_conv_state[(i * H + h) * (K - 1) + tau + K - 1] += gin;"),
+    "fused_bwd_dw_window_shift": ("gw += du_t[t] * conv_in(J, i, t - (K - 1) + j, h, win);",
+                                  "gw += du_t[t] * conv_in(J, i, t - j, h, win);"),
     "decode_ring_not_shifted": ("for (int64_t j = 0; j + 1 < K - 1; j++) cs[j] = cs[j + 1];", ""),
     "decode_newest_tap_first": ("return c + w[K - 1] * xin;", "return c + w[0] * xin;"),
     "decode_gate_is_sigmoid": ("if (z) acc *= silu(z[(i * H + h) * P + p]);",
@@ -62,7 +71,8 @@ def test_pins_catch_planted_mistake(name, tmp_path):
                            "-lm", "-lpthread"])
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
                         "tests/test_oracle_pins.py", "tests/test_oracle_bwd_pins.py",
-                        "tests/test_oracle_conv_bwd_pins.py", "tests/test_oracle_decode_pins.py"],
+                        "tests/test_oracle_conv_bwd_pins.py", "tests/test_oracle_decode_pins.py",
+                        "tests/test_oracle_fused_bwd_pins.py"],
                        cwd=ROOT, env=dict(os.environ, SSM_ORACLE_LIB=str(so)),
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
