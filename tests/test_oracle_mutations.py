@@ -15,7 +15,8 @@ SRC = os.path.join(ROOT, "oracle", "ssm_oracle.c")
 
 MUTANTS = {
     "drop_D": ("if (d->has_D) yv += J->D[h] * u;", ""),
-    "tap_reversed": ("c += J->conv_w[h * K + j] * xv;", "c += J->conv_w[h * K + (K - 1 - j)] * xv;"),
+    "tap_reversed": ("c += J->conv_w[h * K + j] * conv_in(J, i, tau, h, win);",
+                     "c += J->conv_w[h * K + (K - 1 - j)] * conv_in(J, i, tau, h, win);"),
     "conv_window_off_by_one": ("int64_t tau = t - (K - 1) + j;", "int64_t tau = t - K + j;"),
     "B_C_swapped": ("yv += Ct[n] * st[n];", "yv += Bt[n] * st[n];"),
     "dt_missing_from_input": ("st[n] = decay * st[n] + dtv * Bt[n] * u;",
