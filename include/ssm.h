@@ -118,9 +118,11 @@ size_t ssm_scan_state_offset_bytes(const ssm_scan_desc *desc);
 /* Packed gradient of selective_scan_bwd, all f32, in the order of ggml's
  * ssm_scan_back ("ggml_ssm_scan_back packs all six input gradients"):
  * d_s (shape of s) | d_x | d_dt | d_A | d_B | d_C, then d_D [n_head] when
- * SSM_HAS_D.  offsets[k] (k = 0..6) receives the byte offset of block k
- * (d_D's offset equals the total when there is no D); returns the total
- * size in bytes, 0 if the descriptor is invalid. */
+ * SSM_HAS_D, then with d_conv > 0 (selective_scan_bwd_conv) d_conv_w
+ * [n_head][d_conv] and d_conv_state [n_state_rows][n_head][d_conv-1].
+ * offsets[k] (k = 0..6) receives the byte offset of block k (d_D's offset
+ * is the end of d_C; the conv blocks follow d_D, or d_C without D); returns
+ * the total size in bytes, 0 if the descriptor is invalid. */
 size_t ssm_scan_dgrad_layout(const ssm_scan_desc *desc, size_t offsets[7]);
 
 /* Workspace the compute calls need (bytes, a multiple of 256).  backward = 0
@@ -271,30 +273,59 @@ int selective_scan_fwd_ext(const ssm_scan_desc *desc, const ssm_scan_ext *ext, c
 const char *ssm_scan_fwd_plan(const ssm_scan_desc *desc, const ssm_scan_ext *ext);
 
 /* selective_scan_bwd: reverse-time adjoint of selective_scan_fwd without the
- * fused conv (d_conv must be 0).  dout is packed like the forward result
- * (dy in io, then dstate in f32).  dgrad receives the packed f32 gradient
- * (see ssm_scan_dgrad_layout).  Rows of d_s no id refers to are zero;
- * repeated ids accumulate.  A sequence whose id is outside [0, n_state_rows)
- * sets SSM_DEVERR_IDS, adds nothing to d_s, and has its d_x and d_dt written
- * as NaN; sums it takes part in that depend on its initial state (d_A, d_C)
- * are NaN as well.
- * Supported: the Mamba-1 form with d_state <= 16 and one group, and the
- * Mamba-2 form (A per head) with bf16 io, head_dim 32 or 64, d_state 64 or
- * 128 and 16-byte aligned x, dout, B, C, s and dgrad; other shapes return
- * SSM_ERR_UNSUPPORTED.  The adjoint is the one of "kizzasi-model
- * backprop_ssm.rs" (ssm_backward): dL/dh_{t-1} = a_t dL/dh_t + C_{t-1} dy_{t-1},
- * with the per-element terms of "mambazip mamba1/model.rs"
- * (accumulate_token_step_gradients).  Mamba-1: sums over channels and tokens
- * are taken in a fixed order, so results are bitwise repeatable.  Mamba-2:
- * the products run on bf16 MFMA operands (the carried gradient and the
- * checkpointed state as bf16 pairs) with fp32 accumulation, and d_B and d_C
- * collect the heads of a group with fp32 atomic adds, whose order (and so
- * their last bits) varies from run to run. 
+ * fused conv (d_conv must be 0; selective_scan_bwd_conv takes the fused
+ * layer).  dout is packed like the forward result (dy in io, then dstate in
+ * f32).  dgrad receives the packed f32 gradient (see ssm_scan_dgrad_layout).
+ * Rows of d_s no id refers to are zero; repeated ids accumulate.  A sequence
+ * whose id is outside [0, n_state_rows) sets SSM_DEVERR_IDS, adds nothing to
+ * d_s, and has its d_x and d_dt written as NaN; sums it takes part in that
+ * depend on its initial state (d_A, d_C) are NaN as well.
+ * Every shape selective_scan_fwd takes is supported.  The adjoint is the one
+ * of "kizzasi-model backprop_ssm.rs" (ssm_backward): dL/dh_{t-1} = a_t dL/dh_t +
+ * C_{t-1} dy_{t-1}, with the per-element terms of "mambazip mamba1/model.rs"
+ * (accumulate_token_step_gradients).  Kernels:
+ *  - the Mamba-1 form with d_state <= 16 and one group: a checkpointed
+ *    recompute in the forward's four-lanes-per-channel layout;
+ *  - the Mamba-2 form with bf16 io, head_dim 32 or 64, d_state 64 or 128 and
+ *    16-byte aligned x, dout, B, C, s and dgrad: chunked products on bf16
+ *    MFMA operands (the carried gradient and the checkpointed state as bf16
+ *    pairs) with fp32 accumulation; d_B and d_C collect the heads of a group
+ *    with fp32 atomic adds, whose order (and so their last bits) varies from
+ *    run to run;
+ *  - every other shape: one lane group per (sequence, channel) row with
+ *    fp32 arithmetic.
+ * Apart from the d_B/d_C of the MFMA path, every sum over channels, tokens
+ * or sequences is taken in a fixed order, so results are bitwise repeatable.
  * workspace: ssm_scan_workspace_bytes(desc, 1) bytes, 256-byte aligned. */
 int selective_scan_bwd(const ssm_scan_desc *desc, const float *s, const void *x,
                        const void *dt, const float *A, const void *B, const void *C,
                        const float *D, const int32_t *ids, const void *dout, float *dgrad,
                        void *workspace, size_t workspace_bytes, ssm_stream_t stream);
+
+/* selective_scan_bwd_conv: the backward of the fused layer, causal conv +
+ * SiLU + scan (selective_scan_fwd with d_conv > 0): the chain rule through
+ * the scan (as selective_scan_bwd), SiLU (derivative sigma(c)(1 + c(1 -
+ * sigma(c))) at the pre-activation recomputed from x, conv_state and conv_w)
+ * and the depthwise conv in ggml's tap order ("ggmlR
+ * tests/testthat/test-ssm-rwkv.R", ssm_conv and its backward block, which
+ * packs the gradient of the inputs before that of the weights).
+ *  - Arguments as selective_scan_bwd plus the forward's conv_w [n_head]
+ *    [d_conv] (required when d_conv > 0) and conv_state [n_state_rows]
+ *    [n_head][d_conv-1] (NULL: zeros).  With d_conv = 0 it equals
+ *    selective_scan_bwd.
+ *  - d_x in dgrad is the gradient of the pre-conv input x.  After d_D the
+ *    packed gradient holds d_conv_w [n_head][d_conv] and d_conv_state
+ *    [n_state_rows][n_head][d_conv-1]: the gradient of the conv-state row
+ *    each sequence gathered (rows no id names are zero, repeated ids
+ *    accumulate).  The gradient of the forward's conv_state_out output is
+ *    not an input (taken as zero).
+ *  - d_conv 2..4.  A bad id also makes d_conv_w NaN (its inputs are unknown).
+ * workspace: ssm_scan_workspace_bytes(desc, 1) bytes, 256-byte aligned. */
+int selective_scan_bwd_conv(const ssm_scan_desc *desc, const float *s, const void *x,
+                            const void *dt, const float *A, const void *B, const void *C,
+                            const float *D, const int32_t *ids, const float *conv_w,
+                            const float *conv_state, const void *dout, float *dgrad,
+                            void *workspace, size_t workspace_bytes, ssm_stream_t stream);
 
 /* selective_state_update: one decode token of every sequence of a batch,
  * with the states updated in place ("mambazip mamba1/model.rs", forward_impl's

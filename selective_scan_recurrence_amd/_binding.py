@@ -24,7 +24,7 @@ EXPORTS = ("ssm_status_str", "ssm_version", "ssm_scan_out_bytes", "ssm_scan_stat
            "ssm_conv_bwd_workspace_bytes", "ssm_conv_bwd", "selective_scan_fwd",
            "selective_scan_bwd", "selective_state_update", "ssm_get_device_error",
            "ssm_scan_ext_out_bytes", "selective_scan_fwd_ext", "ssm_scan_fwd_plan",
-           "selective_scan_fwd_static")
+           "selective_scan_fwd_static", "selective_scan_bwd_conv")
 
 
 class SsmError(RuntimeError):
@@ -83,6 +83,8 @@ def load():
         lib.selective_scan_fwd.restype = ctypes.c_int
         lib.selective_scan_bwd.argtypes = [D] + [P] * 11 + [SZ, P]
         lib.selective_scan_bwd.restype = ctypes.c_int
+        lib.selective_scan_bwd_conv.argtypes = [D] + [P] * 13 + [SZ, P]
+        lib.selective_scan_bwd_conv.restype = ctypes.c_int
         lib.selective_state_update.argtypes = [D] + [P] * 15
         lib.selective_state_update.restype = ctypes.c_int
         E = ctypes.POINTER(SsmScanExt)
@@ -221,6 +223,15 @@ def selective_scan_bwd(desc, s, x, dt, A, B, C, D, ids, dout, dgrad, workspace,
                                    _ptr(dgrad), _ptr(workspace), int(workspace_bytes),
                                    _stream(stream))
     return _check(rc, "selective_scan_bwd")
+
+
+def selective_scan_bwd_conv(desc, s, x, dt, A, B, C, D, ids, conv_w, conv_state, dout, dgrad,
+                            workspace, workspace_bytes, stream=None):
+    rc = load().selective_scan_bwd_conv(ctypes.byref(desc), _ptr(s), _ptr(x), _ptr(dt), _ptr(A),
+                                        _ptr(B), _ptr(C), _ptr(D), _ptr(ids), _ptr(conv_w),
+                                        _ptr(conv_state), _ptr(dout), _ptr(dgrad), _ptr(workspace),
+                                        int(workspace_bytes), _stream(stream))
+    return _check(rc, "selective_scan_bwd_conv")
 
 
 def selective_state_update(desc, s, x, dt, dt_bias, A, B, C, D, z, ids, conv_w, conv_state, y,

@@ -1,5 +1,6 @@
 // Selective-scan backward for gfx950: reverse-time adjoint of the Mamba-1
-// form with d_state <= 16 and one B/C group (no fused conv).
+// form with d_state <= 16 and one B/C group (no fused conv); other shapes go
+// to the generic kernels of scan_bwd_rows.hip.
 //
 // Per (sequence i, channel c) the forward step is h_t = a_t h_{t-1} + dt_t B_t u_t,
 // a_t = exp(dt_t A_c), y_t = C_t . h_t + D_c u_t.  The adjoint carried from
@@ -637,8 +638,8 @@ bool bwd_supported(const Shape& sh) {
 
 size_t bwd_workspace_bytes(const Shape& sh) {
     if (ssd_bwd_supported(sh)) return ssd_bwd_workspace_bytes(sh);
-    if (!bwd_supported(sh) || sh.S == 0 || sh.L == 0) return 0;
-    return carve(sh, nullptr).total;
+    if (bwd_supported(sh)) return (sh.S == 0 || sh.L == 0) ? 0 : carve(sh, nullptr).total;
+    return rows_bwd_supported(sh) ? rows_bwd_workspace_bytes(sh) : 0;
 }
 
 int launch_quad_ckpt(const BwdArgs& a, float* ckpt, hipStream_t stream);
@@ -646,7 +647,7 @@ int launch_quad_ckpt(const BwdArgs& a, float* ckpt, hipStream_t stream);
 int launch_scan_bwd(const BwdArgs& a, hipStream_t stream) {
     const Shape& sh = a.sh;
     if (ssd_bwd_supported(sh)) return launch_ssd_bwd(a, stream);
-    if (!bwd_supported(sh)) return SSM_ERR_UNSUPPORTED;
+    if (!bwd_supported(sh)) return launch_rows_bwd(a, stream);
     const int64_t per_row = sh.d_inner() * sh.N;
     BwdKP kp = {};
     kp.A = a.A; kp.D = a.D; kp.ids = a.ids; kp.x = a.x; kp.dt = a.dt; kp.B = a.B; kp.C = a.C;

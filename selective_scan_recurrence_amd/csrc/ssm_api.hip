@@ -53,21 +53,31 @@ size_t out_bytes(const Shape& s) {
 
 size_t state_offset(const Shape& s) { return (size_t)s.nelem_x() * s.io_bytes(); }
 
-void dgrad_layout(const Shape& s, size_t off[7]) {
+// Blocks of the packed gradient: d_s, d_x, d_dt, d_A, d_B, d_C, d_D, then
+// with the fused conv d_conv_w and d_conv_state.
+void dgrad_layout9(const Shape& s, size_t off[9], size_t* total) {
     size_t o = 0;
-    const int64_t sizes[7] = {s.R * s.H * s.P * s.N, s.nelem_x(), s.S * s.L * s.H, s.nelem_A(),
-                              s.nelem_BC(), s.nelem_BC(),
-                              (s.flags & SSM_HAS_D) ? s.H : 0};
-    for (int k = 0; k < 7; ++k) {
+    const int64_t K = s.K;
+    const int64_t sizes[9] = {s.R * s.H * s.P * s.N, s.nelem_x(), s.S * s.L * s.H, s.nelem_A(),
+                              s.nelem_BC(), s.nelem_BC(), (s.flags & SSM_HAS_D) ? s.H : 0,
+                              K > 0 ? s.H * K : 0, K > 1 ? s.R * s.H * (K - 1) : 0};
+    for (int k = 0; k < 9; ++k) {
         off[k] = o;
         o += (size_t)sizes[k] * 4;
     }
+    *total = o;
+}
+
+void dgrad_layout(const Shape& s, size_t off[7]) {
+    size_t o9[9], total;
+    dgrad_layout9(s, o9, &total);
+    memcpy(off, o9, 7 * sizeof(size_t));
 }
 
 size_t dgrad_total(const Shape& s) {
-    size_t off[7];
-    dgrad_layout(s, off);
-    return off[6] + ((s.flags & SSM_HAS_D) ? (size_t)s.H * 4 : 0);
+    size_t off[9], total;
+    dgrad_layout9(s, off, &total);
+    return total;
 }
 
 size_t workspace_bytes(const Shape& s, int backward) {
@@ -340,14 +350,20 @@ int selective_scan_fwd_ext(const ssm_scan_desc* desc, const ssm_scan_ext* ext, c
                     conv_state_out, workspace, workspace_bytes_, static_cast<hipStream_t>(stream));
 }
 
-int selective_scan_bwd(const ssm_scan_desc* desc, const float* s, const void* x, const void* dt,
-                       const float* A, const void* B, const void* C, const float* D,
-                       const int32_t* ids, const void* dout, float* dgrad, void* workspace,
-                       size_t workspace_bytes_, ssm_stream_t stream) {
+}  // extern "C"
+
+namespace ssm {
+namespace {
+
+int bwd_impl(const ssm_scan_desc* desc, const float* s, const void* x, const void* dt,
+             const float* A, const void* B, const void* C, const float* D, const int32_t* ids,
+             const float* conv_w, const float* conv_state, bool with_conv, const void* dout,
+             float* dgrad, void* workspace, size_t workspace_bytes_, hipStream_t stream) {
     Shape sh;
     int rc = check_desc(desc, &sh);
     if (rc) return rc;
-    if (sh.K != 0) return SSM_ERR_UNSUPPORTED;
+    if (sh.K != 0 && !with_conv) return SSM_ERR_UNSUPPORTED;
+    if (sh.K > 0 && !conv_w) return SSM_ERR_NULL;
     if (sh.S > 65535) return SSM_ERR_SHAPE;
     const bool has_x = sh.nelem_x() > 0, has_bc = sh.nelem_BC() > 0, has_seq = sh.S > 0;
     if (!s || !A || !dgrad || !workspace || (has_x && (!x || !dt)) || (has_bc && (!B || !C)) ||
@@ -358,12 +374,13 @@ int selective_scan_bwd(const ssm_scan_desc* desc, const float* s, const void* x,
     const size_t es = sh.io_bytes();
     if (!aligned(x, es) || !aligned(dt, es) || !aligned(B, es) || !aligned(C, es) ||
         !aligned(dout, es) || !aligned(s, 4) || !aligned(A, 4) || !aligned(ids, 4) ||
-        (D && !aligned(D, 4)) || !aligned(dgrad, 4) || !aligned(workspace, 256))
+        (D && !aligned(D, 4)) || !aligned(dgrad, 4) || !aligned(workspace, 256) ||
+        !aligned(conv_w, 4) || !aligned(conv_state, 4))
         return SSM_ERR_ALIGN;
     const char* dstate = static_cast<const char*>(dout) + state_offset(sh);
     if (!aligned(dstate, 4)) return SSM_ERR_ALIGN;
-    size_t off[7];
-    dgrad_layout(sh, off);
+    size_t off[9], total;
+    dgrad_layout9(sh, off, &total);
     BwdArgs a;
     a.sh = sh; a.s = s; a.x = x; a.dt = dt; a.A = A; a.B = B; a.C = C;
     a.D = (sh.flags & SSM_HAS_D) ? D : nullptr;
@@ -376,10 +393,36 @@ int selective_scan_bwd(const ssm_scan_desc* desc, const float* s, const void* x,
     a.d_B = reinterpret_cast<float*>(g + off[4]);
     a.d_C = reinterpret_cast<float*>(g + off[5]);
     a.d_D = (sh.flags & SSM_HAS_D) ? reinterpret_cast<float*>(g + off[6]) : nullptr;
+    a.conv_w = sh.K ? conv_w : nullptr;
+    a.conv_state = sh.K ? conv_state : nullptr;
+    a.d_conv_w = sh.K ? reinterpret_cast<float*>(g + off[7]) : nullptr;
+    a.d_conv_state = sh.K ? reinterpret_cast<float*>(g + off[8]) : nullptr;
     a.err = static_cast<uint32_t*>(workspace);
     a.ws = static_cast<char*>(workspace) + kErrBytes;
     a.ws_bytes = workspace_bytes_ - kErrBytes;
-    return launch_scan_bwd(a, static_cast<hipStream_t>(stream));
+    return launch_scan_bwd(a, stream);
+}
+
+}  // namespace
+}  // namespace ssm
+
+extern "C" {
+
+int selective_scan_bwd(const ssm_scan_desc* desc, const float* s, const void* x, const void* dt,
+                       const float* A, const void* B, const void* C, const float* D,
+                       const int32_t* ids, const void* dout, float* dgrad, void* workspace,
+                       size_t workspace_bytes_, ssm_stream_t stream) {
+    return bwd_impl(desc, s, x, dt, A, B, C, D, ids, nullptr, nullptr, false, dout, dgrad,
+                    workspace, workspace_bytes_, static_cast<hipStream_t>(stream));
+}
+
+int selective_scan_bwd_conv(const ssm_scan_desc* desc, const float* s, const void* x,
+                            const void* dt, const float* A, const void* B, const void* C,
+                            const float* D, const int32_t* ids, const float* conv_w,
+                            const float* conv_state, const void* dout, float* dgrad,
+                            void* workspace, size_t workspace_bytes_, ssm_stream_t stream) {
+    return bwd_impl(desc, s, x, dt, A, B, C, D, ids, conv_w, conv_state, true, dout, dgrad,
+                    workspace, workspace_bytes_, static_cast<hipStream_t>(stream));
 }
 
 int selective_state_update(const ssm_scan_desc* desc, float* s, const void* x, const void* dt,

@@ -68,7 +68,10 @@ struct BwdArgs {
     const int32_t* ids;
     const void* dy;
     const float* dstate;
+    const float* conv_w;      // with the fused conv (d_conv > 0), else null
+    const float* conv_state;  // nullable: zeros
     float *d_s, *d_x, *d_dt, *d_A, *d_B, *d_C, *d_D;
+    float *d_conv_w, *d_conv_state;  // with the fused conv, else null
     uint32_t* err;
     char* ws;
     size_t ws_bytes;
@@ -126,6 +129,12 @@ int launch_ssd_bwd(const BwdArgs& a, hipStream_t stream);
 // The forward's kernel family for a call (host-side decision only).
 enum class FwdPath { kNone, kTimeSplit, kQuad, kSsd, kRows };
 FwdPath fwd_path(const FwdArgs& a);
+
+// Backward for every other shape, and the fused conv: one lane group per
+// (sequence, channel) row.
+bool rows_bwd_supported(const Shape& sh);
+size_t rows_bwd_workspace_bytes(const Shape& sh);
+int launch_rows_bwd(const BwdArgs& a, hipStream_t stream);
 
 // Returns SSM_OK, SSM_ERR_UNSUPPORTED, or SSM_ERR_HIP.
 int launch_scan_fwd(const FwdArgs& a, hipStream_t stream);

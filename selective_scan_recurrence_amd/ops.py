@@ -97,29 +97,47 @@ def scan_fwd_ext(desc, s, x, dt, A, Bm, Cm, D, ids, *, dt_bias=None, z=None, cu_
 
 
 def split_dgrad(desc: B.SsmScanDesc, dgrad: torch.Tensor) -> dict:
+    """Views of the packed gradient: d_s, d_x, d_dt, d_A, d_B, d_C, d_D (with
+    D), then d_conv_w and d_conv_state (with the fused conv)."""
     total, offs = B.ssm_scan_dgrad_layout(desc)
-    S, L, H, P, N, G, R = (desc.n_seqs, desc.n_tokens, desc.n_head, desc.head_dim,
-                           desc.d_state, desc.n_group, desc.n_state_rows)
+    S, L, H, P, N, G, R, K = (desc.n_seqs, desc.n_tokens, desc.n_head, desc.head_dim,
+                              desc.d_state, desc.n_group, desc.n_state_rows, desc.d_conv)
     shapes = {"d_s": (R, H, P, N), "d_x": (S, L, H, P), "d_dt": (S, L, H),
               "d_A": (H, N) if desc.a_per_state else (H,), "d_B": (S, L, G, N),
               "d_C": (S, L, G, N)}
     if desc.flags & B.SSM_HAS_D:
         shapes["d_D"] = (H,)
-    ends = offs[1:] + [total]
+    if K > 0:
+        shapes["d_conv_w"] = (H, K)
+        shapes["d_conv_state"] = (R, H, K - 1)
     res = {}
-    for k, (name, shape) in enumerate(shapes.items()):
-        res[name] = dgrad[offs[k]:ends[k]].view(torch.float32).view(*shape)
+    off = 0
+    for name, shape in shapes.items():
+        n = 1
+        for v in shape:
+            n *= v
+        res[name] = dgrad[off:off + 4 * n].view(torch.float32).view(*shape)
+        off += 4 * n
+    assert off == total, (off, total)
     return res
 
 
-def scan_bwd(desc, s, x, dt, A, Bm, Cm, D, ids, dout, ws=None, dgrad=None, stream=None):
-    """Returns (packed dgrad bytes, dict of views)."""
+def scan_bwd(desc, s, x, dt, A, Bm, Cm, D, ids, dout, ws=None, dgrad=None, stream=None,
+             conv_w=None, conv_state=None):
+    """Returns (packed dgrad bytes, dict of views).  With the fused conv
+    (desc.d_conv > 0) conv_w is required and conv_state optional (zeros);
+    the call is selective_scan_bwd_conv and d_x is the gradient of the
+    pre-conv input."""
     total, _ = B.ssm_scan_dgrad_layout(desc)
     if dgrad is None:
         dgrad = torch.empty(total, dtype=torch.uint8, device=x.device)
     if ws is None:
         ws = workspace(desc, True, x.device)
-    B.selective_scan_bwd(desc, s, x, dt, A, Bm, Cm, D, ids, dout, dgrad, ws, ws.numel(), stream)
+    if desc.d_conv > 0 or conv_w is not None:
+        B.selective_scan_bwd_conv(desc, s, x, dt, A, Bm, Cm, D, ids, conv_w, conv_state, dout, dgrad,
+                                  ws, ws.numel(), stream)
+    else:
+        B.selective_scan_bwd(desc, s, x, dt, A, Bm, Cm, D, ids, dout, dgrad, ws, ws.numel(), stream)
     return dgrad, split_dgrad(desc, dgrad)
 
 

@@ -269,6 +269,10 @@ def config(name: str) -> ScanProblem:
                          io="bf16", seed=0xC2)
         add_dout(p, 0xC4)
         return p
+    if name == "C10":  # backward of the whole C2 layer (conv + SiLU + scan): C2's draws, dy ~ N(0,1)
+        p = config("C2")
+        add_dout(p, 0xCA)
+        return p
     if name == "C8":   # backward of the C3 Mamba-2 scan: C3's draws, dy ~ N(0,1), dstate = 0
         p = config("C3")
         add_dout(p, 0xC8)

@@ -178,16 +178,47 @@ def test_conv_argument_checks():
     assert e.value.status == ssm.SSM_ERR_DTYPE
 
 
-@pytest.mark.parametrize("kw", [dict(a_per_state=False, head_dim=2), dict(d_state=17, head_dim=1),
-                                dict(n_group=3, head_dim=1, a_per_state=True)])
-def test_backward_unsupported_shapes_rejected_before_launch(kw):
-    d = _desc(**kw)
+def test_fused_backward_argument_checks():
+    d = _desc(d_conv=4, head_dim=1)
     ws = ssm.ssm_scan_workspace_bytes(d, 1)
     assert ws >= 256
+    # conv weights are required with the fused conv
     with pytest.raises(ssm.SsmError) as e:
-        ssm.selective_scan_bwd(d, 256, 256, 256, 256, 256, 256, 256, 256, 256, 256, 256, ws,
-                               stream=0)
+        ssm.selective_scan_bwd_conv(d, 256, 256, 256, 256, 256, 256, 256, 256, None, None, 256, 256,
+                                    256, ws, stream=0)
+    assert e.value.status == ssm.SSM_ERR_NULL
+    # d_conv 5..8 has no backward kernel
+    d5 = _desc(d_conv=5, head_dim=1)
+    with pytest.raises(ssm.SsmError) as e:
+        ssm.selective_scan_bwd_conv(d5, 256, 256, 256, 256, 256, 256, 256, 256, 256, None, 256, 256,
+                                    256, 1 << 30, stream=0)
     assert e.value.status == ssm.SSM_ERR_UNSUPPORTED
+
+
+def test_fused_gradient_layout_appends_conv_blocks():
+    d = _desc(d_conv=4, head_dim=1, n_state_rows=3)
+    total, offs = ssm.ssm_scan_dgrad_layout(d)
+    d0 = _desc(d_conv=0, head_dim=1, n_state_rows=3)
+    total0, offs0 = ssm.ssm_scan_dgrad_layout(d0)
+    assert offs == offs0
+    H, R = d.n_head, d.n_state_rows
+    assert total == total0 + 4 * (H * 4 + R * H * 3)
+
+
+@pytest.mark.parametrize("kw", [dict(a_per_state=False, head_dim=2), dict(d_state=17, head_dim=1),
+                                dict(n_group=3, head_dim=1, a_per_state=True),
+                                dict(d_state=256, head_dim=3, n_group=3)])
+def test_backward_every_forward_shape_has_a_workspace(kw):
+    """Shapes outside the specialised kernels take the generic backward: the
+    workspace is sized for it (checkpoints, partial slabs) and a short
+    workspace is refused before launch."""
+    d = _desc(**kw)
+    ws = ssm.ssm_scan_workspace_bytes(d, 1)
+    assert ws > 256
+    with pytest.raises(ssm.SsmError) as e:
+        ssm.selective_scan_bwd(d, 256, 256, 256, 256, 256, 256, 256, 256, 256, 256, 256, ws - 256,
+                               stream=0)
+    assert e.value.status == ssm.SSM_ERR_WORKSPACE
 
 
 def test_conv_bwd_argument_checks():
