@@ -54,6 +54,9 @@ WORKLOADS = {
           "d_state 128, bf16 x/dt/B/C/z/y, fp32 states updated in place by permuted ids",
     "C8": "Mamba-2 scan reverse-time backward of the 4x4096, 80 heads x 64, d_state 128 bf16 scan, "
           "fp32 grads",
+    "C10": "backward of the whole Mamba-1 layer (causal conv + SiLU + scan) at 8x4096x5120, d_state 16, "
+           "d_conv 4, bf16 x/dt/B/C/dy, fp32 grads",
+    "C11": "ssm_conv forward (causal depthwise conv + SiLU) of the 8x4096x5120 bf16 activations, d_conv 4",
     "C9": "Mamba-1 fused conv+SiLU+scan forward of 8 packed sequences of mixed lengths (32768 "
           "tokens) at the 5120-channel layer, d_state 16, d_conv 4, with dt bias + softplus and the "
           "SiLU(z) output gate, bf16 x/dt/B/C/z/y, fp32 state/A/D",
@@ -324,6 +327,88 @@ def parity_gate_bwd(name, p, g):
         checked += want.size
     return {"checked_elements": int(checked), "rtol": rtol,
             "atol": f"{fe:g} x rms (per element), {fs:g} x rms (sums)"}
+
+
+def conv_fwd_bytes(c) -> int:
+    """sx read and out written once, w read once."""
+    length = c.n_t + c.d_conv - 1
+    io = 2 if c.io == "bf16" else 4
+    return c.n_s * c.d_inner * length * io + c.n_s * c.n_t * c.d_inner * io + c.d_inner * c.d_conv * 4
+
+
+def main_conv_fwd(args):
+    import torch
+    import ssm_inputs
+    import oracle
+    from selective_scan_recurrence_amd import ops
+    import selective_scan_recurrence_amd as ssm
+
+    ssm.load()
+    dev = torch.device("cuda:0")
+    c = ssm_inputs.conv_config(args.config)
+    step_bytes = conv_fwd_bytes(c)
+    copies = max(2, math.ceil(3 * MALL_BYTES / step_bytes))
+    sets = []
+    for _ in range(copies):
+        t = {"sx": _dev(c.sx, dev), "w": _dev(c.w, dev)}
+        t["out"] = torch.empty(c.n_s, c.n_t, c.d_inner, dtype=t["sx"].dtype, device=dev)
+        sets.append(t)
+
+    def step(t):
+        return ops.conv_fwd(t["sx"], t["w"], apply_silu=c.apply_silu, out=t["out"])
+
+    got = step(sets[0])
+    torch.cuda.synchronize()
+    # parity gate: every output element
+    want = oracle.conv_fwd(c.sx.value, c.w.value, apply_silu=c.apply_silu)
+    g = got.double().cpu().numpy()
+    rtol, atol = (2e-2, 1e-3) if c.io == "bf16" else (1e-4, 1e-5)
+    bad = ~(np.abs(g - want) <= atol + rtol * np.abs(want))
+    if bad.any():
+        raise SystemExit(f"parity gate failed on {args.config}: {int(bad.sum())} elements")
+    parity = {"checked_elements": int(want.size), "rtol": rtol, "atol": atol}
+
+    for k in range(args.warmup):
+        step(sets[k % copies])
+    torch.cuda.synchronize()
+    ms_per_step, wall = timed_steps(torch, step, sets, copies, args.steps)
+    spread = call_distribution(torch, step, sets, copies)
+    avg_s = ms_per_step * 1e-3
+    gbs = step_bytes / avg_s / 1e9
+    roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.config),
+            "traffic_unit": "HBM bytes per call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "kernel": "ssm_conv_fwd (one launch)", "call_us": round(avg_s * 1e6, 3), "call_spread": spread,
+            "floors_us": {"hbm": round(step_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2)},
+            "algorithmic_bytes": step_bytes}
+    line = {
+        "metric": "ssm_conv forward effective HBM GB/s (% of peak), 1 GPU", "value": round(gbs, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": c.io,
+        "data": "synthetic (seeded; distributions of the workload definition)",
+        "config": {"workload": f"{args.config}: {WORKLOADS[args.config]}", "n_seqs": c.n_s,
+                   "n_tokens": c.n_t, "d_inner": c.d_inner, "d_conv": c.d_conv,
+                   "apply_silu": c.apply_silu, "input_copies": copies},
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "roofline": roof, "parity": parity,
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        reps, sec = 0, 0.0
+        ch = 1024
+        while reps < 50 and (reps == 0 or sec < 10.0):
+            t0 = time.perf_counter()
+            oracle.conv_fwd(c.sx.value[:, :ch], c.w.value[:ch], apply_silu=c.apply_silu)
+            sec += time.perf_counter() - t0
+            reps += 1
+        per = sec / reps
+        line["cpu_baseline"] = {
+            "value": round(step_bytes * ch / c.d_inner / per / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "sample": f"first {ch} of {c.d_inner} channels, all sequences and tokens; "
+                                        f"{reps} repetitions",
+            "seconds": round(sec, 3), "cpu": platform.processor() or platform.machine(),
+            "nproc": os.cpu_count()}
+    print(json.dumps(line), flush=True)
 
 
 def conv_bwd_bytes(c) -> int:
@@ -754,6 +839,9 @@ def main():
         return
     if args.config == "C5":
         main_conv_bwd(args)
+        return
+    if args.config == "C11":
+        main_conv_fwd(args)
         return
     if args.config in ("C6", "C7"):
         main_decode(args)

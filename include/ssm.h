@@ -138,7 +138,9 @@ size_t ssm_scan_workspace_bytes(const ssm_scan_desc *desc, int backward);
  * then SiLU when apply_silu != 0.  sx [n_s][d_inner][d_conv-1+n_t] (time
  * fastest, carrying the d_conv-1 earlier inputs) and out [n_s][n_t][d_inner]
  * have dtype io; w [d_inner][d_conv] is f32.  The last tap w[c][d_conv-1]
- * multiplies the newest input. */
+ * multiplies the newest input.  One sequence's tensors are addressed with
+ * 32-bit byte offsets: (d_inner + 64) * (d_conv - 1 + n_t + 128) must not
+ * exceed 2^29 - 1, else SSM_ERR_SHAPE. */
 int ssm_conv_fwd(const void *sx, const float *w, void *out, int64_t n_s, int64_t n_t,
                  int64_t d_inner, int32_t d_conv, int32_t io_dtype, int32_t apply_silu,
                  ssm_stream_t stream);

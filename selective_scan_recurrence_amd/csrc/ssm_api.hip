@@ -140,6 +140,9 @@ int ssm_conv_fwd(const void* sx, const float* w, void* out, int64_t n_s, int64_t
     if (n_s > 65535) return SSM_ERR_SHAPE;
     int64_t len = d_conv - 1 + n_t, t1, t2;
     if (!mul_ok(len, d_inner, &t1) || t1 > INT_MAX || !mul_ok(t1, n_s, &t2)) return SSM_ERR_SHAPE;
+    // per-sequence byte extents, with a margin of one channel block and one
+    // tile, must fit the 31-bit offsets of the kernel's buffer descriptors
+    if (!mul_ok(len + 128, d_inner + 64, &t1) || t1 > (INT_MAX >> 2)) return SSM_ERR_SHAPE;
     if (!sx || !w || !out) return SSM_ERR_NULL;
     const size_t es = io_dtype == SSM_BF16 ? 2 : 4;
     if (!aligned(sx, es) || !aligned(out, es) || !aligned(w, 4)) return SSM_ERR_ALIGN;

@@ -299,6 +299,8 @@ class ConvProblem:
 def conv_config(name: str) -> ConvProblem:
     if name == "C5":   # conv + SiLU backward of the C2 activations: 8 x 4096 x 5120, d_conv 4
         return ConvProblem(8, 4096, 5120, 4, "bf16", True, 0xC5)
+    if name == "C11":  # the standalone conv + SiLU forward of the same activations (dout unused)
+        return ConvProblem(8, 4096, 5120, 4, "bf16", True, 0xCB)
     raise KeyError(name)
 
 

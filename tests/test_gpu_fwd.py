@@ -262,3 +262,26 @@ def test_ssm_conv_parity(gpu, io, d_conv, n_t, d_inner, n_s, silu):
     torch.cuda.synchronize()
     want = oracle.conv_fwd(sx.value, w, apply_silu=silu)
     assert_close(host(got), want, io, "ssm_conv")
+
+
+def test_ssm_conv_full_size(gpu):
+    """The standalone conv + SiLU over the 8 x 4096 x 5120 bf16 activations, in
+    the launch configuration bench.py times: every output element."""
+    c = ssm_inputs.conv_config("C11")
+    got = ops.conv_fwd(dev(c.sx), dev(c.w), apply_silu=c.apply_silu)
+    torch.cuda.synchronize()
+    want = oracle.conv_fwd(c.sx.value, c.w.value, apply_silu=c.apply_silu)
+    assert_close(host(got), want, c.io, "ssm_conv C11")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("d_inner,n_t", [(72, 130), (8, 64), (136, 65)])
+def test_ssm_conv_row_pieces(gpu, io, d_inner, n_t):
+    """Channel counts that are multiples of 8 but not of 64 (the 16-byte row
+    stores of the last channel block stop at d_inner), with ragged tiles."""
+    rng = np.random.default_rng(d_inner + n_t)
+    sx = ssm_inputs._const(rng.uniform(-1, 1, (2, d_inner, 3 + n_t)), io)
+    w = rng.uniform(-1, 1, (d_inner, 4)).astype(np.float32)
+    got = ops.conv_fwd(dev(sx), dev(w), apply_silu=True)
+    torch.cuda.synchronize()
+    assert_close(host(got), oracle.conv_fwd(sx.value, w, apply_silu=True), io, "ssm_conv rows")
