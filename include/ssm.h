@@ -291,13 +291,11 @@ const char *ssm_scan_fwd_plan(const ssm_scan_desc *desc, const ssm_scan_ext *ext
  *  - the Mamba-2 form with bf16 io, head_dim 32 or 64, d_state 64 or 128 and
  *    16-byte aligned x, dout, B, C, s and dgrad: chunked products on bf16
  *    MFMA operands (the carried gradient and the checkpointed state as bf16
- *    pairs) with fp32 accumulation; d_B and d_C collect the heads of a group
- *    with fp32 atomic adds, whose order (and so their last bits) varies from
- *    run to run;
+ *    pairs) with fp32 accumulation;
  *  - every other shape: one lane group per (sequence, channel) row with
  *    fp32 arithmetic.
- * Apart from the d_B/d_C of the MFMA path, every sum over channels, tokens
- * or sequences is taken in a fixed order, so results are bitwise repeatable.
+ * Every sum over channels, heads, tokens or sequences is taken in a fixed
+ * order, so results are bitwise repeatable.
  * workspace: ssm_scan_workspace_bytes(desc, 1) bytes, 256-byte aligned. */
 int selective_scan_bwd(const ssm_scan_desc *desc, const float *s, const void *x,
                        const void *dt, const float *A, const void *B, const void *C,

@@ -38,10 +38,10 @@
 // rows, the next (earlier) chunk's rows being loaded meanwhile.  All products run on v_mfma_f32_16x16x32_bf16: operands
 // whose k index runs along a stored row come from 16-byte LDS row reads, the
 // others from the transposing read ds_read_b64_tr_b16 (as in the forward).
-// dB and dC, which every head of a group adds to, are accumulated with fp32
-// atomic adds (their order, and so their last bits, vary from run to run);
-// dA, dD and dh_0 are written per (sequence, head) and summed in a fixed
-// order by a second kernel.
+// dB and dC, which every head of a group adds to, are written per (sequence,
+// head) as partial sums and added over the group's heads in head order by a
+// second kernel, as are dA, dD (over sequences) and dh_0 (by ids): every
+// sum has a fixed order, so results repeat bitwise.
 #include "device_common.h"
 #include "ssm_internal.h"
 
@@ -74,8 +74,7 @@ struct SsdBwdKP {
     const float* ckpt;   // [S][H][n_chunks][P][N]: state entering each chunk
     float* d_x;
     float* d_dt;
-    float* d_B;          // zeroed before; atomic adds
-    float* d_C;
+    float* bc_part;      // [S][H][n_chunks * Q][2][N]: this head's dB, then dC
     float* dA_part;      // [S][H]
     float* dD_part;      // [S][H]
     float* ds_part;      // [S][H][P][N]: dL/dh_0
@@ -443,8 +442,9 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
             constexpr int NPW = NB / 2;
             const int tb = wave & 3, nb0 = (wave >> 2) * NPW, half = wave >> 2;
             float yo[4] = {0.f, 0.f, 0.f, 0.f}, uu[4] = {0.f, 0.f, 0.f, 0.f};
-            float* dCg = p.d_C + ((int64_t)i * L * p.G + grp) * N;
-            float* dBg = p.d_B + ((int64_t)i * L * p.G + grp) * N;
+            // this head's rows [t][2][N] of the partial sums from the chunk's first
+            // token (rows are padded to whole chunks: no store needs a guard)
+            float* bcc = p.bc_part + (((int64_t)i * p.H + hh) * p.n_chunks * kQ + t0) * 2 * N;
             // the lane's four tokens t = 16 tb + 4 g4 + rr (and s, the same block)
             const float4 et4 = *reinterpret_cast<const float4*>(&ecum_l[tb * 16 + 4 * g4]);
             const float4 ws4 = *reinterpret_cast<const float4*>(&w_l[tb * 16 + 4 * g4]);
@@ -452,7 +452,9 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
             // C[t][n] and B[s][n] of the lane's four rows at column n: one
             // transposing read each (lanes 4k + q address row 4 g4 + k)
             const int trow = (tb * 16 + 4 * g4 + (l16 >> 2)) * NP + 4 * (l16 & 3);
-#pragma unroll
+            // not unrolled: the stores of one state block then leave before the
+            // next block's products, which keeps the register count under the cap
+#pragma unroll 1
             for (int j = 0; j < NPW; ++j) {
                 const int nb = nb0 + j, n = nb * 16 + l16;
                 f32x4 c1 = {0.f, 0.f, 0.f, 0.f}, c2 = {0.f, 0.f, 0.f, 0.f};
@@ -474,8 +476,9 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
                     const int t = tb * 16 + 4 * g4 + rr;
                     const float off = et[rr] * c1[rr];
                     yo[rr] = fmaf(off, (float)cn[rr], yo[rr]);
-                    if (t0 + t < L) unsafeAtomicAdd(dCg + (int64_t)(t0 + t) * p.G * N + n, off + c2[rr]);
+                    bcc[t * 2 * N + N + n] = off + c2[rr];
                 }
+
                 f32x4 b1 = {0.f, 0.f, 0.f, 0.f}, b2 = {0.f, 0.f, 0.f, 0.f};
                 const int sb = tb;
 #pragma unroll
@@ -495,7 +498,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
                 for (int rr = 0; rr < 4; ++rr) {
                     const int s = sb * 16 + 4 * g4 + rr;
                     uu[rr] = fmaf(b2[rr], (float)bn[rr], uu[rr]);
-                    if (t0 + s < L) unsafeAtomicAdd(dBg + (int64_t)(t0 + s) * p.G * N + n, fmaf(wsv[rr], b2[rr], b1[rr]));
+                    bcc[s * 2 * N + n] = fmaf(wsv[rr], b2[rr], b1[rr]);
                 }
             }
             // sums over this wave's n (the 16 lanes of a group)
@@ -630,8 +633,27 @@ __global__ __launch_bounds__(256) void ssd_bwd_reduce(const float* __restrict__ 
     }
 }
 
-__global__ __launch_bounds__(256) void zero_f32(float* p, int64_t n) {
-    for (int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x; k < n; k += (int64_t)gridDim.x * 256) p[k] = 0.0f;
+// d_B, d_C [S][L][G][N]: the partial sums of the group's heads in head order.
+__global__ __launch_bounds__(256) void ssd_bwd_reduce_bc(const float* __restrict__ part, float* d_B,
+                                                         float* d_C, int S, int L, int Lpad, int H, int G,
+                                                         int N) {
+    const int64_t total = (int64_t)S * L * G * N;
+    const int hpg = H / G;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+        const int n = (int)(e % N);
+        const int64_t rest = e / N;
+        const int g = (int)(rest % G);
+        const int64_t tok = rest / G;
+        const int64_t i = tok / L, t = tok % L;
+        const float* src = part + ((i * H + (int64_t)g * hpg) * Lpad + t) * 2 * N + n;
+        float b = 0.0f, c = 0.0f;
+        for (int h = 0; h < hpg; ++h) {
+            b += src[(int64_t)h * Lpad * 2 * N];
+            c += src[(int64_t)h * Lpad * 2 * N + N];
+        }
+        d_B[e] = b;
+        d_C[e] = c;
+    }
 }
 
 template <int P, int N>
@@ -653,7 +675,8 @@ bool ssd_bwd_supported(const Shape& sh) {
 size_t ssd_bwd_workspace_bytes(const Shape& sh) {
     const int64_t n_chunks = (sh.L + kQ - 1) / kQ;
     return align_up((size_t)(sh.S * sh.H * n_chunks * sh.P * sh.N) * 4, 256) +
-           align_up((size_t)(sh.S * sh.H * sh.P * sh.N) * 4, 256) + 2 * align_up((size_t)(sh.S * sh.H) * 4, 256);
+           align_up((size_t)(sh.S * sh.H * sh.P * sh.N) * 4, 256) + 2 * align_up((size_t)(sh.S * sh.H) * 4, 256) +
+           align_up((size_t)(sh.S * sh.H * n_chunks * kQ * 2 * sh.N) * 4, 256);
 }
 
 int launch_ssd_ckpt(const BwdArgs& a, float* ckpt, hipStream_t stream);
@@ -673,22 +696,16 @@ int launch_ssd_bwd(const BwdArgs& a, hipStream_t stream) {
     float* dA_part = reinterpret_cast<float*>(w);
     w += align_up((size_t)(sh.S * sh.H) * 4, 256);
     float* dD_part = reinterpret_cast<float*>(w);
+    w += align_up((size_t)(sh.S * sh.H) * 4, 256);
+    float* bc_part = reinterpret_cast<float*>(w);
     if (ssd_bwd_workspace_bytes(sh) > a.ws_bytes) return SSM_ERR_WORKSPACE;
-
-    // dB and dC collect atomic adds: clear them first (a fill kernel, so that
-    // the call can be captured in a graph)
-    const int64_t nbc = sh.nelem_BC();
-    hipLaunchKernelGGL(zero_f32, dim3((unsigned)std::min<int64_t>((nbc + 255) / 256, 4096)), dim3(256), 0,
-                       stream, a.d_B, nbc);
-    hipLaunchKernelGGL(zero_f32, dim3((unsigned)std::min<int64_t>((nbc + 255) / 256, 4096)), dim3(256), 0,
-                       stream, a.d_C, nbc);
     int rc = launch_ssd_ckpt(a, ckpt, stream);
     if (rc) return rc;
     SsdBwdKP kp;
     kp.x = static_cast<const bf16_t*>(a.x); kp.dt = static_cast<const bf16_t*>(a.dt); kp.A = a.A;
     kp.B = static_cast<const bf16_t*>(a.B); kp.C = static_cast<const bf16_t*>(a.C); kp.D = a.D;
     kp.ids = a.ids; kp.dy = static_cast<const bf16_t*>(a.dy); kp.dstate = a.dstate; kp.ckpt = ckpt;
-    kp.d_x = a.d_x; kp.d_dt = a.d_dt; kp.d_B = a.d_B; kp.d_C = a.d_C;
+    kp.d_x = a.d_x; kp.d_dt = a.d_dt; kp.bc_part = bc_part;
     kp.dA_part = dA_part; kp.dD_part = dD_part; kp.ds_part = ds_part;
     kp.L = (int)sh.L; kp.H = (int)sh.H; kp.G = (int)sh.G; kp.R = (int)sh.R;
     kp.hpg = (int)(sh.H / sh.G); kp.n_chunks = (int)n_chunks;
@@ -699,6 +716,10 @@ int launch_ssd_bwd(const BwdArgs& a, hipStream_t stream) {
     else if (sh.P == 64 && sh.N == 64) launch_ssd_bwd_pn<64, 64>(kp, S, sp, stream);
     else if (sh.P == 32 && sh.N == 128) launch_ssd_bwd_pn<32, 128>(kp, S, sp, stream);
     else launch_ssd_bwd_pn<32, 64>(kp, S, sp, stream);
+    const int64_t nbc = sh.nelem_BC();
+    hipLaunchKernelGGL(ssd_bwd_reduce_bc, dim3((unsigned)std::min<int64_t>((nbc + 255) / 256, 16384)), dim3(256),
+                       0, stream, (const float*)bc_part, a.d_B, a.d_C, (int)sh.S, (int)sh.L, (int)(n_chunks * kQ),
+                       (int)sh.H, (int)sh.G, (int)sh.N);
     const int64_t per_row = sh.H * sh.P * sh.N;
     const int64_t work = std::max<int64_t>(sh.H, sh.R * per_row);
     hipLaunchKernelGGL(ssd_bwd_reduce, dim3((unsigned)std::min<int64_t>((work + 255) / 256, 8192)), dim3(256), 0,

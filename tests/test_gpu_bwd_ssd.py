@@ -8,8 +8,12 @@ bf16 once per chunk) and fp32 accumulation, as the forward's MFMA path does:
 each term carries a relative error of about 2^-8, and sums of many terms of
 either sign carry an absolute error that scales with their terms.  Every
 gradient is compared element by element with rtol 2e-2 and an absolute floor
-of 2e-2 x rms of the oracle's values (the bf16 tolerance the forward uses,
-with the floor of the channel/token sums)."""
+of 1e-2 x rms of the oracle's values for d_x (one channel's gradient) and
+2e-2 x rms for the sums: d_dt (over the head's channels and states, and
+through the decay over the chunk's later tokens), d_A, d_D, d_B, d_C, d_s
+(the bf16 tolerance the forward uses, with the floor of the sums).  Over all
+80 heads of the full-size workload the worst d_dt element uses about 0.7 of
+its bound and would exceed a 1e-2 floor slightly."""
 import numpy as np
 import pytest
 import torch
@@ -22,6 +26,13 @@ from tests.gpu_util import desc_of, device_inputs, dev, host
 pytestmark = pytest.mark.gpu
 
 GRADS = ("d_x", "d_dt", "d_s", "d_A", "d_D", "d_B", "d_C")
+
+
+PER_ELEM = ("d_x",)
+
+
+def _floor(k):
+    return 1e-2 if k in PER_ELEM else 2e-2
 
 
 def _check(name, got, want, rtol=2e-2, floor=2e-2):
@@ -83,7 +94,7 @@ def test_ssd_bwd_parity(case):
     for k in GRADS:
         if o.get(k) is None:
             continue
-        _check(f"{case} {k}", host(g[k]), o[k])
+        _check(f"{case} {k}", host(g[k]), o[k], floor=_floor(k))
 
 
 def test_ssd_bwd_dstate_seed():
@@ -96,7 +107,7 @@ def test_ssd_bwd_dstate_seed():
     g = _run(p)
     o = oracle.problem_bwd(p)
     for k in GRADS:
-        _check(f"dstate {k}", host(g[k]), o[k])
+        _check(f"dstate {k}", host(g[k]), o[k], floor=_floor(k))
 
 
 def test_ssd_bwd_bad_id():
@@ -119,7 +130,7 @@ def test_ssd_bwd_bad_id():
     q = _problem(141, n_seqs=2, n_tokens=70, n_head=2, n_state_rows=3)
     o = oracle.scan_bwd(q.value("s"), q.value("x")[:1], q.value("dt")[:1], q.value("A"), q.value("B")[:1],
                         q.value("C")[:1], q.value("D"), q.ids[:1], q.value("dy")[:1], q.value("dstate")[:1])
-    _check("bad-id d_x of the good sequence", host(g["d_x"])[0], o["d_x"][0])
+    _check("bad-id d_x of the good sequence", host(g["d_x"])[0], o["d_x"][0], floor=1e-2)
     ds = host(g["d_s"])
     _check("bad-id d_s", ds, o["d_s"])
 
@@ -139,10 +150,57 @@ def test_ssd_bwd_full_size_head_subset():
     v = p.value
     o = oracle.scan_bwd(v("s")[:, heads], v("x")[:, :, heads], v("dt")[:, :, heads], v("A")[heads],
                         v("B"), v("C"), v("D")[heads], p.ids, v("dy")[:, :, heads], v("dstate")[:, heads])
-    _check("C8 d_x", host(g["d_x"])[:, :, heads], o["d_x"])
+    _check("C8 d_x", host(g["d_x"])[:, :, heads], o["d_x"], floor=1e-2)
     _check("C8 d_dt", host(g["d_dt"])[:, :, heads], o["d_dt"])
     _check("C8 d_s", host(g["d_s"])[:, heads], o["d_s"])
     _check("C8 d_A", host(g["d_A"])[heads], o["d_A"])
     _check("C8 d_D", host(g["d_D"])[heads], o["d_D"])
     _check("C8 d_B", host(g["d_B"]), o["d_B"])
     _check("C8 d_C", host(g["d_C"]), o["d_C"])
+
+
+def test_ssd_bwd_run_to_run_bitwise():
+    """Every gradient, d_B and d_C (sums over the group's heads) included,
+    repeats bit for bit: the head sums are taken in head order."""
+    p = _problem(151, n_seqs=2, n_tokens=200, n_head=6, head_dim=64, d_state=128, n_group=2)
+    t = device_inputs(p)
+    g1 = {k: v.clone() for k, v in _run(p, t).items()}
+    g2 = _run(p, t)
+    for k in g1:
+        assert torch.equal(g1[k], g2[k]), k
+
+
+@pytest.fixture(scope="module")
+def c8_result():
+    """The backward of the 4 x 4096, 80 heads x 64, d_state 128 bf16 scan, run once."""
+    p = ssm_inputs.config("C8")
+    return {"p": p, "g": _run(p), "partial": {}}
+
+
+def _c8_oracle_seq(p, seq):
+    v = p.value
+    sl = slice(seq, seq + 1)
+    return oracle.scan_bwd(v("s"), v("x")[sl], v("dt")[sl], v("A"), v("B")[sl], v("C")[sl], v("D"),
+                           p.ids[sl], v("dy")[sl], v("dstate")[sl])
+
+
+@pytest.mark.parametrize("seq", range(4))
+def test_ssd_bwd_full_size_every_head(c8_result, seq):
+    """Every head, channel and token of one sequence of the full-size workload:
+    d_x, d_dt and the sequence's d_B, d_C rows (sums over all 80 heads)."""
+    p, g = c8_result["p"], c8_result["g"]
+    o = _c8_oracle_seq(p, seq)
+    sl = slice(seq, seq + 1)
+    for k in ("d_x", "d_dt", "d_B", "d_C"):
+        _check(f"C8 sequence {seq} {k}", host(g[k][sl]), o[k], floor=_floor(k))
+    c8_result["partial"][seq] = {k: o[k] for k in ("d_A", "d_D", "d_s")}
+
+
+def test_ssd_bwd_full_size_sums_over_sequences(c8_result):
+    p, g, part = c8_result["p"], c8_result["g"], c8_result["partial"]
+    for seq in range(p.n_seqs):
+        if seq not in part:
+            o = _c8_oracle_seq(p, seq)
+            part[seq] = {k: o[k] for k in ("d_A", "d_D", "d_s")}
+    for k in ("d_A", "d_D", "d_s"):
+        _check(f"C8 {k}", host(g[k]), sum(part[seq][k] for seq in range(p.n_seqs)))
