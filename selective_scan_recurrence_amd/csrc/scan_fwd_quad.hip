@@ -247,7 +247,12 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int64_t tok0,
     constexpr int CPT = 16 * ES / 16;  // 16-byte chunks per B/C token row (16 states)
     static_assert(TT * CPR == 2 * kThreads, "two x (and dt) chunks per thread per tile");
     static_assert(TT * CPT == kThreads / 2, "one B or C chunk per thread per tile");
-    __shared__ __attribute__((aligned(16))) char x_l[TT * XS];
+    // x is staged as fp32 behind HX history rows (the conv's inputs before the
+    // tile), so that an owner lane reads its K taps straight from LDS; a row
+    // pitch of 8 (mod 32) words keeps the owners' 4 rows x 16 channels apart
+    constexpr int HX = 3;
+    constexpr int XPF = 64 + 8;
+    __shared__ __attribute__((aligned(16))) float xf_l[(HX + TT) * XPF];
     __shared__ __attribute__((aligned(16))) char dt_l[TT * XS];
     // y tile; with the gate and bf16 io the owners' y stays fp32 (row stride
     // XSF) so that y * SiLU(z) is rounded to bf16 once
@@ -256,6 +261,12 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int64_t tok0,
     __shared__ __attribute__((aligned(16))) char y_l[MODE == 1 ? (YF ? TT * XSF : TT * XS) : 16];
     __shared__ __attribute__((aligned(16))) float B_l[TT][16];
     __shared__ __attribute__((aligned(16))) float C_l[TT][16];
+    // y reduce-scatter within each wave: lane (cl, q) leaves its four partial
+    // sums (one per token of the group) at [cl][q][0..3] and reads those of
+    // its own token, [cl][0..3][q]; a pitch of 20 words per channel keeps the
+    // reads to two lanes per bank
+    constexpr int YRP = 20;
+    __shared__ __attribute__((aligned(16))) float yr_l[MODE == 1 ? kThreads / 4 * YRP : 4];
 
     const int tid = threadIdx.x;
     const int c = cb * 64 + cl;
@@ -272,19 +283,25 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int64_t tok0,
     const float dtb = p.dt_bias ? p.dt_bias[c] : 0.0f;
 
     float w[4] = {0.f, 0.f, 0.f, 0.f};
-    float xp = 0.0f;
     if constexpr (K > 0) {
 #pragma unroll
         for (int j = 0; j < K; ++j) w[j] = p.conv_w[(int64_t)c * K + j];
-        const int tp = t_begin - 4 + q;
-        if (tp >= 0) {
-            xp = to_f32(*reinterpret_cast<const T*>(xg + (int64_t)tp * row_stride + cl * ES));
-        } else if (tp >= -(K - 1)) {
-            const int r = bad ? 0 : p.ids[i];
-            xp = bad ? __builtin_nanf("")
-                     : (p.conv_state ? p.conv_state[((int64_t)r * p.d_inner + c) * (K - 1) +
-                                                    (tp + K - 1)]
-                                     : 0.0f);
+        // history rows of the first tile: the inputs t_begin-3 .. t_begin-1 of
+        // the block's 64 channels (tokens before 0 from the gathered conv state)
+        if (tid < HX * 64) {
+            const int hrow = tid >> 6, hch = tid & 63;
+            const int tp = t_begin - HX + hrow;
+            float v = 0.0f;
+            if (tp >= 0) {
+                v = to_f32(*reinterpret_cast<const T*>(xg + (int64_t)tp * row_stride + hch * ES));
+            } else if (tp >= -(K - 1)) {
+                const int r = bad ? 0 : p.ids[i];
+                v = bad ? __builtin_nanf("")
+                        : (p.conv_state ? p.conv_state[((int64_t)r * p.d_inner + cb * 64 + hch) * (K - 1) +
+                                                       (tp + K - 1)]
+                                        : 0.0f);
+            }
+            xf_l[hrow * XPF + hch] = v;
         }
     }
 
@@ -321,7 +338,19 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int64_t tok0,
         for (int r = 0; r < 2; ++r) {
             const int e = tid + kThreads * r;
             const int row = e / CPR, col = e % CPR;
-            *reinterpret_cast<u32x4*>(x_l + row * XS + col * 16) = sx[r];
+            float* xd = xf_l + (HX + row) * XPF + col * (16 / ES);
+            if constexpr (ES == 2) {
+                float f[8];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    f[2 * k] = __uint_as_float(sx[r][k] << 16);
+                    f[2 * k + 1] = __uint_as_float(sx[r][k] & 0xffff0000u);
+                }
+                *reinterpret_cast<float4*>(xd) = make_float4(f[0], f[1], f[2], f[3]);
+                *reinterpret_cast<float4*>(xd + 4) = make_float4(f[4], f[5], f[6], f[7]);
+            } else {
+                *reinterpret_cast<u32x4*>(xd) = sx[r];
+            }
             *reinterpret_cast<u32x4*>(dt_l + row * XS + col * 16) = sdt[r];
         }
         const int e = tid & (kThreads / 2 - 1);
@@ -352,19 +381,18 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int64_t tok0,
             }
         }
         const bool own_ok = full_tile || (tb + tt < t_end);
-        const float xc = to_f32(*reinterpret_cast<const T*>(x_l + tt * XS + cl * ES));
         float dtv = to_f32(*reinterpret_cast<const T*>(dt_l + tt * XS + cl * ES)) + dtb;
         if constexpr (SOFTPLUS) dtv = softplus(dtv);
         float u;
         if constexpr (K > 0) {
-            float cv = w[K - 1] * xc;
-            if constexpr (K >= 2) cv = fmaf(w[K - 2], quad_rot<1>(q <= 2 ? xc : xp), cv);
-            if constexpr (K >= 3) cv = fmaf(w[K - 3], quad_rot<2>(q <= 1 ? xc : xp), cv);
-            if constexpr (K >= 4) cv = fmaf(w[K - 4], quad_rot<3>(q <= 0 ? xc : xp), cv);
+            // the taps' inputs, tokens tt-K+1 .. tt (the first ones in the history rows)
+            const float* xr = xf_l + (HX + tt - (K - 1)) * XPF + cl;
+            float cv = w[0] * xr[0];
+#pragma unroll
+            for (int j = 1; j < K; ++j) cv = fmaf(w[j], xr[j * XPF], cv);
             u = silu(cv);
-            xp = xc;
         } else {
-            u = xc;
+            u = xf_l[(HX + tt) * XPF + cl];
         }
         if (!own_ok) { dtv = 0.0f; u = 0.0f; }
         const float dtu = dtv * u;
@@ -399,14 +427,15 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int64_t tok0,
             }
         }
         if constexpr (MODE == 1) {
-            const bool hi2 = (q & 2) != 0;
-            const float keep0 = hi2 ? yp[2] : yp[0], send0 = hi2 ? yp[0] : yp[2];
-            const float keep1 = hi2 ? yp[3] : yp[1], send1 = hi2 ? yp[1] : yp[3];
-            const float r0 = keep0 + quad_xor2(send0);
-            const float r1 = keep1 + quad_xor2(send1);
-            const bool hi1 = (q & 1) != 0;
-            const float keep = hi1 ? r1 : r0, send = hi1 ? r0 : r1;
-            const float yv = fmaf(Dc, u, keep + quad_xor1(send));
+            // LDS operations of one wave complete in order, so the quad's
+            // partials are in place for the reads that follow; the wave
+            // barrier keeps the compiler from reordering them
+            float* yr = yr_l + cl * YRP;
+            *reinterpret_cast<float4*>(yr + 4 * q) = make_float4(yp[0], yp[1], yp[2], yp[3]);
+            __builtin_amdgcn_wave_barrier();
+            const float ysum = (yr[q] + yr[4 + q]) + (yr[8 + q] + yr[12 + q]);
+            __builtin_amdgcn_wave_barrier();
+            const float yv = fmaf(Dc, u, ysum);
             if constexpr (YF)
                 *reinterpret_cast<float*>(y_l + tt * XSF + cl * 4) = yv;
             else if constexpr (ES == 2)
@@ -439,6 +468,11 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int64_t tok0,
             const int n_g = (t_end - tb + 3) / 4;
             for (int g = 0; g < n_g; ++g) group(g, false, tb);
         }
+        // this tile's last HX inputs become the next tile's history rows: read
+        // them now, write them once every wave is past this tile
+        float hx = 0.0f;
+        if constexpr (K > 0)
+            if (tid < HX * 64) hx = xf_l[(TT + (tid >> 6)) * XPF + (tid & 63)];
         __syncthreads();  // tile fully read (and y tile fully written)
         if constexpr (MODE == 1) {
             const auto ry = rsrc(yg, tb, row_stride);
@@ -468,7 +502,11 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int64_t tok0,
                 __builtin_amdgcn_raw_buffer_store_b128(yv, ry, xoff[r], 0, 0);
             }
         }
-        if (more) store_tile();
+        if (more) {
+            store_tile();
+            if constexpr (K > 0)
+                if (tid < HX * 64) xf_l[(tid >> 6) * XPF + (tid & 63)] = hx;
+        }
         __syncthreads();
     }
 }
