@@ -79,7 +79,10 @@ enum {
 /* Device-side error bits, read back with ssm_get_device_error(). */
 enum {
     SSM_DEVERR_IDS = 1u,     /* an ids[i] was outside [0, n_state_rows) */
-    SSM_DEVERR_SEQLENS = 2u  /* a cu_seqlens span was invalid (selective_scan_fwd_ext) */
+    SSM_DEVERR_SEQLENS = 2u, /* a cu_seqlens span was invalid (selective_scan_fwd_ext) */
+    SSM_DEVERR_RELAY = 4u    /* a forward workgroup gave up waiting for the state of the
+                                time piece before its own (only if the device stalls
+                                for seconds); that call's y and state are unreliable */
 };
 
 typedef struct ssm_scan_desc {
@@ -269,9 +272,11 @@ int selective_scan_fwd_ext(const ssm_scan_desc *desc, const ssm_scan_ext *ext, c
  * 256-byte aligned: "none" (nothing to compute), "time_split" (few
  * (sequence, channel) rows: tokens split across the waves of a workgroup),
  * "quad" or "quad_chunked" (the Mamba-1 form, d_state <= 16, without or with
- * time chunks), "ssd" (the Mamba-2 form on MFMA) or "rows" (every other
- * shape).  NULL if the descriptor or ext is invalid.  Host only; reads no
- * device memory.  For profiling and tests. */
+ * time chunks), "quad_relay" (as "quad", with the last jobs of an uneven grid
+ * cut into time pieces that hand their state on, on the current device),
+ * "ssd" (the Mamba-2 form on MFMA) or "rows" (every other shape).  NULL if
+ * the descriptor or ext is invalid.  Host only; reads no device memory (it
+ * may query the current device's properties).  For profiling and tests. */
 const char *ssm_scan_fwd_plan(const ssm_scan_desc *desc, const ssm_scan_ext *ext);
 
 /* selective_scan_bwd: reverse-time adjoint of selective_scan_fwd without the

@@ -17,7 +17,7 @@ SSM_OK, SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_DTYPE, SSM_ERR_UNSUPPORTED, \
     SSM_ERR_WORKSPACE, SSM_ERR_ALIGN, SSM_ERR_HIP = range(8)
 SSM_F32, SSM_BF16 = 0, 1
 SSM_HAS_D, SSM_DT_SOFTPLUS = 1, 2
-SSM_DEVERR_IDS, SSM_DEVERR_SEQLENS = 1, 2
+SSM_DEVERR_IDS, SSM_DEVERR_SEQLENS, SSM_DEVERR_RELAY = 1, 2, 4
 
 EXPORTS = ("ssm_status_str", "ssm_version", "ssm_scan_out_bytes", "ssm_scan_state_offset_bytes",
            "ssm_scan_dgrad_layout", "ssm_scan_workspace_bytes", "ssm_conv_fwd",

@@ -25,12 +25,26 @@
 // associative scan); kernel 3 re-scans every chunk from its carried-in state
 // and writes y and the final state.
 //
+// Relay (aligned case, no chunks, equal lengths).  The scan of a (sequence,
+// 64-channel block) job is serial in time, so a grid of n jobs on m compute
+// units finishes after ceil(n/m) job lengths even when n/m is 2.5.  To even
+// this out, the last n mod m jobs are cut in time into k pieces (k = m / (n
+// mod m)), so every unit runs its full jobs plus about one piece.  Piece j+1
+// starts from the state piece j ends with: piece j stores it, fences at agent
+// scope and raises a per-job flag; piece j+1 waits for the flag, then reads
+// it.  Pieces are numbered after all full jobs and in piece order, so any
+// piece that waits was dispatched after the one it waits for, and that one
+// never waits on anything later: every wait ends.  A wait is still bounded;
+// if the bound runs out the device error word gets SSM_DEVERR_RELAY.
+//
 // Extras (selective_scan_fwd_ext).  The dt bias is added where dt is read,
 // before softplus; the gate y * SiLU(z) is applied where y is written (in the
 // tiled variant on the 16-byte rows that leave LDS, with z read along the
 // same rows).  With spans on a packed token axis every workgroup takes its
 // sequence's first token and length; a chunk past the end of its sequence
 // is empty, which the carry treats as the identity.
+#include <atomic>
+
 #include "device_common.h"
 #include "ssm_internal.h"
 
@@ -69,7 +83,14 @@ struct QuadKP {
     int n_chunks;
     int has_D, softplus;
     int tiled;       // 1: aligned case, use quad_tiled
+    // relay (quad_out only; relay_k == 0: off): blocks [0, relay_full) are
+    // full jobs, then relay_k rounds of relay_rem pieces of chunk_len tokens
+    int relay_full, relay_rem, relay_k;
+    int* relay_flag;     // [relay_rem]  pieces of the job allowed to start
+    float* relay_h;      // [relay_rem][64][16] state handed to the next piece
 };
+
+constexpr int kRelaySpinMax = 1 << 24;  // polls before a wait gives up
 
 template <typename T>
 __device__ __forceinline__ float ld(const T* p) { return to_f32(*p); }
@@ -574,11 +595,28 @@ __global__ __launch_bounds__(256) void quad_carry(QuadKP p) {
 template <typename T, int K, bool TILED, bool SOFTPLUS, bool GATE>
 __global__ __launch_bounds__(kThreads) void quad_out(QuadKP p) {
     const int q = threadIdx.x & 3;
-    const int c_raw = blockIdx.x * kChanPerBlock + (threadIdx.x >> 2);
+    int cbk = blockIdx.x, i = blockIdx.y, chunk = blockIdx.z;
+    int piece = -1, sj = 0;  // relay: piece of split job sj, or -1 for a full job
+    if (TILED && p.relay_k) {  // 1-D grid
+        const int cblocks = p.d_inner / kChanPerBlock;
+        int job = blockIdx.x;
+        if (job >= p.relay_full) {
+            const int pb = job - p.relay_full;
+            piece = pb / p.relay_rem;
+            sj = pb - piece * p.relay_rem;
+            job = p.relay_full + sj;
+        }
+        cbk = job % cblocks;
+        i = job / cblocks;
+        chunk = 0;
+    }
+    // the pieces of a split job run one after another, so their waves go
+    // first at the instruction arbiter; the full jobs beside them take the
+    // issue slots the pieces leave
+    if (piece >= 0) __builtin_amdgcn_s_setprio(2);
+    const int c_raw = cbk * kChanPerBlock + (threadIdx.x >> 2);
     const bool active = c_raw < p.d_inner;
     const int c = active ? c_raw : p.d_inner - 1;
-    const int i = blockIdx.y;
-    const int chunk = blockIdx.z;
     int r = p.ids[i];
     const SeqSpan sp = seq_span(p.cu, i, p.L, p.T);
     const bool bad_id = (r < 0) | (r >= p.R);
@@ -590,25 +628,57 @@ __global__ __launch_bounds__(kThreads) void quad_out(QuadKP p) {
     }
     float h[4], a2[4];
     const int64_t rows = (int64_t)p.S * p.d_inner;
+    float* relay_h = piece >= 0 ? p.relay_h + ((int64_t)sj * kChanPerBlock + (threadIdx.x >> 2)) * 16 + 4 * q
+                                : nullptr;
+    if (piece > 0) {
+        // the previous piece's end state: one thread waits for the flag, the
+        // barrier holds the others, and each wave's own acquire fence makes
+        // the stores behind the flag visible to its loads
+        if (threadIdx.x == 0) {
+            int n = 0;
+            while (__hip_atomic_load(p.relay_flag + sj, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < piece) {
+                if (++n == kRelaySpinMax) {
+                    atomicOr(p.err, (uint32_t)SSM_DEVERR_RELAY);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(4);
+            }
+        }
+        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         const int n = 4 * q + s;
         a2[s] = n < p.N ? p.A[(int64_t)c * p.N + n] * kLog2e : 0.0f;
-        if (chunk == 0)
+        if (piece > 0)
+            h[s] = relay_h[s];
+        else if (chunk == 0)
             h[s] = n < p.N ? (bad ? __builtin_nanf("") : p.s[((int64_t)r * p.d_inner + c) * p.N + n])
                            : 0.0f;
         else
             h[s] = p.hin[((int64_t)chunk * rows + (int64_t)i * p.d_inner + c) * 16 + n];
     }
     float dt_acc = 0.0f;
-    const int t_begin = chunk * p.chunk_len;
-    const int t_end = min(sp.len, t_begin + p.chunk_len);
+    const int t_begin = (piece > 0 ? piece : chunk) * p.chunk_len;
+    const int t_end = min(sp.len, piece < 0 && p.relay_k ? sp.len : t_begin + p.chunk_len);
     if (t_begin < t_end) {  // workgroup-uniform
         if constexpr (TILED)
-            quad_tiled<T, K, 1, SOFTPLUS, GATE>(p, i, sp.t0, blockIdx.x, q, threadIdx.x >> 2, t_begin, t_end, h, a2,
+            quad_tiled<T, K, 1, SOFTPLUS, GATE>(p, i, sp.t0, cbk, q, threadIdx.x >> 2, t_begin, t_end, h, a2,
                                                 dt_acc, bad);
         else
             quad_chunk<T, K, 1>(p, i, sp.t0, c_raw, q, t_begin, t_end, h, a2, dt_acc, active, bad);
+    }
+    if (piece >= 0 && piece + 1 < p.relay_k) {
+        // hand the state on: every thread's stores reach agent scope before
+        // one thread raises the flag
+#pragma unroll
+        for (int s = 0; s < 4; ++s) relay_h[s] = h[s];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __syncthreads();
+        if (threadIdx.x == 0)
+            __hip_atomic_store(p.relay_flag + sj, piece + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        return;
     }
     if (active && chunk == p.n_chunks - 1) {
         float* so = p.state_out + ((int64_t)i * p.d_inner + c) * p.N;
@@ -662,10 +732,79 @@ __global__ __launch_bounds__(kThreads) void quad_ckpt(QuadKP p) {
         quad_chunk<T, 0, 2>(p, i, (int64_t)i * p.L, c_raw, q, 0, p.L, h, a2, dt_acc, active, bad);
 }
 
+__global__ __launch_bounds__(256) void relay_clear(int* flag, int n) {
+    for (int e = threadIdx.x; e < n; e += 256) flag[e] = 0;
+}
+
+constexpr int kRelayMaxJobs = 1024;  // split jobs the workspace has room for
+
+size_t relay_bytes(int64_t jobs) {
+    return align_up((size_t)jobs * kChanPerBlock * 16 * 4, 256) + align_up((size_t)jobs * 4, 256);
+}
+
+// Compute units of the current device (cached per device); 0 without one.
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+// Relay split for a grid of `jobs` equal jobs of L tokens (see the header):
+// sets kp.relay_{full,rem,k} and kp.chunk_len, or leaves relay_k at 0 when
+// the jobs already divide evenly, the resident blocks per compute unit
+// (cap) cannot hold the extra piece, or the pieces would be shorter than a
+// tile.
+void relay_split(QuadKP& kp, int64_t jobs, int cap, int n_cu, int tile) {
+    kp.relay_k = 0;
+    if (n_cu <= 0 || jobs < n_cu) return;
+    const int64_t full = jobs / n_cu, rem = jobs % n_cu;
+    if (rem == 0 || cap < full + 1 || rem > kRelayMaxJobs) return;
+    const int64_t k0 = n_cu / rem;
+    if (k0 < 2) return;
+    int64_t len = (kp.L + k0 - 1) / k0;
+    len = (len + tile - 1) / tile * tile;
+    const int64_t k = (kp.L + len - 1) / len;
+    if (k < 2) return;
+    kp.relay_full = (int)(full * n_cu);
+    kp.relay_rem = (int)rem;
+    kp.relay_k = (int)k;
+    kp.chunk_len = (int)len;
+}
+
+// dry: decide only (no launch); returns the relay pieces per split job.
 template <typename T, int K, bool TILED, bool SOFTPLUS, bool GATE = false>
-int launch_quad_t(const QuadKP& kp, hipStream_t st) {
+int launch_quad_t(QuadKP kp, hipStream_t st, int* relay_k_out) {
     const dim3 block(kThreads);
     const unsigned cblocks = (unsigned)((kp.d_inner + kChanPerBlock - 1) / kChanPerBlock);
+    if (TILED && kp.relay_h) {
+        static std::atomic<int> cap_cache[64];
+        int dev = 0, cap = 0;
+        const int n_cu = device_cus();
+        if (n_cu > 0 && hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+            cap = cap_cache[dev].load(std::memory_order_relaxed);
+            if (cap == 0 &&
+                hipOccupancyMaxActiveBlocksPerMultiprocessor(&cap, quad_out<T, K, TILED, SOFTPLUS, GATE>, kThreads,
+                                                             0) == hipSuccess)
+                cap_cache[dev].store(cap, std::memory_order_relaxed);
+        }
+        relay_split(kp, (int64_t)kp.S * cblocks, cap, n_cu, TileCfg<T>::TT);
+    }
+    if (relay_k_out) {
+        *relay_k_out = kp.relay_k;
+        return SSM_OK;
+    }
+    if (kp.relay_k) {
+        hipLaunchKernelGGL(relay_clear, dim3(1), dim3(256), 0, st, kp.relay_flag, kp.relay_rem);
+        const unsigned n_blocks = (unsigned)(kp.relay_full + kp.relay_rem * kp.relay_k);
+        hipLaunchKernelGGL((quad_out<T, K, TILED, SOFTPLUS, GATE>), dim3(n_blocks), block, 0, st, kp);
+        return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+    }
     if (kp.n_chunks > 1) {
         hipLaunchKernelGGL((quad_agg<T, K, TILED, SOFTPLUS>), dim3(cblocks, kp.S, kp.n_chunks - 1), block, 0,
                            st, kp);
@@ -677,15 +816,15 @@ int launch_quad_t(const QuadKP& kp, hipStream_t st) {
 }
 
 template <typename T, int K>
-int launch_quad(const QuadKP& kp, hipStream_t st) {
+int launch_quad(const QuadKP& kp, hipStream_t st, int* relay_k_out) {
     if (kp.tiled) {
         if (kp.z)
-            return kp.softplus ? launch_quad_t<T, K, true, true, true>(kp, st)
-                               : launch_quad_t<T, K, true, false, true>(kp, st);
-        return kp.softplus ? launch_quad_t<T, K, true, true>(kp, st)
-                           : launch_quad_t<T, K, true, false>(kp, st);
+            return kp.softplus ? launch_quad_t<T, K, true, true, true>(kp, st, relay_k_out)
+                               : launch_quad_t<T, K, true, false, true>(kp, st, relay_k_out);
+        return kp.softplus ? launch_quad_t<T, K, true, true>(kp, st, relay_k_out)
+                           : launch_quad_t<T, K, true, false>(kp, st, relay_k_out);
     }
-    return launch_quad_t<T, K, false, false>(kp, st);
+    return launch_quad_t<T, K, false, false>(kp, st, relay_k_out);
 }
 
 // Chunk length (tokens, multiple of 4) so that the grid has about
@@ -709,9 +848,19 @@ bool quad_supported(const Shape& sh) {
                                                                       sh.K == 3 || sh.K == 4);
 }
 
-size_t quad_workspace_bytes(const Shape& sh) {
+bool quad_chunked(const Shape& sh) {
     const int len = pick_chunk(sh);
-    if (len == 0 || len >= sh.L) return 0;
+    return len > 0 && len < sh.L;
+}
+
+size_t quad_workspace_bytes(const Shape& sh) {
+    if (!quad_chunked(sh)) {
+        // room for the relay of an aligned, unchunked grid
+        const int64_t jobs = sh.S * (sh.d_inner() / kChanPerBlock);
+        if (sh.N != 16 || sh.d_inner() % kChanPerBlock != 0 || jobs == 0 || sh.L < 2) return 0;
+        return relay_bytes(jobs < kRelayMaxJobs ? jobs : kRelayMaxJobs);
+    }
+    const int len = pick_chunk(sh);
     const int64_t n = (sh.L + len - 1) / len;
     const int64_t rows = sh.S * sh.d_inner();
     return (size_t)((n - 1) * rows * 16 + (n - 1) * rows + n * rows * 16) * 4 + 3 * 256;
@@ -750,7 +899,7 @@ int launch_quad_ckpt(const BwdArgs& a, float* ckpt, hipStream_t stream) {
     return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
-int launch_quad_fwd(const FwdArgs& a, hipStream_t stream) {
+int launch_quad_fwd(const FwdArgs& a, hipStream_t stream, int* relay_k_out) {
     const Shape& sh = a.sh;
     QuadKP kp;
     kp.s = a.s; kp.x = a.x; kp.dt = a.dt; kp.A = a.A; kp.B = a.B; kp.C = a.C; kp.D = a.D;
@@ -776,6 +925,17 @@ int launch_quad_fwd(const FwdArgs& a, hipStream_t stream) {
     kp.n_chunks = (int)((sh.L + len - 1) / len);
     if (kp.n_chunks < 1) kp.n_chunks = 1;
     kp.agg = kp.dtsum = kp.hin = nullptr;
+    kp.relay_full = kp.relay_rem = kp.relay_k = 0;
+    kp.relay_flag = nullptr;
+    kp.relay_h = nullptr;
+    if (kp.n_chunks == 1 && kp.tiled && !a.cu && sh.L >= 2) {
+        const int64_t jobs = sh.S * (sh.d_inner() / kChanPerBlock);
+        const int64_t room = jobs < kRelayMaxJobs ? jobs : kRelayMaxJobs;
+        if (a.ws && a.ws_bytes >= relay_bytes(room)) {
+            kp.relay_h = reinterpret_cast<float*>(a.ws);
+            kp.relay_flag = reinterpret_cast<int*>(a.ws + align_up((size_t)room * kChanPerBlock * 16 * 4, 256));
+        }
+    }
     if (kp.n_chunks > 1) {
         const int64_t rows = sh.S * sh.d_inner();
         char* w = a.ws;
@@ -789,10 +949,10 @@ int launch_quad_fwd(const FwdArgs& a, hipStream_t stream) {
     }
     const bool bf = sh.io == SSM_BF16;
     switch (sh.K) {
-        case 0: return bf ? launch_quad<bf16_t, 0>(kp, stream) : launch_quad<float, 0>(kp, stream);
-        case 2: return bf ? launch_quad<bf16_t, 2>(kp, stream) : launch_quad<float, 2>(kp, stream);
-        case 3: return bf ? launch_quad<bf16_t, 3>(kp, stream) : launch_quad<float, 3>(kp, stream);
-        case 4: return bf ? launch_quad<bf16_t, 4>(kp, stream) : launch_quad<float, 4>(kp, stream);
+        case 0: return bf ? launch_quad<bf16_t, 0>(kp, stream, relay_k_out) : launch_quad<float, 0>(kp, stream, relay_k_out);
+        case 2: return bf ? launch_quad<bf16_t, 2>(kp, stream, relay_k_out) : launch_quad<float, 2>(kp, stream, relay_k_out);
+        case 3: return bf ? launch_quad<bf16_t, 3>(kp, stream, relay_k_out) : launch_quad<float, 3>(kp, stream, relay_k_out);
+        case 4: return bf ? launch_quad<bf16_t, 4>(kp, stream, relay_k_out) : launch_quad<float, 4>(kp, stream, relay_k_out);
         default: return SSM_ERR_UNSUPPORTED;
     }
 }

@@ -336,7 +336,17 @@ const char* ssm_scan_fwd_plan(const ssm_scan_desc* desc, const ssm_scan_ext* ext
     switch (fwd_path(a)) {
         case FwdPath::kNone: return "none";
         case FwdPath::kTimeSplit: return "time_split";
-        case FwdPath::kQuad: return fwd_workspace_bytes(sh) > 0 ? "quad_chunked" : "quad";
+        case FwdPath::kQuad: {
+            if (quad_chunked(sh)) return "quad_chunked";
+            // the relay split depends on the current device (compute units,
+            // resident blocks) and needs the workspace the shape asks for
+            static char ws_probe[256] __attribute__((aligned(256)));
+            a.ws = ws_probe;
+            a.ws_bytes = fwd_workspace_bytes(sh);
+            int relay_k = 0;
+            launch_quad_fwd(a, nullptr, &relay_k);
+            return relay_k > 0 ? "quad_relay" : "quad";
+        }
         case FwdPath::kSsd: return "ssd";
         case FwdPath::kRows: return "rows";
     }

@@ -106,7 +106,10 @@ size_t bwd_workspace_bytes(const Shape& sh);
 // Mamba-1 forward for d_state <= 16 with four lanes per channel.
 bool quad_supported(const Shape& sh);
 size_t quad_workspace_bytes(const Shape& sh);
-int launch_quad_fwd(const FwdArgs& a, hipStream_t stream);
+bool quad_chunked(const Shape& sh);
+// relay_k_out: decide the launch without making it and report the relay
+// pieces per split job (0: no relay)
+int launch_quad_fwd(const FwdArgs& a, hipStream_t stream, int* relay_k_out = nullptr);
 
 // Mamba-1 forward, d_state 16, time split across the waves of a workgroup
 // (for batches with too few channels to fill the GPU otherwise).
