@@ -273,7 +273,9 @@ int selective_scan_fwd_ext(const ssm_scan_desc *desc, const ssm_scan_ext *ext, c
  * (sequence, channel) rows: tokens split across the waves of a workgroup),
  * "quad" or "quad_chunked" (the Mamba-1 form, d_state <= 16, without or with
  * time chunks), "quad_relay" (as "quad", with the last jobs of an uneven grid
- * cut into time pieces that hand their state on, on the current device),
+ * cut into time pieces that hand their state on, on the current device; the
+ * results are bitwise those of "quad", and the environment variable
+ * SSM_RELAY=0 turns the split off),
  * "ssd" (the Mamba-2 form on MFMA) or "rows" (every other shape).  NULL if
  * the descriptor or ext is invalid.  Host only; reads no device memory (it
  * may query the current device's properties).  For profiling and tests. */

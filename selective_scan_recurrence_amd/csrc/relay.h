@@ -1,0 +1,94 @@
+// Relay split of an uneven grid of serial jobs (shared by the forward and
+// backward kernels whose workgroups each run one recurrence through time).
+//
+// A grid of n equal jobs on m compute units, whose workgroups all stay
+// resident, finishes after ceil(n/m) job lengths even when n/m is 1.25 or
+// 2.5.  The relay keeps floor(n/m) whole jobs per unit and cuts each of the
+// remaining n mod m jobs in time into k = m / (n mod m) pieces, one per unit
+// that has room.  Piece j + 1 starts from the state piece j ends with
+// (forward in time, or backward for the adjoint): piece j stores it, fences at
+// agent scope and raises a per-job flag; piece j + 1 waits for the flag and
+// then reads the state.  Block numbers put every whole job first and then the
+// pieces in chain order, and the dispatcher hands out workgroups in number
+// order, so a piece that waits was dispatched after the piece it waits for,
+// and that one never waits on anything later: every wait ends.  Pieces raise
+// their wave priority so that each chain, which is serial, ends with the
+// whole jobs that share its units.  A wait is still bounded; if the bound
+// runs out, SSM_DEVERR_RELAY is set in the error word.  The split changes no
+// arithmetic: pieces start on tile boundaries and pass on every running
+// value, so results are bitwise those of the unsplit grid.  Setting the
+// environment variable SSM_RELAY to 0 turns the split off (for callers that
+// share the device with other work, where the units may not hold the grid).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ssm.h"
+
+namespace ssm {
+
+struct RelaySplit {
+    int full = 0;  // blocks [0, full) are whole jobs
+    int rem = 0;   // jobs cut into pieces (job full + j for j < rem)
+    int k = 0;     // pieces per cut job; 0: no relay
+    int len = 0;   // tokens per piece (a multiple of tile)
+};
+
+// Host: the split for `jobs` jobs of L tokens, pieces a multiple of `tile`
+// tokens, `cap` resident workgroups per compute unit, n_cu units, at most
+// max_jobs cut jobs (the workspace's room).  k == 0 when the jobs divide
+// evenly, the units cannot hold one more workgroup, or pieces would be
+// shorter than a tile.
+RelaySplit relay_split(int64_t jobs, int64_t L, int tile, int cap, int n_cu, int max_jobs);
+
+// Host: compute units of the current device, 0 without one (cached).
+int device_cus();
+
+// Host: resident workgroups per compute unit for kernel fn at `threads`
+// threads and no dynamic LDS on the current device, 0 on error (cached).
+int resident_blocks(const void* fn, int threads);
+
+// Block b of a relay grid: the job it runs and its piece (-1: whole job).
+struct RelayBlock {
+    int job, piece, cut;  // cut: index of the cut job (piece >= 0)
+};
+__device__ __forceinline__ RelayBlock relay_block(int b, int full, int rem) {
+    if (b < full) return RelayBlock{b, -1, 0};
+    const int pb = b - full, piece = pb / rem, cut = pb - piece * rem;
+    return RelayBlock{full + cut, piece, cut};
+}
+
+// Wait until *flag >= want: thread 0 polls, the barrier holds the other
+// threads, and each wave's agent-scope acquire fence then makes the stores
+// the flag publishes visible to its loads.  Every thread of the workgroup
+// must call it.
+__device__ __forceinline__ void relay_wait(const int* flag, int want, uint32_t* err) {
+    if (threadIdx.x == 0) {
+        constexpr int kSpinMax = 1 << 24;  // about ten seconds of polls
+        int n = 0;
+        while (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < want) {
+            if (++n == kSpinMax) {
+                atomicOr(err, (uint32_t)SSM_DEVERR_RELAY);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(4);
+        }
+    }
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// Publish this workgroup's state stores: every thread's stores reach agent
+// scope before thread 0 raises the flag to `value`.  Every thread of the
+// workgroup must call it, after its own stores.
+__device__ __forceinline__ void relay_publish(int* flag, int value) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(flag, value, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Zero n relay flags (one workgroup of 256 threads), before the relay grid.
+__global__ void relay_clear(int* flag, int n);
+
+}  // namespace ssm

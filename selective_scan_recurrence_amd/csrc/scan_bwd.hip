@@ -27,9 +27,15 @@
 // LDS, across channel blocks by kernel 3.  Kernel 3 also sums dA and dD over
 // sequences and gathers dh_0 into d_s by ids; every sum has a fixed order,
 // so results are bitwise repeatable.
+//
+// Relay (fast path): the (sequence, 64-channel block) jobs beyond a whole
+// number per compute unit are cut into pieces of whole blocks, run from the
+// last piece to the first; each hands on its adjoint g and its running dA and
+// dD sums, so every sum keeps the unsplit order (relay.h).
 #include <type_traits>
 
 #include "device_common.h"
+#include "relay.h"
 #include "ssm_internal.h"
 
 namespace ssm {
@@ -58,7 +64,16 @@ struct BwdKP {
     float* ds_part;      // [S][d_inner][16]
     int L, d_inner, N, R, S, n_cb;
     int has_D, softplus;
+    // relay (bwd_fast; relay_k == 0: off): blocks [0, relay_full) are whole
+    // jobs, then relay_k rounds of relay_rem pieces of relay_len checkpoint
+    // blocks, piece 0 being the last in time
+    int relay_full, relay_rem, relay_k, relay_len;
+    int* relay_flag;     // [relay_rem]
+    float* relay_buf;    // [relay_rem][9][256]: g (4), dA sums (4), dD sum per lane
+    uint32_t* err;       // nullable device-error word
 };
+
+constexpr int kRelayMaxJobs = 256;  // cut jobs the workspace has room for
 
 template <int P0, int P1, int P2, int P3>
 __device__ __forceinline__ float qperm(float v) {
@@ -300,7 +315,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const int wave = tid >> 6;
     const int row = (tid >> 4) & 3;     // 16-lane row within the wave
     const int lane_in_row = tid & 15;
-    const int cb = blockIdx.x, i = blockIdx.y;
+    int cb = blockIdx.x, i = blockIdx.y;
+    const int n_blk = (p.L + kBlk - 1) / kBlk;
+    int b_lo = 0, b_hi = n_blk;  // checkpoint blocks [b_lo, b_hi) of this workgroup
+    RelayBlock rb{0, -1, 0};
+    if (p.relay_k) {  // 1-D grid
+        rb = relay_block(blockIdx.x, p.relay_full, p.relay_rem);
+        cb = rb.job % p.n_cb;
+        i = rb.job / p.n_cb;
+        if (rb.piece >= 0) {
+            // the adjoint runs backwards in time: piece 0 takes the last blocks
+            __builtin_amdgcn_s_setprio(2);  // a piece chain goes first (relay.h)
+            b_hi = n_blk - rb.piece * p.relay_len;
+            b_lo = max(0, b_hi - p.relay_len);
+        }
+    }
     const int c = cb * kChan + cl;
     const int L = p.L, d_inner = p.d_inner;
     const int64_t seq = (int64_t)i * L * d_inner;
@@ -317,7 +346,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const float Dc = p.has_D ? p.D[c] : 0.0f;
     float g[4], dA_acc[4] = {0.f, 0.f, 0.f, 0.f};
     float dD_acc = 0.0f;
-    {
+    float* relay = rb.piece >= 0 ? p.relay_buf + (int64_t)rb.cut * 9 * kThreads + tid : nullptr;
+    if (rb.piece > 0) {  // the later piece's adjoint and running sums
+        relay_wait(p.relay_flag + rb.cut, rb.piece, p.err);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            g[s] = relay[s * kThreads];
+            dA_acc[s] = relay[(4 + s) * kThreads];
+        }
+        dD_acc = relay[8 * kThreads];
+    } else {
         const float4 gv = *reinterpret_cast<const float4*>(p.dstate + ((int64_t)i * d_inner + c) * 16 + 4 * q);
         g[0] = gv.x; g[1] = gv.y; g[2] = gv.z; g[3] = gv.w;
     }
@@ -330,7 +368,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const char* bg = static_cast<const char*>(p.B) + (int64_t)i * L * 16 * ES;
     const char* cg = static_cast<const char*>(p.C) + (int64_t)i * L * 16 * ES;
     const int64_t xrow = (int64_t)d_inner * ES;
-    const int n_blk = (L + kBlk - 1) / kBlk;
     const float* ckpt = p.ckpt;
     const int S = p.S;
     float* d_x = p.d_x + seq + (int64_t)cb * kChan;
@@ -421,11 +458,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
     };
 
-    load_tile(n_blk - 1);
-    store_tile((n_blk - 1) & 1, n_blk - 1);
-    load_tile(n_blk - 2);
+    load_tile(b_hi - 1);
+    store_tile((b_hi - 1) & 1, b_hi - 1);
+    load_tile(b_hi - 2);
     __syncthreads();
-    for (int b = n_blk - 1; b >= 0; --b) {
+    for (int b = b_hi - 1; b >= b_lo; --b) {
         const int t0 = b * kBlk, buf = b & 1;
         const int nk = min(kBlk, L - t0);
         const float* xs = xs_l[buf];
@@ -529,7 +566,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         float4 gxv = *reinterpret_cast<const float4*>(&gx_l[tg * 4]);
         float4 gdv = *reinterpret_cast<const float4*>(&gdt_l[tg * 4]);
         // next block's tiles into the other buffer; fetch the one after
-        if (b > 0) store_tile(buf ^ 1, b - 1);
+        if (b > b_lo) store_tile(buf ^ 1, b - 1);
         load_tile(b - 2);
 #pragma unroll
         for (int u = 0; u < NBC; ++u) {
@@ -551,6 +588,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             }
         }
         __syncthreads();
+    }
+    if (rb.piece >= 0 && rb.piece + 1 < p.relay_k) {  // hand on to the earlier piece
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            relay[s * kThreads] = g[s];
+            relay[(4 + s) * kThreads] = dA_acc[s];
+        }
+        relay[8 * kThreads] = dD_acc;
+        relay_publish(p.relay_flag + rb.cut, rb.piece + 1);
+        return;
     }
     {
         const int64_t row_i = ((int64_t)i * d_inner + c) * 16 + 4 * q;
@@ -612,8 +659,15 @@ size_t blocks_of(const Shape& sh) { return (size_t)((sh.L + kBlk - 1) / kBlk); }
 
 struct BwdWs {
     float *ckpt, *dbc, *dA, *dD, *ds;
+    char* relay;   // the relay of bwd_fast
+    size_t relay_bytes;
     size_t total;
 };
+
+size_t relay_room(const Shape& sh) {
+    const int64_t jobs = sh.S * ((sh.d_inner() + kChan - 1) / kChan);
+    return (size_t)(jobs < kRelayMaxJobs ? jobs : kRelayMaxJobs);
+}
 
 BwdWs carve(const Shape& sh, char* base) {
     const size_t rows = (size_t)sh.S * sh.d_inner();
@@ -626,6 +680,9 @@ BwdWs carve(const Shape& sh, char* base) {
     w.dA = take(rows * 16 * 4);
     w.dD = take(rows * 4);
     w.ds = take(rows * 16 * 4);
+    const size_t room = relay_room(sh);
+    w.relay_bytes = align_up(room * 9 * kThreads * 4, 256) + align_up(room * 4, 256);
+    w.relay = reinterpret_cast<char*>(take(w.relay_bytes));
     w.total = off;
     return w;
 }
@@ -642,7 +699,28 @@ size_t bwd_workspace_bytes(const Shape& sh) {
     return rows_bwd_supported(sh) ? rows_bwd_workspace_bytes(sh) : 0;
 }
 
-int launch_quad_ckpt(const BwdArgs& a, float* ckpt, hipStream_t stream);
+template <typename T, bool SOFTPLUS>
+int launch_fast(BwdKP kp, const BwdWs& w, const Shape& sh, hipStream_t stream) {
+    auto fn = bwd_fast<T, SOFTPLUS>;
+    const int64_t jobs = (int64_t)kp.n_cb * kp.S;
+    const int n_cu = device_cus();
+    const int cap = n_cu > 0 ? resident_blocks((const void*)fn, kThreads) : 0;
+    const RelaySplit rs = relay_split(jobs, blocks_of(sh), 1, cap, n_cu, (int)relay_room(sh));
+    if (rs.k) {
+        char* r = w.relay;
+        kp.relay_buf = reinterpret_cast<float*>(r);
+        kp.relay_flag = reinterpret_cast<int*>(r + align_up(relay_room(sh) * 9 * kThreads * 4, 256));
+        kp.relay_full = rs.full;
+        kp.relay_rem = rs.rem;
+        kp.relay_k = rs.k;
+        kp.relay_len = rs.len;
+        hipLaunchKernelGGL(relay_clear, dim3(1), dim3(256), 0, stream, kp.relay_flag, rs.rem);
+        hipLaunchKernelGGL(fn, dim3((unsigned)(rs.full + rs.rem * rs.k)), dim3(kThreads), 0, stream, kp);
+    } else {
+        hipLaunchKernelGGL(fn, dim3((unsigned)kp.n_cb, (unsigned)kp.S), dim3(kThreads), 0, stream, kp);
+    }
+    return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
 
 int launch_scan_bwd(const BwdArgs& a, hipStream_t stream) {
     const Shape& sh = a.sh;
@@ -651,7 +729,7 @@ int launch_scan_bwd(const BwdArgs& a, hipStream_t stream) {
     const int64_t per_row = sh.d_inner() * sh.N;
     BwdKP kp = {};
     kp.A = a.A; kp.D = a.D; kp.ids = a.ids; kp.x = a.x; kp.dt = a.dt; kp.B = a.B; kp.C = a.C;
-    kp.dy = a.dy; kp.dstate = a.dstate; kp.d_x = a.d_x; kp.d_dt = a.d_dt;
+    kp.dy = a.dy; kp.dstate = a.dstate; kp.d_x = a.d_x; kp.d_dt = a.d_dt; kp.err = a.err;
     kp.L = (int)sh.L; kp.d_inner = (int)sh.d_inner(); kp.N = (int)sh.N; kp.R = (int)sh.R;
     kp.S = (int)sh.S; kp.n_cb = (int)((sh.d_inner() + kChan - 1) / kChan);
     kp.has_D = (sh.flags & SSM_HAS_D) ? 1 : 0;
@@ -678,13 +756,11 @@ int launch_scan_bwd(const BwdArgs& a, hipStream_t stream) {
                       al16(a.dy) && al16(a.B) && al16(a.C) && al16(a.A) && al16(a.dstate) &&
                       al16(a.d_x) && al16(a.d_dt);
     if (fast) {
-        if (bf) {
-            if (kp.softplus) hipLaunchKernelGGL((bwd_fast<bf16_t, true>), grid, dim3(kThreads), 0, stream, kp);
-            else hipLaunchKernelGGL((bwd_fast<bf16_t, false>), grid, dim3(kThreads), 0, stream, kp);
-        } else {
-            if (kp.softplus) hipLaunchKernelGGL((bwd_fast<float, true>), grid, dim3(kThreads), 0, stream, kp);
-            else hipLaunchKernelGGL((bwd_fast<float, false>), grid, dim3(kThreads), 0, stream, kp);
-        }
+        if (bf) rc = kp.softplus ? launch_fast<bf16_t, true>(kp, w, sh, stream)
+                                 : launch_fast<bf16_t, false>(kp, w, sh, stream);
+        else rc = kp.softplus ? launch_fast<float, true>(kp, w, sh, stream)
+                              : launch_fast<float, false>(kp, w, sh, stream);
+        if (rc) return rc;
     } else if (bf) {
         if (kp.softplus) hipLaunchKernelGGL((bwd_rev<bf16_t, true>), grid, dim3(kThreads), 0, stream, kp);
         else hipLaunchKernelGGL((bwd_rev<bf16_t, false>), grid, dim3(kThreads), 0, stream, kp);

@@ -25,17 +25,9 @@
 // associative scan); kernel 3 re-scans every chunk from its carried-in state
 // and writes y and the final state.
 //
-// Relay (aligned case, no chunks, equal lengths).  The scan of a (sequence,
-// 64-channel block) job is serial in time, so a grid of n jobs on m compute
-// units finishes after ceil(n/m) job lengths even when n/m is 2.5.  To even
-// this out, the last n mod m jobs are cut in time into k pieces (k = m / (n
-// mod m)), so every unit runs its full jobs plus about one piece.  Piece j+1
-// starts from the state piece j ends with: piece j stores it, fences at agent
-// scope and raises a per-job flag; piece j+1 waits for the flag, then reads
-// it.  Pieces are numbered after all full jobs and in piece order, so any
-// piece that waits was dispatched after the one it waits for, and that one
-// never waits on anything later: every wait ends.  A wait is still bounded;
-// if the bound runs out the device error word gets SSM_DEVERR_RELAY.
+// Relay (aligned case, no chunks, equal lengths): the (sequence, 64-channel
+// block) jobs beyond a whole number per compute unit are cut into time
+// pieces that hand on their fp32 state (relay.h).
 //
 // Extras (selective_scan_fwd_ext).  The dt bias is added where dt is read,
 // before softplus; the gate y * SiLU(z) is applied where y is written (in the
@@ -43,9 +35,8 @@
 // same rows).  With spans on a packed token axis every workgroup takes its
 // sequence's first token and length; a chunk past the end of its sequence
 // is empty, which the carry treats as the identity.
-#include <atomic>
-
 #include "device_common.h"
+#include "relay.h"
 #include "ssm_internal.h"
 
 namespace ssm {
@@ -89,8 +80,6 @@ struct QuadKP {
     int* relay_flag;     // [relay_rem]  pieces of the job allowed to start
     float* relay_h;      // [relay_rem][64][16] state handed to the next piece
 };
-
-constexpr int kRelaySpinMax = 1 << 24;  // polls before a wait gives up
 
 template <typename T>
 __device__ __forceinline__ float ld(const T* p) { return to_f32(*p); }
@@ -596,18 +585,14 @@ template <typename T, int K, bool TILED, bool SOFTPLUS, bool GATE>
 __global__ __launch_bounds__(kThreads) void quad_out(QuadKP p) {
     const int q = threadIdx.x & 3;
     int cbk = blockIdx.x, i = blockIdx.y, chunk = blockIdx.z;
-    int piece = -1, sj = 0;  // relay: piece of split job sj, or -1 for a full job
+    int piece = -1, sj = 0;  // relay: piece of cut job sj, or -1 for a whole job
     if (TILED && p.relay_k) {  // 1-D grid
         const int cblocks = p.d_inner / kChanPerBlock;
-        int job = blockIdx.x;
-        if (job >= p.relay_full) {
-            const int pb = job - p.relay_full;
-            piece = pb / p.relay_rem;
-            sj = pb - piece * p.relay_rem;
-            job = p.relay_full + sj;
-        }
-        cbk = job % cblocks;
-        i = job / cblocks;
+        const RelayBlock rb = relay_block(blockIdx.x, p.relay_full, p.relay_rem);
+        piece = rb.piece;
+        sj = rb.cut;
+        cbk = rb.job % cblocks;
+        i = rb.job / cblocks;
         chunk = 0;
     }
     // the pieces of a split job run one after another, so their waves go
@@ -630,23 +615,7 @@ __global__ __launch_bounds__(kThreads) void quad_out(QuadKP p) {
     const int64_t rows = (int64_t)p.S * p.d_inner;
     float* relay_h = piece >= 0 ? p.relay_h + ((int64_t)sj * kChanPerBlock + (threadIdx.x >> 2)) * 16 + 4 * q
                                 : nullptr;
-    if (piece > 0) {
-        // the previous piece's end state: one thread waits for the flag, the
-        // barrier holds the others, and each wave's own acquire fence makes
-        // the stores behind the flag visible to its loads
-        if (threadIdx.x == 0) {
-            int n = 0;
-            while (__hip_atomic_load(p.relay_flag + sj, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < piece) {
-                if (++n == kRelaySpinMax) {
-                    atomicOr(p.err, (uint32_t)SSM_DEVERR_RELAY);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(4);
-            }
-        }
-        __syncthreads();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    }
+    if (piece > 0) relay_wait(p.relay_flag + sj, piece, p.err);  // the previous piece's end state
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         const int n = 4 * q + s;
@@ -670,14 +639,9 @@ __global__ __launch_bounds__(kThreads) void quad_out(QuadKP p) {
             quad_chunk<T, K, 1>(p, i, sp.t0, c_raw, q, t_begin, t_end, h, a2, dt_acc, active, bad);
     }
     if (piece >= 0 && piece + 1 < p.relay_k) {
-        // hand the state on: every thread's stores reach agent scope before
-        // one thread raises the flag
 #pragma unroll
-        for (int s = 0; s < 4; ++s) relay_h[s] = h[s];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __syncthreads();
-        if (threadIdx.x == 0)
-            __hip_atomic_store(p.relay_flag + sj, piece + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        for (int s = 0; s < 4; ++s) relay_h[s] = h[s];  // hand the state on
+        relay_publish(p.relay_flag + sj, piece + 1);
         return;
     }
     if (active && chunk == p.n_chunks - 1) {
@@ -732,49 +696,10 @@ __global__ __launch_bounds__(kThreads) void quad_ckpt(QuadKP p) {
         quad_chunk<T, 0, 2>(p, i, (int64_t)i * p.L, c_raw, q, 0, p.L, h, a2, dt_acc, active, bad);
 }
 
-__global__ __launch_bounds__(256) void relay_clear(int* flag, int n) {
-    for (int e = threadIdx.x; e < n; e += 256) flag[e] = 0;
-}
-
-constexpr int kRelayMaxJobs = 1024;  // split jobs the workspace has room for
+constexpr int kRelayMaxJobs = 1024;  // cut jobs the workspace has room for
 
 size_t relay_bytes(int64_t jobs) {
     return align_up((size_t)jobs * kChanPerBlock * 16 * 4, 256) + align_up((size_t)jobs * 4, 256);
-}
-
-// Compute units of the current device (cached per device); 0 without one.
-int device_cus() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    int v = cache[dev].load(std::memory_order_relaxed);
-    if (v == 0) {
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        cache[dev].store(v, std::memory_order_relaxed);
-    }
-    return v;
-}
-
-// Relay split for a grid of `jobs` equal jobs of L tokens (see the header):
-// sets kp.relay_{full,rem,k} and kp.chunk_len, or leaves relay_k at 0 when
-// the jobs already divide evenly, the resident blocks per compute unit
-// (cap) cannot hold the extra piece, or the pieces would be shorter than a
-// tile.
-void relay_split(QuadKP& kp, int64_t jobs, int cap, int n_cu, int tile) {
-    kp.relay_k = 0;
-    if (n_cu <= 0 || jobs < n_cu) return;
-    const int64_t full = jobs / n_cu, rem = jobs % n_cu;
-    if (rem == 0 || cap < full + 1 || rem > kRelayMaxJobs) return;
-    const int64_t k0 = n_cu / rem;
-    if (k0 < 2) return;
-    int64_t len = (kp.L + k0 - 1) / k0;
-    len = (len + tile - 1) / tile * tile;
-    const int64_t k = (kp.L + len - 1) / len;
-    if (k < 2) return;
-    kp.relay_full = (int)(full * n_cu);
-    kp.relay_rem = (int)rem;
-    kp.relay_k = (int)k;
-    kp.chunk_len = (int)len;
 }
 
 // dry: decide only (no launch); returns the relay pieces per split job.
@@ -783,17 +708,15 @@ int launch_quad_t(QuadKP kp, hipStream_t st, int* relay_k_out) {
     const dim3 block(kThreads);
     const unsigned cblocks = (unsigned)((kp.d_inner + kChanPerBlock - 1) / kChanPerBlock);
     if (TILED && kp.relay_h) {
-        static std::atomic<int> cap_cache[64];
-        int dev = 0, cap = 0;
         const int n_cu = device_cus();
-        if (n_cu > 0 && hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
-            cap = cap_cache[dev].load(std::memory_order_relaxed);
-            if (cap == 0 &&
-                hipOccupancyMaxActiveBlocksPerMultiprocessor(&cap, quad_out<T, K, TILED, SOFTPLUS, GATE>, kThreads,
-                                                             0) == hipSuccess)
-                cap_cache[dev].store(cap, std::memory_order_relaxed);
+        const int cap = n_cu > 0 ? resident_blocks((const void*)quad_out<T, K, TILED, SOFTPLUS, GATE>, kThreads) : 0;
+        const RelaySplit rs = relay_split((int64_t)kp.S * cblocks, kp.L, TileCfg<T>::TT, cap, n_cu, kRelayMaxJobs);
+        if (rs.k) {
+            kp.relay_full = rs.full;
+            kp.relay_rem = rs.rem;
+            kp.relay_k = rs.k;
+            kp.chunk_len = rs.len;
         }
-        relay_split(kp, (int64_t)kp.S * cblocks, cap, n_cu, TileCfg<T>::TT);
     }
     if (relay_k_out) {
         *relay_k_out = kp.relay_k;

@@ -110,6 +110,8 @@ bool quad_chunked(const Shape& sh);
 // relay_k_out: decide the launch without making it and report the relay
 // pieces per split job (0: no relay)
 int launch_quad_fwd(const FwdArgs& a, hipStream_t stream, int* relay_k_out = nullptr);
+// The backward's checkpoint pass: the state entering every kCkpt-token block into ckpt.
+int launch_quad_ckpt(const BwdArgs& a, float* ckpt, hipStream_t stream);
 
 // Mamba-1 forward, d_state 16, time split across the waves of a workgroup
 // (for batches with too few channels to fill the GPU otherwise).

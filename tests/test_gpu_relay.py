@@ -19,6 +19,7 @@ import ssm_inputs
 import selective_scan_recurrence_amd as ssm
 from selective_scan_recurrence_amd import ops
 from tests.gpu_util import assert_close, desc_of, device_inputs, host
+from tests.test_gpu_bwd import _compare_all, _run_bwd
 
 pytestmark = pytest.mark.gpu
 
@@ -136,3 +137,66 @@ def test_relay_carries_nan_of_invalid_id(gpu):
                                    conv_state=v("conv_state"))
     assert_close(y[0:1], y_o, "bf16", "valid sequence y")
     assert_close(st[0:1], st_o, "bf16", "valid sequence state")
+
+
+
+def _no_relay(fn):
+    """fn() with the relay split turned off (SSM_RELAY=0, read at every launch)."""
+    import os
+    old = os.environ.get("SSM_RELAY")
+    os.environ["SSM_RELAY"] = "0"
+    try:
+        return fn()
+    finally:
+        if old is None:
+            del os.environ["SSM_RELAY"]
+        else:
+            os.environ["SSM_RELAY"] = old
+
+
+@pytest.mark.parametrize("kind,io,d_conv,L", [("half", "bf16", 4, 600), ("three", "f32", 0, 333)])
+def test_forward_relay_bitwise_equals_unsplit(gpu, kind, io, d_conv, L):
+    """Pieces start on tile boundaries and pass the fp32 state on, so the
+    split grid's y, state and conv state are bitwise those of the unsplit one."""
+    p = ssm_inputs.make_problem(n_seqs=1, n_tokens=L, n_head=64 * _jobs(kind), d_state=16,
+                                d_conv=d_conv, io=io, seed=0x401, h0_std=0.3,
+                                conv_state_std=0.5 if d_conv else None)
+    d = desc_of(p)
+    assert ssm.ssm_scan_fwd_plan(d) == "quad_relay"
+    assert _no_relay(lambda: ssm.ssm_scan_fwd_plan(d)) == "quad"
+    t = device_inputs(p)
+
+    def run():
+        r = ops.scan_fwd(d, t["s"], t["x"], t["dt"], t["A"], t["B"], t["C"], t.get("D"), t["ids"],
+                         conv_w=t.get("conv_w"), conv_state=t.get("conv_state"),
+                         want_conv_state=True)
+        torch.cuda.synchronize()
+        return r
+
+    a, b = run(), _no_relay(run)
+    assert torch.equal(a.out, b.out)
+    if d_conv > 1:
+        assert torch.equal(a.conv_state, b.conv_state)
+
+
+@pytest.mark.parametrize("S,jobs_kind,L,io,softplus", [
+    (8, "half", 256, "bf16", False),   # the 5120-channel layer's job count, two pieces
+    (1, "third", 200, "f32", True),    # three pieces, a ragged last block
+])
+def test_backward_relay_bitwise_equals_unsplit(gpu, S, jobs_kind, L, io, softplus):
+    """The backward's reverse-time pass splits the uneven grid into pieces
+    that hand on the adjoint and the running dA / dD sums: every gradient is
+    bitwise that of the unsplit grid, and matches the oracle."""
+    n = _cus()
+    jobs = {"half": 2 * n + n // 2, "third": 2 * n + n // 3}[jobs_kind]
+    assert jobs % S == 0
+    p = ssm_inputs.make_problem(n_seqs=S, n_tokens=L, n_head=64 * (jobs // S), d_state=16, d_conv=0,
+                                io=io, seed=0x402 + S, h0_std=0.3, dt_softplus=softplus,
+                                with_dout=True, dstate_std=0.5, n_state_rows=S + 1, ids="perm")
+    t = device_inputs(p)
+    a = _run_bwd(p, t)
+    b = _no_relay(lambda: _run_bwd(p, t))
+    for k in a:
+        if a[k] is not None:
+            assert torch.equal(a[k], b[k]), f"relay backward {k} differs from the unsplit grid"
+    _compare_all(p, a, f"relay backward S={S}")
