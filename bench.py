@@ -32,9 +32,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
-VALU_PEAK_T = 78.6               # 157.3 TFLOP/s fp32 vector = 78.6 T lane-FMA/s
+# VALU peaks from the unit counts: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz =
+# 39.3 T lane-instructions/s; the published 157.3 TFLOP/s fp32 vector figure
+# counts an FMA as 2 flops and packed FP32 (two lanes' worth per instruction)
+# on top, i.e. 78.6 T lane-FMA/s.  The kernels here use no packed FP32, so
+# their issue ceiling is 39.3 T; both are reported.
+VALU_PEAK_T = 78.6               # T lane-FMA/s with packed FP32 (the published figure)
+VALU_ISSUE_T = 39.3              # T lane-instructions/s, one VALU op per lane per cycle
 MFMA_BF16_PEAK_T = 2500.0        # dense bf16 MFMA, TFLOP/s
-TRANS_COST = 4                   # v_exp_f32 / v_rcp_f32 issue at 1/4 of the VALU rate
+TRANS_COST = 4                   # v_exp_f32 / v_rcp_f32 against the packed peak (1/4 rate)
+TRANS_ISSUE = 2                  # ... against the issue ceiling: measured at half the FMA rate
 MALL_BYTES = 256 << 20
 METRIC = "selective-scan effective HBM GB/s (% of peak) + channel-tokens/s, 1 GPU"
 
@@ -86,6 +93,35 @@ def algorithmic_bytes(p, backward=False) -> int:
     return x + dt + bc + a + d + w + state + ids + dy + state + grads
 
 
+def valu_ops_per_channel_token(p, backward=False):
+    """(VALU ops, transcendentals) the method needs per (sequence, channel,
+    token); see valu_slots_per_channel_token for the count."""
+    N = p.d_state
+    if backward:
+        ops, trans = 12 * N + 4, N
+        if p.d_conv:
+            ops, trans = ops + 3 * p.d_conv + 7, trans + 2
+        return float(ops), float(trans)
+    if p.a_per_state:
+        ops, trans = 4 * N, N
+    else:
+        ops, trans = 3 * N + 1 / p.head_dim, 1 / p.head_dim
+    ops += 2
+    if p.d_conv:
+        ops, trans = ops + p.d_conv + 3, trans + 2
+    return float(ops), float(trans)
+
+
+def issue_model(ops_trans, ch_tok, avg_s):
+    """The same count against the non-packed issue ceiling (VALU_ISSUE_T, a
+    transcendental taking TRANS_ISSUE slots)."""
+    ops, trans = ops_trans
+    slots = (ops + TRANS_ISSUE * trans) * ch_tok
+    floor = slots / (VALU_ISSUE_T * 1e12)
+    return {"peak": VALU_ISSUE_T, "unit": "T lane-instructions/s (no packed FP32)",
+            "slots": int(slots), "floor_us": round(floor * 1e6, 2), "frac": round(floor / avg_s, 4)}
+
+
 def valu_slots_per_channel_token(p, backward=False) -> float:
     """Issue slots the method needs per (sequence, channel, token), counting a
     transcendental (exp, reciprocal) as TRANS_COST slots.
@@ -99,20 +135,11 @@ def valu_slots_per_channel_token(p, backward=False) -> float:
     fma), the adjoint step (fma for C dy, mul for the decay), its products
     for du, ddt, dA, dB, dC (mul/fma each: 6), and the channel sums of dB
     and dC (add each); per channel-token: dt*u, du, ddt, dD (4)."""
-    N = p.d_state
-    if backward:
-        # with the fused conv: the recomputed conv and SiLU (K + 3 + 2 trans), SiLU's
-        # derivative (4), the conv adjoint and the weight gradient (2 K)
-        extra = (3 * p.d_conv + 7 + 2 * TRANS_COST) if p.d_conv else 0
-        return float(N * (TRANS_COST + 12) + 4 + extra)
-    if p.a_per_state:
-        total = N * (4 + TRANS_COST)
-    else:
-        total = N * 3 + (1 + TRANS_COST) / p.head_dim
-    total += 2
-    if p.d_conv:
-        total += p.d_conv + 3 + 2 * TRANS_COST
-    return float(total)
+    # with the fused conv the backward adds the recomputed conv and SiLU (K + 3
+    # and 2 transcendentals), SiLU's derivative (4), the conv adjoint and the
+    # weight gradient (2 K)
+    ops, trans = valu_ops_per_channel_token(p, backward)
+    return ops + TRANS_COST * trans
 
 
 # HBM traffic of one call, from two rocprofv3 --pmc passes over
@@ -134,12 +161,12 @@ MEASURED_TRAFFIC = {
     "C9": {"sha256": "856c2b90a5a1872964550d0184eae879db27307310394725b0eaea81e7700484", "fetch_kib": 505345.6, "write_kib": 330720.0},
 }
 KERNEL_SOURCES = {
-    "C0": ("scan_fwd.hip", "scan_fwd_ts.hip", "scan_fwd_quad.hip", "device_common.h"),
-    "C1": ("scan_fwd.hip", "scan_fwd_ts.hip", "scan_fwd_quad.hip", "device_common.h"),
-    "C2": ("scan_fwd.hip", "scan_fwd_ts.hip", "scan_fwd_quad.hip", "device_common.h"),
-    "C9": ("scan_fwd.hip", "scan_fwd_quad.hip", "device_common.h"),
+    "C0": ("scan_fwd.hip", "scan_fwd_ts.hip", "scan_fwd_quad.hip", "relay.h", "relay.hip", "device_common.h"),
+    "C1": ("scan_fwd.hip", "scan_fwd_ts.hip", "scan_fwd_quad.hip", "relay.h", "relay.hip", "device_common.h"),
+    "C2": ("scan_fwd.hip", "scan_fwd_ts.hip", "scan_fwd_quad.hip", "relay.h", "relay.hip", "device_common.h"),
+    "C9": ("scan_fwd.hip", "scan_fwd_quad.hip", "relay.h", "relay.hip", "device_common.h"),
     "C3": ("scan_fwd.hip", "ssd_fwd.hip", "device_common.h"),
-    "C4": ("scan_bwd.hip", "scan_fwd_quad.hip", "device_common.h"),
+    "C4": ("scan_bwd.hip", "scan_fwd_quad.hip", "relay.h", "relay.hip", "device_common.h"),
     "C5": ("conv_bwd.hip", "device_common.h"),
     "C6": ("decode.hip", "device_common.h"),
     "C7": ("decode.hip", "device_common.h"),
@@ -691,11 +718,17 @@ def varlen_bytes(p) -> int:
     return x + y + z + dt + bc + params + states + S * 4 + (S + 1) * 4
 
 
+def valu_ops_ext(p):
+    """valu_ops_per_channel_token plus the extras per channel-token: the bias
+    (add), softplus (exp, log: 3 ops and 2 transcendentals) and the gate
+    SiLU(z) * y (mul, add, mul and exp, rcp)."""
+    ops, trans = valu_ops_per_channel_token(p)
+    return ops + 1 + 3 + 3, trans + 2 + 2
+
+
 def valu_slots_ext(p) -> float:
-    """valu_slots_per_channel_token plus the extras per channel-token: the
-    bias (add), softplus (exp, log: 2 transcendentals and 3 slots) and the
-    gate SiLU(z) * y (mul, exp, add, rcp, mul)."""
-    return valu_slots_per_channel_token(p) + 1 + (3 + 2 * TRANS_COST) + (3 + 2 * TRANS_COST)
+    ops, trans = valu_ops_ext(p)
+    return ops + TRANS_COST * trans
 
 
 def _oracle_ext_heads(p, heads):
@@ -795,7 +828,8 @@ def main_varlen(args):
                  "kernel": "selective_scan_fwd_ext (all launches of one call)",
                  "call_us": round(avg_s * 1e6, 3), "call_spread": spread,
                  "floors_us": {k: round(v * 1e6, 2) for k, v in floors.items()},
-                 "algorithmic_bytes": step_bytes, "valu_slots": int(slots)})
+                 "algorithmic_bytes": step_bytes, "valu_slots": int(slots),
+                 "issue_model": issue_model(valu_ops_ext(p), ch_tok, avg_s)})
     lengths = np.diff(p.cu_seqlens).tolist()
     line = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
@@ -940,6 +974,7 @@ def main():
                  "algorithmic_bytes": step_bytes})
     if "alu" in floors:
         roof["valu_slots"] = int(slots)
+        roof["issue_model"] = issue_model(valu_ops_per_channel_token(p, backward), ch_tok, avg_s)
     if "mfma" in floors:
         roof["mfma_flops"] = int(flops)
     line = {
