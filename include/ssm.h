@@ -131,7 +131,9 @@ size_t ssm_scan_dgrad_layout(const ssm_scan_desc *desc, size_t offsets[7]);
 /* Workspace the compute calls need (bytes, a multiple of 256).  backward = 0
  * for selective_scan_fwd, 1 for selective_scan_bwd.  The first 256 bytes of
  * a workspace hold the device-error word: zero the workspace once after
- * allocating it; the library sets bits and never clears them. */
+ * allocating it; the library sets bits and never clears them.  The rest may
+ * hold flags of the relay split (see ssm_scan_fwd_plan) that every finished
+ * call leaves at zero; after SSM_DEVERR_RELAY, zero the workspace again. */
 size_t ssm_scan_workspace_bytes(const ssm_scan_desc *desc, int backward);
 
 /* ---- compute -------------------------------------------------------------
@@ -210,7 +212,8 @@ int selective_scan_fwd(const ssm_scan_desc *desc, const float *s, const void *x,
  *  - Every call on one GPU shares that GPU's scratch: calls that overlap in
  *    time on one GPU (on different streams, or from several host threads
  *    without ordering) race on it.  Calls queued on one stream are ordered
- *    and safe.  Nothing in the scratch needs to start at zero. */
+ *    and safe.  The scratch starts at zero (static storage) and every
+ *    finished call leaves its relay flags at zero again. */
 int selective_scan_fwd_static(const ssm_scan_desc *desc, const float *s, const void *x,
                               const void *dt, const float *A, const void *B, const void *C,
                               const float *D, const int32_t *ids, const float *conv_w,

@@ -8,7 +8,8 @@
 // that has room.  Piece j + 1 starts from the state piece j ends with
 // (forward in time, or backward for the adjoint): piece j stores it, fences at
 // agent scope and raises a per-job flag; piece j + 1 waits for the flag and
-// then reads the state.  Block numbers put every whole job first and then the
+// then reads the state; the last piece puts the flag back to zero.  Block
+// numbers put every whole job first and then the
 // pieces in chain order, and the dispatcher hands out workgroups in number
 // order, so a piece that waits was dispatched after the piece it waits for,
 // and that one never waits on anything later: every wait ends.  Pieces raise
@@ -88,7 +89,11 @@ __device__ __forceinline__ void relay_publish(int* flag, int value) {
     if (threadIdx.x == 0) __hip_atomic_store(flag, value, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Zero n relay flags (one workgroup of 256 threads), before the relay grid.
-__global__ void relay_clear(int* flag, int n);
+// The last piece of a chain, once its wait has ended: put the flag back to
+// zero, so that a finished call leaves every flag of its workspace at zero
+// and the next call can start from there (workspaces start zeroed).
+__device__ __forceinline__ void relay_reset(int* flag) {
+    if (threadIdx.x == 0) __hip_atomic_store(flag, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 }  // namespace ssm

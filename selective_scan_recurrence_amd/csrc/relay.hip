@@ -1,4 +1,4 @@
-// Host side of the relay split (see relay.h) and its flag reset.
+// Host side of the relay split (see relay.h).
 #include <stdlib.h>
 
 #include <atomic>
@@ -7,10 +7,6 @@
 #include "relay.h"
 
 namespace ssm {
-
-__global__ __launch_bounds__(256) void relay_clear(int* flag, int n) {
-    for (int e = threadIdx.x; e < n; e += 256) flag[e] = 0;
-}
 
 RelaySplit relay_split(int64_t jobs, int64_t L, int tile, int cap, int n_cu, int max_jobs) {
     RelaySplit r;

@@ -349,6 +349,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     float* relay = rb.piece >= 0 ? p.relay_buf + (int64_t)rb.cut * 9 * kThreads + tid : nullptr;
     if (rb.piece > 0) {  // the later piece's adjoint and running sums
         relay_wait(p.relay_flag + rb.cut, rb.piece, p.err);
+        if (rb.piece + 1 == p.relay_k) relay_reset(p.relay_flag + rb.cut);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             g[s] = relay[s * kThreads];
@@ -714,7 +715,6 @@ int launch_fast(BwdKP kp, const BwdWs& w, const Shape& sh, hipStream_t stream) {
         kp.relay_rem = rs.rem;
         kp.relay_k = rs.k;
         kp.relay_len = rs.len;
-        hipLaunchKernelGGL(relay_clear, dim3(1), dim3(256), 0, stream, kp.relay_flag, rs.rem);
         hipLaunchKernelGGL(fn, dim3((unsigned)(rs.full + rs.rem * rs.k)), dim3(kThreads), 0, stream, kp);
     } else {
         hipLaunchKernelGGL(fn, dim3((unsigned)kp.n_cb, (unsigned)kp.S), dim3(kThreads), 0, stream, kp);

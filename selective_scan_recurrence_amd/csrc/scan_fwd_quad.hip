@@ -615,7 +615,10 @@ __global__ __launch_bounds__(kThreads) void quad_out(QuadKP p) {
     const int64_t rows = (int64_t)p.S * p.d_inner;
     float* relay_h = piece >= 0 ? p.relay_h + ((int64_t)sj * kChanPerBlock + (threadIdx.x >> 2)) * 16 + 4 * q
                                 : nullptr;
-    if (piece > 0) relay_wait(p.relay_flag + sj, piece, p.err);  // the previous piece's end state
+    if (piece > 0) {  // the previous piece's end state
+        relay_wait(p.relay_flag + sj, piece, p.err);
+        if (piece + 1 == p.relay_k) relay_reset(p.relay_flag + sj);
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         const int n = 4 * q + s;
@@ -723,7 +726,6 @@ int launch_quad_t(QuadKP kp, hipStream_t st, int* relay_k_out) {
         return SSM_OK;
     }
     if (kp.relay_k) {
-        hipLaunchKernelGGL(relay_clear, dim3(1), dim3(256), 0, st, kp.relay_flag, kp.relay_rem);
         const unsigned n_blocks = (unsigned)(kp.relay_full + kp.relay_rem * kp.relay_k);
         hipLaunchKernelGGL((quad_out<T, K, TILED, SOFTPLUS, GATE>), dim3(n_blocks), block, 0, st, kp);
         return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;

@@ -74,7 +74,8 @@ def test_relay_parity(gpu, name):
     torch.cuda.synchronize()
     assert int(ws[:4].view(torch.int32).item()) == 0, "device error word set"
     _check(p, r, oracle.problem_fwd(p), name)
-    # a second call on the same workspace (its flags left raised by the first)
+    # a second call on the same workspace: the first must have put every relay
+    # flag back to zero, or a piece of the second would start too early
     r2 = ops.scan_fwd(d, t["s"], t["x"], t["dt"], t["A"], t["B"], t["C"], t.get("D"), t["ids"],
                       conv_w=t.get("conv_w"), conv_state=t.get("conv_state"),
                       want_conv_state=True, ws=ws)
