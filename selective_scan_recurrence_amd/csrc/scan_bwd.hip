@@ -28,10 +28,20 @@
 // sequences and gathers dh_0 into d_s by ids; every sum has a fixed order,
 // so results are bitwise repeatable.
 //
+// Fused conv (fast path, K = 2..4 taps): x is the conv's input, u = SiLU(c)
+// with c = sum_j w_j in(t - (K-1) + j) (in() the gathered conv state before
+// token 0).  The checkpoint pass runs the fused forward; bwd_fast recomputes
+// c and u per block from the staged x and K-1 history rows, and its owner
+// lane turns du into dc = du SiLU'(c), the input gradient
+// d in(t) = sum_j w_j dc_{t + K-1-j} (the last K-1 values of dc ride in
+// registers from block to block), the weight sums dw_j += dc_t in(t-(K-1)+j)
+// and, after the first token, the gradient of the conv-state row.
+//
 // Relay (fast path): the (sequence, 64-channel block) jobs beyond a whole
 // number per compute unit are cut into pieces of whole blocks, run from the
 // last piece to the first; each hands on its adjoint g and its running dA and
 // dD sums, so every sum keeps the unsplit order (relay.h).
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -69,9 +79,16 @@ struct BwdKP {
     // blocks, piece 0 being the last in time
     int relay_full, relay_rem, relay_k, relay_len;
     int* relay_flag;     // [relay_rem]
-    float* relay_buf;    // [relay_rem][9][256]: g (4), dA sums (4), dD sum per lane
+    float* relay_buf;    // [relay_rem][kRelayVals][256]: g (4), dA (4), dD, a dc row, tap sum
     uint32_t* err;       // nullable device-error word
+    const float* conv_w;      // [d_inner][K] (bwd_fast with K > 0)
+    const float* conv_state;  // [R][d_inner][K-1], nullable: zeros
+    float* partW;             // [S][d_inner][K] conv-weight sums per sequence
+    float* partCS;            // [S][d_inner][K-1] conv-state gradient per sequence
+    int K;
 };
+
+constexpr int kRelayVals = 11;  // values a relay piece hands on per lane
 
 constexpr int kRelayMaxJobs = 256;  // cut jobs the workspace has room for
 
@@ -282,8 +299,9 @@ __global__ __launch_bounds__(kThreads) void bwd_rev(BwdKP p) {
 //    stores).
 //  - The products summed across channels (dB, dC) are formed without
 //    contraction so that each DPP row step is a single add.
-template <typename T, bool SOFTPLUS>
+template <typename T, int K, bool SOFTPLUS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void bwd_fast(const BwdKP kp_arg) {
+    static_assert(K == 0 || (K >= 2 && K <= 4), "conv taps");
     // lambdas below capture locals only (capturing the kernel argument would
     // force it into scratch memory)
     const BwdKP p = kp_arg;
@@ -297,6 +315,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     __shared__ __attribute__((aligned(16))) float xs_l[2][kBlk * kChan];
     __shared__ __attribute__((aligned(16))) float dts_l[2][kBlk * kChan];
     __shared__ __attribute__((aligned(16))) float dys_l[2][kBlk * kChan];
+    // the conv's history: x of tokens t0-3 .. t0-1 (conv state before token 0)
+    constexpr int HX = 3;
+    __shared__ __attribute__((aligned(16))) float hx_l[2][K > 0 ? HX * kChan : 4];
+    // u = SiLU(c) and SiLU'(c) of the block's tokens [token][channel]; each
+    // wave writes and reads only its own channels
+    __shared__ __attribute__((aligned(16))) float us_l[K > 0 ? kBlk * kChan : 4];
+    __shared__ __attribute__((aligned(16))) float fs_l[K > 0 ? kBlk * kChan : 4];
+    // dc = du SiLU'(c) of the block's tokens, double-buffered: the block after
+    // (in time) keeps its first rows for the d_x of this block's last tokens
+    __shared__ __attribute__((aligned(16))) float dc_l[2][K > 0 ? kBlk * kChan : 4];
+    __shared__ __attribute__((aligned(16))) float wl[K > 0 ? kChan * 4 : 4];  // conv taps [channel][tap]
     __shared__ __attribute__((aligned(16))) float Bs_l[2][kBlk * 16];
     __shared__ __attribute__((aligned(16))) float Cs_l[2][kBlk * 16];
     // the checkpoint is read into registers right after the barrier that
@@ -346,7 +375,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const float Dc = p.has_D ? p.D[c] : 0.0f;
     float g[4], dA_acc[4] = {0.f, 0.f, 0.f, 0.f};
     float dD_acc = 0.0f;
-    float* relay = rb.piece >= 0 ? p.relay_buf + (int64_t)rb.cut * 9 * kThreads + tid : nullptr;
+    // conv: quad lane q's running weight sum for tap q; the dc rows that the
+    // first block in time after this workgroup's range hands in (lanes q < 3)
+    float dwq = 0.0f, dc_in = 0.0f;
+    if constexpr (K > 0) wl[cl * 4 + q] = q < K ? p.conv_w[(int64_t)c * K + q] : 0.0f;
+    float* relay = rb.piece >= 0 ? p.relay_buf + (int64_t)rb.cut * kRelayVals * kThreads + tid : nullptr;
     if (rb.piece > 0) {  // the later piece's adjoint and running sums
         relay_wait(p.relay_flag + rb.cut, rb.piece, p.err);
         if (rb.piece + 1 == p.relay_k) relay_reset(p.relay_flag + rb.cut);
@@ -356,6 +389,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             dA_acc[s] = relay[(4 + s) * kThreads];
         }
         dD_acc = relay[8 * kThreads];
+        if constexpr (K > 0) {
+            dc_in = relay[9 * kThreads];
+            dwq = relay[10 * kThreads];
+        }
     } else {
         const float4 gv = *reinterpret_cast<const float4*>(p.dstate + ((int64_t)i * d_inner + c) * 16 + 4 * q);
         g[0] = gv.x; g[1] = gv.y; g[2] = gv.z; g[3] = gv.w;
@@ -379,23 +416,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // (128-255); dy (0-127) or B (128-159) or C (160-191); checkpoint.  bf16:
     // x (wave 0) or dt (wave 1) or dy (wave 2) or B (192-207) or C (208-223);
     // checkpoint.
+    // With the conv, 3 history rows of x (array 6): bf16 threads 224-247 of
+    // slot 0, fp32 threads 192-239 of slot 1.
     constexpr int NS = ES == 4 ? 3 : 2;
+    constexpr int CHH = HX * CPR;               // chunks of the history rows
     static_assert(kBlk == 8 && CHK == kThreads &&
-                  (ES == 2 ? CHX == 64 && CHB == 16 : CHX == 128 && CHB == 32), "slot layout");
+                  (ES == 2 ? CHX == 64 && CHB == 16 && 224 + CHH <= kThreads
+                           : CHX == 128 && CHB == 32 && 192 + CHH <= kThreads), "slot layout");
     uint4 stg[NS];
-    // where slot k of this thread comes from: array id (0 x, 1 dt, 2 dy, 3 B, 4 C, 5 ckpt) and chunk
+    // where slot k of this thread comes from: array id (0 x, 1 dt, 2 dy, 3 B, 4 C, 5 ckpt, 6 history) and chunk
     auto slot = [&](int k, int& arr, int& w) __attribute__((always_inline)) {
         if constexpr (ES == 4) {
             if (k == 0) { arr = tid < 128 ? 0 : 1; w = tid & 127; }
-            else if (k == 1) { arr = tid < 128 ? 2 : tid < 160 ? 3 : 4; w = tid < 128 ? tid : (tid - 128) & 31; }
-            else { arr = 5; w = tid; }
+            else if (k == 1) {
+                arr = tid < 128 ? 2 : tid < 160 ? 3 : tid < 192 ? 4 : 6;
+                w = tid < 128 ? tid : tid < 192 ? (tid - 128) & 31 : tid - 192;
+            } else { arr = 5; w = tid; }
         } else {
-            if (k == 0) { arr = tid < 192 ? (tid >> 6) : tid < 208 ? 3 : 4; w = tid < 192 ? (tid & 63) : (tid & 15); }
-            else { arr = 5; w = tid; }
+            if (k == 0) {
+                arr = tid < 192 ? (tid >> 6) : tid < 208 ? 3 : tid < 224 ? 4 : 6;
+                w = tid < 192 ? (tid & 63) : tid < 224 ? (tid & 15) : tid - 224;
+            } else { arr = 5; w = tid; }
         }
     };
     auto slot_used = [&](int k) __attribute__((always_inline)) {
-        return !(ES == 2 && k == 0 && tid >= 224) && !(ES == 4 && k == 1 && tid >= 192);
+        if constexpr (ES == 2) return !(k == 0 && tid >= (K > 0 ? 224 + CHH : 224));
+        else return !(k == 1 && tid >= (K > 0 ? 192 + CHH : 192));
     };
     auto load_tile = [&](int b) __attribute__((always_inline)) {
         const int bb = b < 0 ? 0 : b;
@@ -414,8 +460,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             } else if (arr < 5) {
                 const int t = min(t0 + w / CPB, L - 1);
                 src = (arr == 3 ? bg : cg) + (int64_t)t * 16 * ES + (w % CPB) * 16;
-            } else {
+            } else if (arr == 5) {
                 src = ckb + w * 16;
+            } else {  // history row: tokens before 0 come from the conv state instead
+                const int t = min(max(t0 - HX + w / CPR, 0), L - 1);
+                src = xg + (int64_t)t * xrow + (w % CPR) * 16;
             }
             stg[k] = *reinterpret_cast<const uint4*>(src);
         }
@@ -448,8 +497,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                 put(tile + w * VPC, stg[k], t0 + w / CPR < L);
             } else if (arr < 5) {
                 put((arr == 3 ? Bs_l[buf] : Cs_l[buf]) + w * VPC, stg[k], t0 + w / CPB < L);
-            } else {
+            } else if (arr == 5) {
                 *reinterpret_cast<uint4*>(ck_l + w * 4) = stg[k];
+            } else if constexpr (K > 0) {
+                if (t0 - HX + w / CPR >= 0) put(hx_l[buf] + w * VPC, stg[k], true);
+            }
+        }
+        if constexpr (K > 0) {
+            if (t0 < HX && tid < HX * kChan) {  // the first block: history from the gathered conv state
+                const int hr = tid / kChan, ch = tid % kChan, tau = t0 - HX + hr;
+                if (tau < 0) {
+                    float v = 0.0f;
+                    if (tau >= -(K - 1))
+                        v = bad ? __builtin_nanf("")
+                                : (p.conv_state ? p.conv_state[((int64_t)rid * d_inner + cb * kChan + ch) * (K - 1) +
+                                                               tau + K - 1]
+                                                : 0.0f);
+                    hx_l[buf][hr * kChan + ch] = v;
+                }
             }
         }
     };
@@ -462,6 +527,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     load_tile(b_hi - 1);
     store_tile((b_hi - 1) & 1, b_hi - 1);
     load_tile(b_hi - 2);
+    if constexpr (K > 0)  // dc of the tokens after the range: zero past the end, else handed in
+        if (q < K - 1) dc_l[b_hi & 1][q * kChan + cl] = dc_in;
     __syncthreads();
     for (int b = b_hi - 1; b >= b_lo; --b) {
         const int t0 = b * kBlk, buf = b & 1;
@@ -481,11 +548,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             if constexpr (SOFTPLUS) dk = k < nk ? softplus(dk) : 0.0f;
             return dk;
         };
+        // input row kk of the block for this lane's channel (kk < 0: history)
+        auto xin = [&](int kk) __attribute__((always_inline)) {
+            return kk >= 0 ? xs[kk * kChan + cl] : hx_l[buf][(HX + kk) * kChan + cl];
+        };
+        if constexpr (K > 0) {
+            // quad lane q forms c = sum_j w_j in(t-(K-1)+j) (the forward's order,
+            // oldest input first), u = SiLU(c) and SiLU'(c) of tokens 2q, 2q+1;
+            // LDS operations of a wave complete in order, so its lanes read
+            // them back below without a barrier
+            float win[K + 1];
+#pragma unroll
+            for (int j = 0; j <= K; ++j) win[j] = xin(2 * q - (K - 1) + j);
+            const float4 wv = *reinterpret_cast<const float4*>(&wl[cl * 4]);
+            const float w[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                float cv = w[0] * win[e];
+#pragma unroll
+                for (int j = 1; j < K; ++j) cv = fmaf(w[j], win[e + j], cv);
+                const float sg = __builtin_amdgcn_rcpf(1.0f + fast_exp2(-cv * kLog2e));
+                us_l[(2 * q + e) * kChan + cl] = cv * sg;
+                fs_l[(2 * q + e) * kChan + cl] = sg * fmaf(cv, 1.0f - sg, 1.0f);
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+        auto u_of = [&](int k) __attribute__((always_inline)) {
+            if constexpr (K > 0) return us_l[k * kChan + cl];
+            else return rowv(xs, k);
+        };
         // recompute the block: decays a[k][s] and states h[k][s] (= h_{t0+k})
         float a[kBlk][4], h[kBlk][4];
 #pragma unroll
         for (int k = 0; k < kBlk; ++k) {
-            const float dk = dt_of(k), bk = dk * rowv(xs, k);
+            const float dk = dt_of(k), bk = dk * u_of(k);
             float Bq[4];
             quad4(Bt, k, Bq);
 #pragma unroll
@@ -503,7 +599,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             const float dyk = rowv(dys, k);
             const float draw = rowv(dts, k);
             const float dk = SOFTPLUS ? (k < nk ? softplus(draw) : 0.0f) : draw;
-            const float uk = rowv(xs, k);
+            const float uk = u_of(k);
             const float dtuk = dk * uk;
             float Bq[4], Cq[4];
             quad4(Bt, k, Bq);
@@ -526,7 +622,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             if (q == 0) {
                 float ddt = fmaf(uk, S1, S2);
                 if constexpr (SOFTPLUS) ddt *= sigmoid(draw);
-                gx_l[k * kChan + cl] = fmaf(Dc, dyk, dk * S1);
+                const float du = fmaf(Dc, dyk, dk * S1);
+                if constexpr (K > 0) dc_l[buf][k * kChan + cl] = du * fs_l[k * kChan + cl];  // through SiLU
+                else gx_l[k * kChan + cl] = du;
                 gdt_l[k * kChan + cl] = ddt;
                 if (k < nk) dD_acc = fmaf(dyk, uk, dD_acc);
             }
@@ -564,7 +662,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         // the block's d_x / d_dt rows: thread -> token tid / 16, channels 4 (tid % 16) + 0..3
         constexpr int NGX = kBlk * kChan / 4;  // 16-byte pieces of the d_x tile
         const int tg = tid < NGX ? tid : 0;
-        float4 gxv = *reinterpret_cast<const float4*>(&gx_l[tg * 4]);
+        float4 gxv;
+        if constexpr (K > 0) {
+            // through the conv: d in(t) = sum_m w_{K-1-m} dc_{t+m}, rows past the
+            // block from the later one's buffer
+            const int k = tg >> 4, ch = 4 * (tg & 15);
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < K; ++m) {
+                const int rr = k + m;
+                const float4 d = *reinterpret_cast<const float4*>(
+                    rr < kBlk ? &dc_l[buf][rr * kChan + ch] : &dc_l[buf ^ 1][(rr - kBlk) * kChan + ch]);
+                const float dv[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = fmaf(wl[(ch + e) * 4 + K - 1 - m], dv[e], acc[e]);
+            }
+            gxv = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            // tap q's weight sum: dc_t in(t - (K-1) + q), tokens in reverse order
+            if (q < K) {
+#pragma unroll
+                for (int kk = kBlk - 1; kk >= 0; --kk)
+                    dwq = fmaf(dc_l[buf][kk * kChan + cl], xin(kk - (K - 1) + q), dwq);
+            }
+        } else {
+            gxv = *reinterpret_cast<const float4*>(&gx_l[tg * 4]);
+        }
         float4 gdv = *reinterpret_cast<const float4*>(&gdt_l[tg * 4]);
         // next block's tiles into the other buffer; fetch the one after
         if (b > b_lo) store_tile(buf ^ 1, b - 1);
@@ -597,6 +719,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             relay[(4 + s) * kThreads] = dA_acc[s];
         }
         relay[8 * kThreads] = dD_acc;
+        if constexpr (K > 0) {
+            // the first rows of dc of this range, for the d_x of the range before
+            relay[9 * kThreads] = q < K - 1 ? dc_l[b_lo & 1][q * kChan + cl] : 0.0f;
+            relay[10 * kThreads] = dwq;
+        }
         relay_publish(p.relay_flag + rb.cut, rb.piece + 1);
         return;
     }
@@ -605,8 +732,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         *reinterpret_cast<float4*>(p.ds_part + row_i) = make_float4(g[0], g[1], g[2], g[3]);
         *reinterpret_cast<float4*>(p.dA_part + row_i) = make_float4(dA_acc[0], dA_acc[1], dA_acc[2], dA_acc[3]);
     }
-    // dD: lane q == 0 of each quad holds its channel's sum
-    if (q == 0) p.dD_part[(int64_t)i * d_inner + c] = dD_acc;
+    // dD and the conv-state gradient: lane q == 0 of each quad holds its
+    // channel's; the weight sum of tap q: quad lane q
+    const int64_t rowc = (int64_t)i * d_inner + c;
+    if constexpr (K > 0)
+        if (q < K) p.partW[rowc * K + q] = dwq;
+    if (q == 0) {
+        p.dD_part[rowc] = dD_acc;
+        if constexpr (K > 0) {
+            // the conv-state inputs tau = m - (K-1): sum_j w_j dc_{m-j} (dc of
+            // tokens 0 .. K-2, block 0's buffer)
+#pragma unroll
+            for (int m = 0; m < K - 1; ++m) {
+                float gcs = 0.0f;
+#pragma unroll
+                for (int j = 0; j <= m; ++j) gcs = fmaf(wl[cl * 4 + j], dc_l[0][(m - j) * kChan + cl], gcs);
+                p.partCS[rowc * (K - 1) + m] = gcs;
+            }
+        }
+    }
 }
 
 // d_B, d_C: sum of the channel-block partials in block order.
@@ -627,7 +771,8 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc(BwdKP p, float* d_B, float*
 // ds_src rows have stride ds_stride floats (16 for the partials, d_state for
 // dstate itself when there are no tokens).
 __global__ __launch_bounds__(256) void bwd_reduce_params(BwdKP p, const float* ds_src, int ds_stride,
-                                                         float* d_A, float* d_D, float* d_s) {
+                                                         float* d_A, float* d_D, float* d_s, float* d_cw,
+                                                         float* d_cs) {
     const int64_t per_row = (int64_t)p.d_inner * p.N;
     const int64_t stride = (int64_t)gridDim.x * 256;
     for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < per_row; e += stride) {
@@ -654,12 +799,27 @@ __global__ __launch_bounds__(256) void bwd_reduce_params(BwdKP p, const float* d
             if (p.ids[i] == r) acc += ds_src[((int64_t)i * p.d_inner + c) * ds_stride + n];
         d_s[f] = acc;
     }
+    if (p.K > 0 && d_cw && d_cs) {  // d_conv_w over sequences; d_conv_state rows by ids, in sequence order
+        for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < (int64_t)p.d_inner * p.K; e += stride) {
+            float acc = 0.0f;
+            for (int i = 0; i < p.S; ++i) acc += p.partW[(int64_t)i * p.d_inner * p.K + e];
+            d_cw[e] = acc;
+        }
+        const int64_t per_cs = (int64_t)p.d_inner * (p.K - 1);
+        for (int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x; f < (int64_t)p.R * per_cs; f += stride) {
+            const int64_t r = f / per_cs, rem = f % per_cs;
+            float acc = 0.0f;
+            for (int i = 0; i < p.S; ++i)
+                if (p.ids[i] == r) acc += p.partCS[(int64_t)i * per_cs + rem];
+            d_cs[f] = acc;
+        }
+    }
 }
 
 size_t blocks_of(const Shape& sh) { return (size_t)((sh.L + kBlk - 1) / kBlk); }
 
 struct BwdWs {
-    float *ckpt, *dbc, *dA, *dD, *ds;
+    float *ckpt, *dbc, *dA, *dD, *ds, *partW, *partCS;
     char* relay;   // the relay of bwd_fast
     size_t relay_bytes;
     size_t total;
@@ -681,8 +841,10 @@ BwdWs carve(const Shape& sh, char* base) {
     w.dA = take(rows * 16 * 4);
     w.dD = take(rows * 4);
     w.ds = take(rows * 16 * 4);
+    w.partW = sh.K > 0 ? take(rows * sh.K * 4) : nullptr;
+    w.partCS = sh.K > 0 ? take(rows * (sh.K - 1) * 4) : nullptr;
     const size_t room = relay_room(sh);
-    w.relay_bytes = align_up(room * 9 * kThreads * 4, 256) + align_up(room * 4, 256);
+    w.relay_bytes = align_up(room * kRelayVals * kThreads * 4, 256) + align_up(room * 4, 256);
     w.relay = reinterpret_cast<char*>(take(w.relay_bytes));
     w.total = off;
     return w;
@@ -694,15 +856,27 @@ bool bwd_supported(const Shape& sh) {
     return sh.a_per_state && sh.P == 1 && sh.N <= 16 && sh.G == 1 && sh.K == 0;
 }
 
+// The fused conv on the fast path: the shape side of its conditions (the
+// tensors' alignment decides between it and the generic kernels).
+bool bwd_conv_fast_shape(const Shape& sh) {
+    return sh.a_per_state && sh.P == 1 && sh.N == 16 && sh.G == 1 && sh.K >= 2 && sh.K <= 4 &&
+           sh.d_inner() % kChan == 0;
+}
+
 size_t bwd_workspace_bytes(const Shape& sh) {
     if (ssd_bwd_supported(sh)) return ssd_bwd_workspace_bytes(sh);
     if (bwd_supported(sh)) return (sh.S == 0 || sh.L == 0) ? 0 : carve(sh, nullptr).total;
-    return rows_bwd_supported(sh) ? rows_bwd_workspace_bytes(sh) : 0;
+    const size_t rows = rows_bwd_supported(sh) ? rows_bwd_workspace_bytes(sh) : 0;
+    if (bwd_conv_fast_shape(sh) && sh.S > 0 && sh.L > 0) {
+        const size_t fast = carve(sh, nullptr).total;
+        return fast > rows ? fast : rows;
+    }
+    return rows;
 }
 
-template <typename T, bool SOFTPLUS>
+template <typename T, int K, bool SOFTPLUS>
 int launch_fast(BwdKP kp, const BwdWs& w, const Shape& sh, hipStream_t stream) {
-    auto fn = bwd_fast<T, SOFTPLUS>;
+    auto fn = bwd_fast<T, K, SOFTPLUS>;
     const int64_t jobs = (int64_t)kp.n_cb * kp.S;
     const int n_cu = device_cus();
     const int cap = n_cu > 0 ? resident_blocks((const void*)fn, kThreads) : 0;
@@ -710,7 +884,7 @@ int launch_fast(BwdKP kp, const BwdWs& w, const Shape& sh, hipStream_t stream) {
     if (rs.k) {
         char* r = w.relay;
         kp.relay_buf = reinterpret_cast<float*>(r);
-        kp.relay_flag = reinterpret_cast<int*>(r + align_up(relay_room(sh) * 9 * kThreads * 4, 256));
+        kp.relay_flag = reinterpret_cast<int*>(r + align_up(relay_room(sh) * kRelayVals * kThreads * 4, 256));
         kp.relay_full = rs.full;
         kp.relay_rem = rs.rem;
         kp.relay_k = rs.k;
@@ -722,14 +896,28 @@ int launch_fast(BwdKP kp, const BwdWs& w, const Shape& sh, hipStream_t stream) {
     return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+template <int K>
+int launch_fast_k(const BwdKP& kp, const BwdWs& w, const Shape& sh, bool bf, hipStream_t stream) {
+    if (bf) return kp.softplus ? launch_fast<bf16_t, K, true>(kp, w, sh, stream)
+                               : launch_fast<bf16_t, K, false>(kp, w, sh, stream);
+    return kp.softplus ? launch_fast<float, K, true>(kp, w, sh, stream)
+                       : launch_fast<float, K, false>(kp, w, sh, stream);
+}
+
 int launch_scan_bwd(const BwdArgs& a, hipStream_t stream) {
     const Shape& sh = a.sh;
     if (ssd_bwd_supported(sh)) return launch_ssd_bwd(a, stream);
-    if (!bwd_supported(sh)) return launch_rows_bwd(a, stream);
+    auto al16 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; };
+    const bool fast_io = sh.N == 16 && sh.d_inner() % kChan == 0 && al16(a.x) && al16(a.dt) &&
+                         al16(a.dy) && al16(a.B) && al16(a.C) && al16(a.A) && al16(a.dstate) &&
+                         al16(a.d_x) && al16(a.d_dt);
+    const bool conv_fast = bwd_conv_fast_shape(sh) && fast_io && sh.S > 0 && sh.L > 0;
+    if (!bwd_supported(sh) && !conv_fast) return launch_rows_bwd(a, stream);
     const int64_t per_row = sh.d_inner() * sh.N;
     BwdKP kp = {};
     kp.A = a.A; kp.D = a.D; kp.ids = a.ids; kp.x = a.x; kp.dt = a.dt; kp.B = a.B; kp.C = a.C;
     kp.dy = a.dy; kp.dstate = a.dstate; kp.d_x = a.d_x; kp.d_dt = a.d_dt; kp.err = a.err;
+    kp.conv_w = a.conv_w; kp.conv_state = a.conv_state; kp.K = (int)sh.K;
     kp.L = (int)sh.L; kp.d_inner = (int)sh.d_inner(); kp.N = (int)sh.N; kp.R = (int)sh.R;
     kp.S = (int)sh.S; kp.n_cb = (int)((sh.d_inner() + kChan - 1) / kChan);
     kp.has_D = (sh.flags & SSM_HAS_D) ? 1 : 0;
@@ -741,25 +929,25 @@ int launch_scan_bwd(const BwdArgs& a, hipStream_t stream) {
         kp.dA_part = nullptr;
         kp.dD_part = nullptr;
         hipLaunchKernelGGL(bwd_reduce_params, dim3(par_blocks), dim3(256), 0, stream, kp,
-                           a.dstate, (int)sh.N, a.d_A, a.d_D, a.d_s);
+                           a.dstate, (int)sh.N, a.d_A, a.d_D, a.d_s, nullptr, nullptr);
         return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
     }
     BwdWs w = carve(sh, a.ws);
     if (w.total > a.ws_bytes) return SSM_ERR_WORKSPACE;
     kp.ckpt = w.ckpt; kp.dbc_part = w.dbc; kp.dA_part = w.dA; kp.dD_part = w.dD; kp.ds_part = w.ds;
+    kp.partW = w.partW; kp.partCS = w.partCS;
     int rc = launch_quad_ckpt(a, w.ckpt, stream);
     if (rc) return rc;
     const dim3 grid((unsigned)kp.n_cb, (unsigned)sh.S);
     const bool bf = sh.io == SSM_BF16;
-    auto al16 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; };
-    const bool fast = sh.N == 16 && sh.d_inner() % kChan == 0 && al16(a.x) && al16(a.dt) &&
-                      al16(a.dy) && al16(a.B) && al16(a.C) && al16(a.A) && al16(a.dstate) &&
-                      al16(a.d_x) && al16(a.d_dt);
-    if (fast) {
-        if (bf) rc = kp.softplus ? launch_fast<bf16_t, true>(kp, w, sh, stream)
-                                 : launch_fast<bf16_t, false>(kp, w, sh, stream);
-        else rc = kp.softplus ? launch_fast<float, true>(kp, w, sh, stream)
-                              : launch_fast<float, false>(kp, w, sh, stream);
+    if (fast_io) {
+        switch (sh.K) {
+            case 0: rc = launch_fast_k<0>(kp, w, sh, bf, stream); break;
+            case 2: rc = launch_fast_k<2>(kp, w, sh, bf, stream); break;
+            case 3: rc = launch_fast_k<3>(kp, w, sh, bf, stream); break;
+            case 4: rc = launch_fast_k<4>(kp, w, sh, bf, stream); break;
+            default: rc = SSM_ERR_UNSUPPORTED;
+        }
         if (rc) return rc;
     } else if (bf) {
         if (kp.softplus) hipLaunchKernelGGL((bwd_rev<bf16_t, true>), grid, dim3(kThreads), 0, stream, kp);
@@ -771,8 +959,10 @@ int launch_scan_bwd(const BwdArgs& a, hipStream_t stream) {
     const int64_t tok32 = sh.S * sh.L * 32;
     hipLaunchKernelGGL(bwd_reduce_bc, dim3((unsigned)((tok32 + 255) / 256)), dim3(256), 0, stream, kp,
                        a.d_B, a.d_C);
-    hipLaunchKernelGGL(bwd_reduce_params, dim3(par_blocks), dim3(256), 0, stream, kp,
-                       (const float*)w.ds, 16, a.d_A, a.d_D, a.d_s);
+    const int64_t cpar = sh.R * sh.d_inner() * (sh.K > 0 ? sh.K - 1 : 0);
+    const unsigned red_blocks = cpar > par ? (unsigned)std::min<int64_t>((cpar + 255) / 256, 65535) : par_blocks;
+    hipLaunchKernelGGL(bwd_reduce_params, dim3(red_blocks), dim3(256), 0, stream, kp,
+                       (const float*)w.ds, 16, a.d_A, a.d_D, a.d_s, a.d_conv_w, a.d_conv_state);
     return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 

@@ -673,8 +673,9 @@ __global__ __launch_bounds__(kThreads) void quad_out(QuadKP p) {
 // Forward scan that stores the state entering every kCkpt-token block to
 // p.agg ([n_blocks][S][d_inner][16]); the backward pass recomputes each block
 // from it.
-template <typename T, bool TILED, bool SOFTPLUS>
+template <typename T, int K, bool TILED, bool SOFTPLUS>
 __global__ __launch_bounds__(kThreads) void quad_ckpt(QuadKP p) {
+    static_assert(TILED || K == 0, "the fused conv runs on the tiled variant");
     const int q = threadIdx.x & 3;
     const int c_raw = blockIdx.x * kChanPerBlock + (threadIdx.x >> 2);
     const bool active = c_raw < p.d_inner;
@@ -693,7 +694,7 @@ __global__ __launch_bounds__(kThreads) void quad_ckpt(QuadKP p) {
     }
     float dt_acc = 0.0f;
     if constexpr (TILED)
-        quad_tiled<T, 0, 2, SOFTPLUS>(p, i, (int64_t)i * p.L, blockIdx.x, q, threadIdx.x >> 2, 0, p.L, h, a2, dt_acc,
+        quad_tiled<T, K, 2, SOFTPLUS>(p, i, (int64_t)i * p.L, blockIdx.x, q, threadIdx.x >> 2, 0, p.L, h, a2, dt_acc,
                                       bad);
     else
         quad_chunk<T, 0, 2>(p, i, (int64_t)i * p.L, c_raw, q, 0, p.L, h, a2, dt_acc, active, bad);
@@ -791,12 +792,26 @@ size_t quad_workspace_bytes(const Shape& sh) {
     return (size_t)((n - 1) * rows * 16 + (n - 1) * rows + n * rows * 16) * 4 + 3 * 256;
 }
 
+namespace {
+template <int K>
+void launch_ckpt_k(const QuadKP& kp, dim3 grid, bool bf, hipStream_t stream) {
+    if (bf) {
+        if (kp.softplus) hipLaunchKernelGGL((quad_ckpt<bf16_t, K, true, true>), grid, dim3(kThreads), 0, stream, kp);
+        else hipLaunchKernelGGL((quad_ckpt<bf16_t, K, true, false>), grid, dim3(kThreads), 0, stream, kp);
+    } else {
+        if (kp.softplus) hipLaunchKernelGGL((quad_ckpt<float, K, true, true>), grid, dim3(kThreads), 0, stream, kp);
+        else hipLaunchKernelGGL((quad_ckpt<float, K, true, false>), grid, dim3(kThreads), 0, stream, kp);
+    }
+}
+}  // namespace
+
 int launch_quad_ckpt(const BwdArgs& a, float* ckpt, hipStream_t stream) {
     const Shape& sh = a.sh;
     QuadKP kp = {};
     kp.T = sh.S * sh.L;
     kp.s = a.s; kp.x = a.x; kp.dt = a.dt; kp.A = a.A; kp.B = a.B; kp.C = a.C; kp.D = nullptr;
     kp.ids = a.ids; kp.err = a.err; kp.agg = ckpt;
+    kp.conv_w = a.conv_w; kp.conv_state = a.conv_state;  // the fused conv (sh.K > 0)
     kp.L = (int)sh.L; kp.d_inner = (int)sh.d_inner(); kp.N = (int)sh.N; kp.R = (int)sh.R;
     kp.S = (int)sh.S;
     kp.has_D = 0;
@@ -809,17 +824,18 @@ int launch_quad_ckpt(const BwdArgs& a, float* ckpt, hipStream_t stream) {
     kp.n_chunks = 1;
     const dim3 grid((unsigned)((kp.d_inner + kChanPerBlock - 1) / kChanPerBlock), (unsigned)sh.S);
     const bool bf = sh.io == SSM_BF16;
+    if (sh.K > 0 && !kp.tiled) return SSM_ERR_UNSUPPORTED;  // the fused conv runs tiled only
     if (kp.tiled) {
-        if (bf) {
-            if (kp.softplus) hipLaunchKernelGGL((quad_ckpt<bf16_t, true, true>), grid, dim3(kThreads), 0, stream, kp);
-            else hipLaunchKernelGGL((quad_ckpt<bf16_t, true, false>), grid, dim3(kThreads), 0, stream, kp);
-        } else {
-            if (kp.softplus) hipLaunchKernelGGL((quad_ckpt<float, true, true>), grid, dim3(kThreads), 0, stream, kp);
-            else hipLaunchKernelGGL((quad_ckpt<float, true, false>), grid, dim3(kThreads), 0, stream, kp);
+        switch (sh.K) {
+            case 0: launch_ckpt_k<0>(kp, grid, bf, stream); break;
+            case 2: launch_ckpt_k<2>(kp, grid, bf, stream); break;
+            case 3: launch_ckpt_k<3>(kp, grid, bf, stream); break;
+            case 4: launch_ckpt_k<4>(kp, grid, bf, stream); break;
+            default: return SSM_ERR_UNSUPPORTED;
         }
     } else {
-        if (bf) hipLaunchKernelGGL((quad_ckpt<bf16_t, false, false>), grid, dim3(kThreads), 0, stream, kp);
-        else hipLaunchKernelGGL((quad_ckpt<float, false, false>), grid, dim3(kThreads), 0, stream, kp);
+        if (bf) hipLaunchKernelGGL((quad_ckpt<bf16_t, 0, false, false>), grid, dim3(kThreads), 0, stream, kp);
+        else hipLaunchKernelGGL((quad_ckpt<float, 0, false, false>), grid, dim3(kThreads), 0, stream, kp);
     }
     return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
