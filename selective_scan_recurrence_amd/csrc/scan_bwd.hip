@@ -312,20 +312,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     constexpr int CHB = kBlk * CPB;             // chunks per B / C tile
     constexpr int CHK = kChan * 16 * 4 / 16;    // chunks of the checkpoint tile (f32)
     constexpr int VPC = 16 / ES;                // values per chunk
-    __shared__ __attribute__((aligned(16))) float xs_l[2][kBlk * kChan];
+    // x rows: with the conv the lanes of a quad read different rows of one
+    // channel, so the row pitch is 8 (mod 32) words to keep them in separate banks
+    constexpr int XP = K > 0 ? kChan + 8 : kChan;
+    __shared__ __attribute__((aligned(16))) float xs_l[2][kBlk * XP];
     __shared__ __attribute__((aligned(16))) float dts_l[2][kBlk * kChan];
     __shared__ __attribute__((aligned(16))) float dys_l[2][kBlk * kChan];
     // the conv's history: x of tokens t0-3 .. t0-1 (conv state before token 0)
     constexpr int HX = 3;
-    __shared__ __attribute__((aligned(16))) float hx_l[2][K > 0 ? HX * kChan : 4];
+    __shared__ __attribute__((aligned(16))) float hx_l[2][K > 0 ? HX * XP : 4];
     // u = SiLU(c) and SiLU'(c) of the block's tokens [token][channel]; each
     // wave writes and reads only its own channels
-    __shared__ __attribute__((aligned(16))) float us_l[K > 0 ? kBlk * kChan : 4];
-    __shared__ __attribute__((aligned(16))) float fs_l[K > 0 ? kBlk * kChan : 4];
+    // (row pitch 4 (mod 16) words: the quad lanes write rows 2q, 2q+1)
+    constexpr int UP = kChan + 4;
+    __shared__ __attribute__((aligned(16))) float us_l[K > 0 ? kBlk * UP : 4];
+    __shared__ __attribute__((aligned(16))) float fs_l[K > 0 ? kBlk * UP : 4];
     // dc = du SiLU'(c) of the block's tokens, double-buffered: the block after
     // (in time) keeps its first rows for the d_x of this block's last tokens
     __shared__ __attribute__((aligned(16))) float dc_l[2][K > 0 ? kBlk * kChan : 4];
-    __shared__ __attribute__((aligned(16))) float wl[K > 0 ? kChan * 4 : 4];  // conv taps [channel][tap]
+    __shared__ __attribute__((aligned(16))) float wl[K > 0 ? kChan * 4 : 4];  // conv taps [tap][channel]
     __shared__ __attribute__((aligned(16))) float Bs_l[2][kBlk * 16];
     __shared__ __attribute__((aligned(16))) float Cs_l[2][kBlk * 16];
     // the checkpoint is read into registers right after the barrier that
@@ -378,7 +383,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // conv: quad lane q's running weight sum for tap q; the dc rows that the
     // first block in time after this workgroup's range hands in (lanes q < 3)
     float dwq = 0.0f, dc_in = 0.0f;
-    if constexpr (K > 0) wl[cl * 4 + q] = q < K ? p.conv_w[(int64_t)c * K + q] : 0.0f;
+    if constexpr (K > 0) wl[q * kChan + cl] = q < K ? p.conv_w[(int64_t)c * K + q] : 0.0f;
     float* relay = rb.piece >= 0 ? p.relay_buf + (int64_t)rb.cut * kRelayVals * kThreads + tid : nullptr;
     if (rb.piece > 0) {  // the later piece's adjoint and running sums
         relay_wait(p.relay_flag + rb.cut, rb.piece, p.err);
@@ -493,14 +498,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             int arr, w;
             slot(k, arr, w);
             if (arr < 3) {
-                float* tile = arr == 0 ? xs_l[buf] : (arr == 1 ? dts_l[buf] : dys_l[buf]);
+                float* tile = arr == 0 ? xs_l[buf] + (w / CPR) * (XP - kChan) : (arr == 1 ? dts_l[buf] : dys_l[buf]);
                 put(tile + w * VPC, stg[k], t0 + w / CPR < L);
             } else if (arr < 5) {
                 put((arr == 3 ? Bs_l[buf] : Cs_l[buf]) + w * VPC, stg[k], t0 + w / CPB < L);
             } else if (arr == 5) {
                 *reinterpret_cast<uint4*>(ck_l + w * 4) = stg[k];
             } else if constexpr (K > 0) {
-                if (t0 - HX + w / CPR >= 0) put(hx_l[buf] + w * VPC, stg[k], true);
+                if (t0 - HX + w / CPR >= 0) put(hx_l[buf] + (w / CPR) * XP + (w % CPR) * VPC, stg[k], true);
             }
         }
         if constexpr (K > 0) {
@@ -513,7 +518,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                                 : (p.conv_state ? p.conv_state[((int64_t)rid * d_inner + cb * kChan + ch) * (K - 1) +
                                                                tau + K - 1]
                                                 : 0.0f);
-                    hx_l[buf][hr * kChan + ch] = v;
+                    hx_l[buf][hr * XP + ch] = v;
                 }
             }
         }
@@ -550,7 +555,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         };
         // input row kk of the block for this lane's channel (kk < 0: history)
         auto xin = [&](int kk) __attribute__((always_inline)) {
-            return kk >= 0 ? xs[kk * kChan + cl] : hx_l[buf][(HX + kk) * kChan + cl];
+            return kk >= 0 ? xs[kk * XP + cl] : hx_l[buf][(HX + kk) * XP + cl];
         };
         if constexpr (K > 0) {
             // quad lane q forms c = sum_j w_j in(t-(K-1)+j) (the forward's order,
@@ -560,25 +565,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             float win[K + 1];
 #pragma unroll
             for (int j = 0; j <= K; ++j) win[j] = xin(2 * q - (K - 1) + j);
-            const float4 wv = *reinterpret_cast<const float4*>(&wl[cl * 4]);
-            const float w[4] = {wv.x, wv.y, wv.z, wv.w};
+            const float w[4] = {wl[cl], wl[kChan + cl], wl[2 * kChan + cl], wl[3 * kChan + cl]};
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 float cv = w[0] * win[e];
 #pragma unroll
                 for (int j = 1; j < K; ++j) cv = fmaf(w[j], win[e + j], cv);
                 const float sg = __builtin_amdgcn_rcpf(1.0f + fast_exp2(-cv * kLog2e));
-                us_l[(2 * q + e) * kChan + cl] = cv * sg;
-                fs_l[(2 * q + e) * kChan + cl] = sg * fmaf(cv, 1.0f - sg, 1.0f);
+                us_l[(2 * q + e) * UP + cl] = cv * sg;
+                fs_l[(2 * q + e) * UP + cl] = sg * fmaf(cv, 1.0f - sg, 1.0f);
             }
             __builtin_amdgcn_wave_barrier();
         }
         auto u_of = [&](int k) __attribute__((always_inline)) {
-            if constexpr (K > 0) return us_l[k * kChan + cl];
+            if constexpr (K > 0) return us_l[k * UP + cl];
             else return rowv(xs, k);
         };
-        // recompute the block: decays a[k][s] and states h[k][s] (= h_{t0+k})
-        float a[kBlk][4], h[kBlk][4];
+        // recompute the block: decays a[k][s] and states h[k][s] (= h_{t0+k});
+        // with the conv (more live values) the adjoint forms the decays again
+        // instead of holding them
+        constexpr bool KEEP_A = K == 0;
+        float a[KEEP_A ? kBlk : 1][4], h[kBlk][4];
 #pragma unroll
         for (int k = 0; k < kBlk; ++k) {
             const float dk = dt_of(k), bk = dk * u_of(k);
@@ -586,8 +593,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             quad4(Bt, k, Bq);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                a[k][s] = fast_exp2(dk * a2[s]);
-                h[k][s] = fmaf(a[k][s], k == 0 ? h0[s] : h[k - 1][s], bk * Bq[s]);
+                const float ak = fast_exp2(dk * a2[s]);
+                if constexpr (KEEP_A) a[k][s] = ak;
+                h[k][s] = fmaf(ak, k == 0 ? h0[s] : h[k - 1][s], bk * Bq[s]);
             }
         }
         // adjoint over the block, last token first
@@ -610,7 +618,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                 g[s] = fmaf(Cq[s], dyk, g[s]);
                 dCp[s] = dyk * h[k][s];
                 S1 = fmaf(g[s], Bq[s], S1);
-                const float ga = g[s] * a[k][s];
+                const float ga = g[s] * (KEEP_A ? a[KEEP_A ? k : 0][s] : fast_exp2(dk * a2[s]));
                 const float qv = ga * (k == 0 ? h0[s] : h[k - 1][s]);
                 S2 = fmaf(qv, An[s], S2);
                 dA_acc[s] = fmaf(qv, dk, dA_acc[s]);
@@ -623,7 +631,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                 float ddt = fmaf(uk, S1, S2);
                 if constexpr (SOFTPLUS) ddt *= sigmoid(draw);
                 const float du = fmaf(Dc, dyk, dk * S1);
-                if constexpr (K > 0) dc_l[buf][k * kChan + cl] = du * fs_l[k * kChan + cl];  // through SiLU
+                if constexpr (K > 0) dc_l[buf][k * kChan + cl] = du * fs_l[k * UP + cl];  // through SiLU
                 else gx_l[k * kChan + cl] = du;
                 gdt_l[k * kChan + cl] = ddt;
                 if (k < nk) dD_acc = fmaf(dyk, uk, dD_acc);
@@ -668,19 +676,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             // block from the later one's buffer
             const int k = tg >> 4, ch = 4 * (tg & 15);
             float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
+#pragma unroll 1
             for (int m = 0; m < K; ++m) {
                 const int rr = k + m;
                 const float4 d = *reinterpret_cast<const float4*>(
                     rr < kBlk ? &dc_l[buf][rr * kChan + ch] : &dc_l[buf ^ 1][(rr - kBlk) * kChan + ch]);
                 const float dv[4] = {d.x, d.y, d.z, d.w};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] = fmaf(wl[(ch + e) * 4 + K - 1 - m], dv[e], acc[e]);
+                for (int e = 0; e < 4; ++e) acc[e] = fmaf(wl[(K - 1 - m) * kChan + ch + e], dv[e], acc[e]);
             }
             gxv = make_float4(acc[0], acc[1], acc[2], acc[3]);
             // tap q's weight sum: dc_t in(t - (K-1) + q), tokens in reverse order
             if (q < K) {
-#pragma unroll
+#pragma unroll 1
                 for (int kk = kBlk - 1; kk >= 0; --kk)
                     dwq = fmaf(dc_l[buf][kk * kChan + cl], xin(kk - (K - 1) + q), dwq);
             }
@@ -746,7 +754,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             for (int m = 0; m < K - 1; ++m) {
                 float gcs = 0.0f;
 #pragma unroll
-                for (int j = 0; j <= m; ++j) gcs = fmaf(wl[cl * 4 + j], dc_l[0][(m - j) * kChan + cl], gcs);
+                for (int j = 0; j <= m; ++j) gcs = fmaf(wl[j * kChan + cl], dc_l[0][(m - j) * kChan + cl], gcs);
                 p.partCS[rowc * (K - 1) + m] = gcs;
             }
         }
