@@ -264,11 +264,9 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int64_t tok0,
     constexpr int XPF = 64 + 8;
     __shared__ __attribute__((aligned(16))) float xf_l[(HX + TT) * XPF];
     __shared__ __attribute__((aligned(16))) char dt_l[TT * XS];
-    // y tile; with the gate and bf16 io the owners' y stays fp32 (row stride
-    // XSF) so that y * SiLU(z) is rounded to bf16 once
-    constexpr bool YF = GATE && ES == 2;
-    constexpr int XSF = 64 * 4 + 32;
-    __shared__ __attribute__((aligned(16))) char y_l[MODE == 1 ? (YF ? TT * XSF : TT * XS) : 16];
+    // y tile in the io type; with the gate the owner multiplies its fp32 y by
+    // SiLU(z) before the one rounding
+    __shared__ __attribute__((aligned(16))) char y_l[MODE == 1 ? TT * XS : 16];
     __shared__ __attribute__((aligned(16))) float B_l[TT][16];
     __shared__ __attribute__((aligned(16))) float C_l[TT][16];
     // y reduce-scatter within each wave: lane (cl, q) leaves its four partial
@@ -381,8 +379,19 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int64_t tok0,
         }
     };
 
+    // The gate: the owner's z for group g of the tile at tb (rows past t_end
+    // read as zero); each group loads the next group's, zc holds the current.
+    auto load_z = [&](int g, int tb) -> float {
+        const auto rz = rsrc(zg, tb, row_stride);
+        const int off = (4 * g + q) * (int)row_stride + cl * ES;
+        if constexpr (ES == 2) return to_f32((bf16_t)__builtin_amdgcn_raw_buffer_load_b16(rz, off, 0, 0));
+        else return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rz, off, 0, 0));
+    };
+    float zc = 0.0f;
     // One group of four tokens; FULL: every token of the group is < t_end.
     auto group = [&](int g, bool full_tile, int tb) {
+        float zn = 0.0f;
+        if constexpr (GATE && MODE == 1) zn = load_z(g + 1, tb);
         const int tt = 4 * g + q;  // owned row of this tile
         if constexpr (MODE == 2) {  // state entering each kCkpt-token block
             if (((tb + 4 * g - t_begin) & (kCkpt - 1)) == 0) {
@@ -445,10 +454,12 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int64_t tok0,
             __builtin_amdgcn_wave_barrier();
             const float ysum = (yr[q] + yr[4 + q]) + (yr[8 + q] + yr[12 + q]);
             __builtin_amdgcn_wave_barrier();
-            const float yv = fmaf(Dc, u, ysum);
-            if constexpr (YF)
-                *reinterpret_cast<float*>(y_l + tt * XSF + cl * 4) = yv;
-            else if constexpr (ES == 2)
+            float yv = fmaf(Dc, u, ysum);
+            if constexpr (GATE) {  // y * SiLU(z), rounded once
+                yv *= silu(zc);
+                zc = zn;
+            }
+            if constexpr (ES == 2)
                 *reinterpret_cast<bf16_t*>(y_l + tt * XS + cl * ES) = bf16_rne(yv);
             else
                 *reinterpret_cast<float*>(y_l + tt * XS + cl * ES) = yv;
@@ -462,14 +473,7 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int64_t tok0,
     for (int tile = 0; tile < n_tiles; ++tile) {
         const int tb = t_begin + tile * TT;
         const bool more = tile + 1 < n_tiles;
-        // the gate's z rows of this tile, issued before the next tile's loads
-        // so that waiting for them does not wait for those
-        u32x4 sz[2];
-        if constexpr (GATE && MODE == 1) {
-            const auto rz = rsrc(zg, tb, row_stride);
-#pragma unroll
-            for (int r = 0; r < 2; ++r) sz[r] = __builtin_amdgcn_raw_buffer_load_b128(rz, xoff[r], 0, 0);
-        }
+        if constexpr (GATE && MODE == 1) zc = load_z(0, tb);  // the first group's z
         load_tile(tb + TT);  // past the end: zero rows, never staged
         if (tb + TT <= t_end) {
 #pragma unroll 2
@@ -490,25 +494,7 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int64_t tok0,
             for (int r = 0; r < 2; ++r) {
                 const int e = tid + kThreads * r;
                 const int row = e / CPR, col = e % CPR;
-                u32x4 yv;
-                if constexpr (YF) {  // 8 fp32 y of the row times SiLU(z), rounded once
-                    const float4 ya = *reinterpret_cast<const float4*>(y_l + row * XSF + col * 32);
-                    const float4 yb = *reinterpret_cast<const float4*>(y_l + row * XSF + col * 32 + 16);
-                    const float yf[8] = {ya.x, ya.y, ya.z, ya.w, yb.x, yb.y, yb.z, yb.w};
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const float z0 = __uint_as_float(sz[r][k] << 16), z1 = __uint_as_float(sz[r][k] & 0xffff0000u);
-                        yv[k] = uint32_t(bf16_rne(yf[2 * k] * silu(z0))) |
-                                (uint32_t(bf16_rne(yf[2 * k + 1] * silu(z1))) << 16);
-                    }
-                } else {
-                    yv = *reinterpret_cast<const u32x4*>(y_l + row * XS + col * 16);
-                    if constexpr (GATE) {  // fp32 io: y * SiLU(z)
-#pragma unroll
-                        for (int k = 0; k < 4; ++k)
-                            yv[k] = __float_as_uint(__uint_as_float(yv[k]) * silu(__uint_as_float(sz[r][k])));
-                    }
-                }
+                const u32x4 yv = *reinterpret_cast<const u32x4*>(y_l + row * XS + col * 16);
                 __builtin_amdgcn_raw_buffer_store_b128(yv, ry, xoff[r], 0, 0);
             }
         }

@@ -6,8 +6,8 @@ their state on through the workspace.  These shapes are sized from the
 device's compute-unit count so that the split happens (the plan says
 "quad_relay"): half a unit over (2 pieces per split job), a fifth over
 (5 pieces), and 3 jobs over (pieces of one tile each), with ragged token
-counts, bf16 and f32, with and without the conv, with the dt bias and
-softplus, and with an invalid id whose NaN state must travel through the
+counts, bf16 and f32, with and without the conv, with the dt bias,
+softplus and the z gate, and with an invalid id whose NaN state must travel through the
 relay.  Every element of y, the final state and the conv state is checked,
 and the workspace's error word must stay clear."""
 import numpy as np
@@ -83,34 +83,40 @@ def test_relay_parity(gpu, name):
     assert torch.equal(r2.out, r.out), "second call on the same workspace differs"
 
 
-def test_relay_with_bias_and_softplus(gpu):
-    """selective_scan_fwd_ext without spans takes the relay too.  (With the
-    gate the kernel stages y in fp32 and fits two workgroups per compute
-    unit, too few to hold the extra piece, so it runs without the relay.)"""
+@pytest.mark.parametrize("gate", [False, True])
+def test_relay_with_bias_softplus_and_gate(gpu, gate):
+    """selective_scan_fwd_ext without spans takes the relay too, with the dt
+    bias, softplus and (gate) the SiLU(z) output gate."""
     L = 450
     p = ssm_inputs.make_varlen_problem(lengths=[L], n_head=64 * _jobs("half"), d_state=16,
-                                       d_conv=4, io="bf16", seed=0x3F0, h0_std=0.3,
-                                       conv_state_std=0.5, dt_softplus=True,
+                                       d_conv=4, io="bf16", seed=0x3F0 + gate, h0_std=0.3,
+                                       conv_state_std=0.5, dt_softplus=True, with_z=gate,
                                        dt_bias_range=(-1.5, 0.5))
     d = desc_of(p)
-    ext = ssm.make_ext(dt_bias=1)
-    assert ssm.ssm_scan_fwd_plan(d, ext) == "quad_relay"
-    assert ssm.ssm_scan_fwd_plan(d, ssm.make_ext(dt_bias=1, z=1)) == "quad"
+    assert ssm.ssm_scan_fwd_plan(d, ssm.make_ext(dt_bias=1, z=int(gate))) == "quad_relay"
     t = device_inputs(p)
     ws = ops.workspace(d, False)
     r = ops.scan_fwd_ext(d, t["s"], t["x"], t["dt"], t["A"], t["B"], t["C"], t.get("D"), t["ids"],
-                         dt_bias=t["dt_bias"], conv_w=t.get("conv_w"),
+                         dt_bias=t["dt_bias"], z=t.get("z"), conv_w=t.get("conv_w"),
                          conv_state=t.get("conv_state"), want_conv_state=True, ws=ws)
     torch.cuda.synchronize()
     assert int(ws[:4].view(torch.int32).item()) == 0
     v = lambda n: p.value(n).astype(np.float64)
     # one sequence over the whole token axis: the span form of the oracle
+    z = v("z")[0] if gate else None
     y, st, cso = oracle.scan_fwd_ext(v("s"), v("x")[0], v("dt")[0], v("A"), v("B")[0], v("C")[0],
                                      v("D"), p.ids, cu_seqlens=np.array([0, L], np.int32),
-                                     dt_bias=v("dt_bias"), conv_w=v("conv_w"),
+                                     dt_bias=v("dt_bias"), z=z, conv_w=v("conv_w"),
                                      conv_state=v("conv_state"), dt_softplus=True)
-    assert_close(host(r.y).reshape(y.shape), y, "bf16", "biased y")
-    assert_close(host(r.state), st, "bf16", "biased state")
+    got = host(r.y).reshape(y.shape)
+    if gate:
+        # y is gated in fp32 and rounded once: its absolute floor scales with |SiLU(z)|
+        scale = np.maximum(1.0, np.abs(z / (1.0 + np.exp(-z))))
+        err = np.abs(got - y)
+        assert np.all(err <= 1e-3 * scale + 2e-2 * np.abs(y)), float(np.max(err))
+    else:
+        assert_close(got, y, "bf16", "biased y")
+    assert_close(host(r.state), st, "bf16", "relay state")
     np.testing.assert_array_equal(host(r.conv_state), cso)
 
 
