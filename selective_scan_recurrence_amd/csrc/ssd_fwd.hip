@@ -126,6 +126,15 @@ __device__ __forceinline__ float wave_incl_sum(float v) {
     return v;
 }
 
+// B and C rows sit in LDS with their states in a permuted order: state
+// n = 32b + 16h + 4g + r at position 32b + 8g + 4h + r.  Products over the
+// states (C B^T) pair the same positions and do not see the order; the
+// carried-state product reads the states 4g..4g+3 of a lane's two
+// accumulator tiles (16 apart) as one 16-byte run.
+__device__ __forceinline__ int spos(int n) {
+    return (n & ~31) | ((n & 12) << 1) | ((n & 16) >> 2) | (n & 3);
+}
+
 // transposing LDS read of this lane's 8-byte block (see the layout above)
 __device__ __forceinline__ bf16x4 ldtr(const bf16_t* p) {
     const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -260,8 +269,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         for (int k = 0; k < BPER; ++k) {
             const int e = tid + kThreads * k;
             const int t = e / (N / 8), part = e % (N / 8);
-            *reinterpret_cast<u32x4*>(&B_l[t * NP + part * 8]) = sb[k];
-            if constexpr (!CKPT) *reinterpret_cast<u32x4*>(&C_l[t * NP + part * 8]) = sc[k];
+            // states 8*part .. +7 go to their places in the permuted order (spos)
+            const int pos = 32 * (part >> 2) + 16 * (part & 1) + 4 * ((part >> 1) & 1);
+            *reinterpret_cast<u32x2*>(&B_l[t * NP + pos]) = u32x2{sb[k].x, sb[k].y};
+            *reinterpret_cast<u32x2*>(&B_l[t * NP + pos + 8]) = u32x2{sb[k].z, sb[k].w};
+            if constexpr (!CKPT) {
+                *reinterpret_cast<u32x2*>(&C_l[t * NP + pos]) = u32x2{sc[k].x, sc[k].y};
+                *reinterpret_cast<u32x2*>(&C_l[t * NP + pos + 8]) = u32x2{sc[k].z, sc[k].w};
+            }
         }
         if (wave == 0) {  // decays of the chunk, lane = token
             float d = to_f32((bf16_t)sdt) + dtb;
@@ -373,12 +388,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
             for (int tbk = 0; tbk < 4; ++tbk) {
                 yo[tbk] = f32x4{0.f, 0.f, 0.f, 0.f};
-                const bf16_t* crow = &C_l[(tbk * 16 + l16) * NP + NW * sh + 4 * g4];
+                // C at this lane's states: with the permuted order, states
+                // 32kb + 4g + r and 32kb + 16 + 4g + r of the part sit side by side
+                const bf16_t* crow = &C_l[(tbk * 16 + l16) * NP + spos(NW * sh + 4 * g4)];
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
-                    const bf16x4 c0 = ld4(crow + 32 * kb);
-                    const bf16x4 c1 = 2 * kb + 1 < NH ? ld4(crow + 32 * kb + 16) : bf16x4{0, 0, 0, 0};
-                    const bf16x8 cop = cat(c0, c1);
+                    const bf16x8 cop = 2 * kb + 1 < NH ? ld8(crow + 32 * kb)
+                                                       : cat(ld4(crow + 32 * kb), bf16x4{0, 0, 0, 0});
                     yo[tbk] = mfma(ahi[kb], cop, yo[tbk]);
                     yo[tbk] = mfma(alo[kb], cop, yo[tbk]);
                 }
@@ -464,8 +480,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                 f32x4 a = hacc[j] * e_last;
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    // B column n = 16nb + l16, rows s = 32kk + 8g + j
-                    const bf16_t* br = &B_l[(kk * 32 + 8 * g4 + (l16 >> 2)) * NP + nb * 16 + 4 * (l16 & 3)];
+                    // B column n = 16nb + l16, rows s = 32kk + 8g + j (4 consecutive
+                    // states stay consecutive in the permuted order)
+                    const bf16_t* br = &B_l[(kk * 32 + 8 * g4 + (l16 >> 2)) * NP + spos(nb * 16 + 4 * (l16 & 3))];
                     a = mfma(cat(ldtr(br), ldtr(br + 4 * NP)), xw[kk], a);
                 }
                 hacc[j] = a;
