@@ -150,15 +150,17 @@ def valu_slots_per_channel_token(p, backward=False) -> float:
 # kernel sources it was taken on; bench.py reports null once any of them changes.
 COPY_FACTOR = {"fetch": 1.99993, "write": 1.00000}
 MEASURED_TRAFFIC = {
-    "C1": {"sha256": "16e6eeef9848c1dfb8bcc0084e2262cc3353987d0d4939a7359568a52b206b8f", "fetch_kib": 34140.6, "write_kib": 33024.0},
-    "C2": {"sha256": "16e6eeef9848c1dfb8bcc0084e2262cc3353987d0d4939a7359568a52b206b8f", "fetch_kib": 339350.8, "write_kib": 330240.0},
-    "C3": {"sha256": "b361281832b24d2c5fa3bed6c1adaa6dadd6ce25471c2aded6e156b2cc16cbd6", "fetch_kib": 142741.0, "write_kib": 174081.0},
-    "C4": {"sha256": "dd18f7a60ce21f038f90f17eb1da7da86124d0b03b67e7302e282072df6b3181", "fetch_kib": 1665316.9, "write_kib": 2961396.0},
-    "C5": {"sha256": "19d21d3c16653649e1d9cac38de168171b782e33178b052b1b50c035b9a95dd5", "fetch_kib": 512936.3, "write_kib": 704342.2},
-    "C6": {"sha256": "fefd2284eb86a0bce2f08280980fbc69fc554eef99b5ec7621fddf1b67c6921a", "fetch_kib": 52837.7, "write_kib": 100230.0},
-    "C7": {"sha256": "fefd2284eb86a0bce2f08280980fbc69fc554eef99b5ec7621fddf1b67c6921a", "fetch_kib": 83414.4, "write_kib": 164482.1},
-    "C8": {"sha256": "e17c27a243ebd3f9b3414f1a08bdca51ddbc2cca792ed119a5b5ce51ab8ad89c", "fetch_kib": 681539.8, "write_kib": 2369653.5},
-    "C9": {"sha256": "856c2b90a5a1872964550d0184eae879db27307310394725b0eaea81e7700484", "fetch_kib": 505345.6, "write_kib": 330720.0},
+    "C1": {"sha256": "9d2db653a26b0768b2ceaffb548b58081af25ab8f226ee762d9482f7960b0d17", "fetch_kib": 34138.7, "write_kib": 33024.0},
+    "C2": {"sha256": "9d2db653a26b0768b2ceaffb548b58081af25ab8f226ee762d9482f7960b0d17", "fetch_kib": 341018.7, "write_kib": 330760.0},
+    "C3": {"sha256": "0ad651441327e545fa6ee95cc1b113eebb0136bb38d223ed2320249da77d4ace", "fetch_kib": 143724.4, "write_kib": 174080.8},
+    "C4": {"sha256": "e214c43e708980aac63c214b03170a7782de6f7bba09705b17a5a1e2ed4ffd0c", "fetch_kib": 1667653.6, "write_kib": 2962556.0},
+    "C5": {"sha256": "19d21d3c16653649e1d9cac38de168171b782e33178b052b1b50c035b9a95dd5", "fetch_kib": 512932.3, "write_kib": 704850.3},
+    "C6": {"sha256": "fefd2284eb86a0bce2f08280980fbc69fc554eef99b5ec7621fddf1b67c6921a", "fetch_kib": 52842.3, "write_kib": 100238.6},
+    "C7": {"sha256": "fefd2284eb86a0bce2f08280980fbc69fc554eef99b5ec7621fddf1b67c6921a", "fetch_kib": 83410.2, "write_kib": 164481.8},
+    "C8": {"sha256": "b3d971e6a50acc9e0618b7656018fd56c079f1e9bd9142c4c5157ccd23b634ba", "fetch_kib": 1343096.0, "write_kib": 2382312.2},
+    "C9": {"sha256": "cc57330726b135617c0fdccf0e793ca91d1f5f0ba4a4d47741bf7473a52e0ec9", "fetch_kib": 505010.0, "write_kib": 330720.0},
+    "C10": {"sha256": "e214c43e708980aac63c214b03170a7782de6f7bba09705b17a5a1e2ed4ffd0c", "fetch_kib": 1667819.9, "write_kib": 2964492.0},
+    "C11": {"sha256": "276c97c0ab38954d90eea36e94e56223be1d1cf15921334358e607baa728a14b", "fetch_kib": 164316.9, "write_kib": 327680.0},
 }
 KERNEL_SOURCES = {
     "C0": ("scan_fwd.hip", "scan_fwd_ts.hip", "scan_fwd_quad.hip", "relay.h", "relay.hip", "device_common.h"),
@@ -171,7 +173,7 @@ KERNEL_SOURCES = {
     "C6": ("decode.hip", "device_common.h"),
     "C7": ("decode.hip", "device_common.h"),
     "C8": ("ssd_bwd.hip", "ssd_fwd.hip", "device_common.h"),
-    "C10": ("scan_bwd.hip", "scan_bwd_rows.hip", "device_common.h"),
+    "C10": ("scan_bwd.hip", "scan_fwd_quad.hip", "relay.h", "relay.hip", "device_common.h"),
     "C11": ("conv_fwd.hip", "device_common.h"),
 }
 
