@@ -342,6 +342,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // d_x and d_dt of the block, [token][channel]
     __shared__ __attribute__((aligned(16))) float gx_l[kBlk * kChan];
     __shared__ __attribute__((aligned(16))) float gdt_l[kBlk * kChan];
+    // where quad lanes 2 and 3 put their copies of the per-channel terms (K == 0)
+    __shared__ __attribute__((aligned(16))) float spare_l[K == 0 ? kBlk * kChan : 4];
 
     const int tid = threadIdx.x;
     const int q = tid & 3;
@@ -599,6 +601,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             }
         }
         // adjoint over the block, last token first
+        float* const own_row = (q == 0 ? gx_l : q == 1 ? gdt_l : spare_l) + cl;  // K == 0
 #pragma unroll
         for (int k = kBlk - 1; k >= 0; --k) {
             // no contraction here: a product summed across lanes would otherwise be
@@ -627,12 +630,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             }
             S1 = quad_sum(S1);
             S2 = quad_sum(S2);
-            if (q == 0) {
+            if constexpr (K == 0) {
+                // every lane of the quad forms its channel's terms (no branch):
+                // lane 0 stores du, lane 1 ddt, lanes 2 and 3 a copy of lane
+                // 0's value to a spare row
                 float ddt = fmaf(uk, S1, S2);
                 if constexpr (SOFTPLUS) ddt *= sigmoid(draw);
                 const float du = fmaf(Dc, dyk, dk * S1);
-                if constexpr (K > 0) dc_l[buf][k * kChan + cl] = du * fs_l[k * UP + cl];  // through SiLU
-                else gx_l[k * kChan + cl] = du;
+                own_row[k * kChan] = q == 1 ? ddt : du;
+                if (k < nk) dD_acc = fmaf(dyk, uk, dD_acc);
+            } else if (q == 0) {  // (the conv variants have no registers to spare)
+                float ddt = fmaf(uk, S1, S2);
+                if constexpr (SOFTPLUS) ddt *= sigmoid(draw);
+                const float du = fmaf(Dc, dyk, dk * S1);
+                dc_l[buf][k * kChan + cl] = du * fs_l[k * UP + cl];  // through SiLU
                 gdt_l[k * kChan + cl] = ddt;
                 if (k < nk) dD_acc = fmaf(dyk, uk, dD_acc);
             }

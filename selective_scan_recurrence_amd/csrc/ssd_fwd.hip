@@ -305,6 +305,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     for (int e = tid; e < kQ * MP / 2; e += kThreads) reinterpret_cast<uint32_t*>(M_l)[e] = 0u;
 
     load_chunk(0);
+    bf16x8 xcol[2];  // x columns p = pw + l16, rows s = 32kk + 8g + j
     for (int ch = 0; ch < n_chunks; ++ch) {
         const int t0 = ch * kQ;
         __syncthreads();  // every wave is done with the previous chunk's tiles
@@ -413,8 +414,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 
         const auto ry = rsrc(yg, t0, xrow);
         // Yd^T = X^T M^T over s for the wave's token blocks (x columns of its
-        // channel block, shared by the blocks)
-        bf16x8 xcol[2];
+        // channel block, shared by the blocks and by the state update below)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const bf16_t* xr = &X_l[(kk * 32 + 8 * g4 + (l16 >> 2)) * XP + pw + 4 * (l16 & 3)];
@@ -465,9 +465,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             bf16x8 xw[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                // x column p = pw + l16, rows s = 32kk + 8g + j
-                const bf16_t* xr = &X_l[(kk * 32 + 8 * g4 + (l16 >> 2)) * XP + pw + 4 * (l16 & 3)];
-                const bf16x8 xv = cat(ldtr(xr), ldtr(xr + 4 * XP));
+                if constexpr (CKPT) {  // (the output pass has them already)
+                    const bf16_t* xr = &X_l[(kk * 32 + 8 * g4 + (l16 >> 2)) * XP + pw + 4 * (l16 & 3)];
+                    xcol[kk] = cat(ldtr(xr), ldtr(xr + 4 * XP));
+                }
+                const bf16x8 xv = xcol[kk];
                 const float4 w0 = *reinterpret_cast<const float4*>(&w_l[kk * 32 + 8 * g4]);
                 const float4 w1 = *reinterpret_cast<const float4*>(&w_l[kk * 32 + 8 * g4 + 4]);
                 const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
