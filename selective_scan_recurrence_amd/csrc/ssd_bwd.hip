@@ -437,85 +437,75 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
 
         // (3) dC [t][n] = exp(cum_t) (dY h_in) + Lm B, and dB [s][n] = Lm^T C + w_s (X G),
         // for token block wave % 4 and this wave's half of the states; the
-        // dcum terms o_t and u_s on the way
+        // dcum terms o_t and u_s on the way.  The products are formed
+        // transposed ([n][t]: operands swapped), so that a lane holds four
+        // consecutive states n = 16 nb + 4 g4 .. + 3 of one token t = 16 tb + l16
+        // and stores them as one 16-byte piece of the token's row.
         {
             constexpr int NPW = NB / 2;
             const int tb = wave & 3, nb0 = (wave >> 2) * NPW, half = wave >> 2;
-            float yo[4] = {0.f, 0.f, 0.f, 0.f}, uu[4] = {0.f, 0.f, 0.f, 0.f};
-            // this head's rows [t][2][N] of the partial sums from the chunk's first
-            // token (rows are padded to whole chunks: no store needs a guard)
-            float* bcc = p.bc_part + (((int64_t)i * p.H + hh) * p.n_chunks * kQ + t0) * 2 * N;
-            // the lane's four tokens t = 16 tb + 4 g4 + rr (and s, the same block)
-            const float4 et4 = *reinterpret_cast<const float4*>(&ecum_l[tb * 16 + 4 * g4]);
-            const float4 ws4 = *reinterpret_cast<const float4*>(&w_l[tb * 16 + 4 * g4]);
-            const float et[4] = {et4.x, et4.y, et4.z, et4.w}, wsv[4] = {ws4.x, ws4.y, ws4.z, ws4.w};
-            // C[t][n] and B[s][n] of the lane's four rows at column n: one
-            // transposing read each (lanes 4k + q address row 4 g4 + k)
-            const int trow = (tb * 16 + 4 * g4 + (l16 >> 2)) * NP + 4 * (l16 & 3);
+            const int t = tb * 16 + l16;  // also s for the dB part (the same block)
+            float yo = 0.0f, uu = 0.0f;
+            // this head's row [2][N] of the partial sums for token t (rows are
+            // padded to whole chunks: no store needs a guard)
+            float* bcc = p.bc_part + (((int64_t)i * p.H + hh) * p.n_chunks * kQ + t0 + t) * 2 * N;
+            const float et = ecum_l[t], ws = w_l[t];
             // not unrolled: the stores of one state block then leave before the
             // next block's products, which keeps the register count under the cap
 #pragma unroll 1
             for (int j = 0; j < NPW; ++j) {
-                const int nb = nb0 + j, n = nb * 16 + l16;
+                const int nb = nb0 + j, n0 = nb * 16 + 4 * g4;
                 f32x4 c1 = {0.f, 0.f, 0.f, 0.f}, c2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < P / 32; ++kk) {
                     const bf16x8 yo8 = rowop(Y_l, XP, tb * 16, kk * 32);
-                    c1 = mfma(yo8, colop(H_l, NPH, nb * 16, kk * 32), c1);
-                    c1 = mfma(yo8, colop(Hr_l, NPH, nb * 16, kk * 32), c1);
+                    c1 = mfma(colop(H_l, NPH, nb * 16, kk * 32), yo8, c1);
+                    c1 = mfma(colop(Hr_l, NPH, nb * 16, kk * 32), yo8, c1);
                 }
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
                     if (2 * kk > tb) continue;  // every s of the block is after t
-                    c2 = mfma(rowop(Lm_l, MP, tb * 16, kk * 32), colop(B_l, NP, nb * 16, kk * 32), c2);
+                    c2 = mfma(colop(B_l, NP, nb * 16, kk * 32), rowop(Lm_l, MP, tb * 16, kk * 32), c2);
                 }
-                const bf16x4 cn = ldtr(&C_l[trow + nb * 16]);
-                // lane: t = 16 tb + 4 g4 + rr, n
+                const bf16x4 cn = ld4(&C_l[t * NP + n0]);
+                float dc[4];
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
-                    const int t = tb * 16 + 4 * g4 + rr;
-                    const float off = et[rr] * c1[rr];
-                    yo[rr] = fmaf(off, (float)cn[rr], yo[rr]);
-                    bcc[t * 2 * N + N + n] = off + c2[rr];
+                    const float off = et * c1[rr];
+                    yo = fmaf(off, (float)cn[rr], yo);
+                    dc[rr] = off + c2[rr];
                 }
+                *reinterpret_cast<float4*>(bcc + N + n0) = make_float4(dc[0], dc[1], dc[2], dc[3]);
 
                 f32x4 b1 = {0.f, 0.f, 0.f, 0.f}, b2 = {0.f, 0.f, 0.f, 0.f};
-                const int sb = tb;
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    if (2 * kk + 1 < sb) continue;  // every t of the block is before s
-                    b1 = mfma(colop(Lm_l, MP, sb * 16, kk * 32), colop(C_l, NP, nb * 16, kk * 32), b1);
+                    if (2 * kk + 1 < tb) continue;  // every t of the block is before s
+                    b1 = mfma(colop(C_l, NP, nb * 16, kk * 32), colop(Lm_l, MP, tb * 16, kk * 32), b1);
                 }
 #pragma unroll
                 for (int kk = 0; kk < P / 32; ++kk) {
-                    const bf16x8 xo = rowop(X_l, XP, sb * 16, kk * 32);
-                    b2 = mfma(xo, colop(G_l, NPH, nb * 16, kk * 32), b2);
-                    b2 = mfma(xo, colop(Gr_l, NPH, nb * 16, kk * 32), b2);
+                    const bf16x8 xo = rowop(X_l, XP, tb * 16, kk * 32);
+                    b2 = mfma(colop(G_l, NPH, nb * 16, kk * 32), xo, b2);
+                    b2 = mfma(colop(Gr_l, NPH, nb * 16, kk * 32), xo, b2);
                 }
-                const bf16x4 bn = ldtr(&B_l[trow + nb * 16]);
-                // lane: s = 16 sb + 4 g4 + rr, n
+                const bf16x4 bn = ld4(&B_l[t * NP + n0]);
+                float db[4];
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
-                    const int s = sb * 16 + 4 * g4 + rr;
-                    uu[rr] = fmaf(b2[rr], (float)bn[rr], uu[rr]);
-                    bcc[s * 2 * N + n] = fmaf(wsv[rr], b2[rr], b1[rr]);
+                    uu = fmaf(b2[rr], (float)bn[rr], uu);
+                    db[rr] = fmaf(ws, b2[rr], b1[rr]);
                 }
+                *reinterpret_cast<float4*>(bcc + n0) = make_float4(db[0], db[1], db[2], db[3]);
             }
-            // sums over this wave's n (the 16 lanes of a group)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                float a = yo[rr], b = uu[rr];
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) {
-                    a += __shfl_xor(a, o);
-                    b += __shfl_xor(b, o);
-                }
-                yo[rr] = a;
-                uu[rr] = b;
-            }
-            if (l16 == 0) {
-                *reinterpret_cast<float4*>(&yoff_l[half][tb * 16 + 4 * g4]) = make_float4(yo[0], yo[1], yo[2], yo[3]);
-                *reinterpret_cast<float4*>(&u_l[half][tb * 16 + 4 * g4]) = make_float4(uu[0], uu[1], uu[2], uu[3]);
+            // sums over this wave's states: the lane's own, then its four lane groups
+            yo += __shfl_xor(yo, 16);
+            yo += __shfl_xor(yo, 32);
+            uu += __shfl_xor(uu, 16);
+            uu += __shfl_xor(uu, 32);
+            if (g4 == 0) {
+                yoff_l[half][t] = yo;
+                u_l[half][t] = uu;
             }
         }
 
