@@ -80,9 +80,10 @@ enum {
 enum {
     SSM_DEVERR_IDS = 1u,     /* an ids[i] was outside [0, n_state_rows) */
     SSM_DEVERR_SEQLENS = 2u, /* a cu_seqlens span was invalid (selective_scan_fwd_ext) */
-    SSM_DEVERR_RELAY = 4u    /* a forward workgroup gave up waiting for the state of the
-                                time piece before its own (only if the device stalls
-                                for seconds); that call's y and state are unreliable */
+    SSM_DEVERR_RELAY = 4u    /* a workgroup of a split grid gave up waiting for the
+                                values of the time piece before its own (only if the
+                                device stalls for seconds); that call's results are
+                                unreliable */
 };
 
 typedef struct ssm_scan_desc {
@@ -132,7 +133,8 @@ size_t ssm_scan_dgrad_layout(const ssm_scan_desc *desc, size_t offsets[7]);
  * for selective_scan_fwd, 1 for selective_scan_bwd.  The first 256 bytes of
  * a workspace hold the device-error word: zero the workspace once after
  * allocating it; the library sets bits and never clears them.  The rest may
- * hold flags of the relay split (see ssm_scan_fwd_plan) that every finished
+ * hold flags of the relay split (see ssm_scan_fwd_plan) and of the backward's
+ * split of the Mamba-2 form (selective_scan_bwd) that every finished
  * call leaves at zero; after SSM_DEVERR_RELAY, zero the workspace again. */
 size_t ssm_scan_workspace_bytes(const ssm_scan_desc *desc, int backward);
 
@@ -301,7 +303,10 @@ const char *ssm_scan_fwd_plan(const ssm_scan_desc *desc, const ssm_scan_ext *ext
  *  - the Mamba-2 form with bf16 io, head_dim 32 or 64, d_state 64 or 128 and
  *    16-byte aligned x, dout, B, C, s and dgrad: chunked products on bf16
  *    MFMA operands (the carried gradient and the checkpointed state as bf16
- *    pairs) with fp32 accumulation;
+ *    pairs) with fp32 accumulation; when the (sequence, head) jobs exceed
+ *    the compute units unevenly, each is cut into pieces of whole chunks
+ *    that hand the carried gradient on (bitwise the same results;
+ *    SSM_RELAY=0 turns the split off);
  *  - every other shape: one lane group per (sequence, channel) row with
  *    fp32 arithmetic.
  * Every sum over channels, heads, tokens or sequences is taken in a fixed

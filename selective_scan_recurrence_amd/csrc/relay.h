@@ -6,9 +6,10 @@
 // 2.5.  The relay keeps floor(n/m) whole jobs per unit and cuts each of the
 // remaining n mod m jobs in time into k = m / (n mod m) pieces, one per unit
 // that has room.  Piece j + 1 starts from the state piece j ends with
-// (forward in time, or backward for the adjoint): piece j stores it, fences at
-// agent scope and raises a per-job flag; piece j + 1 waits for the flag and
-// then reads the state; the last piece puts the flag back to zero.  Block
+// (forward in time, or backward for the adjoint): piece j stores it with
+// agent-scope atomic stores, waits for them to complete and raises a per-job
+// flag; piece j + 1 waits for the flag (acquire) and then reads the state;
+// the last piece puts the flag back to zero.  Block
 // numbers put every whole job first and then the
 // pieces in chain order, and the dispatcher hands out workgroups in number
 // order, so a piece that waits was dispatched after the piece it waits for,
@@ -42,6 +43,22 @@ struct RelaySplit {
 // evenly, the units cannot hold one more workgroup, or pieces would be
 // shorter than a tile.
 RelaySplit relay_split(int64_t jobs, int64_t L, int tile, int cap, int n_cu, int max_jobs);
+
+// Round split, for workgroups too large to share a compute unit with the
+// relay's extra piece (one resident workgroup per unit): n jobs on s
+// resident slots run in ceil(n/s) rounds, so 320 jobs on 256 units take two
+// rounds for 1.25 rounds of work.  Every job is cut into k pieces of `len`
+// steps, numbered piece-major (block b: piece b / n of job b % n, piece 0
+// the first in the job's own order), so that pieces fill the rounds evenly;
+// piece j + 1 of a job was dispatched n blocks after piece j and waits on it
+// as in the relay above (every wait ends).  k is chosen by a model of the
+// time, max(ceil(n k / s), k) rounds of (len + 1) steps (one step for the
+// hand-over), over k = 1 .. 8 with len >= min_len; k == 1: no split.
+struct RoundSplit {
+    int k = 0;    // pieces per job; 0 or 1: no split
+    int len = 0;  // steps per piece
+};
+RoundSplit round_split(int64_t jobs, int steps, int64_t slots, int min_len);
 
 // Host: compute units of the current device, 0 without one (cached).
 int device_cus();
@@ -80,13 +97,27 @@ __device__ __forceinline__ void relay_wait(const int* flag, int want, uint32_t* 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
-// Publish this workgroup's state stores: every thread's stores reach agent
-// scope before thread 0 raises the flag to `value`.  Every thread of the
-// workgroup must call it, after its own stores.
-__device__ __forceinline__ void relay_publish(int* flag, int value) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+// Hand-over values stored for another compute unit: agent-scope atomic
+// stores, which go past this unit's L2 without a writeback of the whole
+// cache, so that relay_publish_puts needs no release fence.
+__device__ __forceinline__ void relay_put(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Publish values stored with relay_put only: each thread waits until its own
+// stores are complete (vmcnt(0); expcnt and lgkmcnt left at their maxima),
+// the barrier gathers the workgroup, and thread 0 raises the flag with
+// another agent-scope store.  Every thread of the workgroup must call it,
+// after its own relay_put stores.  An agent-scope release fence would do the
+// same and also write back every dirty line of the unit's L2, which a
+// write-heavy kernel pays for at every hand-over (the Mamba-2 backward's
+// split measured 1.77 ms with it, 1.43 ms without).
+__device__ __forceinline__ void relay_publish_puts(int* flag, int value) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_store(flag, value, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) __hip_atomic_store(flag, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The last piece of a chain, once its wait has ended: put the flag back to

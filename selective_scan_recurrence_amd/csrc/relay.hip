@@ -1,6 +1,7 @@
 // Host side of the relay split (see relay.h).
 #include <stdlib.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -25,6 +26,28 @@ RelaySplit relay_split(int64_t jobs, int64_t L, int tile, int cap, int n_cu, int
     r.rem = (int)rem;
     r.k = (int)k;
     r.len = (int)len;
+    return r;
+}
+
+RoundSplit round_split(int64_t jobs, int steps, int64_t slots, int min_len) {
+    RoundSplit r;
+    const char* env = getenv("SSM_RELAY");  // "0": never split (read at every launch)
+    if (env && env[0] == '0') return r;
+    if (jobs <= 0 || slots <= 0 || steps <= 0 || jobs <= slots) return r;
+    int64_t best = -1;
+    for (int k = 1; k <= 8; ++k) {
+        const int len = (steps + k - 1) / k;
+        if (k > 1 && len < min_len) break;
+        const int kk = (steps + len - 1) / len;  // pieces actually needed
+        const int64_t rounds = std::max<int64_t>((jobs * kk + slots - 1) / slots, kk);
+        const int64_t t = rounds * (len + 1);
+        if (best < 0 || t < best) {
+            best = t;
+            r.k = kk;
+            r.len = len;
+        }
+    }
+    if (r.k <= 1) r = RoundSplit{};
     return r;
 }
 

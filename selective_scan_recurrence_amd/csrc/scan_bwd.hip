@@ -734,16 +734,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     if (rb.piece >= 0 && rb.piece + 1 < p.relay_k) {  // hand on to the earlier piece
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            relay[s * kThreads] = g[s];
-            relay[(4 + s) * kThreads] = dA_acc[s];
+            relay_put(&relay[s * kThreads], g[s]);
+            relay_put(&relay[(4 + s) * kThreads], dA_acc[s]);
         }
-        relay[8 * kThreads] = dD_acc;
+        relay_put(&relay[8 * kThreads], dD_acc);
         if constexpr (K > 0) {
             // the first rows of dc of this range, for the d_x of the range before
-            relay[9 * kThreads] = q < K - 1 ? dc_l[b_lo & 1][q * kChan + cl] : 0.0f;
-            relay[10 * kThreads] = dwq;
+            relay_put(&relay[9 * kThreads], q < K - 1 ? dc_l[b_lo & 1][q * kChan + cl] : 0.0f);
+            relay_put(&relay[10 * kThreads], dwq);
         }
-        relay_publish(p.relay_flag + rb.cut, rb.piece + 1);
+        relay_publish_puts(p.relay_flag + rb.cut, rb.piece + 1);
         return;
     }
     {

@@ -629,8 +629,8 @@ __global__ __launch_bounds__(kThreads) void quad_out(QuadKP p) {
     }
     if (piece >= 0 && piece + 1 < p.relay_k) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) relay_h[s] = h[s];  // hand the state on
-        relay_publish(p.relay_flag + sj, piece + 1);
+        for (int s = 0; s < 4; ++s) relay_put(&relay_h[s], h[s]);  // hand the state on
+        relay_publish_puts(p.relay_flag + sj, piece + 1);
         return;
     }
     if (active && chunk == p.n_chunks - 1) {

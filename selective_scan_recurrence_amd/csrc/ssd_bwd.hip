@@ -42,7 +42,16 @@
 // head) as partial sums and added over the group's heads in head order by a
 // second kernel, as are dA, dD (over sequences) and dh_0 (by ids): every
 // sum has a fixed order, so results repeat bitwise.
+//
+// Round split (relay.h).  The workgroup needs most of a compute unit's LDS,
+// so one runs per unit, and S*H jobs a little above the unit count take two
+// rounds.  Then every job is cut into k pieces of whole chunks, numbered
+// piece-major, the later chunks first: a piece starts from the carried
+// gradient G and the running dA and dD sums the piece before it (later in
+// time) hands on through the workspace, so every value keeps the order of
+// the unsplit grid and results are bitwise the same.
 #include "device_common.h"
+#include "relay.h"
 #include "ssm_internal.h"
 
 #include <algorithm>
@@ -80,7 +89,23 @@ struct SsdBwdKP {
     float* ds_part;      // [S][H][P][N]: dL/dh_0
     int L, H, G, R, hpg, n_chunks;
     int has_D;
+    // round split (relay_k == 0: off): block b runs piece b / (S H) of job
+    // b % (S H), piece 0 holding the last relay_len chunks
+    int relay_k, relay_len;
+    int* relay_flag;     // [S H]
+    float* relay_buf;    // [S H][kRelayVals][kThreads]: G (16), dD, dA
+    uint32_t* err;
 };
+
+constexpr int kRelayVals = 18;  // values a piece hands on per thread
+constexpr int kMinPieceChunks = 8;  // shortest piece of the round split (chunks)
+
+// Workspace of the round split: the hand-over values and a flag per job
+// (none when the sequences are too short to cut).
+size_t ssd_relay_bytes(int64_t jobs, int64_t n_chunks) {
+    if (n_chunks < 2 * kMinPieceChunks) return 0;
+    return align_up((size_t)jobs * kRelayVals * kThreads * 4, 256) + align_up((size_t)jobs * 4, 256);
+}
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -147,7 +172,9 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
-    const int hh = (int)(blockIdx.x % (unsigned)p.H), i = (int)(blockIdx.x / (unsigned)p.H);
+    const int jobs = p.relay_k ? (int)gridDim.x / p.relay_k : (int)gridDim.x;
+    const int job = (int)(blockIdx.x % (unsigned)jobs), piece = p.relay_k ? (int)(blockIdx.x / (unsigned)jobs) : -1;
+    const int hh = job % p.H, i = job / p.H;
     const int grp = hh / p.hpg;
     const int L = p.L;
     const float Ah = p.A[hh];
@@ -161,7 +188,24 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
     const int sp = owns ? wave >> 1 : 0, sh = wave & 1;
     const int pw = sp * 16;
     f32x4 gacc[NH];
-    {
+    float dD_acc = 0.0f, dA_acc = 0.0f;
+    // chunks [c_lo, c_hi) of this workgroup, taken from the last
+    int c_hi = p.n_chunks, c_lo = 0;
+    float* relay = piece >= 0 ? p.relay_buf + (int64_t)job * kRelayVals * kThreads + tid : nullptr;
+    if (piece >= 0) {
+        c_hi = p.n_chunks - piece * p.relay_len;
+        c_lo = max(0, c_hi - p.relay_len);
+    }
+    if (piece > 0) {  // the later piece's carried gradient and running sums
+        relay_wait(p.relay_flag + job, piece, p.err);
+        if (piece + 1 == p.relay_k) relay_reset(p.relay_flag + job);
+#pragma unroll
+        for (int j = 0; j < NH; ++j)
+            gacc[j] = f32x4{relay[(4 * j) * kThreads], relay[(4 * j + 1) * kThreads],
+                            relay[(4 * j + 2) * kThreads], relay[(4 * j + 3) * kThreads]};
+        dD_acc = relay[16 * kThreads];
+        dA_acc = relay[17 * kThreads];
+    } else {
         const float* g0 = p.dstate + (((int64_t)i * p.H + hh) * P + pw + l16) * N + NH * sh * 16;
 #pragma unroll
         for (int j = 0; j < NH; ++j) {
@@ -305,10 +349,8 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
         (&zcol_l[0][0])[e] = 0.0f;
     }
 
-    float dD_acc = 0.0f, dA_acc = 0.0f;
-    const int n_chunks = p.n_chunks;
-    load_chunk(n_chunks - 1);
-    for (int ch = n_chunks - 1; ch >= 0; --ch) {
+    load_chunk(c_hi - 1);
+    for (int ch = c_hi - 1; ch >= c_lo; --ch) {
         const int t0 = ch * kQ;
         __syncthreads();  // every wave is done with the later chunk's tiles and partial sums
         store_chunk(t0);
@@ -450,6 +492,13 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
             // padded to whole chunks: no store needs a guard)
             float* bcc = p.bc_part + (((int64_t)i * p.H + hh) * p.n_chunks * kQ + t0 + t) * 2 * N;
             const float et = ecum_l[t], ws = w_l[t];
+            // the dy and x rows of the token block, shared by every state block
+            bf16x8 yo8[P / 32], xo[P / 32];
+#pragma unroll
+            for (int kk = 0; kk < P / 32; ++kk) {
+                yo8[kk] = rowop(Y_l, XP, tb * 16, kk * 32);
+                xo[kk] = rowop(X_l, XP, tb * 16, kk * 32);
+            }
             // not unrolled: the stores of one state block then leave before the
             // next block's products, which keeps the register count under the cap
 #pragma unroll 1
@@ -458,9 +507,8 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
                 f32x4 c1 = {0.f, 0.f, 0.f, 0.f}, c2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < P / 32; ++kk) {
-                    const bf16x8 yo8 = rowop(Y_l, XP, tb * 16, kk * 32);
-                    c1 = mfma(colop(H_l, NPH, nb * 16, kk * 32), yo8, c1);
-                    c1 = mfma(colop(Hr_l, NPH, nb * 16, kk * 32), yo8, c1);
+                    c1 = mfma(colop(H_l, NPH, nb * 16, kk * 32), yo8[kk], c1);
+                    c1 = mfma(colop(Hr_l, NPH, nb * 16, kk * 32), yo8[kk], c1);
                 }
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
@@ -485,9 +533,8 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
                 }
 #pragma unroll
                 for (int kk = 0; kk < P / 32; ++kk) {
-                    const bf16x8 xo = rowop(X_l, XP, tb * 16, kk * 32);
-                    b2 = mfma(colop(G_l, NPH, nb * 16, kk * 32), xo, b2);
-                    b2 = mfma(colop(Gr_l, NPH, nb * 16, kk * 32), xo, b2);
+                    b2 = mfma(colop(G_l, NPH, nb * 16, kk * 32), xo[kk], b2);
+                    b2 = mfma(colop(Gr_l, NPH, nb * 16, kk * 32), xo[kk], b2);
                 }
                 const bf16x4 bn = ld4(&B_l[t * NP + n0]);
                 float db[4];
@@ -572,6 +619,16 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
         }
     }
 
+    if (piece >= 0 && piece + 1 < p.relay_k) {  // hand on to the earlier piece
+#pragma unroll
+        for (int j = 0; j < NH; ++j)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) relay_put(&relay[(4 * j + rr) * kThreads], gacc[j][rr]);
+        relay_put(&relay[16 * kThreads], dD_acc);
+        relay_put(&relay[17 * kThreads], dA_acc);
+        relay_publish_puts(p.relay_flag + job, piece + 1);
+        return;
+    }
     // dD, dA and dh_0 of this (sequence, head)
     {
         const float v = wave_sum(dD_acc);
@@ -647,8 +704,21 @@ __global__ __launch_bounds__(256) void ssd_bwd_reduce_bc(const float* __restrict
 }
 
 template <int P, int N>
-void launch_ssd_bwd_pn(const SsdBwdKP& kp, int S, bool softplus, hipStream_t st) {
-    const dim3 grid((unsigned)((int64_t)kp.H * S));
+void launch_ssd_bwd_pn(SsdBwdKP kp, int S, bool softplus, hipStream_t st) {
+    const int64_t jobs = (int64_t)kp.H * S;
+    if (kp.relay_buf) {  // the round split, when it shortens the grid
+        const int n_cu = device_cus();
+        const int cap = n_cu > 0 ? resident_blocks(softplus ? (const void*)ssd_bwd<P, N, true>
+                                                            : (const void*)ssd_bwd<P, N, false>, kThreads)
+                                 : 0;
+        const RoundSplit rs = cap > 0 ? round_split(jobs, kp.n_chunks, (int64_t)n_cu * cap, kMinPieceChunks)
+                                      : RoundSplit{};
+        if (rs.k > 1) {
+            kp.relay_k = rs.k;
+            kp.relay_len = rs.len;
+        }
+    }
+    const dim3 grid((unsigned)(jobs * (kp.relay_k ? kp.relay_k : 1)));
     if (softplus) hipLaunchKernelGGL((ssd_bwd<P, N, true>), grid, dim3(kThreads), 0, st, kp);
     else hipLaunchKernelGGL((ssd_bwd<P, N, false>), grid, dim3(kThreads), 0, st, kp);
 }
@@ -666,7 +736,8 @@ size_t ssd_bwd_workspace_bytes(const Shape& sh) {
     const int64_t n_chunks = (sh.L + kQ - 1) / kQ;
     return align_up((size_t)(sh.S * sh.H * n_chunks * sh.P * sh.N) * 4, 256) +
            align_up((size_t)(sh.S * sh.H * sh.P * sh.N) * 4, 256) + 2 * align_up((size_t)(sh.S * sh.H) * 4, 256) +
-           align_up((size_t)(sh.S * sh.H * n_chunks * kQ * 2 * sh.N) * 4, 256);
+           align_up((size_t)(sh.S * sh.H * n_chunks * kQ * 2 * sh.N) * 4, 256) +
+           ssd_relay_bytes(sh.S * sh.H, n_chunks);
 }
 
 int launch_ssd_ckpt(const BwdArgs& a, float* ckpt, hipStream_t stream);
@@ -688,6 +759,12 @@ int launch_ssd_bwd(const BwdArgs& a, hipStream_t stream) {
     float* dD_part = reinterpret_cast<float*>(w);
     w += align_up((size_t)(sh.S * sh.H) * 4, 256);
     float* bc_part = reinterpret_cast<float*>(w);
+    w += align_up((size_t)(sh.S * sh.H * n_chunks * kQ * 2 * sh.N) * 4, 256);
+    const size_t relay_bytes = ssd_relay_bytes(sh.S * sh.H, n_chunks);
+    float* relay_buf = relay_bytes ? reinterpret_cast<float*>(w) : nullptr;
+    int* relay_flag = relay_bytes ? reinterpret_cast<int*>(
+                                        w + align_up((size_t)(sh.S * sh.H) * kRelayVals * kThreads * 4, 256))
+                                  : nullptr;
     if (ssd_bwd_workspace_bytes(sh) > a.ws_bytes) return SSM_ERR_WORKSPACE;
     int rc = launch_ssd_ckpt(a, ckpt, stream);
     if (rc) return rc;
@@ -700,6 +777,8 @@ int launch_ssd_bwd(const BwdArgs& a, hipStream_t stream) {
     kp.L = (int)sh.L; kp.H = (int)sh.H; kp.G = (int)sh.G; kp.R = (int)sh.R;
     kp.hpg = (int)(sh.H / sh.G); kp.n_chunks = (int)n_chunks;
     kp.has_D = a.D ? 1 : 0;
+    kp.relay_k = 0; kp.relay_len = 0;
+    kp.relay_flag = relay_flag; kp.relay_buf = relay_buf; kp.err = a.err;
     const bool sp = (sh.flags & SSM_DT_SOFTPLUS) != 0;
     const int S = (int)sh.S;
     if (sh.P == 64 && sh.N == 128) launch_ssd_bwd_pn<64, 128>(kp, S, sp, stream);

@@ -204,3 +204,36 @@ def test_ssd_bwd_full_size_sums_over_sequences(c8_result):
             part[seq] = {k: o[k] for k in ("d_A", "d_D", "d_s")}
     for k in ("d_A", "d_D", "d_s"):
         _check(f"C8 {k}", host(g[k]), sum(part[seq][k] for seq in range(p.n_seqs)))
+
+
+def _no_relay(fn):
+    """fn() with the relay and round splits turned off (SSM_RELAY=0, read at every launch)."""
+    import os
+    old = os.environ.get("SSM_RELAY")
+    os.environ["SSM_RELAY"] = "0"
+    try:
+        return fn()
+    finally:
+        if old is None:
+            del os.environ["SSM_RELAY"]
+        else:
+            os.environ["SSM_RELAY"] = old
+
+
+@pytest.mark.parametrize("n_tokens,softplus", [(1000, False), (1536, True)])
+def test_ssd_bwd_round_split_bitwise(n_tokens, softplus):
+    """A quarter more (sequence, head) jobs than compute units: the backward
+    runs as pieces of whole chunks in rounds (two pieces at 16 chunks, three
+    at 24), each handing on the carried gradient and the running sums, so
+    every gradient is bitwise that of the unsplit grid (SSM_RELAY=0)."""
+    n = torch.cuda.get_device_properties(0).multi_processor_count
+    jobs = n + n // 4
+    S = 4 if jobs % 4 == 0 else 1
+    p = _problem(161 + softplus, n_seqs=S, n_tokens=n_tokens, n_head=jobs // S, n_state_rows=S + 1,
+                 dt_softplus=softplus)
+    ssm_inputs.add_dout(p, 163, dstate_std=0.5)
+    t = device_inputs(p)
+    a = {k: v.clone() for k, v in _run(p, t).items()}
+    b = _no_relay(lambda: _run(p, t))
+    for k in a:
+        assert torch.equal(a[k], b[k]), f"{k} differs with the round split"
