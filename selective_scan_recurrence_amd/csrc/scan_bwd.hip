@@ -955,7 +955,12 @@ int launch_scan_bwd(const BwdArgs& a, hipStream_t stream) {
     if (w.total > a.ws_bytes) return SSM_ERR_WORKSPACE;
     kp.ckpt = w.ckpt; kp.dbc_part = w.dbc; kp.dA_part = w.dA; kp.dD_part = w.dD; kp.ds_part = w.ds;
     kp.partW = w.partW; kp.partCS = w.partCS;
-    int rc = launch_quad_ckpt(a, w.ckpt, stream);
+    // the checkpoint pass may split its uneven grid too, in the relay room of
+    // bwd_fast (used one after the other; every finished pass leaves the flags at zero)
+    const size_t room = relay_room(sh);
+    int rc = launch_quad_ckpt(a, w.ckpt, reinterpret_cast<float*>(w.relay),
+                              reinterpret_cast<int*>(w.relay + align_up(room * kRelayVals * kThreads * 4, 256)),
+                              (int)room, stream);
     if (rc) return rc;
     const dim3 grid((unsigned)kp.n_cb, (unsigned)sh.S);
     const bool bf = sh.io == SSM_BF16;

@@ -79,6 +79,7 @@ struct QuadKP {
     int relay_full, relay_rem, relay_k;
     int* relay_flag;     // [relay_rem]  pieces of the job allowed to start
     float* relay_h;      // [relay_rem][64][16] state handed to the next piece
+    int relay_max_jobs;  // cut jobs relay_h and relay_flag have room for (quad_ckpt)
 };
 
 template <typename T>
@@ -663,27 +664,52 @@ template <typename T, int K, bool TILED, bool SOFTPLUS>
 __global__ __launch_bounds__(kThreads) void quad_ckpt(QuadKP p) {
     static_assert(TILED || K == 0, "the fused conv runs on the tiled variant");
     const int q = threadIdx.x & 3;
-    const int c_raw = blockIdx.x * kChanPerBlock + (threadIdx.x >> 2);
+    int cbk = blockIdx.x, i = blockIdx.y;
+    int piece = -1, sj = 0;  // relay: piece of cut job sj, or -1 for a whole job
+    if (TILED && p.relay_k) {  // 1-D grid, as quad_out's
+        const int cblocks = p.d_inner / kChanPerBlock;
+        const RelayBlock rb = relay_block(blockIdx.x, p.relay_full, p.relay_rem);
+        piece = rb.piece;
+        sj = rb.cut;
+        cbk = rb.job % cblocks;
+        i = rb.job / cblocks;
+    }
+    if (piece >= 0) __builtin_amdgcn_s_setprio(2);  // a piece chain goes first (relay.h)
+    const int c_raw = cbk * kChanPerBlock + (threadIdx.x >> 2);
     const bool active = c_raw < p.d_inner;
     const int c = active ? c_raw : p.d_inner - 1;
-    const int i = blockIdx.y;
     const int r = p.ids[i];
     const bool bad = (r < 0) | (r >= p.R);
-    if (bad && threadIdx.x == 0 && blockIdx.x == 0) atomicOr(p.err, (uint32_t)SSM_DEVERR_IDS);
+    if (bad && threadIdx.x == 0 && cbk == 0 && piece <= 0) atomicOr(p.err, (uint32_t)SSM_DEVERR_IDS);
     float h[4], a2[4];
+    float* relay_h = piece >= 0 ? p.relay_h + ((int64_t)sj * kChanPerBlock + (threadIdx.x >> 2)) * 16 + 4 * q
+                                : nullptr;
+    if (piece > 0) {  // the previous piece's end state
+        relay_wait(p.relay_flag + sj, piece, p.err);
+        if (piece + 1 == p.relay_k) relay_reset(p.relay_flag + sj);
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         const int n = 4 * q + s;
         a2[s] = n < p.N ? p.A[(int64_t)c * p.N + n] * kLog2e : 0.0f;
-        h[s] = n < p.N ? (bad ? __builtin_nanf("") : p.s[((int64_t)r * p.d_inner + c) * p.N + n])
-                       : 0.0f;
+        if (piece > 0)
+            h[s] = relay_h[s];
+        else
+            h[s] = n < p.N ? (bad ? __builtin_nanf("") : p.s[((int64_t)r * p.d_inner + c) * p.N + n]) : 0.0f;
     }
     float dt_acc = 0.0f;
+    const int t_begin = piece > 0 ? piece * p.chunk_len : 0;
+    const int t_end = piece >= 0 ? min(p.L, t_begin + p.chunk_len) : p.L;
     if constexpr (TILED)
-        quad_tiled<T, K, 2, SOFTPLUS>(p, i, (int64_t)i * p.L, blockIdx.x, q, threadIdx.x >> 2, 0, p.L, h, a2, dt_acc,
-                                      bad);
+        quad_tiled<T, K, 2, SOFTPLUS>(p, i, (int64_t)i * p.L, cbk, q, threadIdx.x >> 2, t_begin, t_end, h, a2,
+                                      dt_acc, bad);
     else
         quad_chunk<T, 0, 2>(p, i, (int64_t)i * p.L, c_raw, q, 0, p.L, h, a2, dt_acc, active, bad);
+    if (piece >= 0 && piece + 1 < p.relay_k) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) relay_put(&relay_h[s], h[s]);  // hand the state on
+        relay_publish_puts(p.relay_flag + sj, piece + 1);
+    }
 }
 
 constexpr int kRelayMaxJobs = 1024;  // cut jobs the workspace has room for
@@ -780,7 +806,25 @@ size_t quad_workspace_bytes(const Shape& sh) {
 
 namespace {
 template <int K>
-void launch_ckpt_k(const QuadKP& kp, dim3 grid, bool bf, hipStream_t stream) {
+void launch_ckpt_k(QuadKP kp, dim3 grid, bool bf, hipStream_t stream) {
+    if (kp.relay_h) {  // the relay split of an uneven grid (as the forward's)
+        const int n_cu = device_cus();
+        const void* fn = bf ? (kp.softplus ? (const void*)quad_ckpt<bf16_t, K, true, true>
+                                           : (const void*)quad_ckpt<bf16_t, K, true, false>)
+                            : (kp.softplus ? (const void*)quad_ckpt<float, K, true, true>
+                                           : (const void*)quad_ckpt<float, K, true, false>);
+        const int cap = n_cu > 0 ? resident_blocks(fn, kThreads) : 0;
+        const int cblocks = kp.d_inner / kChanPerBlock;
+        const RelaySplit rs = relay_split((int64_t)kp.S * cblocks, kp.L, bf ? TileCfg<bf16_t>::TT : TileCfg<float>::TT,
+                                          cap, n_cu, kp.relay_max_jobs);
+        if (rs.k) {
+            kp.relay_full = rs.full;
+            kp.relay_rem = rs.rem;
+            kp.relay_k = rs.k;
+            kp.chunk_len = rs.len;
+            grid = dim3((unsigned)(rs.full + rs.rem * rs.k));
+        }
+    }
     if (bf) {
         if (kp.softplus) hipLaunchKernelGGL((quad_ckpt<bf16_t, K, true, true>), grid, dim3(kThreads), 0, stream, kp);
         else hipLaunchKernelGGL((quad_ckpt<bf16_t, K, true, false>), grid, dim3(kThreads), 0, stream, kp);
@@ -791,7 +835,8 @@ void launch_ckpt_k(const QuadKP& kp, dim3 grid, bool bf, hipStream_t stream) {
 }
 }  // namespace
 
-int launch_quad_ckpt(const BwdArgs& a, float* ckpt, hipStream_t stream) {
+int launch_quad_ckpt(const BwdArgs& a, float* ckpt, float* relay_h, int* relay_flag, int relay_max_jobs,
+                     hipStream_t stream) {
     const Shape& sh = a.sh;
     QuadKP kp = {};
     kp.T = sh.S * sh.L;
@@ -808,6 +853,11 @@ int launch_quad_ckpt(const BwdArgs& a, float* ckpt, hipStream_t stream) {
                 al16(a.C) && sh.d_inner() * 4 * 64 < (int64_t(1) << 31)) ? 1 : 0;
     kp.chunk_len = (int)sh.L;
     kp.n_chunks = 1;
+    if (kp.tiled) {  // (the tiled path covers whole 64-channel blocks)
+        kp.relay_h = relay_h;
+        kp.relay_flag = relay_flag;
+        kp.relay_max_jobs = relay_max_jobs;
+    }
     const dim3 grid((unsigned)((kp.d_inner + kChanPerBlock - 1) / kChanPerBlock), (unsigned)sh.S);
     const bool bf = sh.io == SSM_BF16;
     if (sh.K > 0 && !kp.tiled) return SSM_ERR_UNSUPPORTED;  // the fused conv runs tiled only

@@ -111,7 +111,10 @@ bool quad_chunked(const Shape& sh);
 // pieces per split job (0: no relay)
 int launch_quad_fwd(const FwdArgs& a, hipStream_t stream, int* relay_k_out = nullptr);
 // The backward's checkpoint pass: the state entering every kCkpt-token block into ckpt.
-int launch_quad_ckpt(const BwdArgs& a, float* ckpt, hipStream_t stream);
+// relay_h, relay_flag: room for relay_max_jobs cut jobs of the relay split
+// (64 x 16 floats and a flag each, flags zero), or null: no split
+int launch_quad_ckpt(const BwdArgs& a, float* ckpt, float* relay_h, int* relay_flag, int relay_max_jobs,
+                     hipStream_t stream);
 
 // Mamba-1 forward, d_state 16, time split across the waves of a workgroup
 // (for batches with too few channels to fill the GPU otherwise).
