@@ -172,7 +172,7 @@ KERNEL_SOURCES = {
     "C5": ("conv_bwd.hip", "device_common.h"),
     "C6": ("decode.hip", "device_common.h"),
     "C7": ("decode.hip", "device_common.h"),
-    "C8": ("ssd_bwd.hip", "ssd_fwd.hip", "device_common.h"),
+    "C8": ("ssd_bwd.hip", "ssd_fwd.hip", "relay.h", "relay.hip", "device_common.h"),
     "C10": ("scan_bwd.hip", "scan_fwd_quad.hip", "relay.h", "relay.hip", "device_common.h"),
     "C11": ("conv_fwd.hip", "device_common.h"),
 }
