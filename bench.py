@@ -150,16 +150,16 @@ def valu_slots_per_channel_token(p, backward=False) -> float:
 # kernel sources it was taken on; bench.py reports null once any of them changes.
 COPY_FACTOR = {"fetch": 1.99993, "write": 1.00000}
 MEASURED_TRAFFIC = {
-    "C1": {"sha256": "9d2db653a26b0768b2ceaffb548b58081af25ab8f226ee762d9482f7960b0d17", "fetch_kib": 34138.7, "write_kib": 33024.0},
-    "C2": {"sha256": "9d2db653a26b0768b2ceaffb548b58081af25ab8f226ee762d9482f7960b0d17", "fetch_kib": 341018.7, "write_kib": 330760.0},
-    "C3": {"sha256": "0ad651441327e545fa6ee95cc1b113eebb0136bb38d223ed2320249da77d4ace", "fetch_kib": 143724.4, "write_kib": 174080.8},
-    "C4": {"sha256": "e214c43e708980aac63c214b03170a7782de6f7bba09705b17a5a1e2ed4ffd0c", "fetch_kib": 1667653.6, "write_kib": 2962556.0},
+    "C1": {"sha256": "8fc59cc6ea1fe24b7c2894e87efbaa19f4aa61b9a832f3941e23b6efdb5f974d", "fetch_kib": 34138.7, "write_kib": 33024.0},
+    "C2": {"sha256": "8fc59cc6ea1fe24b7c2894e87efbaa19f4aa61b9a832f3941e23b6efdb5f974d", "fetch_kib": 340951.3, "write_kib": 332296.0},
+    "C3": {"sha256": "c5a6930703d860d5e794dcf75dd2091f82a62579ac176b8384e7843b8f9cfec7", "fetch_kib": 143290.2, "write_kib": 174080.3},
+    "C4": {"sha256": "64855c8681f9d3a8ad203ca4ec08e6ff3c697935fbca2d56997a2e82dab5b988", "fetch_kib": 1670241.1, "write_kib": 2964612.0},
     "C5": {"sha256": "19d21d3c16653649e1d9cac38de168171b782e33178b052b1b50c035b9a95dd5", "fetch_kib": 512932.3, "write_kib": 704850.3},
-    "C6": {"sha256": "fefd2284eb86a0bce2f08280980fbc69fc554eef99b5ec7621fddf1b67c6921a", "fetch_kib": 52842.3, "write_kib": 100238.6},
-    "C7": {"sha256": "fefd2284eb86a0bce2f08280980fbc69fc554eef99b5ec7621fddf1b67c6921a", "fetch_kib": 83410.2, "write_kib": 164481.8},
-    "C8": {"sha256": "b3d971e6a50acc9e0618b7656018fd56c079f1e9bd9142c4c5157ccd23b634ba", "fetch_kib": 1343096.0, "write_kib": 2382312.2},
-    "C9": {"sha256": "cc57330726b135617c0fdccf0e793ca91d1f5f0ba4a4d47741bf7473a52e0ec9", "fetch_kib": 505010.0, "write_kib": 330720.0},
-    "C10": {"sha256": "e214c43e708980aac63c214b03170a7782de6f7bba09705b17a5a1e2ed4ffd0c", "fetch_kib": 1667819.9, "write_kib": 2964492.0},
+    "C6": {"sha256": "365057569e18c41ae6495048cfbeb33cacead190cc03a245029d5ac614a042b7", "fetch_kib": 52810.7, "write_kib": 99843.7},
+    "C7": {"sha256": "365057569e18c41ae6495048cfbeb33cacead190cc03a245029d5ac614a042b7", "fetch_kib": 83410.5, "write_kib": 164502.2},
+    "C8": {"sha256": "23fdfc87152031e7435461f3ca679aa366617a664806d5a3791ed0dad34b2449", "fetch_kib": 1372017.4, "write_kib": 2415523.0},
+    "C9": {"sha256": "aade4013e5e398593b4b3fe9d644aa41cb991d3c70e5a58985a4672e12d49d08", "fetch_kib": 504970.0, "write_kib": 330720.0},
+    "C10": {"sha256": "64855c8681f9d3a8ad203ca4ec08e6ff3c697935fbca2d56997a2e82dab5b988", "fetch_kib": 1670400.7, "write_kib": 2966548.0},
     "C11": {"sha256": "276c97c0ab38954d90eea36e94e56223be1d1cf15921334358e607baa728a14b", "fetch_kib": 164316.9, "write_kib": 327680.0},
 }
 KERNEL_SOURCES = {
