@@ -202,8 +202,7 @@ FwdPath fwd_path(const FwdArgs& a) {
     const Shape& sh = a.sh;
     if (sh.S == 0 || sh.H * sh.P == 0) return FwdPath::kNone;
     // few (sequence, channel) rows and no explicit chunk: split time inside a workgroup
-    if (!a.has_ext() && sh.chunk == 0 && sh.S * ((sh.d_inner() + 63) / 64) * 4 < 2048 &&
-        ts_supported(sh, a))
+    if (sh.chunk == 0 && sh.S * ((sh.d_inner() + 63) / 64) * 4 < 2048 && ts_supported(sh, a))
         return FwdPath::kTimeSplit;
     if (quad_supported(sh)) return FwdPath::kQuad;
     if (ssd_supported(sh, a)) return FwdPath::kSsd;

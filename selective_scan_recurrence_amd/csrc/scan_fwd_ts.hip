@@ -32,6 +32,12 @@
 // Two barriers per tile.  Token rows of 16 channels are 64 B (fp32) or 32 B
 // (bf16); the workgroup order is remapped so that neighbouring channel blocks
 // of one sequence are dispatched to the same XCD and share its L2 lines.
+//
+// The extras of selective_scan_fwd_ext ride along: the dt bias is added where
+// the owner lane reads dt (before the softplus), the owner lane's z values are
+// loaded at the start of each tile and scale y by SiLU(z) before its one
+// rounding, and with packed sequences each workgroup takes its own span of
+// the token axis (its tile count follows the span's length).
 #include "device_common.h"
 #include "ssm_internal.h"
 
@@ -61,6 +67,11 @@ struct TsKP {
     float* state_out;
     float* conv_state_out;
     uint32_t* err;
+    // extras of selective_scan_fwd_ext (null: none)
+    const float* dt_bias;  // [d_inner], added to dt before the softplus
+    const void* z;         // gate, laid out as x: y is multiplied by SiLU(z)
+    const int32_t* cu;     // [S+1] spans on the packed token axis
+    int64_t T;             // tokens on the packed axis
     int L, d_inner, R, S, ncb;
     int has_D;
     int xcd_swizzle;  // 1: workgroup count is a multiple of 8
@@ -85,7 +96,7 @@ __device__ __forceinline__ void unpack_store<bf16_t>(float* dst, const uint4& v)
     *reinterpret_cast<float4*>(dst + 4) = make_float4(f[4], f[5], f[6], f[7]);
 }
 
-template <typename T, int K, bool SOFTPLUS, int J, int M>
+template <typename T, int K, bool SOFTPLUS, bool GATE, int J, int M>
 __global__ __launch_bounds__(64 * J) void ts_fwd(TsKP p) {
     constexpr int NT = 64 * J;
     constexpr int TT = M * J;               // tokens per tile
@@ -113,13 +124,19 @@ __global__ __launch_bounds__(64 * J) void ts_fwd(TsKP p) {
     }
     const int i = b / p.ncb, c0 = (b % p.ncb) * kCh;
     const int c = c0 + cl;
-    const int L = p.L, d_inner = p.d_inner;
+    const int d_inner = p.d_inner;
+    // this sequence's tokens: [t0, t0 + L) of the token axis (an invalid span
+    // scans nothing and ends in a NaN state)
+    const SeqSpan span = seq_span(p.cu, i, p.L, p.T);
+    const int L = span.len;
 
     int r = p.ids[i];
-    const bool bad = (r < 0) | (r >= p.R);
+    const bool bad_id = (r < 0) | (r >= p.R);
+    const bool bad = bad_id | span.bad;
     if (bad) {
         r = 0;
-        if (tid == 0) atomicOr(p.err, (uint32_t)SSM_DEVERR_IDS);
+        if (tid == 0)
+            atomicOr(p.err, (bad_id ? (uint32_t)SSM_DEVERR_IDS : 0u) | (span.bad ? (uint32_t)SSM_DEVERR_SEQLENS : 0u));
     }
 
     float a2[4];
@@ -133,6 +150,7 @@ __global__ __launch_bounds__(64 * J) void ts_fwd(TsKP p) {
         *reinterpret_cast<float4*>(&hT_l[0][cl * 16 + 4 * q]) = hv;
     }
     const float Dc = p.has_D ? p.D[c] : 0.0f;
+    const float dtb = p.dt_bias ? p.dt_bias[c] : 0.0f;
     float w[4] = {0.f, 0.f, 0.f, 0.f};
     if constexpr (K > 0) {
 #pragma unroll
@@ -157,11 +175,13 @@ __global__ __launch_bounds__(64 * J) void ts_fwd(TsKP p) {
     // the per-lane offsets stay the same on every tile (no address register
     // is rewritten while a store from it may be in flight), rows past the
     // end read as zero and stores past it are dropped by the hardware.
-    const char* xg = static_cast<const char*>(p.x) + ((int64_t)i * L * d_inner + c0) * ES;
-    const char* dg = static_cast<const char*>(p.dt) + ((int64_t)i * L * d_inner + c0) * ES;
-    const char* bg = static_cast<const char*>(p.B) + (int64_t)i * L * 16 * ES;
-    const char* cg = static_cast<const char*>(p.C) + (int64_t)i * L * 16 * ES;
-    char* yg = static_cast<char*>(p.y) + ((int64_t)i * L * d_inner + c0) * ES;
+    const int64_t tok0 = span.t0;
+    const char* xg = static_cast<const char*>(p.x) + (tok0 * d_inner + c0) * ES;
+    const char* dg = static_cast<const char*>(p.dt) + (tok0 * d_inner + c0) * ES;
+    const char* bg = static_cast<const char*>(p.B) + tok0 * 16 * ES;
+    const char* cg = static_cast<const char*>(p.C) + tok0 * 16 * ES;
+    char* yg = static_cast<char*>(p.y) + (tok0 * d_inner + c0) * ES;
+    const char* zg = static_cast<const char*>(p.z) + (tok0 * d_inner + c0) * ES;  // GATE only
     const int xrow = d_inner * ES;  // bytes between token rows of x, dt, y (bounded on the host)
     // a descriptor spans at most the TT rows of one tile (the loads and y
     // stores through it never reach further), so its size stays below 2^31
@@ -234,6 +254,18 @@ __global__ __launch_bounds__(64 * J) void ts_fwd(TsKP p) {
         const float* dts = dt_l[buf];
         const float* Bs_l = B_l[buf];
         const float* Cs_l = C_l[buf];
+        // the gate's z at this lane's y positions, needed only at the y stores
+        uint32_t zv[GATE ? M / 4 : 1];
+        if constexpr (GATE) {
+            const auto rz = rsrc(zg, tb, xrow);
+#pragma unroll
+            for (int g = 0; g < M / 4; ++g) {
+                if constexpr (ES == 2)
+                    zv[g] = __builtin_amdgcn_raw_buffer_load_b16(rz, y_off(g), 0, 0);
+                else
+                    zv[g] = __builtin_amdgcn_raw_buffer_load_b32(rz, y_off(g), 0, 0);
+            }
+        }
 
         // sweep 1: lane q owns token 4g+q of each group: conv + SiLU, dt; the
         // quad's four lanes then form decays and input terms of all four tokens
@@ -253,7 +285,7 @@ __global__ __launch_bounds__(64 * J) void ts_fwd(TsKP p) {
             } else {
                 u = xs[(kHalo + row) * kCh + cl];
             }
-            float d = dts[row * kCh + cl];
+            float d = dts[row * kCh + cl] + dtb;
             if constexpr (SOFTPLUS) d = softplus(d);
             if (tb + row >= L) { d = 0.0f; u = 0.0f; }
             u_own[g] = u;
@@ -339,7 +371,12 @@ __global__ __launch_bounds__(64 * J) void ts_fwd(TsKP p) {
             for (int g = 0; g < M / 4; ++g) {
                 // the previous tile's store data stay reserved up to here; the
                 // new data go to the same registers
-                uint32_t v = ES == 2 ? (uint32_t)bf16_rne(y_own[g]) : __float_as_uint(y_own[g]);
+                float yv = y_own[g];
+                if constexpr (GATE) {  // y * SiLU(z), rounded once
+                    const float zf = ES == 2 ? __uint_as_float(zv[g] << 16) : __uint_as_float(zv[g]);
+                    yv *= silu(zf);
+                }
+                uint32_t v = ES == 2 ? (uint32_t)bf16_rne(yv) : __float_as_uint(yv);
                 asm volatile("v_mov_b32 %0, %1" : "+v"(ykeep[g]) : "v"(v));
                 if constexpr (ES == 2)
                     __builtin_amdgcn_raw_buffer_store_b16((unsigned short)ykeep[g], ry, y_off(g), 0, 0);
@@ -374,8 +411,13 @@ __global__ __launch_bounds__(64 * J) void ts_fwd(TsKP p) {
 template <typename T, int K>
 int launch_ts_k(const TsKP& kp, bool softplus, hipStream_t st) {
     const dim3 grid((unsigned)(kp.S * kp.ncb)), block(64 * kJ);
-    if (softplus) hipLaunchKernelGGL((ts_fwd<T, K, true, kJ, kSub>), grid, block, 0, st, kp);
-    else hipLaunchKernelGGL((ts_fwd<T, K, false, kJ, kSub>), grid, block, 0, st, kp);
+    if (kp.z) {
+        if (softplus) hipLaunchKernelGGL((ts_fwd<T, K, true, true, kJ, kSub>), grid, block, 0, st, kp);
+        else hipLaunchKernelGGL((ts_fwd<T, K, false, true, kJ, kSub>), grid, block, 0, st, kp);
+    } else {
+        if (softplus) hipLaunchKernelGGL((ts_fwd<T, K, true, false, kJ, kSub>), grid, block, 0, st, kp);
+        else hipLaunchKernelGGL((ts_fwd<T, K, false, false, kJ, kSub>), grid, block, 0, st, kp);
+    }
     return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
@@ -386,7 +428,7 @@ bool ts_supported(const Shape& sh, const FwdArgs& a) {
     return sh.a_per_state && sh.P == 1 && sh.N == 16 && sh.G == 1 &&
            (sh.K == 0 || sh.K == 2 || sh.K == 3 || sh.K == 4) && sh.d_inner() % kCh == 0 &&
            al16(a.x) && al16(a.dt) && al16(a.B) && al16(a.C) && al16(a.y) && al16(a.A) &&
-           al16(a.s) && al16(a.state_out) && sh.S * (sh.d_inner() / kCh) < (int64_t(1) << 31) &&
+           al16(a.s) && al16(a.state_out) && al16(a.z) && sh.S * (sh.d_inner() / kCh) < (int64_t(1) << 31) &&
            // one tile's rows of x/dt/y (kJ * kSub tokens plus the descriptor's
            // reach) must fit the 31-bit byte sizes and offsets of a descriptor
            sh.d_inner() * sh.io_bytes() * (kJ * kSub + kHalo + 1) < (int64_t(1) << 31);
@@ -398,6 +440,7 @@ int launch_ts_fwd(const FwdArgs& a, hipStream_t stream) {
     kp.s = a.s; kp.x = a.x; kp.dt = a.dt; kp.A = a.A; kp.B = a.B; kp.C = a.C; kp.D = a.D;
     kp.ids = a.ids; kp.conv_w = a.conv_w; kp.conv_state = a.conv_state; kp.y = a.y;
     kp.state_out = a.state_out; kp.conv_state_out = a.conv_state_out; kp.err = a.err;
+    kp.dt_bias = a.dt_bias; kp.z = a.z; kp.cu = a.cu; kp.T = a.T;
     kp.L = (int)sh.L; kp.d_inner = (int)sh.d_inner(); kp.R = (int)sh.R; kp.S = (int)sh.S;
     kp.ncb = (int)(sh.d_inner() / kCh);
     kp.has_D = (sh.flags & SSM_HAS_D) ? 1 : 0;

@@ -372,9 +372,13 @@ def test_forward_plan(kw, want):
 
 def test_forward_plan_with_extras_and_invalid():
     d = ops.make_desc(n_seqs=8, n_tokens=2048, n_head=512, d_state=16, d_conv=4)
-    # extras never take the time-split kernel: with this few rows the quad
-    # kernels split time into chunks instead
-    assert ssm.ssm_scan_fwd_plan(d, ssm.make_ext(cu_seqlens=1, total_tokens=100)) == "quad_chunked"
+    # the extras ride along on the time-split kernel; an explicit chunk asks
+    # for the chunked quad kernels, with or without them
+    ext = ssm.make_ext(dt_bias=1, z=1, cu_seqlens=1, total_tokens=100)
+    assert ssm.ssm_scan_fwd_plan(d, ext) == "time_split"
+    assert ssm.ssm_scan_fwd_plan(d, ssm.make_ext(cu_seqlens=1, total_tokens=100)) == "time_split"
+    d.chunk = 256
+    assert ssm.ssm_scan_fwd_plan(d, ext) == "quad_chunked"
     bad = ops.make_desc(n_seqs=2, n_tokens=8, n_head=3, head_dim=2, d_state=4)
     bad.d_state = 0
     assert ssm.ssm_scan_fwd_plan(bad) is None

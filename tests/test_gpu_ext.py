@@ -1,7 +1,9 @@
 """GPU parity of selective_scan_fwd_ext (the dt bias, the SiLU(z) gate and
 packed variable-length sequences) against ``oracle.scan_fwd_ext``, through
-the C ABI, on every kernel path: the Mamba-1 quad kernels (tiled, untiled,
-chunked), the Mamba-2 chunked MFMA kernel and the generic row kernel."""
+the C ABI, on every kernel path: the Mamba-1 time-split kernel (few rows),
+the quad kernels (tiled, untiled, chunked), the Mamba-2 chunked MFMA kernel
+and the generic row kernel.  Each case first checks which path its shape
+takes."""
 import numpy as np
 import pytest
 import torch
@@ -23,9 +25,15 @@ def _case(name):
     m1 = dict(d_conv=4, conv_state_std=0.5)
     m2 = dict(a_per_state=False, d_conv=0, A_kind="uniform", A_range=(1.0, 16.0))
     cases = {
-        # Mamba-1, d_inner a multiple of 64 and d_state 16: the tiled quad kernel
-        "quad_tiled_bf16": dict(n_head=128, d_state=16, io="bf16", **m1),
-        "quad_tiled_f32": dict(n_head=128, d_state=16, io="f32", **m1),
+        # Mamba-1, d_state 16, few (sequence, channel) rows: the time-split kernel
+        "ts_bf16": dict(n_head=128, d_state=16, io="bf16", **m1),
+        "ts_f32": dict(n_head=128, d_state=16, io="f32", **m1),
+        "ts_bf16_k2": dict(n_head=64, d_state=16, io="bf16", d_conv=2, conv_state_std=0.5),
+        "ts_f32_noconv": dict(n_head=48, d_state=16, io="f32", d_conv=0),
+        # Mamba-1, d_inner a multiple of 64 and d_state 16, 8 sequences x 64
+        # channel blocks: the tiled quad kernel
+        "quad_tiled_bf16": dict(n_head=4096, d_state=16, io="bf16", **m1),
+        "quad_tiled_f32": dict(n_head=4096, d_state=16, io="f32", **m1),
         "quad_tiled_bf16_chunks": dict(n_head=128, d_state=16, io="bf16", chunk=64, **m1),
         # Mamba-1, d_inner 100 and d_state 10: the untiled quad kernel, chunked
         "quad_untiled_bf16": dict(n_head=100, d_state=10, io="bf16", chunk=48, **m1),
@@ -41,6 +49,20 @@ def _case(name):
         "rows_m1_g2": dict(n_head=40, d_state=12, n_group=2, io="bf16", d_conv=3, conv_state_std=0.5),
     }
     return cases[name]
+
+
+# the forward plan each case's shape takes (with the 8-sequence mix)
+PLAN = {"ts_bf16": {"time_split"}, "ts_f32": {"time_split"}, "ts_bf16_k2": {"time_split"},
+        "ts_f32_noconv": {"time_split"}, "quad_tiled_bf16": {"quad", "quad_relay"},
+        "quad_tiled_f32": {"quad", "quad_relay"}, "quad_tiled_bf16_chunks": {"quad_chunked"},
+        "quad_untiled_bf16": {"quad_chunked"}, "ssd_bf16": {"ssd"}, "ssd_bf16_p32_n64": {"ssd"},
+        "rows_m2_f32": {"rows"}, "rows_m1_n32": {"rows"}, "rows_m1_g2": {"rows"}}
+
+
+def _plan(p, varlen=True):
+    ext = ssm.make_ext(dt_bias=int(p.value("dt_bias") is not None), z=int(p.value("z") is not None),
+                       cu_seqlens=int(varlen), total_tokens=p.total_tokens if varlen else 0)
+    return ssm.ssm_scan_fwd_plan(desc_of(p), ext)
 
 
 def _problem(name, lengths=MIX, seed=0x91, with_z=True, bias=True, softplus=True, h0_std=0.3):
@@ -107,13 +129,15 @@ def _check(p, r, want, what, z=None):
         np.testing.assert_array_equal(host(r.conv_state), cso, err_msg=f"{what} conv_state")
 
 
-@pytest.mark.parametrize("name", ["quad_tiled_bf16", "quad_tiled_f32", "quad_tiled_bf16_chunks",
-                                  "quad_untiled_bf16", "ssd_bf16", "ssd_bf16_p32_n64",
-                                  "rows_m2_f32", "rows_m1_n32", "rows_m1_g2"])
+@pytest.mark.parametrize("name", ["ts_bf16", "ts_f32", "ts_bf16_k2", "ts_f32_noconv", "quad_tiled_bf16",
+                                  "quad_tiled_f32", "quad_tiled_bf16_chunks", "quad_untiled_bf16",
+                                  "ssd_bf16", "ssd_bf16_p32_n64", "rows_m2_f32", "rows_m1_n32",
+                                  "rows_m1_g2"])
 def test_varlen_gate_bias_parity(name):
     """A length mix with empty, 1- and 2-token, ragged and multi-tile
     sequences; z gate, dt bias and softplus on."""
     p = _problem(name)
+    assert _plan(p) in PLAN[name]
     r, ws = _run(p)
     _check(p, r, _oracle(p), name, z=_z(p))
     assert ssm.ssm_get_device_error(ws) == 0
@@ -129,22 +153,25 @@ def test_varlen_unit_scale_state(name):
     _check(p, r, _oracle(p), f"{name} h0 N(0,1)", z=_z(p))
 
 
-@pytest.mark.parametrize("name", ["quad_tiled_bf16", "ssd_bf16", "rows_m2_f32"])
+@pytest.mark.parametrize("name", ["ts_bf16", "quad_tiled_bf16", "ssd_bf16", "rows_m2_f32"])
 @pytest.mark.parametrize("with_z,bias", [(False, True), (True, False), (False, False)])
 def test_varlen_feature_subsets(name, with_z, bias):
     """Each extra on its own (and neither) on the fused kernels."""
     p = _problem(name, seed=0x92, with_z=with_z, bias=bias, softplus=bias)
+    assert _plan(p) in PLAN[name]
     r, _ = _run(p)
     _check(p, r, _oracle(p), f"{name} z={with_z} bias={bias}", z=_z(p))
 
 
-@pytest.mark.parametrize("name", ["quad_tiled_bf16", "ssd_bf16", "rows_m1_g2"])
-def test_equal_lengths_with_extras(name):
+@pytest.mark.parametrize("name,S", [("ts_bf16", 3), ("quad_tiled_bf16", 8), ("ssd_bf16", 3),
+                                    ("rows_m1_g2", 3)])
+def test_equal_lengths_with_extras(name, S):
     """Without spans (the [n_seqs][n_tokens] layout), gate and bias only."""
-    p = _problem(name, lengths=[96, 96, 96], seed=0x93)
+    L = 96
+    p = _problem(name, lengths=[L] * S, seed=0x93)
+    assert _plan(p, varlen=False) in PLAN[name]
     r, _ = _run(p, varlen=False)
     v = lambda n: None if p.value(n) is None else p.value(n).astype(np.float64)
-    S, L = 3, 96
     sh = lambda a: None if a is None else a[0].reshape((S, L) + a.shape[2:])
     want = oracle.scan_fwd_ext(v("s"), sh(v("x")), sh(v("dt")), v("A"), sh(v("B")), sh(v("C")), v("D"),
                                p.ids, dt_bias=v("dt_bias"), z=sh(v("z")),
@@ -168,17 +195,22 @@ def test_ext_without_extras_equals_plain_call():
     assert torch.equal(a.out, b.out) and torch.equal(a.conv_state, b.conv_state)
 
 
-@pytest.mark.parametrize("name", ["quad_tiled_bf16", "quad_untiled_bf16", "ssd_bf16", "rows_m2_f32"])
-def test_invalid_spans(name):
+@pytest.mark.parametrize("name,lengths", [
+    ("ts_bf16", [40, 80, 30, 50]), ("quad_tiled_bf16", [40, 80, 30, 50, 20, 10, 5, 7]),
+    ("quad_untiled_bf16", [40, 80, 30, 50]), ("ssd_bf16", [40, 80, 30, 50]),
+    ("rows_m2_f32", [40, 80, 30, 50])])
+def test_invalid_spans(name, lengths):
     """A span longer than desc.n_tokens and one reaching past total_tokens are
     not scanned: NaN final state, y rows untouched, SSM_DEVERR_SEQLENS; the
     valid sequences match the oracle."""
-    p = _problem(name, lengths=[40, 80, 30, 50], seed=0x95)
+    p = _problem(name, lengths=lengths, seed=0x95)
     p.n_tokens = 64                       # the bound: sequence 1 (80 tokens) is too long
-    cu = p.cu_seqlens.copy()              # [0, 40, 120, 150, 200]
+    assert _plan(p) in PLAN[name]
+    cu = p.cu_seqlens.copy()              # [0, 40, 120, 150, 200, ...]
     T = int(cu[-1])
+    S = len(lengths)
     cu_bad = cu.copy()
-    cu_bad[4] = T + 7                     # sequence 3 reaches past the packed axis
+    cu_bad[S] = T + 7                     # the last sequence reaches past the packed axis
     t = device_inputs(p)
     d = desc_of(p)
     total, off = ssm.ssm_scan_ext_out_bytes(d, ssm.make_ext(cu_seqlens=1, total_tokens=T))
@@ -191,14 +223,14 @@ def test_invalid_spans(name):
     torch.cuda.synchronize()
     assert ssm.ssm_get_device_error(ws) & ssm.SSM_DEVERR_SEQLENS
     st = host(r.state)
-    assert np.isnan(st[1]).all() and np.isnan(st[3]).all()
+    assert np.isnan(st[1]).all() and np.isnan(st[S - 1]).all()
     raw = out[:off].cpu().numpy()
     es = 2 if p.io == "bf16" else 4
     row = p.n_head * p.head_dim * es
-    for lo, hi in ((cu[1], cu[2]), (cu[3], T)):
+    for lo, hi in ((cu[1], cu[2]), (cu[S - 1], T)):
         assert (raw[lo * row:hi * row] == 0x7F).all(), "y rows of an invalid span were written"
     want = _oracle(p)
-    for i in (0, 2):
+    for i in [0] + list(range(2, S - 1)):
         a, b = cu[i], cu[i + 1]
         _check_y(p.io, host(r.y)[a:b], want[0][a:b], _z(p)[a:b], f"{name} seq {i}")
         assert_close(st[i], want[1][i], "f32" if p.io == "f32" else "bf16", f"{name} seq {i} state")
@@ -218,11 +250,12 @@ def test_varlen_full_size_sampled():
     assert ssm.ssm_get_device_error(ws) == 0
 
 
-@pytest.mark.parametrize("name", ["quad_tiled_bf16", "ssd_bf16", "rows_m2_f32"])
-def test_all_sequences_empty(name):
+@pytest.mark.parametrize("name,S", [("ts_bf16", 3), ("quad_tiled_bf16", 8), ("ssd_bf16", 3),
+                                    ("rows_m2_f32", 3)])
+def test_all_sequences_empty(name, S):
     """total_tokens = 0 (every span empty, x/dt/B/C/z/y absent): each final state is
     its gathered state row and each conv state its conv-state row; no error."""
-    p = _problem(name, lengths=[0, 0, 0], seed=0x96)
+    p = _problem(name, lengths=[0] * S, seed=0x96)
     t = device_inputs(p)
     d = desc_of(p)
     d.n_tokens = 8                        # a positive bound; every span is empty
