@@ -67,6 +67,15 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kQ = 64;  // tokens per chunk (as the forward's recompute)
+
+// Offset (floats) of tile (token block tb, state block nb, dB / dC) in one
+// head's partial sums of a chunk: each tile is 64 lanes x 16 bytes, lane
+// l16 + 16 g4 holding token 16 tb + l16, states 16 nb + 4 g4 .. + 3, so that
+// a store instruction writes 1 KB of whole cache lines.
+template <int N>
+__device__ __forceinline__ int bc_piece(int tb, int nb, int which) {
+    return (((tb * (N / 16) + nb) * 2 + which) * 64) * 4;
+}
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 
@@ -80,10 +89,10 @@ struct SsdBwdKP {
     const int32_t* ids;
     const bf16_t* dy;
     const float* dstate;
-    const float* ckpt;   // [S][H][n_chunks][P][N]: state entering each chunk
+    const float* ckpt;   // [S][H][n_chunks] x the state entering each chunk (SsdCkptLayout)
     float* d_x;
     float* d_dt;
-    float* bc_part;      // [S][H][n_chunks * Q][2][N]: this head's dB, then dC
+    float* bc_part;      // [S][H][n_chunks] x this head's dB and dC of a chunk (bc_piece)
     float* dA_part;      // [S][H]
     float* dD_part;      // [S][H]
     float* ds_part;      // [S][H][P][N]: dL/dh_0
@@ -285,15 +294,17 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
         }
 #pragma unroll
         for (int k = 0; k < HPER; ++k) {
-            const int e = tid + kThreads * k;  // 16-byte piece e (4 states) of the fp32 [P][N] checkpoint
+            const int e = tid + kThreads * k;  // 16-byte piece e (4 states) of the fp32 checkpoint
             if (e < HCH) {
+                int pp, n0;
+                SsdCkptLayout<P, N>::pn(e, pp, n0);
                 float v[4], rem[4];
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
                     v[rr] = __uint_as_float(sk[k][rr]);
                     rem[rr] = v[rr] - to_f32(bf16_rne(v[rr]));
                 }
-                const int off = (e / (N / 4)) * NPH + (e % (N / 4)) * 4;
+                const int off = pp * NPH + n0;
                 *reinterpret_cast<u32x2*>(&H_l[off]) = pack4(v[0], v[1], v[2], v[3]);
                 *reinterpret_cast<u32x2*>(&Hr_l[off]) = pack4(rem[0], rem[1], rem[2], rem[3]);
             }
@@ -488,9 +499,10 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
             const int tb = wave & 3, nb0 = (wave >> 2) * NPW, half = wave >> 2;
             const int t = tb * 16 + l16;  // also s for the dB part (the same block)
             float yo = 0.0f, uu = 0.0f;
-            // this head's row [2][N] of the partial sums for token t (rows are
-            // padded to whole chunks: no store needs a guard)
-            float* bcc = p.bc_part + (((int64_t)i * p.H + hh) * p.n_chunks * kQ + t0 + t) * 2 * N;
+            // this head's partial sums of the chunk, 16-byte piece of this lane
+            // in each (token block, state block, dB / dC) tile (chunks are
+            // whole: no store needs a guard)
+            float* bcc = p.bc_part + (((int64_t)i * p.H + hh) * p.n_chunks + t0 / kQ) * (kQ * 2 * N) + 4 * lane;
             const float et = ecum_l[t], ws = w_l[t];
             // the dy and x rows of the token block, shared by every state block
             bf16x8 yo8[P / 32], xo[P / 32];
@@ -523,7 +535,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
                     yo = fmaf(off, (float)cn[rr], yo);
                     dc[rr] = off + c2[rr];
                 }
-                *reinterpret_cast<float4*>(bcc + N + n0) = make_float4(dc[0], dc[1], dc[2], dc[3]);
+                *reinterpret_cast<float4*>(bcc + bc_piece<N>(tb, nb, 1)) = make_float4(dc[0], dc[1], dc[2], dc[3]);
 
                 f32x4 b1 = {0.f, 0.f, 0.f, 0.f}, b2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -543,7 +555,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
                     uu = fmaf(b2[rr], (float)bn[rr], uu);
                     db[rr] = fmaf(ws, b2[rr], b1[rr]);
                 }
-                *reinterpret_cast<float4*>(bcc + n0) = make_float4(db[0], db[1], db[2], db[3]);
+                *reinterpret_cast<float4*>(bcc + bc_piece<N>(tb, nb, 0)) = make_float4(db[0], db[1], db[2], db[3]);
             }
             // sums over this wave's states: the lane's own, then its four lane groups
             yo += __shfl_xor(yo, 16);
@@ -681,25 +693,42 @@ __global__ __launch_bounds__(256) void ssd_bwd_reduce(const float* __restrict__ 
 }
 
 // d_B, d_C [S][L][G][N]: the partial sums of the group's heads in head order.
+// A thread takes one 16-byte piece of a chunk's partials (as stored: lane
+// l16 + 16 g4 of tile (tb, nb, which) holds token 16 tb + l16, states
+// 16 nb + 4 g4 .. + 3), so that the reads of a wave are contiguous.
 __global__ __launch_bounds__(256) void ssd_bwd_reduce_bc(const float* __restrict__ part, float* d_B,
-                                                         float* d_C, int S, int L, int Lpad, int H, int G,
+                                                         float* d_C, int S, int L, int n_chunks, int H, int G,
                                                          int N) {
-    const int64_t total = (int64_t)S * L * G * N;
-    const int hpg = H / G;
+    const int hpg = H / G, NB = N / 16;
+    const int per_chunk = kQ * 2 * N / 4;  // pieces of one head's chunk
+    const int64_t total = (int64_t)S * G * n_chunks * per_chunk;
+    const int64_t head_stride = (int64_t)n_chunks * per_chunk;
+    const float4* part4 = reinterpret_cast<const float4*>(part);
     for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-        const int n = (int)(e % N);
-        const int64_t rest = e / N;
-        const int g = (int)(rest % G);
-        const int64_t tok = rest / G;
-        const int64_t i = tok / L, t = tok % L;
-        const float* src = part + ((i * H + (int64_t)g * hpg) * Lpad + t) * 2 * N + n;
-        float b = 0.0f, c = 0.0f;
+        const int within = (int)(e % per_chunk);
+        int64_t r = e / per_chunk;
+        const int chunk = (int)(r % n_chunks);
+        r /= n_chunks;
+        const int g = (int)(r % G);
+        const int64_t i = r / G;
+        const int lane = within & 63, tile = within >> 6;
+        const int which = tile & 1, nb = (tile >> 1) % NB, tb = (tile >> 1) / NB;
+        const int t = chunk * kQ + tb * 16 + (lane & 15);
+        if (t >= L) continue;  // the padding of the last chunk
+        const float4* src = part4 + ((i * H + (int64_t)g * hpg) * n_chunks + chunk) * per_chunk + within;
+        float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
         for (int h = 0; h < hpg; ++h) {
-            b += src[(int64_t)h * Lpad * 2 * N];
-            c += src[(int64_t)h * Lpad * 2 * N + N];
+            const float4 v = src[(int64_t)h * head_stride];
+            a0 += v.x;
+            a1 += v.y;
+            a2 += v.z;
+            a3 += v.w;
         }
-        d_B[e] = b;
-        d_C[e] = c;
+        float* dst = (which ? d_C : d_B) + ((i * L + t) * G + g) * N + nb * 16 + 4 * (lane >> 4);
+        dst[0] = a0;
+        dst[1] = a1;
+        dst[2] = a2;
+        dst[3] = a3;
     }
 }
 
@@ -785,9 +814,9 @@ int launch_ssd_bwd(const BwdArgs& a, hipStream_t stream) {
     else if (sh.P == 64 && sh.N == 64) launch_ssd_bwd_pn<64, 64>(kp, S, sp, stream);
     else if (sh.P == 32 && sh.N == 128) launch_ssd_bwd_pn<32, 128>(kp, S, sp, stream);
     else launch_ssd_bwd_pn<32, 64>(kp, S, sp, stream);
-    const int64_t nbc = sh.nelem_BC();
+    const int64_t nbc = sh.S * sh.G * n_chunks * (kQ * 2 * sh.N / 4);  // 16-byte pieces of the sums
     hipLaunchKernelGGL(ssd_bwd_reduce_bc, dim3((unsigned)std::min<int64_t>((nbc + 255) / 256, 16384)), dim3(256),
-                       0, stream, (const float*)bc_part, a.d_B, a.d_C, (int)sh.S, (int)sh.L, (int)(n_chunks * kQ),
+                       0, stream, (const float*)bc_part, a.d_B, a.d_C, (int)sh.S, (int)sh.L, (int)n_chunks,
                        (int)sh.H, (int)sh.G, (int)sh.N);
     const int64_t per_row = sh.H * sh.P * sh.N;
     const int64_t work = std::max<int64_t>(sh.H, sh.R * per_row);

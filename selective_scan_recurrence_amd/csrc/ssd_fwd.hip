@@ -81,7 +81,7 @@ struct SsdKP {
     const int32_t* ids;
     bf16_t* y;
     float* state_out;
-    float* ckpt;   // CKPT: [S][H][n_chunks][P][N], the state entering each chunk
+    float* ckpt;   // CKPT: [S][H][n_chunks] x the state entering each chunk (SsdCkptLayout)
     uint32_t* err;
     const float* dt_bias;  // [H] or null
     const bf16_t* z;       // like x (GATE), or null
@@ -290,11 +290,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             w_l[lane] = __expf(last - cum) * d;
             if (lane == 0) elast_l = __expf(last);
         }
-        if constexpr (CKPT) {  // the fp32 state entering this chunk
+        if constexpr (CKPT) {  // the fp32 state entering this chunk, in the checkpoint piece order
+            static_assert(SsdCkptLayout<P, N>::NH == NH && SsdCkptLayout<P, N>::NS == NS, "checkpoint layout");
+            float* ck = p.ckpt + (((int64_t)i * p.H + hh) * n_chunks + t0 / kQ) * (P * N);
 #pragma unroll
             for (int j = 0; j < NH; ++j)
-                *reinterpret_cast<f32x4*>(p.ckpt + (((((int64_t)i * p.H + hh) * n_chunks + t0 / kQ) * P + pw + l16) * N +
-                                                    (NH * sh + j) * 16 + 4 * g4)) = hacc[j];
+                *reinterpret_cast<f32x4*>(ck + 4 * SsdCkptLayout<P, N>::piece(wave, j, lane)) = hacc[j];
         }
     };
 

@@ -155,4 +155,24 @@ int launch_conv_bwd(const void* sx, const float* w, const float* dout, float* dg
                     int64_t n_t, int64_t d_inner, int d_conv, int io, int apply_silu, void* ws,
                     hipStream_t stream);
 
+// Chunk checkpoints of the Mamba-2 backward, written by the forward's
+// recompute (ssd_fwd.hip) and read by ssd_bwd.hip.  The fp32 state [P][N]
+// entering a chunk is kept as 16-byte pieces in the order the forward's 8
+// waves hold it in their MFMA accumulators: wave w = NS sp + sh owns channels
+// 16 sp .. + 15 and state tiles NH sh .. + NH - 1, and lane l16 + 16 g4 of
+// its tile j holds channel 16 sp + l16, states 16 (NH sh + j) + 4 g4 .. + 3.
+// Each store instruction of the writer then covers 1 KB of whole cache lines
+// (a [P][N] row order would give it 64-byte halves of 16 lines).
+template <int P, int N>
+struct SsdCkptLayout {
+    static constexpr int PB = P / 16, NS = 8 / PB, NH = N / NS / 16;
+    static __device__ __forceinline__ int piece(int wave, int j, int lane) { return (wave * NH + j) * 64 + lane; }
+    // channel p and first state n0 of piece e
+    static __device__ __forceinline__ void pn(int e, int& p, int& n0) {
+        const int lane = e & 63, wj = e >> 6, j = wj % NH, w = wj / NH;
+        p = 16 * (w / NS) + (lane & 15);
+        n0 = 16 * (NH * (w % NS) + j) + 4 * (lane >> 4);
+    }
+};
+
 }  // namespace ssm
