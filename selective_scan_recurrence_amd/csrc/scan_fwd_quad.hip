@@ -591,6 +591,17 @@ __global__ __launch_bounds__(kThreads) void quad_out(QuadKP p) {
     const int c = active ? c_raw : p.d_inner - 1;
     int r = p.ids[i];
     const SeqSpan sp = seq_span(p.cu, i, p.L, p.T);
+    if (p.cu && piece < 0 && p.n_chunks == 1) {
+        // packed sequences of mixed lengths: a workgroup whose sequence is
+        // longer than the mean (T / S) is on the critical path, so its waves
+        // go first at the instruction arbiter of the compute unit it shares
+        // with shorter ones (length over the mean in eighths: from 10 / 8 up
+        // priority 3, from 9 / 8 2, from 7 / 8 1)
+        const int64_t e8 = (8 * (int64_t)sp.len * p.S) / (p.T > 0 ? p.T : 1);
+        if (e8 >= 10) __builtin_amdgcn_s_setprio(3);
+        else if (e8 >= 9) __builtin_amdgcn_s_setprio(2);
+        else if (e8 >= 7) __builtin_amdgcn_s_setprio(1);
+    }
     const bool bad_id = (r < 0) | (r >= p.R);
     const bool bad = bad_id | sp.bad;
     if (bad) {
@@ -723,7 +734,9 @@ template <typename T, int K, bool TILED, bool SOFTPLUS, bool GATE = false>
 int launch_quad_t(QuadKP kp, hipStream_t st, int* relay_k_out) {
     const dim3 block(kThreads);
     const unsigned cblocks = (unsigned)((kp.d_inner + kChanPerBlock - 1) / kChanPerBlock);
-    if (TILED && kp.relay_h) {
+    // (not for packed sequences: the split assumes jobs of equal length; those
+    // raise the wave priority of the longer sequences instead)
+    if (TILED && kp.relay_h && !kp.cu) {
         const int n_cu = device_cus();
         const int cap = n_cu > 0 ? resident_blocks((const void*)quad_out<T, K, TILED, SOFTPLUS, GATE>, kThreads) : 0;
         const RelaySplit rs = relay_split((int64_t)kp.S * cblocks, kp.L, TileCfg<T>::TT, cap, n_cu, kRelayMaxJobs);
