@@ -148,18 +148,18 @@ def valu_slots_per_channel_token(p, backward=False) -> float:
 # by COPY_FACTOR: the ratio of known bytes to what the same counter reads for a
 # plain device copy of 1 GiB ("bench.py --copy-probe").  A figure holds only for the
 # kernel sources it was taken on; bench.py reports null once any of them changes.
-COPY_FACTOR = {"fetch": 1.99993, "write": 1.00000}
+COPY_FACTOR = {"fetch": 1.99994, "write": 1.00000}
 MEASURED_TRAFFIC = {
-    "C1": {"sha256": "8fc59cc6ea1fe24b7c2894e87efbaa19f4aa61b9a832f3941e23b6efdb5f974d", "fetch_kib": 34138.7, "write_kib": 33024.0},
-    "C2": {"sha256": "8fc59cc6ea1fe24b7c2894e87efbaa19f4aa61b9a832f3941e23b6efdb5f974d", "fetch_kib": 340951.3, "write_kib": 332296.0},
-    "C3": {"sha256": "c5a6930703d860d5e794dcf75dd2091f82a62579ac176b8384e7843b8f9cfec7", "fetch_kib": 143290.2, "write_kib": 174080.3},
-    "C4": {"sha256": "64855c8681f9d3a8ad203ca4ec08e6ff3c697935fbca2d56997a2e82dab5b988", "fetch_kib": 1670241.1, "write_kib": 2964612.0},
+    "C1": {"sha256": "754fbdd94346340ab979b6d2c7f64cbde3acae4df58858abc6b914c2282d1183", "fetch_kib": 34140.2, "write_kib": 33024.0},
+    "C2": {"sha256": "754fbdd94346340ab979b6d2c7f64cbde3acae4df58858abc6b914c2282d1183", "fetch_kib": 340956.4, "write_kib": 332296.0},
+    "C3": {"sha256": "31990f98eaf380717c3c63775088a32352b1482f940ef88122e6e2b21c46a4bf", "fetch_kib": 143277.7, "write_kib": 174080.3},
+    "C4": {"sha256": "78bc46076fb9a2489da942bee8a22f3c688e62ab616cbe10222b5f9bcddf1089", "fetch_kib": 1670336.4, "write_kib": 2964612.0},
     "C5": {"sha256": "19d21d3c16653649e1d9cac38de168171b782e33178b052b1b50c035b9a95dd5", "fetch_kib": 512932.3, "write_kib": 704850.3},
     "C6": {"sha256": "365057569e18c41ae6495048cfbeb33cacead190cc03a245029d5ac614a042b7", "fetch_kib": 52810.7, "write_kib": 99843.7},
     "C7": {"sha256": "365057569e18c41ae6495048cfbeb33cacead190cc03a245029d5ac614a042b7", "fetch_kib": 83410.5, "write_kib": 164502.2},
-    "C8": {"sha256": "23fdfc87152031e7435461f3ca679aa366617a664806d5a3791ed0dad34b2449", "fetch_kib": 1372017.4, "write_kib": 2415523.0},
-    "C9": {"sha256": "aade4013e5e398593b4b3fe9d644aa41cb991d3c70e5a58985a4672e12d49d08", "fetch_kib": 504970.0, "write_kib": 330720.0},
-    "C10": {"sha256": "64855c8681f9d3a8ad203ca4ec08e6ff3c697935fbca2d56997a2e82dab5b988", "fetch_kib": 1670400.7, "write_kib": 2966548.0},
+    "C8": {"sha256": "385c7d0654a2c5adf5211644347a6c7884a7437a5cfee6aa4328e9e873680f70", "fetch_kib": 1373593.4, "write_kib": 2410618.3},
+    "C9": {"sha256": "09c6bb6bc16c79e925d4f00bc44d89e6f9218d2dfa2dc713b482d48275051dac", "fetch_kib": 506802.0, "write_kib": 330720.0},
+    "C10": {"sha256": "78bc46076fb9a2489da942bee8a22f3c688e62ab616cbe10222b5f9bcddf1089", "fetch_kib": 1670374.9, "write_kib": 2966548.0},
     "C11": {"sha256": "276c97c0ab38954d90eea36e94e56223be1d1cf15921334358e607baa728a14b", "fetch_kib": 164316.9, "write_kib": 327680.0},
 }
 KERNEL_SOURCES = {
