@@ -550,7 +550,7 @@ int launch_ssd_fwd(const FwdArgs& a, hipStream_t stream) {
 }
 
 // The backward's recompute: chunk-entry states of every (sequence, head)
-// into ckpt [S][H][n_chunks][P][N].
+// into ckpt [S][H][n_chunks], each state in the SsdCkptLayout piece order.
 int launch_ssd_ckpt(const BwdArgs& a, float* ckpt, hipStream_t stream) {
     const Shape& sh = a.sh;
     SsdKP kp;
