@@ -157,7 +157,7 @@ MEASURED_TRAFFIC = {
     "C5": {"sha256": "19d21d3c16653649e1d9cac38de168171b782e33178b052b1b50c035b9a95dd5", "fetch_kib": 512932.3, "write_kib": 704850.3},
     "C6": {"sha256": "365057569e18c41ae6495048cfbeb33cacead190cc03a245029d5ac614a042b7", "fetch_kib": 52810.7, "write_kib": 99843.7},
     "C7": {"sha256": "365057569e18c41ae6495048cfbeb33cacead190cc03a245029d5ac614a042b7", "fetch_kib": 83410.5, "write_kib": 164502.2},
-    "C8": {"sha256": "3a8095aa44e4ff82547f9535b618092ea0957aa0779c5281df3bb87abb998a31", "fetch_kib": 1373593.4, "write_kib": 2410618.3},
+    "C8": {"sha256": "67caa514582812c07212345c260651dc2881778dd21b3e430715e41d67148ffb", "fetch_kib": 1373990.9, "write_kib": 2410509.7},
     "C9": {"sha256": "09c6bb6bc16c79e925d4f00bc44d89e6f9218d2dfa2dc713b482d48275051dac", "fetch_kib": 506802.0, "write_kib": 330720.0},
     "C10": {"sha256": "78bc46076fb9a2489da942bee8a22f3c688e62ab616cbe10222b5f9bcddf1089", "fetch_kib": 1670374.9, "write_kib": 2966548.0},
     "C11": {"sha256": "276c97c0ab38954d90eea36e94e56223be1d1cf15921334358e607baa728a14b", "fetch_kib": 164316.9, "write_kib": 327680.0},

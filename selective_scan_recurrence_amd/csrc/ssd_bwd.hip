@@ -695,7 +695,9 @@ __global__ __launch_bounds__(256) void ssd_bwd_reduce(const float* __restrict__ 
 // d_B, d_C [S][L][G][N]: the partial sums of the group's heads in head order.
 // A thread takes one 16-byte piece of a chunk's partials (as stored: lane
 // l16 + 16 g4 of tile (tb, nb, which) holds token 16 tb + l16, states
-// 16 nb + 4 g4 .. + 3), so that the reads of a wave are contiguous.
+// 16 nb + 4 g4 .. + 3), so that the reads of a wave are contiguous.  Each
+// partial is read once: the loads stream past the caches (C8's reduction
+// 270 -> 230 us).
 __global__ __launch_bounds__(256) void ssd_bwd_reduce_bc(const float* __restrict__ part, float* d_B,
                                                          float* d_C, int S, int L, int n_chunks, int H, int G,
                                                          int N) {
@@ -703,7 +705,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_reduce_bc(const float* __restrict
     const int per_chunk = kQ * 2 * N / 4;  // pieces of one head's chunk
     const int64_t total = (int64_t)S * G * n_chunks * per_chunk;
     const int64_t head_stride = (int64_t)n_chunks * per_chunk;
-    const float4* part4 = reinterpret_cast<const float4*>(part);
+    const f32x4* part4 = reinterpret_cast<const f32x4*>(part);
     for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
         const int within = (int)(e % per_chunk);
         int64_t r = e / per_chunk;
@@ -715,14 +717,14 @@ __global__ __launch_bounds__(256) void ssd_bwd_reduce_bc(const float* __restrict
         const int which = tile & 1, nb = (tile >> 1) % NB, tb = (tile >> 1) / NB;
         const int t = chunk * kQ + tb * 16 + (lane & 15);
         if (t >= L) continue;  // the padding of the last chunk
-        const float4* src = part4 + ((i * H + (int64_t)g * hpg) * n_chunks + chunk) * per_chunk + within;
+        const f32x4* src = part4 + ((i * H + (int64_t)g * hpg) * n_chunks + chunk) * per_chunk + within;
         float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
         for (int h = 0; h < hpg; ++h) {
-            const float4 v = src[(int64_t)h * head_stride];
-            a0 += v.x;
-            a1 += v.y;
-            a2 += v.z;
-            a3 += v.w;
+            const f32x4 v = __builtin_nontemporal_load(src + (int64_t)h * head_stride);
+            a0 += v[0];
+            a1 += v[1];
+            a2 += v[2];
+            a3 += v[3];
         }
         float* dst = (which ? d_C : d_B) + ((i * L + t) * G + g) * N + nb * 16 + 4 * (lane >> 4);
         dst[0] = a0;
