@@ -283,7 +283,7 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int64_t tok0,
     const char* xg = static_cast<const char*>(p.x) + (tok0 * p.d_inner + cb * 64) * ES;
     const char* dg = static_cast<const char*>(p.dt) + (tok0 * p.d_inner + cb * 64) * ES;
     char* yg = static_cast<char*>(p.y) + (tok0 * p.d_inner + cb * 64) * ES;
-    const char* zg = static_cast<const char*>(p.z) + (tok0 * p.d_inner + cb * 64) * ES;  // GATE only
+    const char* zg = GATE ? static_cast<const char*>(p.z) + (tok0 * p.d_inner + cb * 64) * ES : nullptr;
     // B for waves 0-1, C for waves 2-3 (readfirstlane: wave-uniform, so its
     // buffer descriptor stays in scalar registers)
     const int c_half = __builtin_amdgcn_readfirstlane(tid >> 7);
@@ -331,7 +331,7 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int64_t tok0,
         xoff[r] = (int)((e / CPR) * row_stride) + (e % CPR) * 16;
     }
     const int bcoff = ((tid & (kThreads / 2 - 1)) / CPT) * 16 * ES + ((tid & (kThreads / 2 - 1)) % CPT) * 16;
-    u32x4 sx[2], sdt[2], sbc;
+    u32x4 sx[2], sdt[2], sbc, sz[GATE ? 2 : 1];
     auto load_tile = [&](int tb) {
         const auto rx = rsrc(xg, tb, row_stride), rd = rsrc(dg, tb, row_stride);
         const auto rb = rsrc(bcg, tb, 16 * ES);
@@ -341,6 +341,11 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int64_t tok0,
             sdt[r] = __builtin_amdgcn_raw_buffer_load_b128(rd, xoff[r], 0, 0);
         }
         sbc = __builtin_amdgcn_raw_buffer_load_b128(rb, bcoff, 0, 0);
+        if constexpr (GATE && MODE == 1) {
+            const auto rz = rsrc(zg, tb, row_stride);
+#pragma unroll
+            for (int r = 0; r < 2; ++r) sz[r] = __builtin_amdgcn_raw_buffer_load_b128(rz, xoff[r], 0, 0);
+        }
     };
     auto store_tile = [&]() {
 #pragma unroll
@@ -361,6 +366,11 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int64_t tok0,
                 *reinterpret_cast<u32x4*>(xd) = sx[r];
             }
             *reinterpret_cast<u32x4*>(dt_l + row * XS + col * 16) = sdt[r];
+            // the gate's z goes where this tile's y will go: the owner of
+            // (token, channel) reads its z there and writes its y in its place
+            // (this thread stored the previous tile's y from these same
+            // pieces just before)
+            if constexpr (GATE && MODE == 1) *reinterpret_cast<u32x4*>(y_l + row * XS + col * 16) = sz[r];
         }
         const int e = tid & (kThreads / 2 - 1);
         const int tok = e / CPT, part = e % CPT;
@@ -380,19 +390,8 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int64_t tok0,
         }
     };
 
-    // The gate: the owner's z for group g of the tile at tb (rows past t_end
-    // read as zero); each group loads the next group's, zc holds the current.
-    auto load_z = [&](int g, int tb) -> float {
-        const auto rz = rsrc(zg, tb, row_stride);
-        const int off = (4 * g + q) * (int)row_stride + cl * ES;
-        if constexpr (ES == 2) return to_f32((bf16_t)__builtin_amdgcn_raw_buffer_load_b16(rz, off, 0, 0));
-        else return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rz, off, 0, 0));
-    };
-    float zc = 0.0f;
     // One group of four tokens; FULL: every token of the group is < t_end.
     auto group = [&](int g, bool full_tile, int tb) {
-        float zn = 0.0f;
-        if constexpr (GATE && MODE == 1) zn = load_z(g + 1, tb);
         const int tt = 4 * g + q;  // owned row of this tile
         if constexpr (MODE == 2) {  // state entering each kCkpt-token block
             if (((tb + 4 * g - t_begin) & (kCkpt - 1)) == 0) {
@@ -456,9 +455,9 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int64_t tok0,
             const float ysum = (yr[q] + yr[4 + q]) + (yr[8 + q] + yr[12 + q]);
             __builtin_amdgcn_wave_barrier();
             float yv = fmaf(Dc, u, ysum);
-            if constexpr (GATE) {  // y * SiLU(z), rounded once
-                yv *= silu(zc);
-                zc = zn;
+            if constexpr (GATE) {  // y * SiLU(z), rounded once; z was staged in y's place
+                const float zv = to_f32(*reinterpret_cast<const T*>(y_l + tt * XS + cl * ES));
+                yv *= silu(zv);
             }
             if constexpr (ES == 2)
                 *reinterpret_cast<bf16_t*>(y_l + tt * XS + cl * ES) = bf16_rne(yv);
@@ -474,7 +473,6 @@ __device__ __forceinline__ void quad_tiled(const QuadKP& p, int i, int64_t tok0,
     for (int tile = 0; tile < n_tiles; ++tile) {
         const int tb = t_begin + tile * TT;
         const bool more = tile + 1 < n_tiles;
-        if constexpr (GATE && MODE == 1) zc = load_z(0, tb);  // the first group's z
         load_tile(tb + TT);  // past the end: zero rows, never staged
         if (tb + TT <= t_end) {
 #pragma unroll 2
