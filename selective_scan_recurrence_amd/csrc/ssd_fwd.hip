@@ -312,15 +312,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         __syncthreads();  // every wave is done with the previous chunk's tiles
         store_chunk(t0);
         __syncthreads();
-        // the gate's z at this lane's y positions, issued before the next
-        // chunk's loads so that waiting for them does not wait for those
-        u32x2 zv[GATE ? TBW : 1];
-        if constexpr (GATE && !CKPT) {
-            const auto rz = rsrc(zg, t0, xrow);
-#pragma unroll
-            for (int q = 0; q < TBW; ++q)
-                zv[q] = __builtin_amdgcn_raw_buffer_load_b64(rz, yoff(TBW * sh + q), 0, 0);
-        }
         load_chunk(t0 + kQ);  // next chunk (past the end: reads zero, never used)
 
         if constexpr (!CKPT) {
@@ -370,6 +361,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                 *reinterpret_cast<u32x2*>(&M_l[mt_t * MP + msb[u] * 16 + 4 * g4]) = u32x2{lo, hi};
             }
         }
+        // the gate's z of this chunk as whole-line 16-byte pieces (x's
+        // staging pattern), issued once the M tiles are done (fewer live
+        // registers there); they go to LDS in C's place once every wave is
+        // done with C (below)
+        u32x4 sz[GATE ? XPER : 1];
+        if constexpr (GATE && !CKPT) {
+            const auto rz = rsrc(zg, t0, xrow);
+#pragma unroll
+            for (int k = 0; k < XPER; ++k) {
+                const int e = tid + kThreads * k;
+                if (e < XCH)
+                    sz[k] = __builtin_amdgcn_raw_buffer_load_b128(rz, (int)((e / (P / 8)) * xrow) + (e % (P / 8)) * 16, 0, 0);
+            }
+        }
         // carried-state product over this wave's state part, for all four token
         // blocks: A = the state as bf16 hi + lo from the accumulators, B = C at
         // the same states (see the header); the other parts' blocks go to LDS
@@ -412,6 +417,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             }
         }
         __syncthreads();
+        // the gate's z tile [t][p] (pitch XP) in C's place, which no wave reads
+        // again before the next chunk is staged
+        bf16_t* const Z_l = C_l;
+        if constexpr (GATE) {
+#pragma unroll
+            for (int k = 0; k < XPER; ++k) {
+                const int e = tid + kThreads * k;
+                if (e < XCH) *reinterpret_cast<u32x4*>(&Z_l[(e / (P / 8)) * XP + (e % (P / 8)) * 8]) = sz[k];
+            }
+            __syncthreads();
+        }
 
         const auto ry = rsrc(yg, t0, xrow);
         // Yd^T = X^T M^T over s for the wave's token blocks (x columns of its
@@ -444,14 +460,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             // y[t][p] for p = pw + 4g + r: y = yd + exp(cum_t) yo + D x
             uint32_t packed[2];
             const bf16x4 xv = ld4(&X_l[t * XP + pw + 4 * g4]);
+            bf16x4 zq;
+            if constexpr (GATE) zq = ld4(&Z_l[t * XP + pw + 4 * g4]);
 #pragma unroll
             for (int rr = 0; rr < 4; rr += 2) {
                 float y0 = fmaf(Dh, (float)xv[rr], fmaf(et, yot[rr], yd[rr]));
                 float y1 = fmaf(Dh, (float)xv[rr + 1], fmaf(et, yot[rr + 1], yd[rr + 1]));
                 if constexpr (GATE) {  // y * SiLU(z), rounded once
-                    const uint32_t zw = zv[q][rr / 2];
-                    y0 *= silu(__uint_as_float(zw << 16));
-                    y1 *= silu(__uint_as_float(zw & 0xffff0000u));
+                    y0 *= silu((float)zq[rr]);
+                    y1 *= silu((float)zq[rr + 1]);
                 }
                 packed[rr / 2] = uint32_t(bf16_rne(y0)) | (uint32_t(bf16_rne(y1)) << 16);
             }
