@@ -150,16 +150,16 @@ def valu_slots_per_channel_token(p, backward=False) -> float:
 # kernel sources it was taken on; bench.py reports null once any of them changes.
 COPY_FACTOR = {"fetch": 1.99994, "write": 1.00000}
 MEASURED_TRAFFIC = {
-    "C1": {"sha256": "24adc11fd4210f6b523958b3af2f9dd27a0ba13108983d8be6dcbe6ad756f99e", "fetch_kib": 34140.2, "write_kib": 33024.0},
-    "C2": {"sha256": "24adc11fd4210f6b523958b3af2f9dd27a0ba13108983d8be6dcbe6ad756f99e", "fetch_kib": 340956.4, "write_kib": 332296.0},
-    "C3": {"sha256": "ea671de48bb0f275cb933e914c03bc591dafb14d6edd2a10c70541946b9642e3", "fetch_kib": 143277.7, "write_kib": 174080.3},
-    "C4": {"sha256": "78bc46076fb9a2489da942bee8a22f3c688e62ab616cbe10222b5f9bcddf1089", "fetch_kib": 1670336.4, "write_kib": 2964612.0},
+    "C1": {"sha256": "3faae9c4929597f0b48c263c0f643218feef324c205b8e93f4e5dc1260b16771", "fetch_kib": 34140.2, "write_kib": 33024.0},
+    "C2": {"sha256": "3faae9c4929597f0b48c263c0f643218feef324c205b8e93f4e5dc1260b16771", "fetch_kib": 340956.4, "write_kib": 332296.0},
+    "C3": {"sha256": "27c56410f3fb97518f64e56326d6cfa29a0aafa282a895342f0fbf979bbf928c", "fetch_kib": 143277.7, "write_kib": 174080.3},
+    "C4": {"sha256": "dfce2706dc633e55eb0f9b6077ab1422572cccd4d32738e8ce26c93bc0ac7f58", "fetch_kib": 1670336.4, "write_kib": 2964612.0},
     "C5": {"sha256": "19d21d3c16653649e1d9cac38de168171b782e33178b052b1b50c035b9a95dd5", "fetch_kib": 512932.3, "write_kib": 704850.3},
     "C6": {"sha256": "365057569e18c41ae6495048cfbeb33cacead190cc03a245029d5ac614a042b7", "fetch_kib": 52810.7, "write_kib": 99843.7},
     "C7": {"sha256": "365057569e18c41ae6495048cfbeb33cacead190cc03a245029d5ac614a042b7", "fetch_kib": 83410.5, "write_kib": 164502.2},
-    "C8": {"sha256": "67caa514582812c07212345c260651dc2881778dd21b3e430715e41d67148ffb", "fetch_kib": 1373990.9, "write_kib": 2410509.7},
-    "C9": {"sha256": "09c6bb6bc16c79e925d4f00bc44d89e6f9218d2dfa2dc713b482d48275051dac", "fetch_kib": 506802.0, "write_kib": 330720.0},
-    "C10": {"sha256": "78bc46076fb9a2489da942bee8a22f3c688e62ab616cbe10222b5f9bcddf1089", "fetch_kib": 1670374.9, "write_kib": 2966548.0},
+    "C8": {"sha256": "d21d570b923bc4ba511d038766478ccac0165f587ace9e0438d6bc917b6434b1", "fetch_kib": 1373990.9, "write_kib": 2410509.7},
+    "C9": {"sha256": "3c0e2ea0340a49be790cdacc592eb9c771e4a786aed94dd7657ca3a3703992e7", "fetch_kib": 506996.8, "write_kib": 330720.0},
+    "C10": {"sha256": "dfce2706dc633e55eb0f9b6077ab1422572cccd4d32738e8ce26c93bc0ac7f58", "fetch_kib": 1670374.9, "write_kib": 2966548.0},
     "C11": {"sha256": "276c97c0ab38954d90eea36e94e56223be1d1cf15921334358e607baa728a14b", "fetch_kib": 164316.9, "write_kib": 327680.0},
 }
 KERNEL_SOURCES = {
