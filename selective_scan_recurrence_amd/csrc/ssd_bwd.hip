@@ -81,7 +81,7 @@ constexpr int kThreads = 64 * kWaves;
 
 struct SsdBwdKP {
     const bf16_t* x;
-    const bf16_t* dt;
+    const uint16_t* dt_t;  // [S][H][L] bf16 bits of dt, tokens contiguous (the checkpoint pass writes it)
     const float* A;
     const bf16_t* B;
     const bf16_t* C;
@@ -224,13 +224,13 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
     }
 
     // per-chunk descriptors: rows past the sequence end read as zero / drop stores
-    const int64_t xrow = (int64_t)p.H * P * 2, brow = (int64_t)p.G * N * 2, drow = (int64_t)p.H * 2;
+    const int64_t xrow = (int64_t)p.H * P * 2, brow = (int64_t)p.G * N * 2;
     const int64_t xrow4 = (int64_t)p.H * P * 4, drow4 = (int64_t)p.H * 4;
     const char* xg = reinterpret_cast<const char*>(p.x) + ((int64_t)i * L * p.H + hh) * P * 2;
     const char* yg = reinterpret_cast<const char*>(p.dy) + ((int64_t)i * L * p.H + hh) * P * 2;
     const char* bg = reinterpret_cast<const char*>(p.B) + ((int64_t)i * L * p.G + grp) * N * 2;
     const char* cg = reinterpret_cast<const char*>(p.C) + ((int64_t)i * L * p.G + grp) * N * 2;
-    const char* dg = reinterpret_cast<const char*>(p.dt) + ((int64_t)i * L * p.H + hh) * 2;
+    const char* dg = reinterpret_cast<const char*>(p.dt_t) + ((int64_t)i * p.H + hh) * L * 2;
     char* dxg = reinterpret_cast<char*>(p.d_x) + ((int64_t)i * L * p.H + hh) * P * 4;
     char* ddg = reinterpret_cast<char*>(p.d_dt) + ((int64_t)i * L * p.H + hh) * 4;
     const float* ckg = p.ckpt + ((int64_t)i * p.H + hh) * p.n_chunks * (P * N);
@@ -273,7 +273,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
 #pragma unroll
         for (int k = 0; k < HPER; ++k)
             if (tid + kThreads * k < HCH) sk[k] = __builtin_amdgcn_raw_buffer_load_b128(rk, (tid + kThreads * k) * 16, 0, 0);
-        if (tid < kQ) sdt = __builtin_amdgcn_raw_buffer_load_b16(rsrc(dg, c < 0 ? -1 : t0, drow), (int)(tid * drow), 0, 0);
+        if (tid < kQ) sdt = __builtin_amdgcn_raw_buffer_load_b16(rsrc(dg, c < 0 ? -1 : t0, 2), tid * 2, 0, 0);
     };
     float dt_raw = 0.0f, sdt_pre = 0.0f;  // wave 0, lane = token
     auto store_chunk = [&](int t0) {
@@ -768,10 +768,10 @@ size_t ssd_bwd_workspace_bytes(const Shape& sh) {
     return align_up((size_t)(sh.S * sh.H * n_chunks * sh.P * sh.N) * 4, 256) +
            align_up((size_t)(sh.S * sh.H * sh.P * sh.N) * 4, 256) + 2 * align_up((size_t)(sh.S * sh.H) * 4, 256) +
            align_up((size_t)(sh.S * sh.H * n_chunks * kQ * 2 * sh.N) * 4, 256) +
-           ssd_relay_bytes(sh.S * sh.H, n_chunks);
+           align_up((size_t)(sh.S * sh.H * sh.L) * 2, 256) + ssd_relay_bytes(sh.S * sh.H, n_chunks);
 }
 
-int launch_ssd_ckpt(const BwdArgs& a, float* ckpt, hipStream_t stream);
+int launch_ssd_ckpt(const BwdArgs& a, float* ckpt, uint16_t* dt_t, hipStream_t stream);
 
 int launch_ssd_bwd(const BwdArgs& a, hipStream_t stream) {
     const Shape& sh = a.sh;
@@ -791,16 +791,18 @@ int launch_ssd_bwd(const BwdArgs& a, hipStream_t stream) {
     w += align_up((size_t)(sh.S * sh.H) * 4, 256);
     float* bc_part = reinterpret_cast<float*>(w);
     w += align_up((size_t)(sh.S * sh.H * n_chunks * kQ * 2 * sh.N) * 4, 256);
+    uint16_t* dt_t = reinterpret_cast<uint16_t*>(w);
+    w += align_up((size_t)(sh.S * sh.H * sh.L) * 2, 256);
     const size_t relay_bytes = ssd_relay_bytes(sh.S * sh.H, n_chunks);
     float* relay_buf = relay_bytes ? reinterpret_cast<float*>(w) : nullptr;
     int* relay_flag = relay_bytes ? reinterpret_cast<int*>(
                                         w + align_up((size_t)(sh.S * sh.H) * kRelayVals * kThreads * 4, 256))
                                   : nullptr;
     if (ssd_bwd_workspace_bytes(sh) > a.ws_bytes) return SSM_ERR_WORKSPACE;
-    int rc = launch_ssd_ckpt(a, ckpt, stream);
+    int rc = launch_ssd_ckpt(a, ckpt, dt_t, stream);
     if (rc) return rc;
     SsdBwdKP kp;
-    kp.x = static_cast<const bf16_t*>(a.x); kp.dt = static_cast<const bf16_t*>(a.dt); kp.A = a.A;
+    kp.x = static_cast<const bf16_t*>(a.x); kp.dt_t = dt_t; kp.A = a.A;
     kp.B = static_cast<const bf16_t*>(a.B); kp.C = static_cast<const bf16_t*>(a.C); kp.D = a.D;
     kp.ids = a.ids; kp.dy = static_cast<const bf16_t*>(a.dy); kp.dstate = a.dstate; kp.ckpt = ckpt;
     kp.d_x = a.d_x; kp.d_dt = a.d_dt; kp.bc_part = bc_part;

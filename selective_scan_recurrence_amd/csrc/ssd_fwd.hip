@@ -82,6 +82,7 @@ struct SsdKP {
     bf16_t* y;
     float* state_out;
     float* ckpt;   // CKPT: [S][H][n_chunks] x the state entering each chunk (SsdCkptLayout)
+    const uint16_t* dt_t;  // CKPT: dt's bf16 bits as [S][H][L], tokens contiguous (read in place of dt)
     uint32_t* err;
     const float* dt_bias;  // [H] or null
     const bf16_t* z;       // like x (GATE), or null
@@ -221,12 +222,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     // chunk-based descriptors: rows past the sequence end read as zero / drop stores
     const int64_t xrow = (int64_t)p.H * P * 2;   // bytes between tokens of x / y
     const int64_t brow = (int64_t)p.G * N * 2;   // bytes between tokens of B / C
-    const int64_t drow = (int64_t)p.H * 2;       // bytes between tokens of dt
+    const int64_t drow = CKPT ? 2 : (int64_t)p.H * 2;  // bytes between tokens of dt
     const int64_t tok0 = span.t0;
     const char* xg = reinterpret_cast<const char*>(p.x) + (tok0 * p.H + hh) * P * 2;
     const char* bg = reinterpret_cast<const char*>(p.B) + (tok0 * p.G + grp) * N * 2;
     const char* cg = reinterpret_cast<const char*>(p.C) + (tok0 * p.G + grp) * N * 2;
-    const char* dg = reinterpret_cast<const char*>(p.dt) + (tok0 * p.H + hh) * 2;
+    const char* dg = CKPT ? reinterpret_cast<const char*>(p.dt_t) + ((int64_t)i * p.H + hh) * p.L * 2
+                          : reinterpret_cast<const char*>(p.dt) + (tok0 * p.H + hh) * 2;
     char* yg = reinterpret_cast<char*>(p.y) + (tok0 * p.H + hh) * P * 2;
     const char* zg = reinterpret_cast<const char*>(p.z) + (tok0 * p.H + hh) * P * 2;  // GATE only
     auto rsrc = [&](const char* base, int t0, int64_t row) {
@@ -551,7 +553,7 @@ int launch_ssd_fwd(const FwdArgs& a, hipStream_t stream) {
     kp.s = a.s; kp.x = static_cast<const bf16_t*>(a.x); kp.dt = static_cast<const bf16_t*>(a.dt);
     kp.A = a.A; kp.B = static_cast<const bf16_t*>(a.B); kp.C = static_cast<const bf16_t*>(a.C);
     kp.D = a.D; kp.ids = a.ids; kp.y = static_cast<bf16_t*>(a.y); kp.state_out = a.state_out;
-    kp.ckpt = nullptr;
+    kp.ckpt = nullptr; kp.dt_t = nullptr;
     kp.err = a.err;
     kp.dt_bias = a.dt_bias; kp.z = static_cast<const bf16_t*>(a.z); kp.cu = a.cu; kp.T = a.T;
     kp.L = (int)sh.L; kp.H = (int)sh.H; kp.G = (int)sh.G; kp.R = (int)sh.R;
@@ -566,11 +568,53 @@ int launch_ssd_fwd(const FwdArgs& a, hipStream_t stream) {
     return SSM_ERR_UNSUPPORTED;
 }
 
-// The backward's recompute: chunk-entry states of every (sequence, head)
-// into ckpt [S][H][n_chunks], each state in the SsdCkptLayout piece order.
-int launch_ssd_ckpt(const BwdArgs& a, float* ckpt, hipStream_t stream) {
+// dt [S][L][H] -> dt_t [S][H][L] through an LDS tile of 64 tokens x up to
+// 128 heads, so that a chunk's 64 decays of one head are 128 contiguous bytes
+// (a column of the token-major dt touches 64 cache lines).  With H <= 128 a
+// tile is one contiguous range of dt: every load of a wave reads 128 bytes.
+constexpr int kDtTok = 64, kDtHeads = 128;
+__global__ __launch_bounds__(256) void ssd_dt_transpose(const uint16_t* __restrict__ dt, uint16_t* __restrict__ dt_t,
+                                                        int L, int H) {
+    __shared__ uint16_t tile[kDtHeads * (kDtTok + 1)];  // [head][token], rows padded
+    const int tiles = (L + kDtTok - 1) / kDtTok;  // blockIdx.x = sequence x token tile, blockIdx.y = head tile
+    const int64_t s = blockIdx.x / (unsigned)tiles;
+    const int t0 = (int)(blockIdx.x % (unsigned)tiles) * kDtTok, h0 = blockIdx.y * kDtHeads;
+    const int ht = min(kDtHeads, H - h0), nt = min(kDtTok, L - t0);
+    // every load first (offsets past the tile read zero), then the LDS writes
+    const int lim = ((nt - 1) * H + ht) * 2;
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(dt) + (s * L + t0) * H + h0, 0, lim,
+                                                      0x00020000);
+    constexpr int PER = kDtHeads * kDtTok / 256;
+    uint32_t v[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int e = threadIdx.x + 256 * k, t = e / ht, h = e - t * ht;
+        v[k] = __builtin_amdgcn_raw_buffer_load_b16(rs, t < nt ? (t * H + h) * 2 : lim, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int e = threadIdx.x + 256 * k, t = e / ht, h = e - t * ht;
+        if (t < nt) tile[h * (kDtTok + 1) + t] = (uint16_t)v[k];
+    }
+    __syncthreads();
+    const int c = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int k = 0; k < kDtHeads / 4; ++k) {
+        const int h = w + 4 * k;
+        if (h < ht && c < nt) dt_t[(s * H + h0 + h) * L + t0 + c] = tile[h * (kDtTok + 1) + c];
+    }
+}
+
+// The backward's recompute: dt transposed into dt_t [S][H][L] (the backward
+// reads it too), then the chunk-entry states of every (sequence, head) into
+// ckpt [S][H][n_chunks], each state in the SsdCkptLayout piece order.
+int launch_ssd_ckpt(const BwdArgs& a, float* ckpt, uint16_t* dt_t, hipStream_t stream) {
     const Shape& sh = a.sh;
+    hipLaunchKernelGGL(ssd_dt_transpose, dim3((unsigned)(sh.S * ((sh.L + kDtTok - 1) / kDtTok)),
+                                              (unsigned)((sh.H + kDtHeads - 1) / kDtHeads)),
+                       dim3(256), 0, stream, static_cast<const uint16_t*>(a.dt), dt_t, (int)sh.L, (int)sh.H);
     SsdKP kp;
+    kp.dt_t = dt_t;
     kp.s = a.s; kp.x = static_cast<const bf16_t*>(a.x); kp.dt = static_cast<const bf16_t*>(a.dt);
     kp.A = a.A; kp.B = static_cast<const bf16_t*>(a.B); kp.C = static_cast<const bf16_t*>(a.C);
     kp.D = a.D; kp.ids = a.ids; kp.y = nullptr; kp.state_out = nullptr; kp.ckpt = ckpt;
