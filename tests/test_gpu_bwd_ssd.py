@@ -83,6 +83,9 @@ CASES = {
     # four heads share each of two groups, softplus on, several chunks and a ragged tail
     "p32_n128_groups_softplus": dict(n_seqs=2, n_tokens=200, n_head=8, head_dim=32, n_group=2,
                                      dt_softplus=True, n_state_rows=3),
+    # more heads than one 128-head tile of the dt copy, and a ragged 64-token tile
+    "p32_n64_136_heads": dict(n_seqs=2, n_tokens=70, n_head=136, head_dim=32, d_state=64, n_group=4,
+                              bc_std=0.125, n_state_rows=2),
 }
 
 
