@@ -153,13 +153,13 @@ MEASURED_TRAFFIC = {
     "C1": {"sha256": "3faae9c4929597f0b48c263c0f643218feef324c205b8e93f4e5dc1260b16771", "fetch_kib": 34140.2, "write_kib": 33024.0},
     "C2": {"sha256": "3faae9c4929597f0b48c263c0f643218feef324c205b8e93f4e5dc1260b16771", "fetch_kib": 340956.4, "write_kib": 332296.0},
     "C3": {"sha256": "dfa33a9f4015ac56424fbdd57fb520ae911aa72b6a87607f9a9f96108eb09043", "fetch_kib": 143255.0, "write_kib": 174080.3},
-    "C4": {"sha256": "dfce2706dc633e55eb0f9b6077ab1422572cccd4d32738e8ce26c93bc0ac7f58", "fetch_kib": 1670336.4, "write_kib": 2964612.0},
+    "C4": {"sha256": "2a46b022932ac6ec6fec633ef5221432a0374beec1c3222e02b0cf240b04e297", "fetch_kib": 1670396.2, "write_kib": 2964692.1},
     "C5": {"sha256": "19d21d3c16653649e1d9cac38de168171b782e33178b052b1b50c035b9a95dd5", "fetch_kib": 512932.3, "write_kib": 704850.3},
     "C6": {"sha256": "365057569e18c41ae6495048cfbeb33cacead190cc03a245029d5ac614a042b7", "fetch_kib": 52810.7, "write_kib": 99843.7},
     "C7": {"sha256": "365057569e18c41ae6495048cfbeb33cacead190cc03a245029d5ac614a042b7", "fetch_kib": 83410.5, "write_kib": 164502.2},
     "C8": {"sha256": "b004ae6b9bcf1f2ecd6b28c9149e6a1442974dd41129dc7cd1c88fb804ad4a4a", "fetch_kib": 1350539.0, "write_kib": 2413849.8},
     "C9": {"sha256": "3c0e2ea0340a49be790cdacc592eb9c771e4a786aed94dd7657ca3a3703992e7", "fetch_kib": 506996.8, "write_kib": 330720.0},
-    "C10": {"sha256": "dfce2706dc633e55eb0f9b6077ab1422572cccd4d32738e8ce26c93bc0ac7f58", "fetch_kib": 1670374.9, "write_kib": 2966548.0},
+    "C10": {"sha256": "2a46b022932ac6ec6fec633ef5221432a0374beec1c3222e02b0cf240b04e297", "fetch_kib": 1670588.0, "write_kib": 2966628.4},
     "C11": {"sha256": "276c97c0ab38954d90eea36e94e56223be1d1cf15921334358e607baa728a14b", "fetch_kib": 164316.9, "write_kib": 327680.0},
 }
 KERNEL_SOURCES = {

@@ -774,15 +774,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 
 // d_B, d_C: sum of the channel-block partials in block order.
 __global__ __launch_bounds__(256) void bwd_reduce_bc(BwdKP p, float* d_B, float* d_C) {
+    // a thread sums one 16-byte piece (4 states of dB or of dC) of a token
+    // over the channel blocks, in block order; the partials are read once
+    using v4 = float __attribute__((ext_vector_type(4)));
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t tokens = (int64_t)p.S * p.L;
-    if (e >= tokens * 32) return;
-    const int64_t tok = e >> 5;
-    const int m = (int)(e & 31), n = m & 15;
-    if (n >= p.N) return;
-    float acc = 0.0f;
-    for (int cb = 0; cb < p.n_cb; ++cb) acc += p.dbc_part[((int64_t)cb * tokens + tok) * 32 + m];
-    (m < 16 ? d_B : d_C)[tok * p.N + n] = acc;
+    if (e >= tokens * 8) return;
+    const int64_t tok = e >> 3;
+    const int m0 = 4 * (int)(e & 7), n0 = m0 & 15;
+    if (n0 >= p.N) return;
+    const v4* src = reinterpret_cast<const v4*>(p.dbc_part + tok * 32 + m0);
+    const int64_t cb_stride = tokens * 8;  // 16-byte pieces between channel blocks
+    v4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    int cb = 0;
+    for (; cb + 8 <= p.n_cb; cb += 8) {
+        v4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(src + (cb + u) * cb_stride);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += v[u];
+    }
+    for (; cb < p.n_cb; ++cb) acc += __builtin_nontemporal_load(src + cb * cb_stride);
+    float* dst = (m0 < 16 ? d_B : d_C) + tok * p.N;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (n0 + j < p.N) dst[n0 + j] = acc[j];
 }
 
 // d_A, d_D: sums over sequences in sequence order; d_s: dh_0 of every
@@ -980,8 +996,8 @@ int launch_scan_bwd(const BwdArgs& a, hipStream_t stream) {
         if (kp.softplus) hipLaunchKernelGGL((bwd_rev<float, true>), grid, dim3(kThreads), 0, stream, kp);
         else hipLaunchKernelGGL((bwd_rev<float, false>), grid, dim3(kThreads), 0, stream, kp);
     }
-    const int64_t tok32 = sh.S * sh.L * 32;
-    hipLaunchKernelGGL(bwd_reduce_bc, dim3((unsigned)((tok32 + 255) / 256)), dim3(256), 0, stream, kp,
+    const int64_t tok8 = sh.S * sh.L * 8;  // 16-byte pieces of the sums
+    hipLaunchKernelGGL(bwd_reduce_bc, dim3((unsigned)((tok8 + 255) / 256)), dim3(256), 0, stream, kp,
                        a.d_B, a.d_C);
     const int64_t cpar = sh.R * sh.d_inner() * (sh.K > 0 ? sh.K - 1 : 0);
     const unsigned red_blocks = cpar > par ? (unsigned)std::min<int64_t>((cpar + 255) / 256, 65535) : par_blocks;
