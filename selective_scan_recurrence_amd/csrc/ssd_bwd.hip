@@ -33,8 +33,9 @@
 // waves that own a 16-channel block and half of the states (as the forward
 // holds h^T).  G is staged in LDS as a bf16 value plus a bf16 remainder, so
 // that the products that read it keep about 16 significant bits of the
-// carried gradient, and so is the fp32 checkpoint of h_in (the decay
-// gradient multiplies its errors by A); with them the chunk's x, dy, B and C
+// carried gradient, and so are the fp32 checkpoint of h_in (the decay
+// gradient multiplies its errors by A) and Lm (dB and dC sum it over the
+// group's heads, whose terms can cancel); with them the chunk's x, dy, B and C
 // rows, the next (earlier) chunk's rows being loaded meanwhile.  All products run on v_mfma_f32_16x16x32_bf16: operands
 // whose k index runs along a stored row come from 16-byte LDS row reads, the
 // others from the transposing read ds_read_b64_tr_b16 (as in the forward).
@@ -173,6 +174,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
     __shared__ __attribute__((aligned(16))) bf16_t Gr_l[P * NPH];   // ... and its remainder, G - G_l in bf16
     __shared__ __attribute__((aligned(16))) bf16_t M_l[kQ * MP];
     __shared__ __attribute__((aligned(16))) bf16_t Lm_l[kQ * MP];
+    __shared__ __attribute__((aligned(16))) bf16_t Lmr_l[kQ * MP];  // Lm - Lm_l in bf16
     __shared__ __attribute__((aligned(16))) float dt_l[kQ], cum_l[kQ], ecum_l[kQ], w_l[kQ];
     __shared__ __attribute__((aligned(16))) float zrow_l[4][kQ], zcol_l[4][kQ];  // per tile block
     __shared__ __attribute__((aligned(16))) float yoff_l[2][kQ], u_l[2][kQ];
@@ -354,6 +356,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
     for (int e = tid; e < kQ * MP / 2; e += kThreads) {
         reinterpret_cast<uint32_t*>(M_l)[e] = 0u;
         reinterpret_cast<uint32_t*>(Lm_l)[e] = 0u;
+        reinterpret_cast<uint32_t*>(Lmr_l)[e] = 0u;
     }
     for (int e = tid; e < 4 * kQ; e += kThreads) {
         (&zrow_l[0][0])[e] = 0.0f;
@@ -411,6 +414,10 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
                 }
                 *reinterpret_cast<u32x2*>(&M_l[t * MP + msb[u] * 16 + 4 * g4]) = pack4(m[0], m[1], m[2], m[3]);
                 *reinterpret_cast<u32x2*>(&Lm_l[t * MP + msb[u] * 16 + 4 * g4]) = pack4(lm[0], lm[1], lm[2], lm[3]);
+                float lr[4];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) lr[rr] = lm[rr] - to_f32(bf16_rne(lm[rr]));
+                *reinterpret_cast<u32x2*>(&Lmr_l[t * MP + msb[u] * 16 + 4 * g4]) = pack4(lr[0], lr[1], lr[2], lr[3]);
                 // row sum of Z for token t over this tile's s (the four lane groups)
                 zs += __shfl_xor(zs, 16);
                 zs += __shfl_xor(zs, 32);
@@ -526,6 +533,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
                 for (int kk = 0; kk < 2; ++kk) {
                     if (2 * kk > tb) continue;  // every s of the block is after t
                     c2 = mfma(colop(B_l, NP, nb * 16, kk * 32), rowop(Lm_l, MP, tb * 16, kk * 32), c2);
+                    c2 = mfma(colop(B_l, NP, nb * 16, kk * 32), rowop(Lmr_l, MP, tb * 16, kk * 32), c2);
                 }
                 const bf16x4 cn = ld4(&C_l[t * NP + n0]);
                 float dc[4];
@@ -542,6 +550,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
                 for (int kk = 0; kk < 2; ++kk) {
                     if (2 * kk + 1 < tb) continue;  // every t of the block is before s
                     b1 = mfma(colop(C_l, NP, nb * 16, kk * 32), colop(Lm_l, MP, tb * 16, kk * 32), b1);
+                    b1 = mfma(colop(C_l, NP, nb * 16, kk * 32), colop(Lmr_l, MP, tb * 16, kk * 32), b1);
                 }
 #pragma unroll
                 for (int kk = 0; kk < P / 32; ++kk) {
