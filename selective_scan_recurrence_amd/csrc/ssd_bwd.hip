@@ -34,8 +34,10 @@
 // holds h^T).  G is staged in LDS as a bf16 value plus a bf16 remainder, so
 // that the products that read it keep about 16 significant bits of the
 // carried gradient, and so are the fp32 checkpoint of h_in (the decay
-// gradient multiplies its errors by A) and Lm (dB and dC sum it over the
-// group's heads, whose terms can cancel); with them the chunk's x, dy, B and C
+// gradient multiplies its errors by A), Lm (dB and dC sum it over the
+// group's heads, whose terms can cancel) and M (dX sums it over the chunk's
+// later tokens; its remainder takes Lm's remainder tile once dB and dC are
+// formed, so dX comes after them); with them the chunk's x, dy, B and C
 // rows, the next (earlier) chunk's rows being loaded meanwhile.  All products run on v_mfma_f32_16x16x32_bf16: operands
 // whose k index runs along a stored row come from 16-byte LDS row reads, the
 // others from the transposing read ds_read_b64_tr_b16 (as in the forward).
@@ -372,9 +374,13 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
 
         // (1) the causal 16x16 tiles of S^T = B C^T and R^T = X dY^T: M, Lm and
         // the sums of Z.  Tile k (row by row: (tb,sb) = (0,0),(1,0),(1,1),...)
-        // goes to wave k % 8.
+        // goes to wave k % 8.  M's remainder waits in registers until (3) is
+        // done with Lmr's tile, which then takes it for (2).
+        u32x2 mrem[2];
+        int mr_off[2];
+        const bool mr_two = wave + kWaves < 10;
         {
-            const bool two = wave + kWaves < 10;
+            const bool two = mr_two;
             int mtb[2], msb[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
@@ -414,10 +420,15 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
                 }
                 *reinterpret_cast<u32x2*>(&M_l[t * MP + msb[u] * 16 + 4 * g4]) = pack4(m[0], m[1], m[2], m[3]);
                 *reinterpret_cast<u32x2*>(&Lm_l[t * MP + msb[u] * 16 + 4 * g4]) = pack4(lm[0], lm[1], lm[2], lm[3]);
-                float lr[4];
+                float lr[4], mr[4];
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) lr[rr] = lm[rr] - to_f32(bf16_rne(lm[rr]));
+                for (int rr = 0; rr < 4; ++rr) {
+                    lr[rr] = lm[rr] - to_f32(bf16_rne(lm[rr]));
+                    mr[rr] = m[rr] - to_f32(bf16_rne(m[rr]));
+                }
                 *reinterpret_cast<u32x2*>(&Lmr_l[t * MP + msb[u] * 16 + 4 * g4]) = pack4(lr[0], lr[1], lr[2], lr[3]);
+                mrem[u] = pack4(mr[0], mr[1], mr[2], mr[3]);
+                mr_off[u] = t * MP + msb[u] * 16 + 4 * g4;
                 // row sum of Z for token t over this tile's s (the four lane groups)
                 zs += __shfl_xor(zs, 16);
                 zs += __shfl_xor(zs, 32);
@@ -455,45 +466,6 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
             gh_l[wave] = 0.0f;
         }
         __syncthreads();
-
-        // (2) dX^T [p][s] = dY^T M (t >= s) + w_s (G B^T) + D dY, for s-block
-        // wave % 4 and this wave's channel blocks
-        {
-            constexpr int YPW = PB / 2;
-            const int sb = wave & 3, pb0 = (wave >> 2) * YPW;
-            const int s = sb * 16 + l16;
-            const float ws = w_l[s];
-            const auto rdx = rsrc(dxg, t0, xrow4);
-#pragma unroll
-            for (int q = 0; q < YPW; ++q) {
-                const int pb = pb0 + q;
-                f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    if (2 * kk + 1 < sb) continue;  // every t of the block is before s
-                    a1 = mfma(colop(Y_l, XP, pb * 16, kk * 32), colop(M_l, MP, sb * 16, kk * 32), a1);
-                }
-#pragma unroll
-                for (int kk = 0; kk < N / 32; ++kk) {
-                    const bf16x8 bo = rowop(B_l, NP, sb * 16, kk * 32);
-                    a2 = mfma(rowop(G_l, NPH, pb * 16, kk * 32), bo, a2);
-                    a2 = mfma(rowop(Gr_l, NPH, pb * 16, kk * 32), bo, a2);
-                }
-                // lane: p = 16 pb + 4 g4 + rr, s
-                const bf16x4 yv = ld4(&Y_l[s * XP + pb * 16 + 4 * g4]);
-                const bf16x4 xv = ld4(&X_l[s * XP + pb * 16 + 4 * g4]);
-                float dx[4];
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    dx[rr] = fmaf(ws, a2[rr], fmaf(Dh, (float)yv[rr], a1[rr]));
-                    if (bad) dx[rr] = __builtin_nanf("");
-                    dD_acc = fmaf((float)yv[rr], (float)xv[rr], dD_acc);
-                }
-                __builtin_amdgcn_raw_buffer_store_b128(
-                    u32x4{__float_as_uint(dx[0]), __float_as_uint(dx[1]), __float_as_uint(dx[2]), __float_as_uint(dx[3])},
-                    rdx, (int)(s * xrow4) + (pb * 16 + 4 * g4) * 4, 0, 0);
-            }
-        }
 
         // (3) dC [t][n] = exp(cum_t) (dY h_in) + Lm B, and dB [s][n] = Lm^T C + w_s (X G),
         // for token block wave % 4 and this wave's half of the states; the
@@ -574,6 +546,52 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
             if (g4 == 0) {
                 yoff_l[half][t] = yo;
                 u_l[half][t] = uu;
+            }
+        }
+
+        // M's remainder into Lmr's tile, once every wave is done with Lm
+        __syncthreads();
+        *reinterpret_cast<u32x2*>(&Lmr_l[mr_off[0]]) = mrem[0];
+        if (mr_two) *reinterpret_cast<u32x2*>(&Lmr_l[mr_off[1]]) = mrem[1];
+        __syncthreads();
+
+        // (2) dX^T [p][s] = dY^T M (t >= s) + w_s (G B^T) + D dY, for s-block
+        // wave % 4 and this wave's channel blocks
+        {
+            constexpr int YPW = PB / 2;
+            const int sb = wave & 3, pb0 = (wave >> 2) * YPW;
+            const int s = sb * 16 + l16;
+            const float ws = w_l[s];
+            const auto rdx = rsrc(dxg, t0, xrow4);
+#pragma unroll
+            for (int q = 0; q < YPW; ++q) {
+                const int pb = pb0 + q;
+                f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    if (2 * kk + 1 < sb) continue;  // every t of the block is before s
+                    a1 = mfma(colop(Y_l, XP, pb * 16, kk * 32), colop(M_l, MP, sb * 16, kk * 32), a1);
+                    a1 = mfma(colop(Y_l, XP, pb * 16, kk * 32), colop(Lmr_l, MP, sb * 16, kk * 32), a1);
+                }
+#pragma unroll
+                for (int kk = 0; kk < N / 32; ++kk) {
+                    const bf16x8 bo = rowop(B_l, NP, sb * 16, kk * 32);
+                    a2 = mfma(rowop(G_l, NPH, pb * 16, kk * 32), bo, a2);
+                    a2 = mfma(rowop(Gr_l, NPH, pb * 16, kk * 32), bo, a2);
+                }
+                // lane: p = 16 pb + 4 g4 + rr, s
+                const bf16x4 yv = ld4(&Y_l[s * XP + pb * 16 + 4 * g4]);
+                const bf16x4 xv = ld4(&X_l[s * XP + pb * 16 + 4 * g4]);
+                float dx[4];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    dx[rr] = fmaf(ws, a2[rr], fmaf(Dh, (float)yv[rr], a1[rr]));
+                    if (bad) dx[rr] = __builtin_nanf("");
+                    dD_acc = fmaf((float)yv[rr], (float)xv[rr], dD_acc);
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    u32x4{__float_as_uint(dx[0]), __float_as_uint(dx[1]), __float_as_uint(dx[2]), __float_as_uint(dx[3])},
+                    rdx, (int)(s * xrow4) + (pb * 16 + 4 * g4) * 4, 0, 0);
             }
         }
 

@@ -3,20 +3,17 @@ B/C shared by the heads of a group; bf16 io), the chunked backward on MFMA,
 against the float64 oracle through the C ABI.
 
 Tolerance.  The products run with bf16 operands (x, dy, B, C as stored; the
-checkpointed state, the carried gradient and the Lm tile as a bf16 value plus
-a bf16 remainder, about 16 significant bits; the M tile rounded to bf16 once
-per chunk) and fp32 accumulation: a term rounded once carries a relative
-error of about 2^-8, and sums of many terms of either sign carry an absolute
-error that scales with their terms.  Every gradient is compared element by
-element with rtol 2e-2 and an absolute floor of 1e-2 x rms of the oracle's
-values for d_x (one channel's gradient, through M) and 2e-2 x rms for the
-sums: d_dt (over the head's channels and states, and through the decay over
-the chunk's later tokens), d_A, d_D, d_C, d_s (the bf16 tolerance the forward
-uses, with the floor of the sums).  d_B = Lm^T C + diag(w) X G takes only the
-16-bit operands and is held to rtol 1e-3 with a 1e-3 x rms floor: over these
-cases and 150 seeded random Mamba-2 shapes its worst element needs 5e-5.
-Over all 80 heads of the full-size workload the worst d_dt element uses
-about 0.7 of its bound and would exceed a 1e-2 floor slightly."""
+checkpointed state, the carried gradient and the M and Lm tiles as a bf16
+value plus a bf16 remainder, about 16 significant bits) and fp32
+accumulation.  d_x = M^T dY + diag(w) B G^T + D dY, d_B = Lm^T C + diag(w) X G
+and d_s take only such operands and are held to rtol 1e-3 with an absolute
+floor of 1e-3 x rms of the oracle's values: over these cases and 210 seeded
+random Mamba-2 shapes their worst elements need 5e-5 of (rms + |value|).
+d_C also reads the checkpoint, which the forward's recompute forms from
+single-bf16 products, and d_dt, d_A through the decay carry a term rounded
+once (about 2^-8 relative); they and d_D keep rtol 2e-2 with a 2e-2 x rms
+floor, the bf16 tolerance the forward uses with the floor of the sums (their
+worst elements need up to 6.9e-3)."""
 import numpy as np
 import pytest
 import torch
@@ -31,17 +28,18 @@ pytestmark = pytest.mark.gpu
 GRADS = ("d_x", "d_dt", "d_s", "d_A", "d_D", "d_B", "d_C")
 
 
-PER_ELEM = ("d_x",)
+TIGHT = ("d_x", "d_B", "d_s")  # gradients formed from 16-bit operands only
 
 
 def _floor(k):
-    return 1e-3 if k == "d_B" else 1e-2 if k in PER_ELEM else 2e-2
+    return 1e-3 if k in TIGHT else 2e-2
 
 
 def _check(name, got, want, rtol=None, floor=2e-2):
+    tight = name.split()[-1] in TIGHT
     if rtol is None:
-        rtol = 1e-3 if name.endswith("d_B") else 2e-2
-    if name.endswith("d_B"):
+        rtol = 1e-3 if tight else 2e-2
+    if tight:
         floor = min(floor, 1e-3)
     got = np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)
