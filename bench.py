@@ -160,7 +160,7 @@ MEASURED_TRAFFIC = {
     "C8": {"sha256": "4b94dd407f30cd46da969e6fa81a21f455fe7552909ad44e50035de3090e3268", "fetch_kib": 1350057.7, "write_kib": 2413218.4},
     "C9": {"sha256": "3c0e2ea0340a49be790cdacc592eb9c771e4a786aed94dd7657ca3a3703992e7", "fetch_kib": 506996.8, "write_kib": 330720.0},
     "C10": {"sha256": "2a46b022932ac6ec6fec633ef5221432a0374beec1c3222e02b0cf240b04e297", "fetch_kib": 1670588.0, "write_kib": 2966628.4},
-    "C11": {"sha256": "276c97c0ab38954d90eea36e94e56223be1d1cf15921334358e607baa728a14b", "fetch_kib": 164316.9, "write_kib": 327680.0},
+    "C11": {"sha256": "4953558e4e65ac64e2be02ba4b598fe802356a85f0e8fe0be0a7f4cac01e0dea", "fetch_kib": 164316.8, "write_kib": 327680.0},
 }
 KERNEL_SOURCES = {
     "C0": ("scan_fwd.hip", "scan_fwd_ts.hip", "scan_fwd_quad.hip", "relay.h", "relay.hip", "device_common.h"),

@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256) void conv_fwd_tile(const T* __restrict__ sx, c
             const u32x4 v = *reinterpret_cast<const u32x4*>(&ol[r * kOP + part * (16 / ES)]);
             const int t = t0 + r;
             const int off = (t < n_t && c < d_inner) ? (t * d_inner + c) * ES : INT_MIN;
-            __builtin_amdgcn_raw_buffer_store_b128(v, ro, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(v, ro, off, 0, 2);  // nontemporal: out is not read back here
         }
     }
 }
