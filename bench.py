@@ -157,7 +157,7 @@ MEASURED_TRAFFIC = {
     "C5": {"sha256": "19d21d3c16653649e1d9cac38de168171b782e33178b052b1b50c035b9a95dd5", "fetch_kib": 512932.3, "write_kib": 704850.3},
     "C6": {"sha256": "365057569e18c41ae6495048cfbeb33cacead190cc03a245029d5ac614a042b7", "fetch_kib": 52810.7, "write_kib": 99843.7},
     "C7": {"sha256": "365057569e18c41ae6495048cfbeb33cacead190cc03a245029d5ac614a042b7", "fetch_kib": 83410.5, "write_kib": 164502.2},
-    "C8": {"sha256": "4b94dd407f30cd46da969e6fa81a21f455fe7552909ad44e50035de3090e3268", "fetch_kib": 1350057.7, "write_kib": 2413218.4},
+    "C8": {"sha256": "d400dd9f758bb898e47e5e8f43f2fb3cf32c2dab8cc83229deafe8dfe4da3fc5", "fetch_kib": 1351315.0, "write_kib": 2411816.2},
     "C9": {"sha256": "3c0e2ea0340a49be790cdacc592eb9c771e4a786aed94dd7657ca3a3703992e7", "fetch_kib": 506996.8, "write_kib": 330720.0},
     "C10": {"sha256": "2a46b022932ac6ec6fec633ef5221432a0374beec1c3222e02b0cf240b04e297", "fetch_kib": 1670588.0, "write_kib": 2966628.4},
     "C11": {"sha256": "4953558e4e65ac64e2be02ba4b598fe802356a85f0e8fe0be0a7f4cac01e0dea", "fetch_kib": 164316.8, "write_kib": 327680.0},

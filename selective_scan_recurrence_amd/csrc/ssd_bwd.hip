@@ -549,6 +549,11 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
             }
         }
 
+        // the earlier chunk's loads: issued here, they fly through the
+        // remainder hand-over, (2) and (4); before (3) their registers would
+        // not fit beside its products
+        load_chunk(ch - 1);
+
         // M's remainder into Lmr's tile, once every wave is done with Lm
         __syncthreads();
         *reinterpret_cast<u32x2*>(&Lmr_l[mr_off[0]]) = mrem[0];
@@ -595,9 +600,6 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd(SsdBwdKP p) {
             }
         }
 
-        // the earlier chunk's loads, issued only here: held from the staging
-        // barrier on, their registers spilled through the products above
-        load_chunk(ch - 1);
 
         // (4) the carry: G^T [n][p] = exp(cum_last) G^T + C^T diag(exp(cum)) dY
         if (owns) {
